@@ -1,0 +1,244 @@
+"""Benchmark of the RecSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+build the tree over the L cached tokens, decode a batch at length L, append
+the prefill chunk (growing the tree) and run the causal prefill of that
+chunk.  Each call is timed with HIP events on the stream it is launched on.
+
+Prints one JSON line: value = decode queries/s; prefill tokens/s, tree-build
+bandwidth and the roofline fractions of every kernel ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def level_sizes(n, b):
+    out = [n]
+    while out[-1] // b >= 1:
+        out.append(out[-1] // b)
+    return out
+
+
+def row_entries(n_ctx, b, k):
+    """(keys scored, values read) of one row: candidate counts per level."""
+    N = level_sizes(n_ctx, b)
+    H = len(N) - 1
+    keys = vals = 0
+    c = N[H]
+    for l in range(H, -1, -1):
+        keys += c
+        if l == 0:
+            vals += c
+            break
+        m = min(k, c)
+        vals += c - m
+        c = b * m + (N[l - 1] - b * N[l])
+    return keys, vals
+
+
+def algorithmic(w, B):
+    """Bytes (and FLOPs) each call must move, from the tree geometry."""
+    esz = 2 if w.dtype == "bf16" else 4
+    row_b = w.d * esz
+    N = level_sizes(w.L, w.b)
+    build_bytes = 2 * w.n_kv * w.L * row_b + 2 * w.n_kv * sum(N[1:]) * row_b
+    kd, vd = row_entries(w.L, w.b, w.k)
+    decode_bytes = B * w.n_q * (kd + vd) * row_b
+    decode_flops = B * w.n_q * (kd + vd) * 2 * w.d
+    pk = pv = 0
+    for j in range(w.prefill_n):
+        a, c = row_entries(w.L + j + 1, w.b, w.k)
+        pk += a
+        pv += c
+    prefill_bytes = w.n_q * (pk + pv) * row_b
+    prefill_flops = w.n_q * (pk + pv) * 2 * w.d
+    Lt = w.L + w.prefill_n
+    Nt = level_sizes(Lt, w.b)
+    new_nodes = sum(Nt[l] - (N[l] if l < len(N) else 0) for l in range(1, len(Nt)))
+    append_bytes = 2 * 2 * w.n_kv * w.prefill_n * row_b + 2 * w.n_kv * new_nodes * row_b
+    return dict(build=build_bytes, decode=decode_bytes, decode_flops=decode_flops,
+                prefill=prefill_bytes, prefill_flops=prefill_flops, append=append_bytes,
+                decode_entries_per_row=kd + vd)
+
+
+def cpu_baseline(w, B, seconds=15.0):
+    """The oracle (never tuned) on the host: tree over one KV head, then decode
+    rows of that head until about `seconds` have passed."""
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import recsa as O
+    with threadpool_limits(1):
+        K, V = synth.gen_kv(w, 0, w.L, heads=[0])
+        W = synth.pool_w(w)[:1]
+        Q = synth.decode_queries(w, B)
+        t0 = time.perf_counter()
+        tree = O.build_tree(K, V, W, w.b, w.dtype, w.pool_scale, w.L)
+        t_build = time.perf_counter() - t0
+        rows = 0
+        t0 = time.perf_counter()
+        G = w.n_q // w.n_kv
+        while True:
+            i, h = divmod(rows, G)
+            O.descend(tree, Q[i % B, h].astype(np.float64), 0, w.L, w.k, w.rope_base,
+                      w.softmax_scale)
+            rows += 1
+            if time.perf_counter() - t0 > seconds or rows >= 4096:
+                break
+        t_dec = time.perf_counter() - t0
+    return {
+        "value": rows / t_dec / w.n_q, "unit": "decode queries/s", "cores": 1, "kind": "oracle",
+        "sample": f"{rows} decode rows (query x head) of KV head 0 at L={w.L}, single thread, "
+                  f"after building that head's tree in {t_build:.1f} s; queries/s = rows/s / {w.n_q}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_4b_524k")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by KV head "
+              f"without communication, so the one-GPU figure is the per-GPU rate", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_recsa_amd as R
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    B = args.batch or w.max_batch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    Lt = w.L + w.prefill_n
+    K, V = synth.gen_kv(w, 0, Lt)
+    W = synth.pool_w(w)
+    Qd = synth.decode_queries(w, B)
+    Qp = synth.prefill_queries(w) if w.prefill_n else None
+
+    def dev_store(x):
+        bits = synth.storage_bits(x, w.dtype)
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    p = R.make_params(w.n_kv, w.n_q, w.d, w.b, w.k, Lt, store=w.dtype, out="f32",
+                      rope_base=w.rope_base, softmax_scale=w.softmax_scale, pool_scale=w.pool_scale)
+    layer = R.RecsaLayer(p, dev)
+    for g in range(w.n_kv):
+        layer.k_cache[g, :w.L].copy_(dev_store(K[g, :w.L]))
+        layer.v_cache[g, :w.L].copy_(dev_store(V[g, :w.L]))
+    layer.pool_w.copy_(torch.from_numpy(W))
+    q_dec = dev_store(Qd)
+    if w.prefill_n:
+        k_new = dev_store(np.ascontiguousarray(K[:, w.L:].transpose(1, 0, 2)))
+        v_new = dev_store(np.ascontiguousarray(V[:, w.L:].transpose(1, 0, 2)))
+        q_pre = dev_store(Qp)
+        out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
+    out_dec = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
+    del K, V
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    ops = ["build", "decode"] + (["append", "prefill"] if w.prefill_n else [])
+    ev = {o: [] for o in ops}
+
+    def step(record):
+        marks = {}
+        def mark(name):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks[name] = e
+        mark("t0")
+        layer.build(w.L)
+        mark("build")
+        layer.decode(q_dec, out=out_dec)
+        mark("decode")
+        if w.prefill_n:
+            layer.append(k_new, v_new)
+            mark("append")
+            layer.prefill(q_pre, out=out_pre)
+            mark("prefill")
+        if record:
+            order = ["t0"] + ops
+            ev_pairs = [(order[i], order[i + 1]) for i in range(len(ops))]
+            for a_, b_ in ev_pairs:
+                ev[b_].append((marks[a_], marks[b_]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {o: float(np.mean([a.elapsed_time(b) for a, b in ev[o]])) for o in ops}
+
+    alg = algorithmic(w, B)
+    kern = {}
+    kern["tree_build"] = {"bound": "hbm", "bytes": alg["build"], "ms": ms["build"],
+                          "achieved": alg["build"] / ms["build"] / 1e6, "unit": "GB/s"}
+    kern["decode"] = {"bound": "hbm", "bytes": alg["decode"], "ms": ms["decode"],
+                      "achieved": alg["decode"] / ms["decode"] / 1e6, "unit": "GB/s"}
+    if w.prefill_n:
+        kern["prefill"] = {"bound": "hbm", "bytes": alg["prefill"], "flops": alg["prefill_flops"],
+                           "ms": ms["prefill"], "achieved": alg["prefill"] / ms["prefill"] / 1e6,
+                           "unit": "GB/s",
+                           "mfma_frac": alg["prefill_flops"] / ms["prefill"] / 1e9 / BF16_PEAK_TFLOPS}
+        kern["append"] = {"bound": "hbm", "bytes": alg["append"], "ms": ms["append"],
+                          "achieved": alg["append"] / ms["append"] / 1e6, "unit": "GB/s"}
+    for v in kern.values():
+        v["frac"] = v["achieved"] / HBM_PEAK_GBS
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": kern[dom]["achieved"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac"], "traffic": None}
+
+    step_ms = wall / args.steps * 1e3
+    res = {
+        "metric": "decode queries/s & prefill tokens/s at L=524K; % of HBM / bf16-MFMA roofline",
+        "value": B / (ms["decode"] / 1e3),
+        "unit": "decode queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 storage, f32 compute" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "L": w.L, "n_kv_heads": w.n_kv, "n_q_heads": w.n_q,
+                   "head_dim": w.d, "b": w.b, "k": w.k, "decode_batch": B,
+                   "prefill_chunk": w.prefill_n},
+        "prefill_tokens_per_s": (w.prefill_n / ((ms["append"] + ms["prefill"]) / 1e3)
+                                 if w.prefill_n else None),
+        "ms": ms,
+        "kernels": kern,
+        "roofline": roof,
+        "setup_s": t_setup,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, B, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * recsa.h -- C ABI of the RecSA hot path on one AMD Instinct MI355X (gfx950).
+ *
+ * RecSA ("Recursive Sparse Attention: Million-Token Length Extrapolation at
+ * Logarithmic Cost", arXiv 2611.07232, abstract) builds a tree over the KV
+ * cache in which every node summarizes its subtree with one key and one
+ * mean-pooled value (abstract, sentence on the tree).  The keys come from one
+ * pooler per layer shared by all levels (sentence on the pooler).  A query
+ * descends the tree, keeping at most k candidates per level; the summaries of
+ * the candidates it does not keep share one softmax with the exact tokens it
+ * reaches (sentence on selection), and every entry's RoPE position is its
+ * index among the candidates of its level (sentence on RoPE).
+ *
+ * Conventions shared by every call
+ *  - All tensors are caller-owned device memory.  The library allocates
+ *    nothing, frees nothing and keeps no pointer after a call returns; inputs
+ *    are borrowed for the stream-ordered duration of the work it enqueues.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work of a call is enqueued on it; no call synchronizes the device.
+ *  - Arguments are validated on the host before any HIP call.  A failure
+ *    returns a status other than RECSA_OK, enqueues nothing and leaves the
+ *    tree descriptor unchanged; recsa_last_error() then describes it.  Launch
+ *    failures return RECSA_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronization.  Nothing throws or aborts.
+ *  - Storage: K, V, Q and the tree's summaries are in `store_dtype` (fp32 or
+ *    bf16 bit patterns); all arithmetic is fp32.
+ *  - Tree shape: level l has N_l = floor(n / b^l) complete nodes over n
+ *    tokens (aligned blocks of b^l tokens); only complete nodes have
+ *    summaries.  Levels run 1..recsa_num_levels(params) for `capacity` tokens.
+ *  - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ */
+#ifndef RECSA_H
+#define RECSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define RECSA_API __attribute__((visibility("default")))
+#else
+#define RECSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RECSA_OK = 0,
+    RECSA_ERR_INVALID_ARG = 1,   /* a null/misaligned pointer, a size out of range, bad params */
+    RECSA_ERR_UNSUPPORTED = 2,   /* valid but not built for: head_dim, LDS limits */
+    RECSA_ERR_CAPACITY = 3,      /* length or append past `capacity` */
+    RECSA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} recsa_status;
+
+typedef enum { RECSA_FP32 = 0, RECSA_BF16 = 1 } recsa_dtype;
+
+typedef struct {
+    int32_t n_kv_heads;      /* >= 1 */
+    int32_t n_q_heads;       /* multiple of n_kv_heads */
+    int32_t head_dim;        /* 64 or 128 */
+    int32_t fanout_b;        /* tree fanout b >= 2 */
+    int32_t budget_k;        /* candidates kept per level, 1 <= k */
+    int32_t store_dtype;     /* recsa_dtype of K, V, Q and summaries */
+    int32_t out_dtype;       /* recsa_dtype of the attention output */
+    int32_t reserved;        /* must be 0 */
+    double  rope_base;       /* RoPE base (1e6 for the Qwen3 family); > 0 */
+    float   softmax_scale;   /* logit scale s, usually 1/sqrt(head_dim) */
+    float   pool_scale;      /* pooler logit scale, usually 1/sqrt(head_dim) */
+    int64_t capacity;        /* tokens the cache and tree can hold, >= 1 */
+} recsa_params;
+
+typedef struct {
+    void       *k_cache;     /* [n_kv_heads][capacity][head_dim] store_dtype, pre-RoPE keys */
+    void       *v_cache;     /* [n_kv_heads][capacity][head_dim] store_dtype */
+    void       *tree;        /* recsa_tree_bytes() bytes, 256-byte aligned; library-defined layout */
+    const float *pool_w;     /* [n_kv_heads][head_dim] fp32 pooler vectors */
+    int64_t     length;      /* tokens in the tree; written by build/append only */
+} recsa_tree_desc;
+
+typedef struct {             /* optional per-row outputs; NULL fields are skipped */
+    int32_t *selected;       /* [rows][n_levels][budget_k]: at [r][l-1][:] the node ids kept at
+                                level l, ascending, -1 padded (also for levels above the row's top) */
+    float   *kth_gap;        /* [rows][n_levels]: z_(m) - z_(m+1) of level l's sorted logits,
+                                m = min(k, candidates); NaN when no candidate is left out */
+    int32_t *n_keys;         /* [rows]: keys scored over all levels (= entries read + kept nodes) */
+} recsa_debug;
+
+/* Levels above the tokens that `capacity` tokens can fill: max{l : capacity / b^l >= 1}.
+ * Returns -1 on invalid params. */
+RECSA_API int32_t recsa_num_levels(const recsa_params *p);
+
+/* Bytes the `tree` buffer needs (summaries of every level, fp32 running means
+ * for bf16 storage, and the RoPE cos/sin table).  0 on invalid params. */
+RECSA_API size_t recsa_tree_bytes(const recsa_params *p);
+
+/* Byte offsets inside `tree` of level l's key and value arrays (each
+ * [n_kv_heads][nodes][head_dim] store_dtype) and that level's node capacity.
+ * Level 1..recsa_num_levels().  For inspection and tests. */
+RECSA_API recsa_status recsa_tree_layout(const recsa_params *p, int32_t level, size_t *key_offset,
+                               size_t *val_offset, int64_t *node_capacity);
+
+/* Largest number of candidates any level can hold for these params
+ * (min(capacity, k*b + b - 1)); RoPE positions run 0..this value. */
+RECSA_API int64_t recsa_max_candidates(const recsa_params *p);
+
+/* Workspace bytes recsa_decode/recsa_prefill need for `max_rows` rows (0 today:
+ * every per-row intermediate lives in LDS).  `ws` may be NULL when this is 0. */
+RECSA_API size_t recsa_workspace_bytes(const recsa_params *p, int64_t max_rows);
+
+/* Build the tree over the first `length` tokens already stored in
+ * k_cache/v_cache (tree, sentence on the tree; pooler, sentence on the pooler):
+ * every complete node at every level gets its pooled key
+ *   alpha_c = softmax_c(pool_scale * pool_w[g] . child_key_c),  key = sum_c alpha_c child_key_c
+ * (children are tokens at level 1 and the stored level l-1 keys above) and
+ * its value = mean of the subtree's token values.  Also fills the RoPE table.
+ * Sets desc->length = length.  0 <= length <= capacity. */
+RECSA_API recsa_status recsa_build_tree(const recsa_params *p, recsa_tree_desc *desc, int64_t length,
+                              void *stream);
+
+/* Append n_new tokens (k_new, v_new: [n_new][n_kv_heads][head_dim] store_dtype,
+ * token-major) after desc->length and summarize every node that became
+ * complete, lowest level first.  Existing nodes are not touched.
+ * desc->length += n_new.  The tree must have been built (any length). */
+RECSA_API recsa_status recsa_append(const recsa_params *p, recsa_tree_desc *desc, const void *k_new,
+                          const void *v_new, int64_t n_new, void *stream);
+
+/* Decode: `batch` queries q[batch][n_q_heads][head_dim] (store_dtype, pre-RoPE),
+ * each attending to all desc->length tokens (sentence on selection; sentence on RoPE):
+ * per level from the top, every candidate i is scored
+ *   z_i = softmax_scale * <rope(q, n), rope(key_i, i)>,  n = the level's candidate count,
+ * the min(k, n) best are kept (equal logits: lower candidate index), every
+ * other candidate becomes a softmax entry with its summary value, and the
+ * kept nodes' children followed by the level's orphan nodes (children of the
+ * partial parent) become the next level's candidates.  At level 0 every
+ * candidate token (the kept nodes' tokens, then the partial tail) is an entry
+ * with its exact value.  out[batch][n_q_heads][head_dim] (out_dtype) is the
+ * softmax over all entries.  RoPE is rotate-half: pair (i, i + head_dim/2)
+ * turns by pos * rope_base^(-2i/head_dim).  `dbg` may be NULL. */
+RECSA_API recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                          int32_t batch, void *out, const recsa_debug *dbg, void *ws,
+                          void *stream);
+
+/* Causal prefill of the last n_q tokens of the tree (append them first):
+ * q[n_q][n_q_heads][head_dim]; query j sits at token L0 + j, L0 = length - n_q,
+ * and attends to tokens [0, L0 + j] through the tree of that prefix (complete
+ * nodes only), with the same per-level rule as recsa_decode.
+ * out[n_q][n_q_heads][head_dim].  `dbg` may be NULL. */
+RECSA_API recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                           int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
+                           void *stream);
+
+/* Static name of a status code. */
+RECSA_API const char *recsa_status_string(recsa_status s);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+RECSA_API const char *recsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RECSA_H */

@@ -1,0 +1,332 @@
+// Host side of librecsa: argument validation, the tree buffer's layout, and
+// the launches of each ABI call on the caller's stream.  See include/recsa.h
+// for the contract of every entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "recsa_internal.hpp"
+
+namespace recsa {
+size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t D);
+int32_t descend_max_candidates();
+}  // namespace recsa
+
+namespace {
+
+using namespace recsa;
+
+thread_local char g_err[512] = "";
+
+recsa_status fail(recsa_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+recsa_status hip_fail(hipError_t e, const char *what) {
+    return fail(RECSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxCapacity = 0x7FFFFFFF;      // node ids and candidate indices are int32
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(int32_t dt) { return dt == RECSA_BF16 ? 2 : 4; }
+
+struct Layout {
+    int32_t n_levels = 0;
+    int64_t node_cap[kMaxLevels + 1] = {};
+    size_t key_off[kMaxLevels + 1] = {};
+    size_t val_off[kMaxLevels + 1] = {};
+    size_t mean_off[kMaxLevels + 1] = {};
+    bool has_mean[kMaxLevels + 1] = {};
+    size_t rope_off = 0;
+    int32_t rope_rows = 0;
+    int64_t max_cand = 0;
+    size_t total = 0;
+};
+
+recsa_status check_params(const recsa_params *p) {
+    if (p == nullptr) return fail(RECSA_ERR_INVALID_ARG, "params is NULL");
+    if (p->n_kv_heads < 1) return fail(RECSA_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+    if (p->n_q_heads < p->n_kv_heads || p->n_q_heads % p->n_kv_heads != 0)
+        return fail(RECSA_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(RECSA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+    if (p->fanout_b < 2) return fail(RECSA_ERR_INVALID_ARG, "fanout_b must be >= 2");
+    if (p->budget_k < 1) return fail(RECSA_ERR_INVALID_ARG, "budget_k must be >= 1");
+    if (p->store_dtype != RECSA_FP32 && p->store_dtype != RECSA_BF16)
+        return fail(RECSA_ERR_INVALID_ARG, "store_dtype must be RECSA_FP32 or RECSA_BF16");
+    if (p->out_dtype != RECSA_FP32 && p->out_dtype != RECSA_BF16)
+        return fail(RECSA_ERR_INVALID_ARG, "out_dtype must be RECSA_FP32 or RECSA_BF16");
+    if (p->reserved != 0) return fail(RECSA_ERR_INVALID_ARG, "reserved must be 0");
+    if (!(p->rope_base > 0.0) || !isfinite(p->rope_base))
+        return fail(RECSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+    if (!isfinite(p->softmax_scale) || !isfinite(p->pool_scale))
+        return fail(RECSA_ERR_INVALID_ARG, "scales must be finite");
+    if (p->capacity < 1 || p->capacity > kMaxCapacity)
+        return fail(RECSA_ERR_INVALID_ARG, "capacity must be in [1, 2^31 - 1]");
+    return RECSA_OK;
+}
+
+// Requires valid params.
+Layout make_layout(const recsa_params *p) {
+    Layout L;
+    const int64_t b = p->fanout_b, D = p->head_dim;
+    const size_t es = elem_bytes(p->store_dtype);
+    int64_t n = p->capacity / b;
+    while (n >= 1 && L.n_levels < kMaxLevels) {
+        ++L.n_levels;
+        L.node_cap[L.n_levels] = n;
+        n /= b;
+    }
+    size_t off = 0;
+    for (int l = 1; l <= L.n_levels; ++l) {
+        const size_t arr = (size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)D;
+        L.key_off[l] = off;
+        off = align_up(off + arr * es);
+        L.val_off[l] = off;
+        off = align_up(off + arr * es);
+        // fp32 running means feed the next level's values when storage rounds to bf16
+        L.has_mean[l] = (p->store_dtype == RECSA_BF16) && (l < L.n_levels);
+        if (L.has_mean[l]) {
+            L.mean_off[l] = off;
+            off = align_up(off + arr * sizeof(float));
+        }
+    }
+    const int64_t kb = (int64_t)p->budget_k * b + b - 1;
+    L.max_cand = kb < p->capacity ? kb : p->capacity;
+    L.rope_rows = (int32_t)(L.max_cand + 1);
+    L.rope_off = off;
+    off = align_up(off + (size_t)L.rope_rows * (size_t)(D / 2) * sizeof(float2));
+    L.total = off;
+    return L;
+}
+
+recsa_status check_limits(const recsa_params *p, const Layout &L) {
+    if (L.max_cand > descend_max_candidates())
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "a level can hold %lld candidates (min(capacity, k*b + b - 1)); at most %d "
+                    "are supported",
+                    (long long)L.max_cand, descend_max_candidates());
+    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->head_dim) > kMaxLds)
+        return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
+    return RECSA_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+recsa_status check_desc(const recsa_params *p, const recsa_tree_desc *d) {
+    if (d == nullptr) return fail(RECSA_ERR_INVALID_ARG, "tree descriptor is NULL");
+    if (d->k_cache == nullptr || d->v_cache == nullptr || d->tree == nullptr ||
+        d->pool_w == nullptr)
+        return fail(RECSA_ERR_INVALID_ARG, "k_cache, v_cache, tree and pool_w must be non-NULL");
+    if (!aligned(d->k_cache, 16) || !aligned(d->v_cache, 16) || !aligned(d->pool_w, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "k_cache, v_cache and pool_w must be 16-byte aligned");
+    if (!aligned(d->tree, kAlign)) return fail(RECSA_ERR_INVALID_ARG, "tree must be 256-byte aligned");
+    if (d->length < 0 || d->length > p->capacity)
+        return fail(RECSA_ERR_CAPACITY, "length %lld outside [0, capacity]", (long long)d->length);
+    return RECSA_OK;
+}
+
+TreeView make_view(const recsa_params *p, const recsa_tree_desc *d, const Layout &L) {
+    TreeView tv{};
+    char *base = static_cast<char *>(d->tree);
+    tv.k_cache = d->k_cache;
+    tv.v_cache = d->v_cache;
+    tv.cap = p->capacity;
+    tv.n_levels = L.n_levels;
+    for (int l = 1; l <= L.n_levels; ++l) {
+        tv.key[l] = base + L.key_off[l];
+        tv.val[l] = base + L.val_off[l];
+        tv.mean[l] = L.has_mean[l] ? reinterpret_cast<float *>(base + L.mean_off[l]) : nullptr;
+        tv.node_cap[l] = L.node_cap[l];
+    }
+    tv.rope = reinterpret_cast<const float2 *>(base + L.rope_off);
+    tv.rope_rows = L.rope_rows;
+    return tv;
+}
+
+// Summarize every node that is complete at new_len and was not at old_len.
+recsa_status grow_levels(const recsa_params *p, const recsa_tree_desc *d, const Layout &L,
+                         const TreeView &tv, int64_t old_len, int64_t new_len, hipStream_t s) {
+    int64_t pw = 1;
+    for (int l = 1; l <= L.n_levels; ++l) {
+        pw *= p->fanout_b;
+        const int64_t n0 = old_len / pw, n1 = new_len / pw;
+        if (n1 == 0) break;
+        if (n1 > n0) {
+            hipError_t e = launch_level(tv, (recsa_dtype)p->store_dtype, p->n_kv_heads,
+                                        p->head_dim, p->fanout_b, l, n0, n1, d->pool_w,
+                                        p->pool_scale, s);
+            if (e != hipSuccess) return hip_fail(e, "tree level launch");
+        }
+    }
+    return RECSA_OK;
+}
+
+recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const void *q,
+                         int64_t n_queries, int64_t ctx_base, int32_t ctx_step, void *out,
+                         const recsa_debug *dbg, hipStream_t s) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if ((st = check_desc(p, d)) != RECSA_OK) return st;
+    if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    const int64_t rows = n_queries * p->n_q_heads;
+    if (rows > 0x7FFFFFFF) return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    const TreeView tv = make_view(p, d, L);
+    DescendArgs a{};
+    a.q = q;
+    a.out = out;
+    a.rows = rows;
+    a.Hq = p->n_q_heads;
+    a.G = p->n_q_heads / p->n_kv_heads;
+    a.ctx_base = ctx_base;
+    a.ctx_step = ctx_step;
+    a.b = p->fanout_b;
+    a.k = p->budget_k;
+    a.max_cand = (int32_t)L.max_cand;
+    a.scale = p->softmax_scale;
+    a.out_bf16 = p->out_dtype == RECSA_BF16;
+    DebugView dv{};
+    if (dbg != nullptr) {
+        dv.selected = dbg->selected;
+        dv.kth_gap = dbg->kth_gap;
+        dv.n_keys = dbg->n_keys;
+    }
+    hipError_t e = launch_descend(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "descend launch");
+    return RECSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t recsa_num_levels(const recsa_params *p) {
+    if (check_params(p) != RECSA_OK) return -1;
+    return make_layout(p).n_levels;
+}
+
+size_t recsa_tree_bytes(const recsa_params *p) {
+    if (check_params(p) != RECSA_OK) return 0;
+    return make_layout(p).total;
+}
+
+int64_t recsa_max_candidates(const recsa_params *p) {
+    if (check_params(p) != RECSA_OK) return -1;
+    return make_layout(p).max_cand;
+}
+
+recsa_status recsa_tree_layout(const recsa_params *p, int32_t level, size_t *key_offset,
+                               size_t *val_offset, int64_t *node_capacity) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if (level < 1 || level > L.n_levels)
+        return fail(RECSA_ERR_INVALID_ARG, "level %d outside [1, %d]", level, L.n_levels);
+    if (key_offset) *key_offset = L.key_off[level];
+    if (val_offset) *val_offset = L.val_off[level];
+    if (node_capacity) *node_capacity = L.node_cap[level];
+    return RECSA_OK;
+}
+
+size_t recsa_workspace_bytes(const recsa_params *p, int64_t max_rows) {
+    (void)p;
+    (void)max_rows;
+    return 0;
+}
+
+recsa_status recsa_build_tree(const recsa_params *p, recsa_tree_desc *desc, int64_t length,
+                              void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if ((st = check_desc(p, desc)) != RECSA_OK) return st;
+    if (length < 0 || length > p->capacity)
+        return fail(RECSA_ERR_CAPACITY, "length %lld outside [0, capacity]", (long long)length);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const TreeView tv = make_view(p, desc, L);
+    hipError_t e = launch_rope_table(const_cast<float2 *>(tv.rope), L.rope_rows, p->head_dim,
+                                     p->rope_base, s);
+    if (e != hipSuccess) return hip_fail(e, "rope table launch");
+    if ((st = grow_levels(p, desc, L, tv, 0, length, s)) != RECSA_OK) return st;
+    desc->length = length;
+    return RECSA_OK;
+}
+
+recsa_status recsa_append(const recsa_params *p, recsa_tree_desc *desc, const void *k_new,
+                          const void *v_new, int64_t n_new, void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if ((st = check_desc(p, desc)) != RECSA_OK) return st;
+    if (n_new < 0) return fail(RECSA_ERR_INVALID_ARG, "n_new must be >= 0");
+    if (n_new > p->capacity - desc->length)
+        return fail(RECSA_ERR_CAPACITY, "append of %lld tokens past capacity (%lld of %lld used)",
+                    (long long)n_new, (long long)desc->length, (long long)p->capacity);
+    if (n_new == 0) return RECSA_OK;
+    if (k_new == nullptr || v_new == nullptr)
+        return fail(RECSA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const TreeView tv = make_view(p, desc, L);
+    hipError_t e = launch_scatter(tv, (recsa_dtype)p->store_dtype, p->n_kv_heads, p->head_dim,
+                                  k_new, v_new, desc->length, n_new, s);
+    if (e != hipSuccess) return hip_fail(e, "append scatter launch");
+    if ((st = grow_levels(p, desc, L, tv, desc->length, desc->length + n_new, s)) != RECSA_OK)
+        return st;
+    desc->length += n_new;
+    return RECSA_OK;
+}
+
+recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                          int32_t batch, void *out, const recsa_debug *dbg, void *ws,
+                          void *stream) {
+    (void)ws;
+    if (batch < 1) return fail(RECSA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (desc != nullptr && desc->length < 1)
+        return fail(RECSA_ERR_INVALID_ARG, "decode needs at least one cached token");
+    return run_descend(p, desc, q, batch, desc ? desc->length : 0, 0, out, dbg,
+                       static_cast<hipStream_t>(stream));
+}
+
+recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                           int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
+                           void *stream) {
+    (void)ws;
+    if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
+    if (desc != nullptr && n_q > desc->length)
+        return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld); append first",
+                    (long long)n_q, (long long)desc->length);
+    return run_descend(p, desc, q, n_q, desc ? desc->length - n_q + 1 : 0, 1, out, dbg,
+                       static_cast<hipStream_t>(stream));
+}
+
+const char *recsa_status_string(recsa_status s) {
+    switch (s) {
+        case RECSA_OK: return "RECSA_OK";
+        case RECSA_ERR_INVALID_ARG: return "RECSA_ERR_INVALID_ARG";
+        case RECSA_ERR_UNSUPPORTED: return "RECSA_ERR_UNSUPPORTED";
+        case RECSA_ERR_CAPACITY: return "RECSA_ERR_CAPACITY";
+        case RECSA_ERR_HIP: return "RECSA_ERR_HIP";
+    }
+    return "RECSA_UNKNOWN_STATUS";
+}
+
+const char *recsa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Internal definitions shared by the RecSA host library and its gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "recsa.h"
+
+namespace recsa {
+
+constexpr int kMaxLevels = 32;     // b >= 2 and capacity < 2^31 give at most 31 levels
+
+using bf16_t = uint16_t;           // bf16 bit pattern
+
+// Everything a kernel needs to find the cache, the tree and the RoPE table.
+struct TreeView {
+    const void *k_cache;
+    const void *v_cache;
+    int64_t cap;                        // token capacity (row stride of a head)
+    void *key[kMaxLevels + 1];          // key[l]: [Hkv][node_cap[l]][D] store type (l >= 1)
+    void *val[kMaxLevels + 1];          // val[l]: same, subtree means in store type
+    float *mean[kMaxLevels + 1];        // fp32 subtree means (bf16 storage only; else null)
+    int64_t node_cap[kMaxLevels + 1];
+    const float2 *rope;                 // [rope_rows][D/2] (cos, sin) of pos * theta_j
+    int32_t rope_rows;
+    int32_t n_levels;
+};
+
+struct DebugView {
+    int32_t *selected;   // [rows][n_levels][k]
+    float *kth_gap;      // [rows][n_levels]
+    int32_t *n_keys;     // [rows]
+};
+
+// ---- storage conversions ---------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);            // round to nearest, ties to even (finite inputs)
+    return u >> 16;
+}
+
+// Load N consecutive elements of type T starting at p (N*sizeof(T) in {4, 8, 16, 32}
+// bytes, naturally aligned) and widen them to fp32.
+template <typename T, int N> struct Vec;
+
+template <int N> struct Vec<float, N> {
+    __device__ __forceinline__ static void load(const float *p, float *out) {
+        if constexpr (N == 1) {
+            out[0] = p[0];
+        } else if constexpr (N == 2) {
+            float2 v = *reinterpret_cast<const float2 *>(p);
+            out[0] = v.x; out[1] = v.y;
+        } else {
+            #pragma unroll
+            for (int i = 0; i < N; i += 4) {
+                float4 v = *reinterpret_cast<const float4 *>(p + i);
+                out[i] = v.x; out[i + 1] = v.y; out[i + 2] = v.z; out[i + 3] = v.w;
+            }
+        }
+    }
+    __device__ __forceinline__ static void store(float *p, const float *in) {
+        if constexpr (N == 1) {
+            p[0] = in[0];
+        } else if constexpr (N == 2) {
+            *reinterpret_cast<float2 *>(p) = make_float2(in[0], in[1]);
+        } else {
+            #pragma unroll
+            for (int i = 0; i < N; i += 4)
+                *reinterpret_cast<float4 *>(p + i) = make_float4(in[i], in[i + 1], in[i + 2], in[i + 3]);
+        }
+    }
+};
+
+template <int N> struct Vec<bf16_t, N> {
+    __device__ __forceinline__ static void load(const bf16_t *p, float *out) {
+        if constexpr (N == 2) {
+            uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+            out[0] = bf16_to_f32(v & 0xFFFFu); out[1] = bf16_to_f32(v >> 16);
+        } else if constexpr (N == 4) {
+            uint2 v = *reinterpret_cast<const uint2 *>(p);
+            out[0] = bf16_to_f32(v.x & 0xFFFFu); out[1] = bf16_to_f32(v.x >> 16);
+            out[2] = bf16_to_f32(v.y & 0xFFFFu); out[3] = bf16_to_f32(v.y >> 16);
+        } else {
+            static_assert(N % 8 == 0, "bf16 vector width");
+            #pragma unroll
+            for (int i = 0; i < N; i += 8) {
+                uint4 v = *reinterpret_cast<const uint4 *>(p + i);
+                out[i + 0] = bf16_to_f32(v.x & 0xFFFFu); out[i + 1] = bf16_to_f32(v.x >> 16);
+                out[i + 2] = bf16_to_f32(v.y & 0xFFFFu); out[i + 3] = bf16_to_f32(v.y >> 16);
+                out[i + 4] = bf16_to_f32(v.z & 0xFFFFu); out[i + 5] = bf16_to_f32(v.z >> 16);
+                out[i + 6] = bf16_to_f32(v.w & 0xFFFFu); out[i + 7] = bf16_to_f32(v.w >> 16);
+            }
+        }
+    }
+    __device__ __forceinline__ static void store(bf16_t *p, const float *in) {
+        if constexpr (N == 2) {
+            *reinterpret_cast<uint32_t *>(p) = f32_to_bf16(in[0]) | (f32_to_bf16(in[1]) << 16);
+        } else if constexpr (N == 4) {
+            *reinterpret_cast<uint2 *>(p) = make_uint2(f32_to_bf16(in[0]) | (f32_to_bf16(in[1]) << 16),
+                                                       f32_to_bf16(in[2]) | (f32_to_bf16(in[3]) << 16));
+        } else {
+            static_assert(N % 8 == 0, "bf16 vector width");
+            #pragma unroll
+            for (int i = 0; i < N; i += 8)
+                *reinterpret_cast<uint4 *>(p + i) =
+                    make_uint4(f32_to_bf16(in[i + 0]) | (f32_to_bf16(in[i + 1]) << 16),
+                               f32_to_bf16(in[i + 2]) | (f32_to_bf16(in[i + 3]) << 16),
+                               f32_to_bf16(in[i + 4]) | (f32_to_bf16(in[i + 5]) << 16),
+                               f32_to_bf16(in[i + 6]) | (f32_to_bf16(in[i + 7]) << 16));
+        }
+    }
+};
+
+// ---- launchers (defined in the kernel translation units) --------------------
+hipError_t launch_rope_table(float2 *table, int32_t rows, int32_t D, double base, hipStream_t s);
+
+hipError_t launch_scatter(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D,
+                          const void *k_new, const void *v_new, int64_t at, int64_t n,
+                          hipStream_t s);
+
+// Summarize level-`level` nodes [n0, n1) of every KV head from level level-1.
+hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D, int32_t b,
+                        int32_t level, int64_t n0, int64_t n1, const float *pool_w,
+                        float pool_scale, hipStream_t s);
+
+struct DescendArgs {
+    const void *q;             // [rows / Hq][Hq][D]
+    void *out;                 // same shape, out dtype
+    int64_t rows;              // queries * Hq
+    int32_t Hq, G;             // query heads, query heads per KV head
+    int64_t ctx_base;          // n_ctx of query 0
+    int32_t ctx_step;          // n_ctx of query i = ctx_base + i * ctx_step
+    int32_t b, k;
+    int32_t max_cand;          // largest candidate count of any level
+    float scale;
+    int32_t out_bf16;
+};
+
+hipError_t launch_descend(const TreeView &tv, recsa_dtype st, int32_t D, const DescendArgs &a,
+                          const DebugView &dbg, hipStream_t s);
+
+}  // namespace recsa

@@ -1,0 +1,220 @@
+// Tree build and append kernels for gfx950.
+//
+// RecSA, abstract: every node of the tree over the KV cache summarizes its
+// subtree with one key and one mean-pooled value; the keys come from one
+// pooler per layer shared by all levels.  The pooler here is attention
+// pooling with a per-KV-head vector w: alpha_c = softmax_c(pool_scale * w .
+// child_c), key = sum_c alpha_c child_c.
+//
+// Level 1 is the one full scan of K and V (HBM-bound).  A wave owns one node:
+// its b child rows are read with 16-byte loads, 16 lanes per row and four
+// rows per wave instruction, so every 64-byte segment is consumed whole.  The
+// pooler logits are reduced across the 16 lanes of a row, and softmax and the
+// weighted sum run online over the rows a lane group owns; the four lane
+// groups are merged with cross-lane shuffles.  Upper levels run the same
+// kernel over the stored child keys and the fp32 child means.
+#include <math.h>
+
+#include "recsa_internal.hpp"
+
+namespace recsa {
+namespace {
+
+constexpr int kNodesPerBlock = 4;     // one wave per node
+constexpr int kRowsInFlight = 4;      // child rows per lane group loaded before use
+
+template <typename TK, typename TVC, typename TS, int D>
+__global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
+    const TK *__restrict__ child_key, int64_t child_key_stride,
+    const TVC *__restrict__ child_val, int64_t child_val_stride,
+    TS *__restrict__ out_key, TS *__restrict__ out_val, float *__restrict__ out_mean,
+    int64_t out_stride, const float *__restrict__ pool_w, float pool_scale, int b,
+    int64_t n0, int64_t n1) {
+    constexpr int E = D / 16;                       // elements of a row per lane
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, sub = lane & 15;
+    const int g = blockIdx.y;
+    const int64_t node = n0 + (int64_t)blockIdx.x * kNodesPerBlock + wave;
+    if (node >= n1) return;                          // whole wave leaves; no block barrier used
+
+    const TK *ck = child_key + (int64_t)g * child_key_stride + node * b * D + sub * E;
+    const TVC *cv = child_val + (int64_t)g * child_val_stride + node * b * D + sub * E;
+    float w[E];
+    Vec<float, E>::load(pool_w + (int64_t)g * D + sub * E, w);
+
+    float m = -INFINITY, l = 0.f, acc[E], vacc[E];
+    #pragma unroll
+    for (int e = 0; e < E; ++e) { acc[e] = 0.f; vacc[e] = 0.f; }
+
+    for (int r0 = grp; r0 < b; r0 += 4 * kRowsInFlight) {
+        float kf[kRowsInFlight][E], vf[kRowsInFlight][E];
+        #pragma unroll
+        for (int t = 0; t < kRowsInFlight; ++t) {
+            const int r = r0 + 4 * t;
+            if (r < b) {
+                Vec<TK, E>::load(ck + (int64_t)r * D, kf[t]);
+                Vec<TVC, E>::load(cv + (int64_t)r * D, vf[t]);
+            }
+        }
+        #pragma unroll
+        for (int t = 0; t < kRowsInFlight; ++t) {
+            const int r = r0 + 4 * t;
+            if (r < b) {                                         // uniform within a lane group
+                float s = 0.f;
+                #pragma unroll
+                for (int e = 0; e < E; ++e) s += w[e] * kf[t][e];
+                s += __shfl_xor(s, 8, 16);
+                s += __shfl_xor(s, 4, 16);
+                s += __shfl_xor(s, 2, 16);
+                s += __shfl_xor(s, 1, 16);
+                s *= pool_scale;
+                const float mn = fmaxf(m, s);
+                const float c = expf(m - mn);                    // m = -inf on the first row: 0
+                const float p = expf(s - mn);
+                l = l * c + p;
+                #pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    acc[e] = acc[e] * c + p * kf[t][e];
+                    vacc[e] += vf[t][e];
+                }
+                m = mn;
+            }
+        }
+    }
+    // merge the four lane groups (rows grp, grp+4, ...)
+    #pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        const float mo = __shfl_xor(m, off);
+        const float lo = __shfl_xor(l, off);
+        const float mn = fmaxf(m, mo);
+        const float ca = (m == -INFINITY) ? 0.f : expf(m - mn);
+        const float cb = (mo == -INFINITY) ? 0.f : expf(mo - mn);
+        l = l * ca + lo * cb;
+        #pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float ao = __shfl_xor(acc[e], off);
+            acc[e] = acc[e] * ca + ao * cb;
+            vacc[e] += __shfl_xor(vacc[e], off);
+        }
+        m = mn;
+    }
+    if (grp == 0) {
+        float key[E], mean[E];
+        #pragma unroll
+        for (int e = 0; e < E; ++e) {
+            key[e] = acc[e] / l;
+            mean[e] = vacc[e] / (float)b;
+        }
+        const int64_t o = (int64_t)g * out_stride + node * D + sub * E;
+        Vec<TS, E>::store(out_key + o, key);
+        Vec<TS, E>::store(out_val + o, mean);
+        if (out_mean != nullptr) Vec<float, E>::store(out_mean + o, mean);
+    }
+}
+
+template <typename TK, typename TVC, typename TS, int D>
+hipError_t launch_level_t(const TK *ck, int64_t cks, const TVC *cv, int64_t cvs, TS *ok, TS *ov,
+                          float *om, int64_t os, int32_t Hkv, int32_t b, int64_t n0, int64_t n1,
+                          const float *pool_w, float pool_scale, hipStream_t s) {
+    const int64_t nodes = n1 - n0;
+    dim3 grid((unsigned)((nodes + kNodesPerBlock - 1) / kNodesPerBlock), (unsigned)Hkv);
+    hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
+                       cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_level_d(const TreeView &tv, int32_t Hkv, int32_t b, int32_t level, int64_t n0,
+                          int64_t n1, const float *pool_w, float pool_scale, hipStream_t s) {
+    T *ok = static_cast<T *>(tv.key[level]);
+    T *ov = static_cast<T *>(tv.val[level]);
+    float *om = tv.mean[level];
+    const int64_t os = tv.node_cap[level] * D;
+    if (level == 1) {
+        return launch_level_t<T, T, T, D>(static_cast<const T *>(tv.k_cache), tv.cap * D,
+                                          static_cast<const T *>(tv.v_cache), tv.cap * D, ok, ov,
+                                          om, os, Hkv, b, n0, n1, pool_w, pool_scale, s);
+    }
+    const T *ck = static_cast<const T *>(tv.key[level - 1]);
+    const int64_t cs = tv.node_cap[level - 1] * D;
+    if (tv.mean[level - 1] != nullptr)                   // bf16 storage: fp32 child means
+        return launch_level_t<T, float, T, D>(ck, cs, tv.mean[level - 1], cs, ok, ov, om, os, Hkv,
+                                              b, n0, n1, pool_w, pool_scale, s);
+    return launch_level_t<T, T, T, D>(ck, cs, static_cast<const T *>(tv.val[level - 1]), cs, ok,
+                                      ov, om, os, Hkv, b, n0, n1, pool_w, pool_scale, s);
+}
+
+// ---- scatter of token-major new rows into the head-major cache -------------
+__global__ __launch_bounds__(256) void scatter_kernel(const uint4 *__restrict__ src,
+                                                      uint4 *__restrict__ dst, int64_t n,
+                                                      int32_t Hkv, int32_t row16, int64_t cap16,
+                                                      int64_t at16) {
+    // src: [n][Hkv][row16] 16-byte chunks; dst: [Hkv][cap][row16]
+    const int64_t total = n * Hkv * row16;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = i % row16;
+        const int64_t rest = i / row16;
+        const int64_t g = rest % Hkv;
+        const int64_t t = rest / Hkv;
+        dst[g * cap16 + at16 + t * row16 + c] = src[i];
+    }
+}
+
+// ---- RoPE table: (cos, sin) of pos * base^(-2j/D), computed in double --------
+__global__ __launch_bounds__(256) void rope_table_kernel(float2 *__restrict__ table, int32_t rows,
+                                                         int32_t D, double base) {
+    const int h = D / 2;
+    const int64_t total = (int64_t)rows * h;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t pos = i / h;
+        const int j = (int)(i % h);
+        const double theta = pow(base, -2.0 * (double)j / (double)D);
+        const double a = (double)pos * theta;
+        table[i] = make_float2((float)cos(a), (float)sin(a));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D, int32_t b,
+                        int32_t level, int64_t n0, int64_t n1, const float *pool_w,
+                        float pool_scale, hipStream_t s) {
+    if (n1 <= n0) return hipSuccess;
+    if (st == RECSA_BF16) {
+        if (D == 128) return launch_level_d<bf16_t, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+        return launch_level_d<bf16_t, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+    }
+    if (D == 128) return launch_level_d<float, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+    return launch_level_d<float, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+}
+
+hipError_t launch_scatter(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D,
+                          const void *k_new, const void *v_new, int64_t at, int64_t n,
+                          hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int32_t row16 = D * (st == RECSA_BF16 ? 2 : 4) / 16;
+    const int64_t total = n * Hkv * row16;
+    const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+    const int64_t cap16 = tv.cap * row16, at16 = at * row16;
+    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint4 *>(k_new), (uint4 *)tv.k_cache, n, Hkv, row16,
+                       cap16, at16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint4 *>(v_new), (uint4 *)tv.v_cache, n, Hkv, row16,
+                       cap16, at16);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2 *table, int32_t rows, int32_t D, double base, hipStream_t s) {
+    const int64_t total = (int64_t)rows * (D / 2);
+    const unsigned blocks = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, table, rows, D, base);
+    return hipGetLastError();
+}
+
+}  // namespace recsa

@@ -1,0 +1,106 @@
+"""Owner of one attention layer's RecSA state in device memory (torch tensors)
+and thin wrappers of the C calls.  Marshalling only: no arithmetic here."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import (RECSA_BF16, recsa_append, recsa_build_tree, recsa_debug, recsa_decode,
+               recsa_max_candidates, recsa_num_levels, recsa_params, recsa_prefill,
+               recsa_tree_bytes, recsa_tree_desc, recsa_tree_layout)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class RecsaLayer:
+    """K/V cache, tree buffer and pooler vectors of one layer on one GPU."""
+
+    def __init__(self, params: recsa_params, device: str | torch.device = "cuda"):
+        self.p = params
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.store = torch.bfloat16 if params.store_dtype == RECSA_BF16 else torch.float32
+        self.out_dtype = torch.bfloat16 if params.out_dtype == RECSA_BF16 else torch.float32
+        Hkv, D, cap = params.n_kv_heads, params.head_dim, params.capacity
+        nbytes = recsa_tree_bytes(params)
+        if nbytes == 0:
+            raise ValueError("invalid recsa_params")
+        self.k_cache = torch.zeros((Hkv, cap, D), dtype=self.store, device=self.device)
+        self.v_cache = torch.zeros((Hkv, cap, D), dtype=self.store, device=self.device)
+        self.tree = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        self.pool_w = torch.zeros((Hkv, D), dtype=torch.float32, device=self.device)
+        self.n_levels = recsa_num_levels(params)
+        self.max_candidates = recsa_max_candidates(params)
+        self.desc = recsa_tree_desc(self.k_cache.data_ptr(), self.v_cache.data_ptr(),
+                                    self.tree.data_ptr(), self.pool_w.data_ptr(), 0)
+
+    @property
+    def length(self) -> int:
+        return int(self.desc.length)
+
+    @staticmethod
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def _check_dev(self, t: torch.Tensor, shape, dtype):
+        if t.device != self.device or not t.is_contiguous() or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"expected contiguous {dtype} {tuple(shape)} on {self.device}, got "
+                             f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+    # ---- calls ----------------------------------------------------------------
+    def build(self, length: int) -> None:
+        recsa_build_tree(self.p, self.desc, length, self.stream())
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        n = k_new.shape[0]
+        shape = (n, self.p.n_kv_heads, self.p.head_dim)
+        self._check_dev(k_new, shape, self.store)
+        self._check_dev(v_new, shape, self.store)
+        recsa_append(self.p, self.desc, _ptr(k_new), _ptr(v_new), n, self.stream())
+
+    def _debug(self, rows: int, debug: bool):
+        if not debug:
+            return None, None
+        d = {
+            "selected": torch.full((rows, self.n_levels, self.p.budget_k), -7, dtype=torch.int32,
+                                   device=self.device),
+            "kth_gap": torch.zeros((rows, self.n_levels), dtype=torch.float32, device=self.device),
+            "n_keys": torch.zeros((rows,), dtype=torch.int32, device=self.device),
+        }
+        return d, recsa_debug(d["selected"].data_ptr(), d["kth_gap"].data_ptr(),
+                              d["n_keys"].data_ptr())
+
+    def decode(self, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+        B = q.shape[0]
+        shape = (B, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        if out is None:
+            out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
+        d, dbg = self._debug(B * self.p.n_q_heads, debug)
+        recsa_decode(self.p, self.desc, _ptr(q), B, _ptr(out), dbg, None, self.stream())
+        return (out, d) if debug else out
+
+    def prefill(self, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+        n = q.shape[0]
+        shape = (n, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        if out is None:
+            out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
+        d, dbg = self._debug(n * self.p.n_q_heads, debug)
+        recsa_prefill(self.p, self.desc, _ptr(q), n, _ptr(out), dbg, None, self.stream())
+        return (out, d) if debug else out
+
+    # ---- inspection -------------------------------------------------------------
+    def level(self, l: int):
+        """(keys, values) of level l as views [n_kv][node_capacity][head_dim] of the tree."""
+        ko, vo, nc = recsa_tree_layout(self.p, l)
+        esz = 2 if self.store == torch.bfloat16 else 4
+        n = self.p.n_kv_heads * nc * self.p.head_dim
+        shape = (self.p.n_kv_heads, nc, self.p.head_dim)
+        keys = self.tree[ko:ko + n * esz].view(self.store).view(shape)
+        vals = self.tree[vo:vo + n * esz].view(self.store).view(shape)
+        return keys, vals

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every symbol include/recsa.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  -- load torch's HIP runtime first, as the binding does
+
+import long_context_recsa_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "recsa.h")).read()
+    return re.findall(r"RECSA_API\s+[\w\s\*]+?\b(recsa_\w+)\s*\(", txt)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.load_library()
+    names = _declared()
+    assert len(names) == len(R.EXPORTED) and set(names) == set(R.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_mapped():
+    R.load_library()
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+
+
+def _p(**kw):
+    base = dict(n_kv_heads=8, n_q_heads=32, head_dim=128, fanout_b=32, budget_k=8,
+                capacity=524288 + 4096)
+    base.update(kw)
+    return R.make_params(**base)
+
+
+def test_geometry_queries():
+    p = _p()
+    assert R.recsa_num_levels(p) == 3          # 528384 / 32^3 = 16
+    assert R.recsa_max_candidates(p) == 8 * 32 + 31
+    ko, vo, nc = R.recsa_tree_layout(p, 1)
+    assert nc == 528384 // 32 and ko % 256 == 0 and vo % 256 == 0 and vo > ko
+    assert R.recsa_tree_layout(p, 3)[2] == 16
+    nbytes = R.recsa_tree_bytes(p)
+    assert nbytes % 256 == 0
+    # summaries of 3 levels (bf16 keys + values, fp32 means below the top) + RoPE table
+    n1, n2, n3 = 16512, 516, 16
+    want = 8 * 128 * (4 * (n1 + n2 + n3) + 4 * (n1 + n2)) + 288 * 64 * 8
+    assert want <= nbytes <= want + 256 * 12
+    assert R.recsa_workspace_bytes(p, 1000) == 0
+    with pytest.raises(R.RecsaError):
+        R.recsa_tree_layout(p, 4)
+    assert R.recsa_num_levels(_p(capacity=31)) == 0
+    assert R.recsa_num_levels(_p(fanout_b=2, capacity=1 << 20)) == 20
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_kv_heads=0), dict(n_q_heads=12), dict(head_dim=96), dict(fanout_b=1),
+    dict(budget_k=0), dict(capacity=0), dict(capacity=1 << 31), dict(rope_base=-1.0),
+])
+def test_invalid_params_rejected(kw):
+    p = _p(**kw)
+    assert R.recsa_tree_bytes(p) == 0
+    assert R.recsa_num_levels(p) == -1
+
+
+def test_unsupported_candidate_count():
+    p = _p(budget_k=200)        # 200*32 + 31 candidates per level > 4096
+    d = R.recsa_tree_desc(256, 256, 256, 256, 0)
+    with pytest.raises(R.RecsaError) as e:
+        R.recsa_build_tree(p, d, 0)
+    assert e.value.status == R.RECSA_ERR_UNSUPPORTED
+
+
+def test_calls_validate_before_any_hip_call():
+    p = _p(capacity=1000)
+    fake = 1 << 20          # never dereferenced: every case below fails validation
+    d = R.recsa_tree_desc(fake, fake, fake, fake, 0)
+    cases = [
+        (lambda: R.recsa_build_tree(p, R.recsa_tree_desc(None, fake, fake, fake, 0), 0), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_build_tree(p, R.recsa_tree_desc(fake + 8, fake, fake, fake, 0), 0), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_build_tree(p, R.recsa_tree_desc(fake, fake, fake + 16, fake, 0), 0), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_build_tree(p, d, 1001), R.RECSA_ERR_CAPACITY),
+        (lambda: R.recsa_build_tree(p, d, -1), R.RECSA_ERR_CAPACITY),
+        (lambda: R.recsa_append(p, R.recsa_tree_desc(fake, fake, fake, fake, 990), fake, fake, 11), R.RECSA_ERR_CAPACITY),
+        (lambda: R.recsa_append(p, d, None, fake, 5), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_append(p, d, fake, fake, -1), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode(p, d, fake, 1, fake), R.RECSA_ERR_INVALID_ARG),      # empty tree
+        (lambda: R.recsa_decode(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake, 0, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), None, 1, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake + 4, 1, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_prefill(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake, 11, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_prefill(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake, 0, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode(_p(n_q_heads=12), d, fake, 1, fake), R.RECSA_ERR_INVALID_ARG),
+    ]
+    for i, (fn, status) in enumerate(cases):
+        with pytest.raises(R.RecsaError) as e:
+            fn()
+        assert e.value.status == status, (i, str(e.value))
+        assert str(e.value)
+    # a rejected call leaves the descriptor unchanged
+    d2 = R.recsa_tree_desc(fake, fake, fake, fake, 990)
+    with pytest.raises(R.RecsaError):
+        R.recsa_append(p, d2, fake, fake, 11)
+    assert d2.length == 990
+
+
+def test_status_strings():
+    lib = R.load_library()
+    for s in range(5):
+        assert lib.recsa_status_string(s).decode().startswith("RECSA_")
+
+
+def test_params_struct_layout():
+    # offsets must match the C struct: 8 int32, double, 2 floats, int64
+    assert ctypes.sizeof(R.recsa_params) == 56
+    assert R.recsa_params.rope_base.offset == 32
+    assert R.recsa_params.capacity.offset == 48
+    assert ctypes.sizeof(R.recsa_tree_desc) == 40
