@@ -9,7 +9,7 @@
 #include "recsa_internal.hpp"
 
 namespace recsa {
-size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t D);
+size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D);
 int32_t descend_max_candidates();
 }  // namespace recsa
 
@@ -102,7 +102,11 @@ Layout make_layout(const recsa_params *p) {
     }
     const int64_t kb = (int64_t)p->budget_k * b + b - 1;
     L.max_cand = kb < p->capacity ? kb : p->capacity;
-    L.rope_rows = (int32_t)(L.max_cand + 1);
+    // positions 0..max_cand, and at least 0..max(64, b): the descent also reads the
+    // rotation of every child offset c < b
+    int64_t rows = L.max_cand > 64 ? L.max_cand : 64;
+    if (rows < b) rows = b;
+    L.rope_rows = (int32_t)(rows + 1);
     L.rope_off = off;
     off = align_up(off + (size_t)L.rope_rows * (size_t)(D / 2) * sizeof(float2));
     L.total = off;
@@ -110,12 +114,16 @@ Layout make_layout(const recsa_params *p) {
 }
 
 recsa_status check_limits(const recsa_params *p, const Layout &L) {
+    // the descent addresses one KV head's rows with 32-bit byte offsets
+    if ((uint64_t)p->capacity * (uint64_t)p->head_dim * elem_bytes(p->store_dtype) > 0xFFFFFFFFull)
+        return fail(RECSA_ERR_UNSUPPORTED, "one KV head's cache must be under 4 GiB (capacity %lld)",
+                    (long long)p->capacity);
     if (L.max_cand > descend_max_candidates())
         return fail(RECSA_ERR_UNSUPPORTED,
                     "a level can hold %lld candidates (min(capacity, k*b + b - 1)); at most %d "
                     "are supported",
                     (long long)L.max_cand, descend_max_candidates());
-    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->head_dim) > kMaxLds)
+    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->fanout_b, p->head_dim) > kMaxLds)
         return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
     return RECSA_OK;
 }

@@ -1,0 +1,258 @@
+// Wave-level selection of the m largest of n fp32 logits for gfx950.
+//
+// RecSA, abstract: each level above the tokens keeps at most k candidates.
+// Equal logits go to the lower candidate index.
+//
+// Serial chains of wave-wide reductions and scalar ballots are slow on CDNA
+// (every ballot -> scalar -> vector handoff costs tens of cycles), so this
+// selection uses a constant number of them:
+//   1. every lane maps its logits (candidates lane, lane+64, ...) to ordered
+//      32-bit keys and takes their max;
+//   2. DPP reduces the lane maxima to the max of each group of G lanes
+//      (G = 16, 8, 4 or 2, so that there are at least m groups); tau, the
+//      smallest group max, is a lower bound of the m-th largest key: each
+//      group holds a key >= tau;
+//   3. the candidates with key >= tau (usually a few dozen) are compacted
+//      into LDS with a DPP prefix sum;
+//   4. each surviving candidate is ranked exactly against the others
+//      (larger key first, then lower index), reading them back by LDS
+//      broadcast; rank < m keeps it, and the kept ones are ordered by index.
+// When more than 2 * 64 candidates survive (adversarial ties), a 32-step
+// bisection over the keys finds the m-th largest exactly instead.
+#pragma once
+
+#include <math.h>
+
+#include "recsa_internal.hpp"
+
+namespace recsa {
+namespace sel {
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;                     // -0 and +0 compare equal
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Max / min over the 64 lanes, uniform result.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = max(v, dpp<0x111, 0xf>(0u, v));
+    v = max(v, dpp<0x112, 0xf>(0u, v));
+    v = max(v, dpp<0x114, 0xf>(0u, v));
+    v = max(v, dpp<0x118, 0xf>(0u, v));
+    v = max(v, dpp<0x142, 0xa>(0u, v));   // row_bcast:15
+    v = max(v, dpp<0x143, 0xc>(0u, v));   // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+    v = min(v, dpp<0x111, 0xf>(~0u, v));
+    v = min(v, dpp<0x112, 0xf>(~0u, v));
+    v = min(v, dpp<0x114, 0xf>(~0u, v));
+    v = min(v, dpp<0x118, 0xf>(~0u, v));
+    v = min(v, dpp<0x142, 0xa>(~0u, v));
+    v = min(v, dpp<0x143, 0xc>(~0u, v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
+    v += dpp<0x111, 0xf>(0u, v);
+    v += dpp<0x112, 0xf>(0u, v);
+    v += dpp<0x114, 0xf>(0u, v);
+    v += dpp<0x118, 0xf>(0u, v);
+    v += dpp<0x142, 0xa>(0u, v);
+    v += dpp<0x143, 0xc>(0u, v);
+    return v;
+}
+
+// Max over aligned groups of G lanes, in every lane of the group.
+template <int G>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+    v = max(v, dpp<0xB1, 0xf>(0u, v));                 // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = max(v, dpp<0x4E, 0xf>(0u, v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = max(v, dpp<0x141, 0xf>(0u, v));  // row_half_mirror
+    if constexpr (G >= 16) v = max(v, dpp<0x140, 0xf>(0u, v)); // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
+
+struct Result {
+    float zmax;       // largest logit
+    float gap;        // m-th largest minus (m+1)-th largest; NaN if n == m
+};
+
+// LDS scratch the selection needs (per wave that selects).
+constexpr int kScratchBytes = 128 * 8 + 128 * 4 + 16;
+
+// Keep the m largest of z[0..n) (1 <= m <= n).  node_of(i) gives the node id of
+// candidate i; the kept ids go to kept[0..m) in ascending candidate order, and
+// flag[i] = 1 marks them.  KT >= ceil(n / 64) logits per lane are held in
+// registers.  Returns the level max and k-th gap in every lane.
+template <int KT, typename NodeOf>
+__device__ Result select(const float *z, uint8_t *flag, int32_t *kept, int32_t n, int32_t m,
+                         int lane, unsigned char *scratch, NodeOf node_of) {
+    uint2 *list = reinterpret_cast<uint2 *>(scratch);                 // [128] (key, index)
+    uint32_t *keep = reinterpret_cast<uint32_t *>(scratch + 128 * 8);  // [128]
+    float *out = reinterpret_cast<float *>(scratch + 128 * 12);       // [4]
+
+    uint32_t kk[KT];
+    uint32_t lmax = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int32_t i = lane + 64 * t;
+        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;    // valid keys are >= 0x007FFFFF
+        lmax = max(lmax, kk[t]);
+    }
+    uint32_t gmax;
+    if (m <= 4) gmax = group_umax<16>(lmax);
+    else if (m <= 8) gmax = group_umax<8>(lmax);
+    else if (m <= 16) gmax = group_umax<4>(lmax);
+    else gmax = group_umax<2>(lmax);
+    // at least m groups (of the 64 / G), each with a key >= tau -- unless a group has no
+    // valid key (n < 64), then tau = 0 and every valid candidate survives
+    const uint32_t tau = (m <= 32) ? wave_umin(gmax) : 0u;
+    uint32_t cnt = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) cnt += (lane + 64 * t < n && kk[t] >= tau) ? 1u : 0u;
+    const uint32_t incl = wave_scan_add(cnt);
+    const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    Result res;
+    if (C <= 128) {
+        uint32_t at = incl - cnt;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int32_t i = lane + 64 * t;
+            if (i < n && kk[t] >= tau) list[at++] = make_uint2(kk[t], (uint32_t)i);
+        }
+        __threadfence_block();
+        // exact rank of each survivor: larger key first, then lower index
+        uint2 e0 = make_uint2(0u, 0u), e1 = make_uint2(0u, 0u);
+        if ((uint32_t)lane < C) e0 = list[lane];
+        if ((uint32_t)lane + 64 < C) e1 = list[lane + 64];
+        uint32_t r0 = 0, r1 = 0;
+        const uint4 *list4 = reinterpret_cast<const uint4 *>(list);
+        for (uint32_t j0 = 0; j0 < C; j0 += 8) {          // 8 entries per LDS round trip
+            uint4 q[4];
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = list4[j0 / 2 + u];
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t ox = (u & 1) ? q[u >> 1].z : q[u >> 1].x;
+                const uint32_t oy = (u & 1) ? q[u >> 1].w : q[u >> 1].y;
+                const bool valid = j0 + u < C;
+                r0 += (valid && (ox > e0.x || (ox == e0.x && oy < e0.y))) ? 1u : 0u;
+                r1 += (valid && (ox > e1.x || (ox == e1.x && oy < e1.y))) ? 1u : 0u;
+            }
+        }
+        const bool k0 = (uint32_t)lane < C && r0 < (uint32_t)m;
+        const bool k1 = (uint32_t)lane + 64 < C && r1 < (uint32_t)m;
+        if ((uint32_t)lane < C) keep[lane] = k0 ? e0.y : 0xFFFFFFFFu;
+        if ((uint32_t)lane + 64 < C) keep[lane + 64] = k1 ? e1.y : 0xFFFFFFFFu;
+        // order statistics for the softmax max and the k-th gap
+        if ((uint32_t)lane < C) {
+            if (r0 == 0) out[0] = from_ordered(e0.x);
+            if (r0 == (uint32_t)m - 1) out[1] = from_ordered(e0.x);
+            if (r0 == (uint32_t)m) out[2] = from_ordered(e0.x);
+        }
+        if ((uint32_t)lane + 64 < C) {
+            if (r1 == 0) out[0] = from_ordered(e1.x);
+            if (r1 == (uint32_t)m - 1) out[1] = from_ordered(e1.x);
+            if (r1 == (uint32_t)m) out[2] = from_ordered(e1.x);
+        }
+        __threadfence_block();
+        // ascending position among the kept
+        uint32_t p0 = 0, p1 = 0;
+        const uint4 *keep4 = reinterpret_cast<const uint4 *>(keep);
+        for (uint32_t j0 = 0; j0 < C; j0 += 16) {         // 16 entries per LDS round trip
+            uint4 q[4];
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = keep4[j0 / 4 + u];
+            #pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint4 v = q[u >> 2];
+                const uint32_t o = (u & 3) == 0 ? v.x : (u & 3) == 1 ? v.y : (u & 3) == 2 ? v.z : v.w;
+                const bool valid = j0 + u < C;
+                p0 += (valid && o < e0.y) ? 1u : 0u;
+                p1 += (valid && o < e1.y) ? 1u : 0u;
+            }
+        }
+        if (k0) {
+            kept[p0] = (int32_t)node_of((int32_t)e0.y);
+            flag[e0.y] = 1;
+        }
+        if (k1) {
+            kept[p1] = (int32_t)node_of((int32_t)e1.y);
+            flag[e1.y] = 1;
+        }
+        res.zmax = out[0];
+        float zn;
+        if (n == m) {
+            zn = NAN;
+        } else if (C > (uint32_t)m) {
+            zn = out[2];
+        } else {  // every survivor kept: the (m+1)-th is the largest key below tau
+            uint32_t below = 0;
+            #pragma unroll
+            for (int t = 0; t < KT; ++t)
+                below = max(below, (lane + 64 * t < n && kk[t] < tau) ? kk[t] : 0u);
+            zn = from_ordered(wave_umax(below));
+        }
+        res.gap = (n == m) ? NAN : out[1] - zn;
+    } else {
+        // exact bisection for the m-th largest key T
+        uint32_t T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = T | (1u << bit);
+            int c = 0;
+            #pragma unroll
+            for (int t = 0; t < KT; ++t) c += __popcll(__ballot(kk[t] >= trial));
+            if (c >= m) T = trial;
+        }
+        int gt = 0, eq = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            gt += __popcll(__ballot(kk[t] > T));
+            eq += __popcll(__ballot(kk[t] == T));
+        }
+        int need = m - gt;
+        int32_t pos = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int32_t i = lane + 64 * t;
+            const uint64_t e = __ballot(kk[t] == T);
+            const bool f = (i < n) && ((kk[t] > T) || (kk[t] == T && __popcll(e & lanes_below(lane)) < need));
+            const int ce = __popcll(e);
+            need -= ce < need ? ce : need;
+            const uint64_t mask = __ballot(f);
+            if (f) {
+                kept[pos + __popcll(mask & lanes_below(lane))] = (int32_t)node_of(i);
+                flag[i] = 1;
+            }
+            pos += __popcll(mask);
+        }
+        res.zmax = from_ordered(wave_umax(lmax));
+        uint32_t kn = T;
+        if (n > m && gt + eq <= m) {
+            uint32_t below = 0;
+            #pragma unroll
+            for (int t = 0; t < KT; ++t) below = max(below, kk[t] < T ? kk[t] : 0u);
+            kn = wave_umax(below);
+        }
+        res.gap = (n > m) ? from_ordered(T) - from_ordered(kn) : NAN;
+    }
+    return res;
+}
+
+}  // namespace sel
+}  // namespace recsa
