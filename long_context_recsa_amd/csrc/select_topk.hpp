@@ -3,22 +3,24 @@
 // RecSA, abstract: each level above the tokens keeps at most k candidates.
 // Equal logits go to the lower candidate index.
 //
-// Serial chains of wave-wide reductions and scalar ballots are slow on CDNA
-// (every ballot -> scalar -> vector handoff costs tens of cycles), so this
-// selection uses a constant number of them:
+// On CDNA a wave-wide reduction followed by a read of its result (or an LDS
+// round trip) costs on the order of a hundred cycles, so this selection uses
+// a constant number of them instead of one per kept candidate:
 //   1. every lane maps its logits (candidates lane, lane+64, ...) to ordered
 //      32-bit keys and takes their max;
 //   2. DPP reduces the lane maxima to the max of each group of G lanes
 //      (G = 16, 8, 4 or 2, so that there are at least m groups); tau, the
 //      smallest group max, is a lower bound of the m-th largest key: each
 //      group holds a key >= tau;
-//   3. the candidates with key >= tau (usually a few dozen) are compacted
-//      into LDS with a DPP prefix sum;
-//   4. each surviving candidate is ranked exactly against the others
-//      (larger key first, then lower index), reading them back by LDS
+//   3. the candidates with key >= tau (a few dozen) are compacted into LDS
+//      with a DPP prefix sum;
+//   4. each survivor is ranked exactly against the others (larger key
+//      first, then lower index), reading them back 8 at a time by LDS
 //      broadcast; rank < m keeps it, and the kept ones are ordered by index.
-// When more than 2 * 64 candidates survive (adversarial ties), a 32-step
-// bisection over the keys finds the m-th largest exactly instead.
+// Levels of at most 5 * 64 candidates instead find the m-th largest key by a
+// 32-step bisection with ballots over register-resident keys, which is faster
+// there; so do levels too wide for registers and the rare filter that lets
+// more than 128 candidates through (many equal logits).
 #pragma once
 
 #include <math.h>
@@ -78,57 +80,189 @@ __device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
 // Max over aligned groups of G lanes, in every lane of the group.
 template <int G>
 __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
-    v = max(v, dpp<0xB1, 0xf>(0u, v));                 // quad_perm [1,0,3,2]
-    if constexpr (G >= 4) v = max(v, dpp<0x4E, 0xf>(0u, v));   // quad_perm [2,3,0,1]
-    if constexpr (G >= 8) v = max(v, dpp<0x141, 0xf>(0u, v));  // row_half_mirror
-    if constexpr (G >= 16) v = max(v, dpp<0x140, 0xf>(0u, v)); // row_mirror
+    v = max(v, dpp<0xB1, 0xf>(0u, v));                          // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = max(v, dpp<0x4E, 0xf>(0u, v));    // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = max(v, dpp<0x141, 0xf>(0u, v));   // row_half_mirror
+    if constexpr (G >= 16) v = max(v, dpp<0x140, 0xf>(0u, v));  // row_mirror
     return v;
 }
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-struct Result {
-    float zmax;       // largest logit
-    float gap;        // m-th largest minus (m+1)-th largest; NaN if n == m
+// Candidates of one level: i < nchild is child (i mod b) of kept parent
+// parents[i / b]; the rest are orphans from node orphan0 on; at the top
+// level (top != 0) candidate i is node i.
+struct Cands {
+    int32_t n, nchild, b, top;
+    int32_t orphan0;
 };
 
-// LDS scratch the selection needs (per wave that selects).
+__device__ __forceinline__ int32_t node_id(int32_t i, const Cands &c, const int32_t *parents) {
+    if (c.top) return i;
+    if (i < c.nchild) {
+        const int32_t q = i / c.b;
+        return parents[q] * c.b + (i - q * c.b);
+    }
+    return c.orphan0 + (i - c.nchild);
+}
+
+// LDS scratch the selection needs.
 constexpr int kScratchBytes = 128 * 8 + 128 * 4 + 16;
 
-// Keep the m largest of z[0..n) (1 <= m <= n).  node_of(i) gives the node id of
-// candidate i; the kept ids go to kept[0..m) in ascending candidate order, and
-// flag[i] = 1 marks them.  KT >= ceil(n / 64) logits per lane are held in
-// registers.  Returns the level max and k-th gap in every lane.
-template <int KT, typename NodeOf>
-__device__ Result select(const float *z, uint8_t *flag, int32_t *kept, int32_t n, int32_t m,
-                         int lane, unsigned char *scratch, NodeOf node_of) {
-    uint2 *list = reinterpret_cast<uint2 *>(scratch);                 // [128] (key, index)
-    uint32_t *keep = reinterpret_cast<uint32_t *>(scratch + 128 * 8);  // [128]
-    float *out = reinterpret_cast<float *>(scratch + 128 * 12);       // [4]
+// out[0] = level max, out[1] = m-th largest, out[2] = (m+1)-th largest logit.
+__device__ __noinline__ void select_bisect(const float *z, uint8_t *flag, int32_t *kept, int32_t m,
+                                           Cands cd, const int32_t *parents, int lane,
+                                           float *out) {
+    const int32_t n = cd.n;
+    const int nT = (n + 63) >> 6;
+    auto key = [&](int t) -> uint32_t {
+        const int32_t i = lane + 64 * t;
+        return i < n ? ordered_bits(z[i]) : 0u;
+    };
+    uint32_t lmax = 0;
+    for (int t = 0; t < nT; ++t) lmax = max(lmax, key(t));
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = T | (1u << bit);
+        int c = 0;
+        for (int t = 0; t < nT; ++t) c += __popcll(__ballot(key(t) >= trial));
+        if (c >= m) T = trial;
+    }
+    int gt = 0, eq = 0;
+    for (int t = 0; t < nT; ++t) {
+        gt += __popcll(__ballot(key(t) > T));
+        eq += __popcll(__ballot(key(t) == T));
+    }
+    int need = m - gt;
+    int32_t pos = 0;
+    uint32_t below = 0;
+    for (int t = 0; t < nT; ++t) {
+        const int32_t i = lane + 64 * t;
+        const uint32_t kv = key(t);
+        if (i < n && kv < T) below = max(below, kv);
+        const uint64_t e = __ballot(kv == T);
+        const bool f = (i < n) && ((kv > T) || (kv == T && __popcll(e & lanes_below(lane)) < need));
+        const int ce = __popcll(e);
+        need -= ce < need ? ce : need;
+        const uint64_t mask = __ballot(f);
+        if (f) {
+            kept[pos + __popcll(mask & lanes_below(lane))] = node_id(i, cd, parents);
+            flag[i] = 1;
+        }
+        pos += __popcll(mask);
+    }
+    const uint32_t kmax = wave_umax(lmax);
+    const uint32_t kn = (gt + eq > m) ? T : wave_umax(below);
+    if (lane == 0) {
+        out[0] = from_ordered(kmax);
+        out[1] = from_ordered(T);
+        out[2] = (n > m) ? from_ordered(kn) : NAN;
+    }
+}
 
+// Keep the m largest of z[0..cd.n) (1 <= m <= n): kept[0..m) gets their node ids in
+// ascending candidate order and flag[i] = 1 marks them.  KT >= ceil(n / 64) logits
+// per lane live in registers (KT == 0: bisection over LDS).  Results in out[0..3):
+// level max, m-th and (m+1)-th largest logit (NaN when n == m); visible to the
+// calling wave on return.
+// Bisection for the m-th largest key with the keys in registers (narrow levels:
+// 32 ballot rounds over KT registers beat the filter's LDS round trips there).
+template <int KT>
+__device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag, int32_t *kept,
+                                                   int32_t m, Cands cd, const int32_t *parents,
+                                                   int lane, float *out) {
+    const int32_t n = cd.n;
     uint32_t kk[KT];
     uint32_t lmax = 0;
     #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int32_t i = lane + 64 * t;
-        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;    // valid keys are >= 0x007FFFFF
+        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;
         lmax = max(lmax, kk[t]);
     }
-    uint32_t gmax;
-    if (m <= 4) gmax = group_umax<16>(lmax);
-    else if (m <= 8) gmax = group_umax<8>(lmax);
-    else if (m <= 16) gmax = group_umax<4>(lmax);
-    else gmax = group_umax<2>(lmax);
-    // at least m groups (of the 64 / G), each with a key >= tau -- unless a group has no
-    // valid key (n < 64), then tau = 0 and every valid candidate survives
-    const uint32_t tau = (m <= 32) ? wave_umin(gmax) : 0u;
-    uint32_t cnt = 0;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = T | (1u << bit);
+        int c = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) c += __popcll(__ballot(kk[t] >= trial));
+        if (c >= m) T = trial;
+    }
+    int gt = 0, eq = 0;
     #pragma unroll
-    for (int t = 0; t < KT; ++t) cnt += (lane + 64 * t < n && kk[t] >= tau) ? 1u : 0u;
-    const uint32_t incl = wave_scan_add(cnt);
-    const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    Result res;
-    if (C <= 128) {
+    for (int t = 0; t < KT; ++t) {
+        gt += __popcll(__ballot(kk[t] > T));
+        eq += __popcll(__ballot(kk[t] == T));
+    }
+    int need = m - gt;
+    int32_t pos = 0;
+    uint32_t below = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int32_t i = lane + 64 * t;
+        if (i < n && kk[t] < T) below = max(below, kk[t]);
+        const uint64_t e = __ballot(kk[t] == T);
+        const bool f = (i < n) && ((kk[t] > T) || (kk[t] == T && __popcll(e & lanes_below(lane)) < need));
+        const int ce = __popcll(e);
+        need -= ce < need ? ce : need;
+        const uint64_t mask = __ballot(f);
+        if (f) {
+            kept[pos + __popcll(mask & lanes_below(lane))] = node_id(i, cd, parents);
+            flag[i] = 1;
+        }
+        pos += __popcll(mask);
+    }
+    const uint32_t kmax = wave_umax(lmax);
+    const uint32_t kn = (gt + eq > m) ? T : wave_umax(below);
+    if (lane == 0) {
+        out[0] = from_ordered(kmax);
+        out[1] = from_ordered(T);
+        out[2] = (n > m) ? from_ordered(kn) : NAN;
+    }
+}
+
+template <int KT>
+__device__ __forceinline__ void select(const float *z, uint8_t *flag, int32_t *kept, int32_t m,
+                                       Cands cd, const int32_t *parents, int lane,
+                                       unsigned char *scratch, float *out) {
+    if constexpr (KT == 0) {
+        select_bisect(z, flag, kept, m, cd, parents, lane, out);
+        __threadfence_block();
+        return;
+    } else if constexpr (KT <= 5) {
+        select_bisect_regs<KT>(z, flag, kept, m, cd, parents, lane, out);
+        __threadfence_block();
+        return;
+    } else {
+        const int32_t n = cd.n;
+        uint2 *list = reinterpret_cast<uint2 *>(scratch);                 // [128] (key, index)
+        uint32_t *keep = reinterpret_cast<uint32_t *>(scratch + 128 * 8);  // [128]
+        uint32_t kk[KT];
+        uint32_t lmax = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int32_t i = lane + 64 * t;
+            kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;    // valid keys are > 0
+            lmax = max(lmax, kk[t]);
+        }
+        uint32_t gmax;
+        if (m <= 4) gmax = group_umax<16>(lmax);
+        else if (m <= 8) gmax = group_umax<8>(lmax);
+        else if (m <= 16) gmax = group_umax<4>(lmax);
+        else gmax = group_umax<2>(lmax);
+        // at least m groups each hold a key >= tau (or a group holds no valid key,
+        // n < 64, and tau = 0 lets every valid candidate through)
+        const uint32_t tau = (m <= 32) ? wave_umin(gmax) : 0u;
+        uint32_t cnt = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) cnt += (lane + 64 * t < n && kk[t] >= tau) ? 1u : 0u;
+        const uint32_t incl = wave_scan_add(cnt);
+        const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        if (C > 128) {
+            select_bisect(z, flag, kept, m, cd, parents, lane, out);
+            __threadfence_block();
+            return;
+        }
         uint32_t at = incl - cnt;
         #pragma unroll
         for (int t = 0; t < KT; ++t) {
@@ -137,12 +271,12 @@ __device__ Result select(const float *z, uint8_t *flag, int32_t *kept, int32_t n
         }
         __threadfence_block();
         // exact rank of each survivor: larger key first, then lower index
-        uint2 e0 = make_uint2(0u, 0u), e1 = make_uint2(0u, 0u);
-        if ((uint32_t)lane < C) e0 = list[lane];
-        if ((uint32_t)lane + 64 < C) e1 = list[lane + 64];
+        const bool h0 = (uint32_t)lane < C, h1 = (uint32_t)lane + 64 < C;
+        const uint2 e0 = h0 ? list[lane] : make_uint2(0u, 0u);
+        const uint2 e1 = h1 ? list[lane + 64] : make_uint2(0u, 0u);
         uint32_t r0 = 0, r1 = 0;
         const uint4 *list4 = reinterpret_cast<const uint4 *>(list);
-        for (uint32_t j0 = 0; j0 < C; j0 += 8) {          // 8 entries per LDS round trip
+        for (uint32_t j0 = 0; j0 < C; j0 += 8) {
             uint4 q[4];
             #pragma unroll
             for (int u = 0; u < 4; ++u) q[u] = list4[j0 / 2 + u];
@@ -155,26 +289,33 @@ __device__ Result select(const float *z, uint8_t *flag, int32_t *kept, int32_t n
                 r1 += (valid && (ox > e1.x || (ox == e1.x && oy < e1.y))) ? 1u : 0u;
             }
         }
-        const bool k0 = (uint32_t)lane < C && r0 < (uint32_t)m;
-        const bool k1 = (uint32_t)lane + 64 < C && r1 < (uint32_t)m;
-        if ((uint32_t)lane < C) keep[lane] = k0 ? e0.y : 0xFFFFFFFFu;
-        if ((uint32_t)lane + 64 < C) keep[lane + 64] = k1 ? e1.y : 0xFFFFFFFFu;
-        // order statistics for the softmax max and the k-th gap
-        if ((uint32_t)lane < C) {
+        const bool k0 = h0 && r0 < (uint32_t)m;
+        const bool k1 = h1 && r1 < (uint32_t)m;
+        if (h0) keep[lane] = k0 ? e0.y : 0xFFFFFFFFu;
+        if (h1) keep[lane + 64] = k1 ? e1.y : 0xFFFFFFFFu;
+        if (h0) {
             if (r0 == 0) out[0] = from_ordered(e0.x);
             if (r0 == (uint32_t)m - 1) out[1] = from_ordered(e0.x);
             if (r0 == (uint32_t)m) out[2] = from_ordered(e0.x);
         }
-        if ((uint32_t)lane + 64 < C) {
+        if (h1) {
             if (r1 == 0) out[0] = from_ordered(e1.x);
             if (r1 == (uint32_t)m - 1) out[1] = from_ordered(e1.x);
             if (r1 == (uint32_t)m) out[2] = from_ordered(e1.x);
+        }
+        if (C == (uint32_t)m) {          // the (m+1)-th largest is below tau
+            uint32_t below = 0;
+            #pragma unroll
+            for (int t = 0; t < KT; ++t)
+                below = max(below, (lane + 64 * t < n && kk[t] < tau) ? kk[t] : 0u);
+            below = wave_umax(below);
+            if (lane == 0) out[2] = (n > m) ? from_ordered(below) : NAN;
         }
         __threadfence_block();
         // ascending position among the kept
         uint32_t p0 = 0, p1 = 0;
         const uint4 *keep4 = reinterpret_cast<const uint4 *>(keep);
-        for (uint32_t j0 = 0; j0 < C; j0 += 16) {         // 16 entries per LDS round trip
+        for (uint32_t j0 = 0; j0 < C; j0 += 16) {
             uint4 q[4];
             #pragma unroll
             for (int u = 0; u < 4; ++u) q[u] = keep4[j0 / 4 + u];
@@ -188,70 +329,15 @@ __device__ Result select(const float *z, uint8_t *flag, int32_t *kept, int32_t n
             }
         }
         if (k0) {
-            kept[p0] = (int32_t)node_of((int32_t)e0.y);
+            kept[p0] = node_id((int32_t)e0.y, cd, parents);
             flag[e0.y] = 1;
         }
         if (k1) {
-            kept[p1] = (int32_t)node_of((int32_t)e1.y);
+            kept[p1] = node_id((int32_t)e1.y, cd, parents);
             flag[e1.y] = 1;
         }
-        res.zmax = out[0];
-        float zn;
-        if (n == m) {
-            zn = NAN;
-        } else if (C > (uint32_t)m) {
-            zn = out[2];
-        } else {  // every survivor kept: the (m+1)-th is the largest key below tau
-            uint32_t below = 0;
-            #pragma unroll
-            for (int t = 0; t < KT; ++t)
-                below = max(below, (lane + 64 * t < n && kk[t] < tau) ? kk[t] : 0u);
-            zn = from_ordered(wave_umax(below));
-        }
-        res.gap = (n == m) ? NAN : out[1] - zn;
-    } else {
-        // exact bisection for the m-th largest key T
-        uint32_t T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t trial = T | (1u << bit);
-            int c = 0;
-            #pragma unroll
-            for (int t = 0; t < KT; ++t) c += __popcll(__ballot(kk[t] >= trial));
-            if (c >= m) T = trial;
-        }
-        int gt = 0, eq = 0;
-        #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            gt += __popcll(__ballot(kk[t] > T));
-            eq += __popcll(__ballot(kk[t] == T));
-        }
-        int need = m - gt;
-        int32_t pos = 0;
-        #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int32_t i = lane + 64 * t;
-            const uint64_t e = __ballot(kk[t] == T);
-            const bool f = (i < n) && ((kk[t] > T) || (kk[t] == T && __popcll(e & lanes_below(lane)) < need));
-            const int ce = __popcll(e);
-            need -= ce < need ? ce : need;
-            const uint64_t mask = __ballot(f);
-            if (f) {
-                kept[pos + __popcll(mask & lanes_below(lane))] = (int32_t)node_of(i);
-                flag[i] = 1;
-            }
-            pos += __popcll(mask);
-        }
-        res.zmax = from_ordered(wave_umax(lmax));
-        uint32_t kn = T;
-        if (n > m && gt + eq <= m) {
-            uint32_t below = 0;
-            #pragma unroll
-            for (int t = 0; t < KT; ++t) below = max(below, kk[t] < T ? kk[t] : 0u);
-            kn = wave_umax(below);
-        }
-        res.gap = (n > m) ? from_ordered(T) - from_ordered(kn) : NAN;
+        __threadfence_block();
     }
-    return res;
 }
 
 }  // namespace sel

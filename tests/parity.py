@@ -81,7 +81,7 @@ def check_row(tree, q, g, n_ctx, k, base, scale, gpu_sel_row, max_excuses=3):
 
 
 def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype,
-               all_out_rms=None):
+               all_out_rms=None, head_of=None):
     """rows: list of (query index, head); Q [n][Hq][d] host fp32; gpu_out [n][Hq][d];
     dbg: the debug dict (device tensors).  Asserts selection parity and the output
     tolerance (1e-5 max-abs for fp32 storage, 2e-2 * RMS of the oracle output for bf16)."""
@@ -94,7 +94,8 @@ def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype,
     excused = 0
     for idx, (qi, h) in enumerate(rows):
         r = qi * Hq + h
-        res, ex = check_row(tree, Q[qi, h], h // G, n_ctx_of(qi), k, base, scale, sel[r])
+        g = h // G if head_of is None else head_of(h)
+        res, ex = check_row(tree, Q[qi, h], g, n_ctx_of(qi), k, base, scale, sel[r])
         excused += ex > 0
         if ex == 0:
             assert nkeys[r] == res.keys_read, (qi, h, nkeys[r], res.keys_read)
@@ -108,3 +109,8 @@ def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype,
         tol = 2e-2 * rms
     assert err <= tol, f"max abs error {err:.3g} > {tol:.3g}"
     return {"max_abs_err": float(err), "tol": tol, "excused_rows": excused, "rows": len(rows)}
+
+
+def head_tree(K, V, W, g, w, length):
+    """Oracle tree of KV head g alone (K, V [n_kv][>=length][d])."""
+    return O.build_tree(K[g:g + 1], V[g:g + 1], W[g:g + 1], w.b, w.dtype, w.pool_scale, length)
