@@ -242,6 +242,26 @@ def test_positions_bounded_at_any_length(b, k):
     assert len(set(seen[1:])) <= 1
 
 
+def test_rope_is_rotation_by_position():
+    """Pair j of rope(x, p), read as the complex number x_j + i x_{j+d/2}, is that
+    number times exp(i p base^(-2j/d)); so norms are kept and scores depend only
+    on the position difference (what makes candidate indices relative positions)."""
+    r = np.random.default_rng(11)
+    d, base = 16, 1e4
+    x = r.standard_normal(d)
+    y = r.standard_normal(d)
+    for p in (0, 1, 7, 1000, 123457):
+        got = O.rope(x, p, base)
+        z = (x[:d // 2] + 1j * x[d // 2:]) * np.exp(1j * p * base ** (-np.arange(0, d, 2) / d))
+        np.testing.assert_allclose(got[:d // 2], z.real, atol=1e-12)
+        np.testing.assert_allclose(got[d // 2:], z.imag, atol=1e-12)
+        assert abs(np.linalg.norm(got) - np.linalg.norm(x)) < 1e-12
+    for n, i, t in ((5, 2, 3), (300, 0, 1000), (64, 63, 77777)):
+        a = O.rope(x, n, base) @ O.rope(y, i, base)
+        b_ = O.rope(x, n + t, base) @ O.rope(y, i + t, base)
+        assert abs(a - b_) < 1e-9
+
+
 def test_q_zero_closed_form():
     """q = 0: every logit is 0, each level keeps its first min(k, n)
     candidates, and the output is the plain mean of the entry values."""
