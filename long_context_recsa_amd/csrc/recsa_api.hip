@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "recsa_internal.hpp"
@@ -11,6 +12,12 @@
 namespace recsa {
 size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D);
 int32_t descend_max_candidates();
+size_t tiled_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
+                             int32_t maxc, int64_t capacity);
+size_t tiled_select_lds_bytes(int32_t maxc, int32_t k);
+hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
+                                int64_t length, int64_t capacity, const DebugView &dbg, void *ws,
+                                hipStream_t s);
 }  // namespace recsa
 
 namespace {
@@ -38,6 +45,21 @@ constexpr size_t kMaxLds = 160 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 size_t elem_bytes(int32_t dt) { return dt == RECSA_BF16 ? 2 : 4; }
+
+// Prefill of at least this many rows (queries x query heads) over bf16 storage
+// runs parent-major (rows grouped by the parents they keep, bf16 MFMA); fewer
+// rows, or fp32 storage, run one workgroup per row.  RECSA_PREFILL_PATH=rowwise
+// or =tiled forces one of the two.
+constexpr int64_t kTiledMinRows = 4096;
+
+bool use_tiled(const recsa_params *p, int64_t rows) {
+    if (p->store_dtype != RECSA_BF16) return false;
+    if (const char *e = getenv("RECSA_PREFILL_PATH")) {
+        if (strcmp(e, "rowwise") == 0) return false;
+        if (strcmp(e, "tiled") == 0) return true;
+    }
+    return rows >= kTiledMinRows;
+}
 
 struct Layout {
     int32_t n_levels = 0;
@@ -181,7 +203,7 @@ recsa_status grow_levels(const recsa_params *p, const recsa_tree_desc *d, const 
 
 recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const void *q,
                          int64_t n_queries, int64_t ctx_base, int32_t ctx_step, void *out,
-                         const recsa_debug *dbg, hipStream_t s) {
+                         const recsa_debug *dbg, bool tiled, void *ws, hipStream_t s) {
     recsa_status st = check_params(p);
     if (st != RECSA_OK) return st;
     const Layout L = make_layout(p);
@@ -211,6 +233,20 @@ recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const 
         dv.selected = dbg->selected;
         dv.kth_gap = dbg->kth_gap;
         dv.n_keys = dbg->n_keys;
+    }
+    if (tiled) {
+        if (ws == nullptr || !aligned(ws, 256))
+            return fail(RECSA_ERR_INVALID_ARG,
+                        "this prefill (%lld rows) needs a 256-byte aligned workspace of "
+                        "recsa_workspace_bytes(params, %lld) bytes",
+                        (long long)rows, (long long)rows);
+        if (tiled_select_lds_bytes((int32_t)L.max_cand, p->budget_k) > kMaxLds)
+            return fail(RECSA_ERR_UNSUPPORTED, "selection of %lld candidates needs too much LDS",
+                        (long long)L.max_cand);
+        hipError_t e = launch_prefill_tiled(tv, p->head_dim, a, p->n_kv_heads, d->length, p->capacity,
+                                            dv, ws, s);
+        if (e != hipSuccess) return hip_fail(e, "tiled prefill launch");
+        return RECSA_OK;
     }
     hipError_t e = launch_descend(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
     if (e != hipSuccess) return hip_fail(e, "descend launch");
@@ -250,9 +286,11 @@ recsa_status recsa_tree_layout(const recsa_params *p, int32_t level, size_t *key
 }
 
 size_t recsa_workspace_bytes(const recsa_params *p, int64_t max_rows) {
-    (void)p;
-    (void)max_rows;
-    return 0;
+    if (check_params(p) != RECSA_OK || max_rows < 1) return 0;
+    if (!use_tiled(p, max_rows)) return 0;
+    const Layout L = make_layout(p);
+    return tiled_workspace_bytes(max_rows, p->n_q_heads, p->n_kv_heads, p->head_dim, p->fanout_b,
+                                 p->budget_k, (int32_t)L.max_cand, p->capacity);
 }
 
 recsa_status recsa_build_tree(const recsa_params *p, recsa_tree_desc *desc, int64_t length,
@@ -308,19 +346,19 @@ recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, co
     if (batch < 1) return fail(RECSA_ERR_INVALID_ARG, "batch must be >= 1");
     if (desc != nullptr && desc->length < 1)
         return fail(RECSA_ERR_INVALID_ARG, "decode needs at least one cached token");
-    return run_descend(p, desc, q, batch, desc ? desc->length : 0, 0, out, dbg,
+    return run_descend(p, desc, q, batch, desc ? desc->length : 0, 0, out, dbg, false, nullptr,
                        static_cast<hipStream_t>(stream));
 }
 
 recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
                            int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
                            void *stream) {
-    (void)ws;
     if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
     if (desc != nullptr && n_q > desc->length)
         return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld); append first",
                     (long long)n_q, (long long)desc->length);
-    return run_descend(p, desc, q, n_q, desc ? desc->length - n_q + 1 : 0, 1, out, dbg,
+    const bool tiled = check_params(p) == RECSA_OK && use_tiled(p, n_q * p->n_q_heads);
+    return run_descend(p, desc, q, n_q, desc ? desc->length - n_q + 1 : 0, 1, out, dbg, tiled, ws,
                        static_cast<hipStream_t>(stream));
 }
 

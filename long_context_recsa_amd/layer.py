@@ -8,7 +8,7 @@ import torch
 
 from . import (RECSA_BF16, recsa_append, recsa_build_tree, recsa_debug, recsa_decode,
                recsa_max_candidates, recsa_num_levels, recsa_params, recsa_prefill,
-               recsa_tree_bytes, recsa_tree_desc, recsa_tree_layout)
+               recsa_tree_bytes, recsa_tree_desc, recsa_tree_layout, recsa_workspace_bytes)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -37,6 +37,18 @@ class RecsaLayer:
         self.max_candidates = recsa_max_candidates(params)
         self.desc = recsa_tree_desc(self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                                     self.tree.data_ptr(), self.pool_w.data_ptr(), 0)
+        self._ws = None
+
+    def workspace(self, rows: int):
+        """Device scratch for a call over `rows` rows, as the library sizes it (kept and
+        grown across calls; None when the call needs none)."""
+        nbytes = recsa_workspace_bytes(self.p, rows)
+        if nbytes == 0:
+            return None
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = None
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return _ptr(self._ws)
 
     @property
     def length(self) -> int:
@@ -91,7 +103,8 @@ class RecsaLayer:
         if out is None:
             out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
         d, dbg = self._debug(n * self.p.n_q_heads, debug)
-        recsa_prefill(self.p, self.desc, _ptr(q), n, _ptr(out), dbg, None, self.stream())
+        ws = self.workspace(n * self.p.n_q_heads)
+        recsa_prefill(self.p, self.desc, _ptr(q), n, _ptr(out), dbg, ws, self.stream())
         return (out, d) if debug else out
 
     # ---- inspection -------------------------------------------------------------

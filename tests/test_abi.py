@@ -52,7 +52,13 @@ def test_geometry_queries():
     n1, n2, n3 = 16512, 516, 16
     want = 8 * 128 * (4 * (n1 + n2 + n3) + 4 * (n1 + n2)) + 288 * 64 * 8
     assert want <= nbytes <= want + 256 * 12
-    assert R.recsa_workspace_bytes(p, 1000) == 0
+    assert R.recsa_workspace_bytes(p, 1000) == 0           # few rows: one workgroup per row
+    rows = 4096 * 32                                         # a 4096-query prefill chunk
+    ws = R.recsa_workspace_bytes(p, rows)
+    # at least the per-row logits and one partial sum per (row, parent) of a level
+    assert ws >= rows * (8 * 32 + 31) * 4 + rows * 9 * 128 * 4
+    assert ws % 256 == 0
+    assert R.recsa_workspace_bytes(_p(store="f32"), rows) == 0
     with pytest.raises(R.RecsaError):
         R.recsa_tree_layout(p, 4)
     assert R.recsa_num_levels(_p(capacity=31)) == 0
@@ -97,6 +103,8 @@ def test_calls_validate_before_any_hip_call():
         (lambda: R.recsa_prefill(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake, 11, fake), R.RECSA_ERR_INVALID_ARG),
         (lambda: R.recsa_prefill(p, R.recsa_tree_desc(fake, fake, fake, fake, 10), fake, 0, fake), R.RECSA_ERR_INVALID_ARG),
         (lambda: R.recsa_decode(_p(n_q_heads=12), d, fake, 1, fake), R.RECSA_ERR_INVALID_ARG),
+        # a bf16 prefill of 200 x 32 rows runs parent-major and needs its workspace
+        (lambda: R.recsa_prefill(p, R.recsa_tree_desc(fake, fake, fake, fake, 990), fake, 200, fake), R.RECSA_ERR_INVALID_ARG),
     ]
     for i, (fn, status) in enumerate(cases):
         with pytest.raises(R.RecsaError) as e:

@@ -139,11 +139,25 @@ def test_append_equals_build(chunks):
         assert torch.equal(fk[:, :n], ik[:, :n]) and torch.equal(fv[:, :n], iv[:, :n]), l
 
 
-@pytest.mark.parametrize("name,L,n", [("qwen3_4b_524k", 16384, 512), ("qwen3_4b_1m_drift", 8192, 300),
-                                      ("tiny_f32_4k", 4000, 96)])
-def test_prefill_small(name, L, n):
-    w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=n)
-    _say(f"case prefill {name} L={L} n={n}")
+PREFILL_CASES = [
+    ("qwen3_4b_524k", 16384, 512, {}),
+    ("qwen3_4b_1m_drift", 8192, 300, {}),
+    # contexts 901..1200 cross b^2 = 1024: rows of one chunk have different top levels
+    ("qwen3_4b_524k", 900, 300, {}),
+    # head_dim 64 in bf16, b = 16, k = 4, one head: 300 rows
+    ("tiny_f32_4k", 4000, 300, {"dtype": "bf16"}),
+    ("tiny_f32_4k", 4000, 96, {}),
+]
+
+
+@pytest.mark.parametrize("path", ["tiled", "rowwise"])
+@pytest.mark.parametrize("name,L,n,kw", PREFILL_CASES)
+def test_prefill_small(name, L, n, kw, path, monkeypatch):
+    """Causal prefill against the oracle, parent-major (bf16 MFMA, the default for
+    large bf16 chunks) and one workgroup per row (fp32 storage always runs this way)."""
+    monkeypatch.setenv("RECSA_PREFILL_PATH", path)
+    w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=n, **kw)
+    _say(f"case prefill {name} L={L} n={n} {kw} path={path}")
     Lt = L + n
     K, V = synth.gen_kv(w, 0, Lt)
     W = synth.pool_w(w)
