@@ -21,13 +21,15 @@
 //           rank-rotated queries on bf16 MFMA (fp32 operands split into a bf16
 //           high and low part; three products give about 16 correct bits);
 //   select  per row: the top-min(k, n) logits become the next level's parents
-//           (equal logits: lower index), the others are entries: the row's
-//           running max and normaliser absorb them and their logits stay;
-//   pv      per 16 pairs of one parent: exp(z - max) of the entries times the
-//           children's values (bf16, exact) on MFMA, one partial sum per pair;
-// and the partial sums of a level are folded into the row's accumulator when
-// the next level is selected (or at the end).  At level 0 the children are
-// tokens and every candidate is an entry.
+//           (equal logits: lower index); the others are entries; kept logits
+//           become -inf;
+//   pv      per 16 pairs of one parent: the pair's entries as a softmax state
+//           of their own (max m, sum l of exp(z - m), and the sum of
+//           exp(z - m) times the children's values, bf16 exact, on MFMA);
+// At level 0 the children are tokens, every candidate is an entry and nothing
+// is selected, so scoring, the pairs' softmax states and P.V are one kernel.
+// One last pass merges all pairs' states of a row (as split attention merges
+// its splits) into the output.
 #include <math.h>
 
 #include <algorithm>
@@ -42,46 +44,45 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kTile = 16;             // pairs per MFMA tile (the M side)
-constexpr int kHistMax = 8192;        // parents per KV head counted in LDS before one global add
-constexpr int64_t kRowsPerPass = 1 << 18;
-
-struct RowStat {
-    float m_acc;     // the max the accumulator is expressed in
-    float m_cur;     // the running max over all entries so far
-    float l;         // the running normaliser, in units of m_cur
-    int32_t n_keys;  // candidates scored so far
-};
+constexpr int kTile = 16;               // pairs per MFMA tile (the M side)
+constexpr int kMaxFanout = 128;         // children per parent the P.V tiles hold
+constexpr int kHistSplit = 4096;        // up to this many parents per head: one LDS count per 256 rows
+constexpr int kRange = 2048;            // else: parents per counting block
+constexpr int kScanPer = 16;            // bucket sizes per thread in the scans
+constexpr int kScanChunk = kScanPer * 256;
+constexpr int64_t kRowsPerPass = 1 << 17;
 
 struct TP {
     const bf16_t *q;           // [rows][D]
     void *out;                 // [rows][D]
     int32_t out_bf16;
     int32_t Hq, G, Hkv, D;
-    int64_t rows;
+    int64_t rows;              // rows of this pass
+    int64_t rows_cap;          // rows per pass the workspace holds
     int64_t ctx_base;          // n_ctx of row 0's query
     int32_t ctx_step;
     int32_t b, k, zs;          // zs: row stride of z (floats)
     float scale;
     int32_t top;               // highest level any row reaches
     int32_t n_levels;          // levels of the tree (debug layout)
+    int32_t lv;                // level slots of the per-level arrays (n_levels + 1)
     int64_t length;            // tokens in the tree
     int64_t pw[kMaxLevels + 2];  // b^l
     // workspace
     float *z;                  // [rows][zs]
     int32_t *par[2];           // [rows][k]: parents by level parity
     int32_t *mk[2];            // [rows]: kept parents by level parity
-    int32_t *np;               // [rows]: pairs of the last selected level
     int32_t *pairpos;          // [rows][k+1]
     int32_t *counts;           // [nb]
     int32_t *offs;             // [nb+1]
     int32_t *itemoff;          // [nb+1]
-    int2 *sorted;              // [pairs]: (row, rank) grouped by parent
+    int2 *bsum;                // [nb / kScanChunk + 1]
+    int4 *sorted;              // [pairs]: (row, rank, query position, children) grouped by parent
     int4 *items;               // (bucket, first pair, pairs, 0)
     int32_t *n_items;
-    float *partial;            // [rows][k+1][D]
-    float *acc;                // [rows][D]
-    RowStat *stat;             // [rows]
+    float *partial;            // [lv][rows_cap][k+1][D]: sum of exp(z - m) v per pair
+    float2 *pml;               // [lv][rows_cap][k+1]: (m, sum of exp(z - m)) per pair
+    int32_t *nplev;            // [rows][lv]: pairs at each level
 };
 
 struct RowLevel {
@@ -103,6 +104,10 @@ __device__ __forceinline__ RowLevel row_level(const TP &a, int64_t row, int l) {
 __device__ __forceinline__ int64_t parent_of(const TP &a, int64_t row, int l, int rank,
                                              const RowLevel &rl) {
     return rank < rl.m ? (int64_t)a.par[l & 1][row * a.k + rank] : rl.part;
+}
+
+__device__ __forceinline__ int64_t head_row(const TP &a, int g, int64_t t) {
+    return (t / a.G) * a.Hq + (int64_t)g * a.G + (t % a.G);
 }
 
 // keys or values of level l (tokens at l = 0) of KV head g
@@ -145,17 +150,44 @@ __device__ __forceinline__ void load_cs(const float2 *p, float *c, float *s) {
     }
 }
 
+// Exclusive scan of (x, y) over a 256-thread block; `total` gets the block sums.
+__device__ __forceinline__ int2 block_scan(int2 v, int2 &total) {
+    __shared__ int2 wsum[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int2 inc = v;
+    #pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int yx = __shfl_up(inc.x, o), yy = __shfl_up(inc.y, o);
+        if (lane >= o) {
+            inc.x += yx;
+            inc.y += yy;
+        }
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    int2 base = make_int2(0, 0);
+    total = make_int2(0, 0);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < w) {
+            base.x += wsum[i].x;
+            base.y += wsum[i].y;
+        }
+        total.x += wsum[i].x;
+        total.y += wsum[i].y;
+    }
+    __syncthreads();
+    return make_int2(base.x + inc.x - v.x, base.y + inc.y - v.y);
+}
+
 // ---------------------------------------------------------------- set-up --
 __global__ void tp_init(TP a, DebugView dbg, int64_t nb) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = t; i < a.rows; i += stride) {
-        a.stat[i] = RowStat{-INFINITY, -INFINITY, 0.f, 0};
-        a.np[i] = 0;
         a.mk[a.top & 1][i] = 0;
         if (dbg.n_keys) dbg.n_keys[i] = 0;
     }
-    for (int64_t i = t; i < a.rows * a.D; i += stride) a.acc[i] = 0.f;
     for (int64_t i = t; i < nb; i += stride) a.counts[i] = 0;
     if (dbg.selected)
         for (int64_t i = t; i < a.rows * a.n_levels * a.k; i += stride) dbg.selected[i] = -1;
@@ -164,92 +196,146 @@ __global__ void tp_init(TP a, DebugView dbg, int64_t nb) {
 }
 
 // Position of every pair of level l inside its (head, parent) bucket, and the
-// bucket sizes.  One block holds rows of one KV head; with few parents it
-// counts in LDS first, so a bucket takes one global atomic per block.
-__global__ __launch_bounds__(256) void tp_count(TP a, int l, int32_t NP, int use_lds) {
+// bucket sizes.  mode 0 (few parents): each block counts 256 rows of one head
+// in LDS, then adds to the global sizes (one atomic per parent and block).
+// mode 1 (many parents): each block owns a range of kRange parents of one head,
+// counts the pairs of all of the head's rows that fall in it, and stores the
+// sizes of its range; no global atomics.
+__global__ __launch_bounds__(1024) void tp_count(TP a, int l, int32_t NP, int mode) {
     extern __shared__ int32_t hist[];
     const int g = blockIdx.y;
     const int64_t per_head = a.rows / a.Hq * a.G;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t row = -1;
-    if (t < per_head) row = (t / a.G) * a.Hq + (int64_t)g * a.G + (t % a.G);
-    if (use_lds) {
-        for (int p = threadIdx.x; p < NP; p += blockDim.x) hist[p] = 0;
+    if (mode == 1) {
+        const int64_t p0 = (int64_t)blockIdx.x * kRange;
+        const int32_t np_blk = (int32_t)min<int64_t>(kRange, NP - p0);
+        for (int p = threadIdx.x; p < np_blk; p += blockDim.x) hist[p] = 0;
         __syncthreads();
+        for (int64_t t = threadIdx.x; t < per_head; t += blockDim.x) {
+            const int64_t row = head_row(a, g, t);
+            const RowLevel rl = row_level(a, row, l);
+            const int32_t np = rl.m + (rl.o > 0 ? 1 : 0);
+            int32_t *pp = a.pairpos + row * (a.k + 1);
+            for (int r = 0; r < np; ++r) {
+                const int64_t p = parent_of(a, row, l, r, rl) - p0;
+                if (p >= 0 && p < np_blk) pp[r] = atomicAdd(&hist[p], 1);
+            }
+        }
+        __syncthreads();
+        for (int p = threadIdx.x; p < np_blk; p += blockDim.x) a.counts[(int64_t)g * NP + p0 + p] = hist[p];
+        return;
     }
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int p = threadIdx.x; p < NP; p += blockDim.x) hist[p] = 0;
+    __syncthreads();
+    int64_t row = -1;
     RowLevel rl{0, 0, 0};
     int32_t np = 0;
-    if (row >= 0) {
+    if (t < per_head) {
+        row = head_row(a, g, t);
         rl = row_level(a, row, l);
         np = rl.m + (rl.o > 0 ? 1 : 0);
     }
     int32_t *pp = a.pairpos + (row >= 0 ? row : 0) * (a.k + 1);
-    for (int r = 0; r < np; ++r) {
-        const int64_t p = parent_of(a, row, l, r, rl);
-        pp[r] = use_lds ? atomicAdd(&hist[p], 1) : atomicAdd(&a.counts[(int64_t)g * NP + p], 1);
-    }
-    if (use_lds) {
-        __syncthreads();
-        for (int p = threadIdx.x; p < NP; p += blockDim.x) {
-            const int32_t c = hist[p];
-            if (c) hist[p] = atomicAdd(&a.counts[(int64_t)g * NP + p], c);
-        }
-        __syncthreads();
-        for (int r = 0; r < np; ++r) pp[r] += hist[parent_of(a, row, l, r, rl)];
-    }
-}
-
-// Exclusive scans of the bucket sizes (pair offsets) and of their tiles
-// (item offsets); clears the sizes for the next level.
-__global__ __launch_bounds__(1024) void tp_scan(TP a, int64_t nb) {
-    __shared__ int32_t s0[1024], s1[1024];
-    const int t = threadIdx.x;
-    const int64_t per = (nb + 1023) / 1024;
-    const int64_t b0 = t * per, b1 = min(nb, b0 + per);
-    int32_t c0 = 0, c1 = 0;
-    for (int64_t i = b0; i < b1; ++i) {
-        const int32_t c = a.counts[i];
-        c0 += c;
-        c1 += (c + kTile - 1) / kTile;
-    }
-    s0[t] = c0;
-    s1[t] = c1;
+    for (int r = 0; r < np; ++r) pp[r] = atomicAdd(&hist[parent_of(a, row, l, r, rl)], 1);
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v0 = t >= off ? s0[t - off] : 0;
-        const int32_t v1 = t >= off ? s1[t - off] : 0;
-        __syncthreads();
-        s0[t] += v0;
-        s1[t] += v1;
-        __syncthreads();
+    for (int p = threadIdx.x; p < NP; p += blockDim.x) {
+        const int32_t c = hist[p];
+        if (c) hist[p] = atomicAdd(&a.counts[(int64_t)g * NP + p], c);
     }
-    int32_t e0 = s0[t] - c0, e1 = s1[t] - c1;
-    for (int64_t i = b0; i < b1; ++i) {
-        const int32_t c = a.counts[i];
-        a.offs[i] = e0;
-        a.itemoff[i] = e1;
-        e0 += c;
-        e1 += (c + kTile - 1) / kTile;
-        a.counts[i] = 0;
-    }
-    if (t == 1023) {
-        a.offs[nb] = s0[1023];
-        a.itemoff[nb] = s1[1023];
-        *a.n_items = s1[1023];
+    __syncthreads();
+    for (int r = 0; r < np; ++r) pp[r] += hist[parent_of(a, row, l, r, rl)];
+}
+
+// Exclusive scans of the bucket sizes (pair offsets) and of their tiles (item
+// offsets) in three steps: per-chunk sums, a scan of the chunk sums, per-chunk
+// scans; the last step also clears the sizes for the next level.
+__device__ __forceinline__ void scan_load(const TP &a, int64_t nb, int64_t e0, int32_t *c) {
+    if (e0 + kScanPer <= nb) {
+        #pragma unroll
+        for (int i = 0; i < kScanPer; i += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(a.counts + e0 + i);
+            c[i] = v.x; c[i + 1] = v.y; c[i + 2] = v.z; c[i + 3] = v.w;
+        }
+    } else {
+        #pragma unroll
+        for (int i = 0; i < kScanPer; ++i) c[i] = e0 + i < nb ? a.counts[e0 + i] : 0;
     }
 }
 
-// Pairs into bucket order; one item per tile of a bucket.
-__global__ __launch_bounds__(256) void tp_scatter(TP a, int l, int32_t NP, int64_t nb) {
+__global__ __launch_bounds__(256) void tp_scan_sums(TP a, int64_t nb) {
+    const int64_t e0 = (int64_t)blockIdx.x * kScanChunk + threadIdx.x * kScanPer;
+    int32_t c[kScanPer];
+    scan_load(a, nb, e0, c);
+    int2 v = make_int2(0, 0);
+    #pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+        v.x += c[i];
+        v.y += (c[i] + kTile - 1) / kTile;
+    }
+    int2 total;
+    block_scan(v, total);
+    if (threadIdx.x == 0) a.bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(256) void tp_scan_chunks(TP a, int64_t nb, int64_t nchunks) {
+    int2 carry = make_int2(0, 0);
+    for (int64_t c0 = 0; c0 < nchunks; c0 += 256) {
+        const int64_t i = c0 + threadIdx.x;
+        const int2 v = i < nchunks ? a.bsum[i] : make_int2(0, 0);
+        int2 total;
+        const int2 ex = block_scan(v, total);
+        if (i < nchunks) a.bsum[i] = make_int2(carry.x + ex.x, carry.y + ex.y);
+        carry.x += total.x;
+        carry.y += total.y;
+    }
+    if (threadIdx.x == 0) {
+        a.offs[nb] = carry.x;
+        a.itemoff[nb] = carry.y;
+        *a.n_items = carry.y;
+    }
+}
+
+__global__ __launch_bounds__(256) void tp_scan_write(TP a, int64_t nb) {
+    const int64_t e0 = (int64_t)blockIdx.x * kScanChunk + threadIdx.x * kScanPer;
+    int32_t c[kScanPer];
+    scan_load(a, nb, e0, c);
+    int2 v = make_int2(0, 0);
+    #pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+        v.x += c[i];
+        v.y += (c[i] + kTile - 1) / kTile;
+    }
+    int2 total;
+    int2 ex = block_scan(v, total);
+    const int2 base = a.bsum[blockIdx.x];
+    ex.x += base.x;
+    ex.y += base.y;
+    for (int i = 0; i < kScanPer && e0 + i < nb; ++i) {
+        a.offs[e0 + i] = ex.x;
+        a.itemoff[e0 + i] = ex.y;
+        ex.x += c[i];
+        ex.y += (c[i] + kTile - 1) / kTile;
+        a.counts[e0 + i] = 0;
+    }
+}
+
+// Pairs into bucket order, each with what scoring needs: (row, rank, the
+// query's RoPE position n - rank*b, the parent's children in the row's view);
+// one item per tile of a bucket.
+__global__ __launch_bounds__(256) void tp_scatter(TP a, DebugView dbg, int l, int32_t NP, int64_t nb) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t < a.rows) {
         const int64_t row = t;
         const RowLevel rl = row_level(a, row, l);
         const int32_t np = rl.m + (rl.o > 0 ? 1 : 0);
+        const int32_t n = rl.m * a.b + rl.o;
         const int64_t g = (row % a.Hq) / a.G;
+        a.nplev[row * a.lv + l] = np;
+        if (dbg.n_keys) dbg.n_keys[row] += n;
         for (int r = 0; r < np; ++r) {
             const int64_t bkt = g * NP + parent_of(a, row, l, r, rl);
-            a.sorted[a.offs[bkt] + a.pairpos[row * (a.k + 1) + r]] = make_int2((int32_t)row, r);
+            a.sorted[a.offs[bkt] + a.pairpos[row * (a.k + 1) + r]] =
+                make_int4((int32_t)row, r, n - r * a.b, r < rl.m ? a.b : rl.o);
         }
     } else if (t - a.rows < nb) {
         const int64_t bkt = t - a.rows;
@@ -263,97 +349,121 @@ __global__ __launch_bounds__(256) void tp_scatter(TP a, int l, int32_t NP, int64
 // One wave per item: up to 16 pairs of one parent against its b children.
 // MFMA 16x16x32: lane L supplies A row L%16 and B column L%16 for the 8
 // k-slots of group L/16.  The k-slots are mapped to dimensions so that a lane
-// group owns RoPE pairs [grp*D/8, grp*D/8 + D/8) of both halves: every rotation
-// stays inside a lane and each row slice is a contiguous load.
-template <int D>
-__global__ __launch_bounds__(256) void tp_score(TreeView tv, TP a, int l, int32_t NP) {
-    constexpr int H = D / 2, PG = D / 8, KS = D / 32, KS1 = D / 64;
-    const int lane = threadIdx.x & 63;
+// group owns RoPE pairs [grp*D/8, grp*D/8 + D/8) of both halves: k-slot
+// (ks, v) is dimension grp*D/8 + 8*ks + v for ks < D/64 and its partner
+// (+ D/2) at ks + D/64.  Every rotation stays inside a lane and each row
+// slice is a contiguous load.
+struct Item {
+    int g;          // KV head
+    int64_t p;      // parent node
+    int cnt;        // pairs
+    int4 pr;        // this lane's pair (lane % 16): row, rank, query position, children
+    int32_t orow[4], orank[4], onc[4];   // the output rows of this lane: pairs 4*(lane/16) + v
+};
+
+__device__ __forceinline__ bool load_item(const TP &a, int32_t NP, int lane, Item &it) {
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= *a.n_items) return;
-    const int4 it = a.items[item];
-    const int g = it.x / NP;
-    const int64_t p = it.x % NP;
-    const int cnt = it.z;
+    if (item >= *a.n_items) return false;
+    const int4 rec = a.items[item];
+    it.g = rec.x / NP;
+    it.p = rec.x % NP;
+    it.cnt = rec.z;
     const int i16 = lane & 15, grp = lane >> 4;
-    const int2 pr = a.sorted[it.y + (i16 < cnt ? i16 : 0)];
-    const int64_t row = pr.x;
-    const int rank = pr.y;
-    const RowLevel rl = row_level(a, row, l);
-    const int32_t n = rl.m * a.b + rl.o;
-    const int32_t nc = rank < rl.m ? a.b : rl.o;
-    const int32_t pos = n - rank * a.b;
-
-    bf16x8 ah[KS], al[KS];
-    {
-        float q1[PG], q2[PG], c[PG], s[PG], u[D / 4];
-        const bf16_t *qr = a.q + row * D;
-        Vec<bf16_t, PG>::load(qr + grp * PG, q1);
-        Vec<bf16_t, PG>::load(qr + H + grp * PG, q2);
-        load_cs<PG>(tv.rope + (int64_t)pos * H + grp * PG, c, s);
-        const float live = i16 < cnt ? 1.f : 0.f;
-        #pragma unroll
-        for (int j = 0; j < PG; ++j) {
-            u[j] = live * (q1[j] * c[j] - q2[j] * s[j]);
-            u[PG + j] = live * (q2[j] * c[j] + q1[j] * s[j]);
-        }
-        #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) split8(u + 8 * ks, ah[ks], al[ks]);
-    }
-    static_assert(KS1 * 8 == PG, "first-half slots");
-
-    // the output rows of this lane: pairs 4*grp + v
-    int32_t orow[4], orank[4], onc[4];
+    it.pr = a.sorted[rec.y + (i16 < it.cnt ? i16 : 0)];
     #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        orow[v] = __shfl((int32_t)row, 4 * grp + v);
-        orank[v] = __shfl(rank, 4 * grp + v);
-        onc[v] = __shfl(nc, 4 * grp + v);
+        it.orow[v] = __shfl(it.pr.x, 4 * grp + v);
+        it.orank[v] = __shfl(it.pr.y, 4 * grp + v);
+        it.onc[v] = 4 * grp + v < it.cnt ? __shfl(it.pr.w, 4 * grp + v) : 0;
     }
+    return true;
+}
 
-    const bf16_t *keys = level_rows(tv, false, l, g, D);
+// The pairs' rank-rotated queries as MFMA A operands, high and low bf16 parts.
+template <int D>
+__device__ __forceinline__ void query_operands(const TreeView &tv, const TP &a, const Item &it, int lane,
+                                               bf16x8 *ah, bf16x8 *al) {
+    constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
+    const int i16 = lane & 15, grp = lane >> 4;
+    const bf16_t *qr = a.q + (int64_t)it.pr.x * D + grp * PG;
+    const float2 *cs = tv.rope + (int64_t)it.pr.z * H + grp * PG;
+    const float live = i16 < it.cnt ? 1.f : 0.f;
+    #pragma unroll
+    for (int pc = 0; pc < KS1; ++pc) {
+        float q1[8], q2[8], c[8], sn[8], u1[8], u2[8];
+        Vec<bf16_t, 8>::load(qr + 8 * pc, q1);
+        Vec<bf16_t, 8>::load(qr + H + 8 * pc, q2);
+        load_cs<8>(cs + 8 * pc, c, sn);
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            u1[j] = live * (q1[j] * c[j] - q2[j] * sn[j]);
+            u2[j] = live * (q2[j] * c[j] + q1[j] * sn[j]);
+        }
+        split8(u1, ah[pc], al[pc]);
+        split8(u2, ah[pc + KS1], al[pc + KS1]);
+    }
+}
+
+// Logits of pairs 4*(lane/16) + v against child ct + lane%16 (unscaled).
+template <int D>
+__device__ __forceinline__ f32x4 score_tile(const TreeView &tv, const bf16_t *keys, int64_t c0,
+                                            int64_t nexist, int b, int ct, int lane, const bf16x8 *ah,
+                                            const bf16x8 *al) {
+    constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int c = ct + i16;
+    const bool ok = c < b && c0 + c < nexist;
+    const bf16_t *kp = keys + (ok ? c0 + c : 0) * D + grp * PG;
+    const float2 *cs = tv.rope + (int64_t)(ok ? c : 0) * H + grp * PG;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int pc = 0; pc < KS1; ++pc) {
+        float k1[8], k2[8], cc[8], ss[8], r1[8], r2[8];
+        Vec<bf16_t, 8>::load(kp + 8 * pc, k1);
+        Vec<bf16_t, 8>::load(kp + H + 8 * pc, k2);
+        load_cs<8>(cs + 8 * pc, cc, ss);
+        const float live = ok ? 1.f : 0.f;
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            r1[j] = live * (k1[j] * cc[j] - k2[j] * ss[j]);
+            r2[j] = live * (k2[j] * cc[j] + k1[j] * ss[j]);
+        }
+        bf16x8 bh, bl;
+        split8(r1, bh, bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc], bh, acc, 0, 0, 0);
+        split8(r2, bh, bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc + KS1], bh, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tp_score(TreeView tv, TP a, int l, int32_t NP) {
+    const int lane = threadIdx.x & 63;
+    Item it;
+    if (!load_item(a, NP, lane, it)) return;
+    bf16x8 ah[D / 32], al[D / 32];
+    query_operands<D>(tv, a, it, lane, ah, al);
+    const bf16_t *keys = level_rows(tv, false, l, it.g, D);
     const int64_t nexist = a.length / a.pw[l];
-    const int64_t c0 = p * a.b;
+    const int64_t c0 = it.p * a.b;
     for (int ct = 0; ct < a.b; ct += 16) {
-        const int c = ct + i16;
-        const bool ok = c < a.b && c0 + c < nexist;
-        float k1[PG], k2[PG], cc[PG], ss[PG], kr[D / 4];
-        if (ok) {
-            const bf16_t *kp = keys + (c0 + c) * D;
-            Vec<bf16_t, PG>::load(kp + grp * PG, k1);
-            Vec<bf16_t, PG>::load(kp + H + grp * PG, k2);
-            load_cs<PG>(tv.rope + (int64_t)c * H + grp * PG, cc, ss);
-        } else {
-            #pragma unroll
-            for (int j = 0; j < PG; ++j) { k1[j] = 0.f; k2[j] = 0.f; cc[j] = 1.f; ss[j] = 0.f; }
-        }
+        const f32x4 acc = score_tile<D>(tv, keys, c0, nexist, a.b, ct, lane, ah, al);
+        const int c = ct + (lane & 15);
         #pragma unroll
-        for (int j = 0; j < PG; ++j) {
-            kr[j] = k1[j] * cc[j] - k2[j] * ss[j];
-            kr[PG + j] = k2[j] * cc[j] + k1[j] * ss[j];
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 bh, bl;
-            split8(kr + 8 * ks, bh, bl);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh, acc, 0, 0, 0);
-        }
-        #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            if (4 * grp + v < cnt && c < onc[v])
-                a.z[(int64_t)orow[v] * a.zs + orank[v] * a.b + c] = a.scale * acc[v];
-        }
+        for (int v = 0; v < 4; ++v)
+            if (c < it.onc[v]) a.z[(int64_t)it.orow[v] * a.zs + it.orank[v] * a.b + c] = a.scale * acc[v];
     }
 }
 
 // ---------------------------------------------------------------- select --
-// One wave per row.  Folds the previous level's partial sums into the row's
-// accumulator, keeps the top min(k, n) candidates of level l (l >= 1) as the
-// next level's parents, and adds this level's entries to the running max and
-// normaliser; kept candidates' logits become -inf so the P.V pass skips them.
+// One wave per row: keeps the top min(k, n) candidates of level l (l >= 1) as
+// the next level's parents; kept candidates' logits become -inf so the P.V
+// pass skips them.
 template <int KT>
 __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int smem_wave) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -367,138 +477,67 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
     float *zl = reinterpret_cast<float *>(base + sel::kScratchBytes + 16 + ((a.k * 4 + 15) & ~15));
     uint8_t *flag = reinterpret_cast<uint8_t *>(zl + a.zs);
 
-    RowStat st = a.stat[row];
-    const int D = a.D;
-    {
-        const int npp = a.np[row];
-        const float sa = st.m_acc == -INFINITY ? 0.f : __expf(st.m_acc - st.m_cur);
-        float *ac = a.acc + row * D;
-        const float *pa = a.partial + row * (a.k + 1) * D;
-        for (int d = lane; d < D; d += 64) {
-            float v = ac[d] * sa;
-            for (int r = 0; r < npp; ++r) v += pa[r * D + d];
-            ac[d] = v;
-        }
-        st.m_acc = st.m_cur;
-    }
     const RowLevel rl = row_level(a, row, l);
     const int32_t n = rl.m * a.b + rl.o;
-    st.n_keys += n;
+    const int32_t mm = min(a.k, n);
+    if (lane == 0) a.mk[(l + 1) & 1][row] = mm;
+    if (n == 0) return;
     float *zr = a.z + row * a.zs;
-    int32_t mm = 0;
-    float mz = -INFINITY;
-    if (n > 0) {
-        for (int i = lane; i < n; i += 64) {
-            zl[i] = zr[i];
-            flag[i] = 0;
-        }
-        __threadfence_block();
-        if (l >= 1) {
-            mm = min(a.k, n);
-            sel::Cands cd;
-            cd.n = n;
-            cd.nchild = rl.m * a.b;
-            cd.b = a.b;
-            cd.top = 0;
-            cd.orphan0 = (int32_t)(rl.part * a.b);
-            sel::select<KT>(zl, flag, kept, mm, cd, a.par[l & 1] + row * a.k, lane, scratch, outv);
-            int32_t *pn = a.par[(l + 1) & 1] + row * a.k;
-            for (int r = lane; r < mm; r += 64) pn[r] = kept[r];
-            if (dbg.selected)
-                for (int r = lane; r < mm; r += 64)
-                    dbg.selected[(row * a.n_levels + (l - 1)) * a.k + r] = kept[r];
-            if (dbg.kth_gap && lane == 0) dbg.kth_gap[row * a.n_levels + (l - 1)] = outv[1] - outv[2];
-            for (int i = lane; i < n; i += 64)
-                if (flag[i]) {
-                    zr[i] = -INFINITY;
-                    zl[i] = -INFINITY;
-                }
-            __threadfence_block();
-        }
-        for (int i = lane; i < n; i += 64) mz = fmaxf(mz, zl[i]);
-        mz = wave_max(mz);
+    for (int i = lane; i < n; i += 64) {
+        zl[i] = zr[i];
+        flag[i] = 0;
     }
-    if (l >= 1 && lane == 0) a.mk[(l + 1) & 1][row] = mm;
-    const float mn = fmaxf(st.m_cur, mz);
-    if (mn > -INFINITY && mz > -INFINITY) {
-        float s = 0.f;
-        for (int i = lane; i < n; i += 64) s += zl[i] == -INFINITY ? 0.f : __expf(zl[i] - mn);
-        s = wave_sum(s);
-        st.l = (st.m_cur == -INFINITY ? 0.f : st.l * __expf(st.m_cur - mn)) + s;
-        st.m_cur = mn;
-    }
-    if (lane == 0) {
-        a.stat[row] = st;
-        a.np[row] = rl.m + (rl.o > 0 ? 1 : 0);
-    }
+    __threadfence_block();
+    sel::Cands cd;
+    cd.n = n;
+    cd.nchild = rl.m * a.b;
+    cd.b = a.b;
+    cd.top = 0;
+    cd.orphan0 = (int32_t)(rl.part * a.b);
+    sel::select<KT>(zl, flag, kept, mm, cd, a.par[l & 1] + row * a.k, lane, scratch, outv);
+    int32_t *pn = a.par[(l + 1) & 1] + row * a.k;
+    for (int r = lane; r < mm; r += 64) pn[r] = kept[r];
+    if (dbg.selected)
+        for (int r = lane; r < mm; r += 64) dbg.selected[(row * a.n_levels + (l - 1)) * a.k + r] = kept[r];
+    if (dbg.kth_gap && lane == 0) dbg.kth_gap[row * a.n_levels + (l - 1)] = outv[1] - outv[2];
+    for (int i = lane; i < n; i += 64)
+        if (flag[i]) zr[i] = -INFINITY;
 }
 
 // -------------------------------------------------------------------- pv --
-// One wave per item: sum over the parent's children c of exp(z_c - max) v_c
-// for up to 16 pairs.  MFMA 16x16x32 with k = children (lane group grp holds
-// children 8*grp .. 8*grp + 7 of each 32) and n = dimensions: lane column L%16
-// of tile t is dimension (D/16)*(L%16) + t, so a lane reads D/16 contiguous
-// bf16 of each child row and writes D/16 contiguous floats per pair.
-template <int D>
-__global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t NP) {
+// The softmax state of a pair's entries: m = max z, l = sum exp(z - m), and
+// sum exp(z - m) v over the parent's children on MFMA 16x16x32 with k =
+// children (lane group grp holds children 8*grp .. 8*grp + 7 of each 32) and
+// n = dimensions: lane column L%16 of tile t is dimension (D/16)*(L%16) + t, so
+// a lane reads D/16 contiguous bf16 of each child row and writes D/16
+// contiguous floats per pair.  `w` holds the lane's weights exp(z - m) for
+// children kc + 8*grp + v, kc = 0, 32, ...
+template <int D, int KC>
+__device__ __forceinline__ void pv_tiles(const TP &a, const Item &it, const bf16_t *vals, int64_t c0,
+                                         int64_t nexist, int lane, const float (*w)[8], float *slice) {
     constexpr int NT = D / 16;
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= *a.n_items) return;
-    const int4 it = a.items[item];
-    const int g = it.x / NP;
-    const int64_t p = it.x % NP;
-    const int cnt = it.z;
     const int i16 = lane & 15, grp = lane >> 4;
-    const bool live = i16 < cnt;
-    const int2 pr = a.sorted[it.y + (live ? i16 : 0)];
-    const int64_t row = pr.x;
-    const int rank = pr.y;
-    const RowLevel rl = row_level(a, row, l);
-    const int32_t nc = live ? (rank < rl.m ? a.b : rl.o) : 0;
-    const float M = a.stat[row].m_cur;
-    const float *zr = a.z + row * a.zs + rank * a.b;
-
-    int32_t orow[4], orank[4];
-    #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        orow[v] = __shfl((int32_t)row, 4 * grp + v);
-        orank[v] = __shfl(rank, 4 * grp + v);
-    }
-
-    const bf16_t *vals = level_rows(tv, true, l, g, D);
-    const int64_t nexist = a.length / a.pw[l];
-    const int64_t c0 = p * a.b;
     f32x4 acc[NT];
     #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kc = 0; kc < a.b; kc += 32) {
-        float w[8];
-        #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int c = kc + 8 * grp + v;
-            const float zz = c < nc ? zr[c] : -INFINITY;
-            w[v] = zz == -INFINITY ? 0.f : __expf(zz - M);
-        }
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+        const int kc = 32 * kk;
         bf16x8 ph, pl;
-        split8(w, ph, pl);
+        split8(w[kk], ph, pl);
         u16x8 raw[8];
         #pragma unroll
         for (int v = 0; v < 8; ++v) {
             const int c = kc + 8 * grp + v;
-            if (c < a.b && c0 + c < nexist) {
-                const bf16_t *vp = vals + (c0 + c) * D + NT * i16;
-                if constexpr (NT == 8) {
-                    const uint4 x = *reinterpret_cast<const uint4 *>(vp);
-                    raw[v] = __builtin_bit_cast(u16x8, x);
-                } else {
-                    const uint2 x = *reinterpret_cast<const uint2 *>(vp);
-                    raw[v] = u16x8{(unsigned short)(x.x & 0xFFFF), (unsigned short)(x.x >> 16),
-                                   (unsigned short)(x.y & 0xFFFF), (unsigned short)(x.y >> 16),
-                                   0, 0, 0, 0};
-                }
+            const bool ok = c < a.b && c0 + c < nexist;
+            const bf16_t *vp = vals + (ok ? c0 + c : 0) * D + NT * i16;
+            if constexpr (NT == 8) {
+                const uint4 x = ok ? *reinterpret_cast<const uint4 *>(vp) : make_uint4(0u, 0u, 0u, 0u);
+                raw[v] = __builtin_bit_cast(u16x8, x);
             } else {
-                raw[v] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                const uint2 x = ok ? *reinterpret_cast<const uint2 *>(vp) : make_uint2(0u, 0u);
+                raw[v] = u16x8{(unsigned short)(x.x & 0xFFFF), (unsigned short)(x.x >> 16),
+                               (unsigned short)(x.y & 0xFFFF), (unsigned short)(x.y >> 16), 0, 0, 0, 0};
             }
         }
         #pragma unroll
@@ -513,8 +552,8 @@ __global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t N
     }
     #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        if (4 * grp + v < cnt) {
-            float *dst = a.partial + ((int64_t)orow[v] * (a.k + 1) + orank[v]) * D + NT * i16;
+        if (4 * grp + v < it.cnt) {
+            float *dst = slice + ((int64_t)it.orow[v] * (a.k + 1) + it.orank[v]) * D + NT * i16;
             float o[NT];
             #pragma unroll
             for (int t = 0; t < NT; ++t) o[t] = acc[t][v];
@@ -523,47 +562,147 @@ __global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t N
     }
 }
 
-// ----------------------------------------------------------------- final --
-__global__ __launch_bounds__(256) void tp_final(TP a, DebugView dbg) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + w;
-    if (row >= a.rows) return;
-    const RowStat st = a.stat[row];
-    const int D = a.D;
-    const int npp = a.np[row];
-    const float sa = st.m_acc == -INFINITY ? 0.f : __expf(st.m_acc - st.m_cur);
-    const float inv = 1.f / st.l;
-    const float *ac = a.acc + row * D;
-    const float *pa = a.partial + row * (a.k + 1) * D;
-    for (int d = lane; d < D; d += 64) {
-        float v = ac[d] * sa;
-        for (int r = 0; r < npp; ++r) v += pa[r * D + d];
-        v *= inv;
-        if (a.out_bf16)
-            static_cast<bf16_t *>(a.out)[row * D + d] = (bf16_t)f32_to_bf16(v);
-        else
-            static_cast<float *>(a.out)[row * D + d] = v;
+// exp(z - m) for this lane's children given its logits (-inf: not an entry);
+// m and l reduced over the pair's four lane groups; lane group 0 stores (m, l).
+template <int KC>
+__device__ __forceinline__ void pair_softmax(const TP &a, const Item &it, int l, int lane, float (*w)[8]) {
+    float m = -INFINITY;
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) m = fmaxf(m, w[kk][v]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float sum = 0.f;
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float e = w[kk][v] == -INFINITY ? 0.f : __expf(w[kk][v] - m);
+            w[kk][v] = e;
+            sum += e;
+        }
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    const int i16 = lane & 15;
+    if (lane < 16 && i16 < it.cnt)
+        a.pml[((int64_t)l * a.rows_cap + it.pr.x) * (a.k + 1) + it.pr.y] = make_float2(m, sum);
+}
+
+template <int D, int KC>
+__global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t NP) {
+    const int lane = threadIdx.x & 63;
+    Item it;
+    if (!load_item(a, NP, lane, it)) return;
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int32_t nc = i16 < it.cnt ? it.pr.w : 0;
+    const float *zr = a.z + (int64_t)it.pr.x * a.zs + it.pr.y * a.b;
+    float w[KC][8];
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int c = 32 * kk + 8 * grp + v;
+            w[kk][v] = c < nc ? zr[c] : -INFINITY;
+        }
+    pair_softmax<KC>(a, it, l, lane, w);
+    pv_tiles<D, KC>(a, it, level_rows(tv, true, l, it.g, D), it.p * a.b, a.length / a.pw[l], lane, w,
+                    a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D);
+}
+
+// ---------------------------------------------------------------- attend --
+// Level 0: the tokens of each parent scored against its pairs, the pairs'
+// softmax states and their P.V in one pass (logits go through LDS to move from
+// the score tile's layout to the P.V operand's).
+template <int D, int KC>
+__global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) {
+    __shared__ float zt[4][kTile][32 * KC + 1];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    Item it;
+    if (!load_item(a, NP, lane, it)) return;
+    const int i16 = lane & 15, grp = lane >> 4;
+    bf16x8 ah[D / 32], al[D / 32];
+    query_operands<D>(tv, a, it, lane, ah, al);
+    const int64_t nexist = a.length;
+    const int64_t c0 = it.p * a.b;
+    const bf16_t *keys = level_rows(tv, false, 0, it.g, D);
+    float (*zw)[32 * KC + 1] = zt[wv];
+    for (int ct = 0; ct < 32 * KC; ct += 16) {
+        const f32x4 acc = ct < a.b ? score_tile<D>(tv, keys, c0, nexist, a.b, ct, lane, ah, al)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int c = ct + i16;
+        #pragma unroll
+        for (int v = 0; v < 4; ++v) zw[4 * grp + v][c] = c < it.onc[v] ? a.scale * acc[v] : -INFINITY;
     }
-    if (dbg.n_keys && lane == 0) dbg.n_keys[row] = st.n_keys;
+    __threadfence_block();
+    float w[KC][8];
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) w[kk][v] = zw[i16][32 * kk + 8 * grp + v];
+    pair_softmax<KC>(a, it, 0, lane, w);
+    pv_tiles<D, KC>(a, it, level_rows(tv, true, 0, it.g, D), c0, nexist, lane, w, a.partial);
+}
+
+// ----------------------------------------------------------------- final --
+// Merges every pair state (m, l, acc) of a row: with M the largest m,
+// out = sum exp(m - M) acc / sum exp(m - M) l.  One thread per (row, 4 dimensions).
+__global__ __launch_bounds__(256) void tp_final(TP a) {
+    const int D4 = a.D / 4;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t / D4;
+    const int j = (int)(t % D4);
+    if (row >= a.rows) return;
+    const int64_t pslice = a.rows_cap * (a.k + 1);
+    float M = -INFINITY;
+    for (int l = 0; l <= a.top; ++l) {
+        const int np = a.nplev[row * a.lv + l];
+        const float2 *ml = a.pml + l * pslice + row * (a.k + 1);
+        for (int r = 0; r < np; ++r) M = fmaxf(M, ml[r].x);
+    }
+    float L = 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 *base = reinterpret_cast<const float4 *>(a.partial) + row * (a.k + 1) * D4 + j;
+    for (int l = 0; l <= a.top; ++l) {
+        const int np = a.nplev[row * a.lv + l];
+        const float2 *ml = a.pml + l * pslice + row * (a.k + 1);
+        const float4 *pa = base + l * pslice * D4;
+        #pragma unroll 4
+        for (int r = 0; r < np; ++r) {
+            const float2 s = ml[r];
+            if (s.x == -INFINITY) continue;
+            const float e = __expf(s.x - M);
+            const float4 x = pa[r * D4];
+            L += e * s.y;
+            v.x += e * x.x; v.y += e * x.y; v.z += e * x.z; v.w += e * x.w;
+        }
+    }
+    const float inv = 1.f / L;
+    const float o[4] = {v.x * inv, v.y * inv, v.z * inv, v.w * inv};
+    if (a.out_bf16)
+        Vec<bf16_t, 4>::store(static_cast<bf16_t *>(a.out) + row * a.D + 4 * j, o);
+    else
+        Vec<float, 4>::store(static_cast<float *>(a.out) + row * a.D + 4 * j, o);
 }
 
 // ------------------------------------------------------------------ host --
 struct Plan {
     int64_t rows;        // rows per pass
     int64_t nb;          // buckets at the widest level
-    int32_t zs;
-    size_t off_z, off_par0, off_par1, off_mk0, off_mk1, off_np, off_pp, off_cnt, off_offs, off_ioff,
-        off_sorted, off_items, off_nitems, off_partial, off_acc, off_stat, total;
+    int32_t zs, lv;
+    size_t off_z, off_par0, off_par1, off_mk0, off_mk1, off_pp, off_cnt, off_offs, off_ioff, off_bsum,
+        off_sorted, off_items, off_nitems, off_partial, off_pml, off_nplev, total;
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 Plan make_plan(int64_t rows, int32_t Hkv, int32_t D, int32_t b, int32_t k, int32_t maxc,
-               int64_t capacity) {
+               int64_t capacity, int32_t n_levels) {
     Plan P{};
     P.rows = rows;
     P.nb = (int64_t)Hkv * (capacity / b + 1);
     P.zs = (maxc + 3) / 4 * 4;
+    P.lv = n_levels + 1;
     const int64_t pairs = rows * (k + 1);
     const int64_t items = pairs / kTile + P.nb + 1;
     size_t o = 0;
@@ -573,17 +712,17 @@ Plan make_plan(int64_t rows, int32_t Hkv, int32_t D, int32_t b, int32_t k, int32
     P.off_par1 = put((size_t)rows * k * 4);
     P.off_mk0 = put((size_t)rows * 4);
     P.off_mk1 = put((size_t)rows * 4);
-    P.off_np = put((size_t)rows * 4);
     P.off_pp = put((size_t)pairs * 4);
     P.off_cnt = put((size_t)P.nb * 4);
     P.off_offs = put((size_t)(P.nb + 1) * 4);
     P.off_ioff = put((size_t)(P.nb + 1) * 4);
-    P.off_sorted = put((size_t)pairs * 8);
+    P.off_bsum = put((size_t)(P.nb / kScanChunk + 1) * 8);
+    P.off_sorted = put((size_t)pairs * 16);
     P.off_items = put((size_t)items * 16);
     P.off_nitems = put(16);
-    P.off_partial = put((size_t)pairs * D * 4);
-    P.off_acc = put((size_t)rows * D * 4);
-    P.off_stat = put((size_t)rows * sizeof(RowStat));
+    P.off_partial = put((size_t)P.lv * pairs * D * 4);
+    P.off_pml = put((size_t)P.lv * pairs * 8);
+    P.off_nplev = put((size_t)rows * P.lv * 4);
     P.total = o;
     return P;
 }
@@ -619,45 +758,74 @@ hipError_t launch_select(const TP &a, const DebugView &dbg, int l, int32_t maxc,
     return launch_select_t<0>(a, dbg, l, smw, s);
 }
 
-template <int D>
+hipError_t launch_count(const TP &a, int l, int32_t NP, hipStream_t s) {
+    const int64_t per_head = a.rows / a.Hq * a.G;
+    if (NP <= kHistSplit) {
+        hipLaunchKernelGGL(tp_count, dim3((unsigned)((per_head + 255) / 256), (unsigned)a.Hkv), dim3(256),
+                           (size_t)NP * 4, s, a, l, NP, 0);
+    } else {
+        hipLaunchKernelGGL(tp_count, dim3((unsigned)((NP + kRange - 1) / kRange), (unsigned)a.Hkv),
+                           dim3(1024), (size_t)kRange * 4, s, a, l, NP, 1);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KC>
 hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_ctx, const Plan &P,
                     int32_t maxc, hipStream_t s) {
     const int64_t rows = a.rows;
     {
-        const int64_t n = std::max<int64_t>(std::max<int64_t>(rows * D, P.nb), rows * a.n_levels * a.k);
+        const int64_t n = std::max<int64_t>(std::max<int64_t>(rows, P.nb), rows * a.n_levels * a.k);
         const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
         hipLaunchKernelGGL(tp_init, dim3((unsigned)blocks), dim3(256), 0, s, a, dbg, P.nb);
     }
     const int smw = (int)select_smem_wave(a.zs, a.k);
-    const int64_t per_head = rows / a.Hq * a.G;
+    hipError_t e;
     for (int l = a.top; l >= 0; --l) {
         const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
         const int64_t nb = (int64_t)a.Hkv * NP;
-        const int use_lds = NP <= kHistMax;
-        hipLaunchKernelGGL(tp_count, dim3((unsigned)((per_head + 255) / 256), (unsigned)a.Hkv), dim3(256),
-                           use_lds ? (size_t)NP * 4 : 0, s, a, l, NP, use_lds);
-        hipLaunchKernelGGL(tp_scan, dim3(1), dim3(1024), 0, s, a, nb);
-        hipLaunchKernelGGL(tp_scatter, dim3((unsigned)((rows + nb + 255) / 256)), dim3(256), 0, s, a, l, NP,
-                           nb);
+        const int64_t nchunks = (nb + kScanChunk - 1) / kScanChunk;
+        if ((e = launch_count(a, l, NP, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL(tp_scan_sums, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+        hipLaunchKernelGGL(tp_scan_chunks, dim3(1), dim3(256), 0, s, a, nb, nchunks);
+        hipLaunchKernelGGL(tp_scan_write, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+        hipLaunchKernelGGL(tp_scatter, dim3((unsigned)((rows + nb + 255) / 256)), dim3(256), 0, s, a, dbg, l,
+                           NP, nb);
         const int64_t pairs = rows * (int64_t)std::min(a.k + 1, (int)NP);
         const int64_t items = pairs / kTile + nb + 1;
         const unsigned ib = (unsigned)((items + 3) / 4);
-        hipLaunchKernelGGL(tp_score<D>, dim3(ib), dim3(256), 0, s, tv, a, l, NP);
-        hipError_t e = launch_select(a, dbg, l, maxc, smw, s);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(tp_pv<D>, dim3(ib), dim3(256), 0, s, tv, a, l, NP);
+        if (l == 0) {
+            hipLaunchKernelGGL((tp_attend<D, KC>), dim3(ib), dim3(256), 0, s, tv, a, NP);
+        } else {
+            hipLaunchKernelGGL(tp_score<D>, dim3(ib), dim3(256), 0, s, tv, a, l, NP);
+            if ((e = launch_select(a, dbg, l, maxc, smw, s)) != hipSuccess) return e;
+            hipLaunchKernelGGL((tp_pv<D, KC>), dim3(ib), dim3(256), 0, s, tv, a, l, NP);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(tp_final, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, dbg);
+    hipLaunchKernelGGL(tp_final, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_pass_d(const TreeView &tv, const TP &a, const DebugView &dbg, int64_t max_ctx,
+                      const Plan &P, int32_t maxc, hipStream_t s) {
+    switch ((a.b + 31) / 32) {
+        case 1: return run_pass<D, 1>(tv, a, dbg, max_ctx, P, maxc, s);
+        case 2: return run_pass<D, 2>(tv, a, dbg, max_ctx, P, maxc, s);
+        case 3: return run_pass<D, 3>(tv, a, dbg, max_ctx, P, maxc, s);
+        default: return run_pass<D, 4>(tv, a, dbg, max_ctx, P, maxc, s);
+    }
 }
 
 }  // namespace
 
 size_t tiled_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
-                             int32_t maxc, int64_t capacity) {
-    return make_plan(pass_rows(rows, Hq), Hkv, D, b, k, maxc, capacity).total;
+                             int32_t maxc, int64_t capacity, int32_t n_levels) {
+    return make_plan(pass_rows(rows, Hq), Hkv, D, b, k, maxc, capacity, n_levels).total;
 }
+
+int32_t tiled_max_fanout() { return kMaxFanout; }
 
 size_t tiled_select_lds_bytes(int32_t maxc, int32_t k) {
     return 4 * select_smem_wave((maxc + 3) / 4 * 4, k);
@@ -667,17 +835,19 @@ hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs
                                 int64_t length, int64_t capacity, const DebugView &dbg, void *ws,
                                 hipStream_t s) {
     const int64_t per = pass_rows(da.rows, da.Hq);
-    const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity);
+    const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
     unsigned char *w = static_cast<unsigned char *>(ws);
     TP a{};
     a.Hq = da.Hq;
     a.G = da.G;
     a.Hkv = Hkv;
     a.D = D;
+    a.rows_cap = P.rows;
     a.ctx_step = da.ctx_step;
     a.b = da.b;
     a.k = da.k;
     a.zs = P.zs;
+    a.lv = P.lv;
     a.scale = da.scale;
     a.out_bf16 = da.out_bf16;
     a.n_levels = tv.n_levels;
@@ -687,17 +857,17 @@ hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs
     a.par[1] = reinterpret_cast<int32_t *>(w + P.off_par1);
     a.mk[0] = reinterpret_cast<int32_t *>(w + P.off_mk0);
     a.mk[1] = reinterpret_cast<int32_t *>(w + P.off_mk1);
-    a.np = reinterpret_cast<int32_t *>(w + P.off_np);
     a.pairpos = reinterpret_cast<int32_t *>(w + P.off_pp);
     a.counts = reinterpret_cast<int32_t *>(w + P.off_cnt);
     a.offs = reinterpret_cast<int32_t *>(w + P.off_offs);
     a.itemoff = reinterpret_cast<int32_t *>(w + P.off_ioff);
-    a.sorted = reinterpret_cast<int2 *>(w + P.off_sorted);
+    a.bsum = reinterpret_cast<int2 *>(w + P.off_bsum);
+    a.sorted = reinterpret_cast<int4 *>(w + P.off_sorted);
     a.items = reinterpret_cast<int4 *>(w + P.off_items);
     a.n_items = reinterpret_cast<int32_t *>(w + P.off_nitems);
     a.partial = reinterpret_cast<float *>(w + P.off_partial);
-    a.acc = reinterpret_cast<float *>(w + P.off_acc);
-    a.stat = reinterpret_cast<RowStat *>(w + P.off_stat);
+    a.pml = reinterpret_cast<float2 *>(w + P.off_pml);
+    a.nplev = reinterpret_cast<int32_t *>(w + P.off_nplev);
     const size_t esz_q = 2, esz_o = da.out_bf16 ? 2 : 4;
     for (int64_t r0 = 0; r0 < da.rows; r0 += per) {
         const int64_t rows = std::min(per, da.rows - r0);
@@ -717,8 +887,8 @@ hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs
         if (d.selected) d.selected += r0 * tv.n_levels * da.k;
         if (d.kth_gap) d.kth_gap += r0 * tv.n_levels;
         if (d.n_keys) d.n_keys += r0;
-        const hipError_t e = D == 128 ? run_pass<128>(tv, a, d, max_ctx, P, da.max_cand, s)
-                                      : run_pass<64>(tv, a, d, max_ctx, P, da.max_cand, s);
+        const hipError_t e = D == 128 ? run_pass_d<128>(tv, a, d, max_ctx, P, da.max_cand, s)
+                                      : run_pass_d<64>(tv, a, d, max_ctx, P, da.max_cand, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

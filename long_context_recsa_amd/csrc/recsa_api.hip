@@ -13,8 +13,9 @@ namespace recsa {
 size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D);
 int32_t descend_max_candidates();
 size_t tiled_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
-                             int32_t maxc, int64_t capacity);
+                             int32_t maxc, int64_t capacity, int32_t n_levels);
 size_t tiled_select_lds_bytes(int32_t maxc, int32_t k);
+int32_t tiled_max_fanout();
 hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                 int64_t length, int64_t capacity, const DebugView &dbg, void *ws,
                                 hipStream_t s);
@@ -48,12 +49,12 @@ size_t elem_bytes(int32_t dt) { return dt == RECSA_BF16 ? 2 : 4; }
 
 // Prefill of at least this many rows (queries x query heads) over bf16 storage
 // runs parent-major (rows grouped by the parents they keep, bf16 MFMA); fewer
-// rows, or fp32 storage, run one workgroup per row.  RECSA_PREFILL_PATH=rowwise
+// rows, fp32 storage or a fanout above 128 run one workgroup per row.  RECSA_PREFILL_PATH=rowwise
 // or =tiled forces one of the two.
 constexpr int64_t kTiledMinRows = 4096;
 
 bool use_tiled(const recsa_params *p, int64_t rows) {
-    if (p->store_dtype != RECSA_BF16) return false;
+    if (p->store_dtype != RECSA_BF16 || p->fanout_b > tiled_max_fanout()) return false;
     if (const char *e = getenv("RECSA_PREFILL_PATH")) {
         if (strcmp(e, "rowwise") == 0) return false;
         if (strcmp(e, "tiled") == 0) return true;
@@ -290,7 +291,7 @@ size_t recsa_workspace_bytes(const recsa_params *p, int64_t max_rows) {
     if (!use_tiled(p, max_rows)) return 0;
     const Layout L = make_layout(p);
     return tiled_workspace_bytes(max_rows, p->n_q_heads, p->n_kv_heads, p->head_dim, p->fanout_b,
-                                 p->budget_k, (int32_t)L.max_cand, p->capacity);
+                                 p->budget_k, (int32_t)L.max_cand, p->capacity, L.n_levels);
 }
 
 recsa_status recsa_build_tree(const recsa_params *p, recsa_tree_desc *desc, int64_t length,
