@@ -77,8 +77,8 @@ struct TP {
     int32_t *offs;             // [nb+1]
     int32_t *itemoff;          // [nb+1]
     int2 *bsum;                // [nb / kScanChunk + 1]
-    int4 *sorted;              // [pairs]: (row, rank, query position, children) grouped by parent
-    int4 *items;               // (bucket, first pair, pairs, 0)
+    int4 *sorted;              // [items][16]: (row, rank, query position, children) by parent
+    int4 *items;               // (bucket, 0, pairs, 0)
     int32_t *n_items;
     float *partial;            // [lv][rows_cap][k+1][D]: sum of exp(z - m) v per pair
     float2 *pml;               // [lv][rows_cap][k+1]: (m, sum of exp(z - m)) per pair
@@ -334,130 +334,315 @@ __global__ __launch_bounds__(256) void tp_scatter(TP a, DebugView dbg, int l, in
         if (dbg.n_keys) dbg.n_keys[row] += n;
         for (int r = 0; r < np; ++r) {
             const int64_t bkt = g * NP + parent_of(a, row, l, r, rl);
-            a.sorted[a.offs[bkt] + a.pairpos[row * (a.k + 1) + r]] =
+            a.sorted[(int64_t)a.itemoff[bkt] * kTile + a.pairpos[row * (a.k + 1) + r]] =
                 make_int4((int32_t)row, r, n - r * a.b, r < rl.m ? a.b : rl.o);
         }
     } else if (t - a.rows < nb) {
         const int64_t bkt = t - a.rows;
-        const int32_t o0 = a.offs[bkt], c = a.offs[bkt + 1] - o0, i0 = a.itemoff[bkt];
+        const int32_t c = a.offs[bkt + 1] - a.offs[bkt], i0 = a.itemoff[bkt];
         for (int32_t s = 0; s < c; s += kTile)
-            a.items[i0 + s / kTile] = make_int4((int32_t)bkt, o0 + s, min(kTile, c - s), 0);
+            a.items[i0 + s / kTile] = make_int4((int32_t)bkt, 0, min(kTile, c - s), 0);
+        for (int32_t s = c; s % kTile != 0; ++s)
+            a.sorted[(int64_t)i0 * kTile + s] = make_int4(0, 0, 0, 0);
     }
 }
 
-// ----------------------------------------------------------------- score --
-// One wave per item: up to 16 pairs of one parent against its b children.
-// MFMA 16x16x32: lane L supplies A row L%16 and B column L%16 for the 8
-// k-slots of group L/16.  The k-slots are mapped to dimensions so that a lane
-// group owns RoPE pairs [grp*D/8, grp*D/8 + D/8) of both halves: k-slot
-// (ks, v) is dimension grp*D/8 + 8*ks + v for ks < D/64 and its partner
-// (+ D/2) at ks + D/64.  Every rotation stays inside a lane and each row
-// slice is a contiguous load.
+// ----------------------------------------------------------------- items --
+// An item is a tile of up to 16 pairs of one (KV head, parent) bucket; its
+// pairs are sorted[16 i .. 16 i + 15] (unused slots: row 0, rank 0, position
+// 0, no children).  The kernels over items run persistent waves that fetch the
+// next item's records while working on the current one, and issue every load
+// of an item before its arithmetic.
+//
+// MFMA 16x16x32 (bf16 in, fp32 accumulate): lane L supplies A row L%16 and B
+// column L%16 for the 8 k-slots of lane group grp = L/16, and gets D rows
+// 4*grp .. 4*grp + 3 of column L%16.
 struct Item {
     int g;          // KV head
     int64_t p;      // parent node
     int cnt;        // pairs
-    int4 pr;        // this lane's pair (lane % 16): row, rank, query position, children
-    int32_t orow[4], orank[4], onc[4];   // the output rows of this lane: pairs 4*(lane/16) + v
+    int4 pr;        // this lane's pair (L%16): row, rank, query position, children
+    int32_t orow[4], orank[4], onc[4];   // pairs 4*grp + v, the D rows of this lane
 };
 
-__device__ __forceinline__ bool load_item(const TP &a, int32_t NP, int lane, Item &it) {
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= *a.n_items) return false;
-    const int4 rec = a.items[item];
-    it.g = rec.x / NP;
-    it.p = rec.x % NP;
-    it.cnt = rec.z;
+template <typename F>
+__device__ __forceinline__ void for_items(const TP &a, int32_t NP, int lane, F &&body) {
+    const int64_t n = *a.n_items;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (item >= n) return;
     const int i16 = lane & 15, grp = lane >> 4;
-    it.pr = a.sorted[rec.y + (i16 < it.cnt ? i16 : 0)];
-    #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        it.orow[v] = __shfl(it.pr.x, 4 * grp + v);
-        it.orank[v] = __shfl(it.pr.y, 4 * grp + v);
-        it.onc[v] = 4 * grp + v < it.cnt ? __shfl(it.pr.w, 4 * grp + v) : 0;
+    int4 rec = a.items[item];
+    int4 pr = a.sorted[item * kTile + i16];
+    for (;;) {
+        const int64_t next = item + nw;
+        int4 rn = rec, pn = pr;
+        if (next < n) {
+            rn = a.items[next];
+            pn = a.sorted[next * kTile + i16];
+        }
+        Item it;
+        it.g = rec.x / NP;
+        it.p = rec.x % NP;
+        it.cnt = rec.z;
+        it.pr = pr;
+        #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            it.orow[v] = __shfl(pr.x, 4 * grp + v);
+            it.orank[v] = __shfl(pr.y, 4 * grp + v);
+            it.onc[v] = __shfl(pr.w, 4 * grp + v);
+        }
+        body(it);
+        if (next >= n) break;
+        item = next;
+        rec = rn;
+        pr = pn;
     }
-    return true;
 }
 
-// The pairs' rank-rotated queries as MFMA A operands, high and low bf16 parts.
+// cos/sin of child offsets 0..b-1 into LDS, rows padded by two pairs against bank conflicts
+constexpr int crot_stride(int D) { return D / 2 + 2; }
+
+__device__ __forceinline__ void load_crot(const TreeView &tv, int b, int D, float2 *crot) {
+    const int H = D / 2;
+    for (int i = threadIdx.x; i < b * H; i += blockDim.x) crot[(i / H) * (H + 2) + i % H] = tv.rope[i];
+    __syncthreads();
+}
+
+// Query slices of this lane's pair: k-slot (ks, v) of lane group grp is dimension
+// grp*D/8 + 8*ks + v for ks < D/64 and its RoPE partner (+ D/2) at ks + D/64, so
+// rotations stay inside a lane and row slices are contiguous.
 template <int D>
-__device__ __forceinline__ void query_operands(const TreeView &tv, const TP &a, const Item &it, int lane,
-                                               bf16x8 *ah, bf16x8 *al) {
+struct QRaw {
+    uint4 q[2 * (D / 64)];
+    float4 cs[4 * (D / 64)];
+};
+
+template <int D>
+__device__ __forceinline__ void load_query(const TreeView &tv, const TP &a, const Item &it, int lane,
+                                           QRaw<D> &r) {
     constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
-    const int i16 = lane & 15, grp = lane >> 4;
+    const int grp = lane >> 4;
     const bf16_t *qr = a.q + (int64_t)it.pr.x * D + grp * PG;
-    const float2 *cs = tv.rope + (int64_t)it.pr.z * H + grp * PG;
-    const float live = i16 < it.cnt ? 1.f : 0.f;
+    const float4 *cs = reinterpret_cast<const float4 *>(tv.rope + (int64_t)it.pr.z * H + grp * PG);
     #pragma unroll
     for (int pc = 0; pc < KS1; ++pc) {
-        float q1[8], q2[8], c[8], sn[8], u1[8], u2[8];
-        Vec<bf16_t, 8>::load(qr + 8 * pc, q1);
-        Vec<bf16_t, 8>::load(qr + H + 8 * pc, q2);
-        load_cs<8>(cs + 8 * pc, c, sn);
+        r.q[2 * pc] = *reinterpret_cast<const uint4 *>(qr + 8 * pc);
+        r.q[2 * pc + 1] = *reinterpret_cast<const uint4 *>(qr + H + 8 * pc);
         #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            u1[j] = live * (q1[j] * c[j] - q2[j] * sn[j]);
-            u2[j] = live * (q2[j] * c[j] + q1[j] * sn[j]);
-        }
-        split8(u1, ah[pc], al[pc]);
-        split8(u2, ah[pc + KS1], al[pc + KS1]);
+        for (int u = 0; u < 4; ++u) r.cs[4 * pc + u] = cs[4 * pc + u];
     }
 }
 
-// Logits of pairs 4*(lane/16) + v against child ct + lane%16 (unscaled).
+__device__ __forceinline__ void unpack8(uint4 x, float *f) {
+    f[0] = bf16_to_f32(x.x & 0xFFFFu); f[1] = bf16_to_f32(x.x >> 16);
+    f[2] = bf16_to_f32(x.y & 0xFFFFu); f[3] = bf16_to_f32(x.y >> 16);
+    f[4] = bf16_to_f32(x.z & 0xFFFFu); f[5] = bf16_to_f32(x.z >> 16);
+    f[6] = bf16_to_f32(x.w & 0xFFFFu); f[7] = bf16_to_f32(x.w >> 16);
+}
+
+// rotate (x1, x2) by the 8 (cos, sin) pairs in cs, times `live`, and split to bf16
+__device__ __forceinline__ void rotate_split(uint4 a1, uint4 a2, const float4 *cs, float live,
+                                             bf16x8 &h1, bf16x8 &l1, bf16x8 &h2, bf16x8 &l2) {
+    float x1[8], x2[8], r1[8], r2[8];
+    unpack8(a1, x1);
+    unpack8(a2, x2);
+    #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float4 v = cs[u];
+        r1[2 * u] = live * (x1[2 * u] * v.x - x2[2 * u] * v.y);
+        r2[2 * u] = live * (x2[2 * u] * v.x + x1[2 * u] * v.y);
+        r1[2 * u + 1] = live * (x1[2 * u + 1] * v.z - x2[2 * u + 1] * v.w);
+        r2[2 * u + 1] = live * (x2[2 * u + 1] * v.z + x1[2 * u + 1] * v.w);
+    }
+    split8(r1, h1, l1);
+    split8(r2, h2, l2);
+}
+
 template <int D>
-__device__ __forceinline__ f32x4 score_tile(const TreeView &tv, const bf16_t *keys, int64_t c0,
-                                            int64_t nexist, int b, int ct, int lane, const bf16x8 *ah,
-                                            const bf16x8 *al) {
+__device__ __forceinline__ void query_operands(const QRaw<D> &r, const Item &it, int lane, bf16x8 *ah,
+                                               bf16x8 *al) {
+    constexpr int KS1 = D / 64;
+    const float live = (lane & 15) < it.cnt ? 1.f : 0.f;
+    #pragma unroll
+    for (int pc = 0; pc < KS1; ++pc)
+        rotate_split(r.q[2 * pc], r.q[2 * pc + 1], &r.cs[4 * pc], live, ah[pc], al[pc], ah[pc + KS1],
+                     al[pc + KS1]);
+}
+
+// Key slices of children 32*kk + 16*t + L%16 (t = 0, 1) in the same k-slot layout.
+template <int D>
+struct KRaw {
+    uint4 k[2][2 * (D / 64)];
+};
+
+template <int D>
+__device__ __forceinline__ void load_keys(const bf16_t *keys, int64_t c0, int64_t nexist, int b, int kk,
+                                          int lane, KRaw<D> &r) {
     constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
     const int i16 = lane & 15, grp = lane >> 4;
-    const int c = ct + i16;
+    #pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int c = 32 * kk + 16 * t + i16;
+        const bool ok = c < b && c0 + c < nexist;
+        const bf16_t *kp = keys + (ok ? c0 + c : 0) * D + grp * PG;
+        #pragma unroll
+        for (int pc = 0; pc < KS1; ++pc) {
+            r.k[t][2 * pc] = *reinterpret_cast<const uint4 *>(kp + 8 * pc);
+            r.k[t][2 * pc + 1] = *reinterpret_cast<const uint4 *>(kp + H + 8 * pc);
+        }
+    }
+}
+
+// Logits (unscaled) of pairs 4*grp + v against child 32*kk + 16*t + L%16.
+template <int D>
+__device__ __forceinline__ f32x4 score_tile(const KRaw<D> &r, int t, const float2 *crot, int64_t c0,
+                                            int64_t nexist, int b, int kk, int lane, const bf16x8 *ah,
+                                            const bf16x8 *al) {
+    constexpr int PG = D / 8, KS1 = D / 64;
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int c = 32 * kk + 16 * t + i16;
     const bool ok = c < b && c0 + c < nexist;
-    const bf16_t *kp = keys + (ok ? c0 + c : 0) * D + grp * PG;
-    const float2 *cs = tv.rope + (int64_t)(ok ? c : 0) * H + grp * PG;
+    const float4 *cs = reinterpret_cast<const float4 *>(crot + (ok ? c : 0) * crot_stride(D) + grp * PG);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
     for (int pc = 0; pc < KS1; ++pc) {
-        float k1[8], k2[8], cc[8], ss[8], r1[8], r2[8];
-        Vec<bf16_t, 8>::load(kp + 8 * pc, k1);
-        Vec<bf16_t, 8>::load(kp + H + 8 * pc, k2);
-        load_cs<8>(cs + 8 * pc, cc, ss);
-        const float live = ok ? 1.f : 0.f;
+        float4 c4[4];
         #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            r1[j] = live * (k1[j] * cc[j] - k2[j] * ss[j]);
-            r2[j] = live * (k2[j] * cc[j] + k1[j] * ss[j]);
-        }
-        bf16x8 bh, bl;
-        split8(r1, bh, bl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc], bh, acc, 0, 0, 0);
-        split8(r2, bh, bl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc + KS1], bh, acc, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) c4[u] = cs[4 * pc + u];
+        bf16x8 h1, l1, h2, l2;
+        rotate_split(r.k[t][2 * pc], r.k[t][2 * pc + 1], c4, ok ? 1.f : 0.f, h1, l1, h2, l2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], h1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], l1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc], h1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], h2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc + KS1], l2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc + KS1], h2, acc, 0, 0, 0);
     }
     return acc;
 }
 
+// Value slices of children 32*kk + 8*grp + v: lane column L%16 of output tile
+// t is dimension (D/16)*(L%16) + t, so a lane reads D/16 contiguous bf16 per child.
 template <int D>
-__global__ __launch_bounds__(256) void tp_score(TreeView tv, TP a, int l, int32_t NP) {
-    const int lane = threadIdx.x & 63;
-    Item it;
-    if (!load_item(a, NP, lane, it)) return;
-    bf16x8 ah[D / 32], al[D / 32];
-    query_operands<D>(tv, a, it, lane, ah, al);
-    const bf16_t *keys = level_rows(tv, false, l, it.g, D);
-    const int64_t nexist = a.length / a.pw[l];
-    const int64_t c0 = it.p * a.b;
-    for (int ct = 0; ct < a.b; ct += 16) {
-        const f32x4 acc = score_tile<D>(tv, keys, c0, nexist, a.b, ct, lane, ah, al);
-        const int c = ct + (lane & 15);
-        #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (c < it.onc[v]) a.z[(int64_t)it.orow[v] * a.zs + it.orank[v] * a.b + c] = a.scale * acc[v];
+struct VRaw {
+    uint4 v[8];     // D/16 bf16 of each child (upper half unused for D = 64)
+};
+
+template <int D>
+__device__ __forceinline__ void load_values(const bf16_t *vals, int64_t c0, int64_t nexist, int b, int kk,
+                                            int lane, VRaw<D> &r) {
+    constexpr int NT = D / 16;
+    const int i16 = lane & 15, grp = lane >> 4;
+    #pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int c = 32 * kk + 8 * grp + v;
+        const bool ok = c < b && c0 + c < nexist;
+        const bf16_t *vp = vals + (ok ? c0 + c : 0) * D + NT * i16;
+        uint4 x;
+        if constexpr (NT == 8) {
+            x = *reinterpret_cast<const uint4 *>(vp);
+        } else {
+            const uint2 y = *reinterpret_cast<const uint2 *>(vp);
+            x = make_uint4(y.x, y.y, 0u, 0u);
+        }
+        r.v[v] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
     }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_accumulate(const VRaw<D> &r, const float *w, f32x4 *acc) {
+    constexpr int NT = D / 16;
+    bf16x8 ph, pl;
+    split8(w, ph, pl);
+    #pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        u16x8 bt;
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const uint32_t word = t < 2 ? r.v[v].x : t < 4 ? r.v[v].y : t < 6 ? r.v[v].z : r.v[v].w;
+            bt[v] = (unsigned short)((t & 1) ? (word >> 16) : (word & 0xFFFFu));
+        }
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bt);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bv, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bv, acc[t], 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_store(const TP &a, const Item &it, int lane, const f32x4 *acc, float *slice) {
+    constexpr int NT = D / 16;
+    const int i16 = lane & 15, grp = lane >> 4;
+    #pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        if (4 * grp + v < it.cnt) {
+            float *dst = slice + ((int64_t)it.orow[v] * (a.k + 1) + it.orank[v]) * D + NT * i16;
+            float o[NT];
+            #pragma unroll
+            for (int t = 0; t < NT; ++t) o[t] = acc[t][v];
+            Vec<float, NT>::store(dst, o);
+        }
+    }
+}
+
+// exp(z - m) of this lane's children given their logits (-inf: not an entry),
+// with m and l reduced over the pair's four lane groups; lane group 0 stores (m, l).
+template <int KC>
+__device__ __forceinline__ void pair_softmax(const TP &a, const Item &it, int l, int lane, float (*w)[8]) {
+    float m = -INFINITY;
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) m = fmaxf(m, w[kk][v]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float sum = 0.f;
+    #pragma unroll
+    for (int kk = 0; kk < KC; ++kk)
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float e = w[kk][v] == -INFINITY ? 0.f : __expf(w[kk][v] - m);
+            w[kk][v] = e;
+            sum += e;
+        }
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    if (lane < 16 && lane < it.cnt)
+        a.pml[((int64_t)l * a.rows_cap + it.pr.x) * (a.k + 1) + it.pr.y] = make_float2(m, sum);
+}
+
+// ----------------------------------------------------------------- score --
+// Level l >= 1: each item's pairs against the parent's children; logits to z.
+template <int D, int KC>
+__global__ __launch_bounds__(256) void tp_score(TreeView tv, TP a, int l, int32_t NP) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float2 *crot = reinterpret_cast<float2 *>(smem);
+    load_crot(tv, a.b, D, crot);
+    const int lane = threadIdx.x & 63;
+    const int64_t nexist = a.length / a.pw[l];
+    for_items(a, NP, lane, [&](const Item &it) {
+        const bf16_t *keys = level_rows(tv, false, l, it.g, D);
+        const int64_t c0 = it.p * a.b;
+        QRaw<D> qr;
+        KRaw<D> kr;
+        load_query<D>(tv, a, it, lane, qr);
+        load_keys<D>(keys, c0, nexist, a.b, 0, lane, kr);
+        bf16x8 ah[D / 32], al[D / 32];
+        query_operands<D>(qr, it, lane, ah, al);
+        #pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            if (kk > 0) load_keys<D>(keys, c0, nexist, a.b, kk, lane, kr);
+            #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f32x4 acc = score_tile<D>(kr, t, crot, c0, nexist, a.b, kk, lane, ah, al);
+                const int c = 32 * kk + 16 * t + (lane & 15);
+                #pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (c < it.onc[v])
+                        a.z[(int64_t)it.orow[v] * a.zs + it.orank[v] * a.b + c] = a.scale * acc[v];
+            }
+        }
+    });
 }
 
 // ---------------------------------------------------------------- select --
@@ -505,143 +690,99 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
 }
 
 // -------------------------------------------------------------------- pv --
-// The softmax state of a pair's entries: m = max z, l = sum exp(z - m), and
-// sum exp(z - m) v over the parent's children on MFMA 16x16x32 with k =
-// children (lane group grp holds children 8*grp .. 8*grp + 7 of each 32) and
-// n = dimensions: lane column L%16 of tile t is dimension (D/16)*(L%16) + t, so
-// a lane reads D/16 contiguous bf16 of each child row and writes D/16
-// contiguous floats per pair.  `w` holds the lane's weights exp(z - m) for
-// children kc + 8*grp + v, kc = 0, 32, ...
-template <int D, int KC>
-__device__ __forceinline__ void pv_tiles(const TP &a, const Item &it, const bf16_t *vals, int64_t c0,
-                                         int64_t nexist, int lane, const float (*w)[8], float *slice) {
-    constexpr int NT = D / 16;
-    const int i16 = lane & 15, grp = lane >> 4;
-    f32x4 acc[NT];
-    #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-        const int kc = 32 * kk;
-        bf16x8 ph, pl;
-        split8(w[kk], ph, pl);
-        u16x8 raw[8];
-        #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int c = kc + 8 * grp + v;
-            const bool ok = c < a.b && c0 + c < nexist;
-            const bf16_t *vp = vals + (ok ? c0 + c : 0) * D + NT * i16;
-            if constexpr (NT == 8) {
-                const uint4 x = ok ? *reinterpret_cast<const uint4 *>(vp) : make_uint4(0u, 0u, 0u, 0u);
-                raw[v] = __builtin_bit_cast(u16x8, x);
-            } else {
-                const uint2 x = ok ? *reinterpret_cast<const uint2 *>(vp) : make_uint2(0u, 0u);
-                raw[v] = u16x8{(unsigned short)(x.x & 0xFFFF), (unsigned short)(x.x >> 16),
-                               (unsigned short)(x.y & 0xFFFF), (unsigned short)(x.y >> 16), 0, 0, 0, 0};
-            }
-        }
-        #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            u16x8 bt;
-            #pragma unroll
-            for (int v = 0; v < 8; ++v) bt[v] = raw[v][t];
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, bt);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bv, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bv, acc[t], 0, 0, 0);
-        }
-    }
-    #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        if (4 * grp + v < it.cnt) {
-            float *dst = slice + ((int64_t)it.orow[v] * (a.k + 1) + it.orank[v]) * D + NT * i16;
-            float o[NT];
-            #pragma unroll
-            for (int t = 0; t < NT; ++t) o[t] = acc[t][v];
-            Vec<float, NT>::store(dst, o);
-        }
-    }
-}
-
-// exp(z - m) for this lane's children given its logits (-inf: not an entry);
-// m and l reduced over the pair's four lane groups; lane group 0 stores (m, l).
-template <int KC>
-__device__ __forceinline__ void pair_softmax(const TP &a, const Item &it, int l, int lane, float (*w)[8]) {
-    float m = -INFINITY;
-    #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-        #pragma unroll
-        for (int v = 0; v < 8; ++v) m = fmaxf(m, w[kk][v]);
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float sum = 0.f;
-    #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-        #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const float e = w[kk][v] == -INFINITY ? 0.f : __expf(w[kk][v] - m);
-            w[kk][v] = e;
-            sum += e;
-        }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    const int i16 = lane & 15;
-    if (lane < 16 && i16 < it.cnt)
-        a.pml[((int64_t)l * a.rows_cap + it.pr.x) * (a.k + 1) + it.pr.y] = make_float2(m, sum);
-}
-
+// Level l >= 1: each pair's entries (children whose logits are not -inf) as a
+// softmax state: (m, l) to pml, sum exp(z - m) v to the level's partial slice.
 template <int D, int KC>
 __global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t NP) {
     const int lane = threadIdx.x & 63;
-    Item it;
-    if (!load_item(a, NP, lane, it)) return;
-    const int i16 = lane & 15, grp = lane >> 4;
-    const int32_t nc = i16 < it.cnt ? it.pr.w : 0;
-    const float *zr = a.z + (int64_t)it.pr.x * a.zs + it.pr.y * a.b;
-    float w[KC][8];
-    #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
+    const int grp = lane >> 4;
+    const int64_t nexist = a.length / a.pw[l];
+    float *slice = a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D;
+    for_items(a, NP, lane, [&](const Item &it) {
+        const bf16_t *vals = level_rows(tv, true, l, it.g, D);
+        const int64_t c0 = it.p * a.b;
+        const int32_t nc = (lane & 15) < it.cnt ? it.pr.w : 0;
+        const float *zr = a.z + (int64_t)it.pr.x * a.zs + it.pr.y * a.b;
+        float w[KC][8];
         #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int c = 32 * kk + 8 * grp + v;
-            w[kk][v] = c < nc ? zr[c] : -INFINITY;
+        for (int kk = 0; kk < KC; ++kk)
+            #pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int c = 32 * kk + 8 * grp + v;
+                const float zz = zr[c < nc ? c : 0];
+                w[kk][v] = c < nc ? zz : -INFINITY;
+            }
+        VRaw<D> vr;
+        load_values<D>(vals, c0, nexist, a.b, 0, lane, vr);
+        pair_softmax<KC>(a, it, l, lane, w);
+        f32x4 acc[D / 16];
+        #pragma unroll
+        for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            if (kk > 0) load_values<D>(vals, c0, nexist, a.b, kk, lane, vr);
+            pv_accumulate<D>(vr, w[kk], acc);
         }
-    pair_softmax<KC>(a, it, l, lane, w);
-    pv_tiles<D, KC>(a, it, level_rows(tv, true, l, it.g, D), it.p * a.b, a.length / a.pw[l], lane, w,
-                    a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D);
+        pv_store<D>(a, it, lane, acc, slice);
+    });
 }
 
 // ---------------------------------------------------------------- attend --
-// Level 0: the tokens of each parent scored against its pairs, the pairs'
-// softmax states and their P.V in one pass (logits go through LDS to move from
-// the score tile's layout to the P.V operand's).
+// Level 0: each item's pairs against the parent's tokens, the pairs' softmax
+// states and P.V in one pass; the logits go through LDS from the score tile's
+// layout (pair rows 4*grp + v) to the P.V operand's (pair row L%16).
 template <int D, int KC>
 __global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) {
-    __shared__ float zt[4][kTile][32 * KC + 1];
+    extern __shared__ __align__(16) unsigned char smem[];
+    float2 *crot = reinterpret_cast<float2 *>(smem);
+    load_crot(tv, a.b, D, crot);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    Item it;
-    if (!load_item(a, NP, lane, it)) return;
     const int i16 = lane & 15, grp = lane >> 4;
-    bf16x8 ah[D / 32], al[D / 32];
-    query_operands<D>(tv, a, it, lane, ah, al);
+    constexpr int ZS = 32 * KC + 1;
+    float *zw = reinterpret_cast<float *>(smem + (size_t)a.b * crot_stride(D) * sizeof(float2)) +
+                wv * kTile * ZS;
     const int64_t nexist = a.length;
-    const int64_t c0 = it.p * a.b;
-    const bf16_t *keys = level_rows(tv, false, 0, it.g, D);
-    float (*zw)[32 * KC + 1] = zt[wv];
-    for (int ct = 0; ct < 32 * KC; ct += 16) {
-        const f32x4 acc = ct < a.b ? score_tile<D>(tv, keys, c0, nexist, a.b, ct, lane, ah, al)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
-        const int c = ct + i16;
+    for_items(a, NP, lane, [&](const Item &it) {
+        const bf16_t *keys = level_rows(tv, false, 0, it.g, D);
+        const bf16_t *vals = level_rows(tv, true, 0, it.g, D);
+        const int64_t c0 = it.p * a.b;
+        QRaw<D> qr;
+        KRaw<D> kr;
+        VRaw<D> vr;
+        load_query<D>(tv, a, it, lane, qr);
+        load_keys<D>(keys, c0, nexist, a.b, 0, lane, kr);
+        load_values<D>(vals, c0, nexist, a.b, 0, lane, vr);
+        bf16x8 ah[D / 32], al[D / 32];
+        query_operands<D>(qr, it, lane, ah, al);
         #pragma unroll
-        for (int v = 0; v < 4; ++v) zw[4 * grp + v][c] = c < it.onc[v] ? a.scale * acc[v] : -INFINITY;
-    }
-    __threadfence_block();
-    float w[KC][8];
-    #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
+        for (int kk = 0; kk < KC; ++kk) {
+            if (kk > 0) load_keys<D>(keys, c0, nexist, a.b, kk, lane, kr);
+            #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f32x4 acc = score_tile<D>(kr, t, crot, c0, nexist, a.b, kk, lane, ah, al);
+                const int c = 32 * kk + 16 * t + i16;
+                #pragma unroll
+                for (int v = 0; v < 4; ++v) zw[(4 * grp + v) * ZS + c] = c < it.onc[v] ? a.scale * acc[v] : -INFINITY;
+            }
+        }
+        __threadfence_block();
+        float w[KC][8];
         #pragma unroll
-        for (int v = 0; v < 8; ++v) w[kk][v] = zw[i16][32 * kk + 8 * grp + v];
-    pair_softmax<KC>(a, it, 0, lane, w);
-    pv_tiles<D, KC>(a, it, level_rows(tv, true, 0, it.g, D), c0, nexist, lane, w, a.partial);
+        for (int kk = 0; kk < KC; ++kk)
+            #pragma unroll
+            for (int v = 0; v < 8; ++v) w[kk][v] = zw[i16 * ZS + 32 * kk + 8 * grp + v];
+        __threadfence_block();
+        pair_softmax<KC>(a, it, 0, lane, w);
+        f32x4 acc[D / 16];
+        #pragma unroll
+        for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            if (kk > 0) load_values<D>(vals, c0, nexist, a.b, kk, lane, vr);
+            pv_accumulate<D>(vr, w[kk], acc);
+        }
+        pv_store<D>(a, it, lane, acc, a.partial);
+    });
 }
 
 // ----------------------------------------------------------------- final --
@@ -717,7 +858,7 @@ Plan make_plan(int64_t rows, int32_t Hkv, int32_t D, int32_t b, int32_t k, int32
     P.off_offs = put((size_t)(P.nb + 1) * 4);
     P.off_ioff = put((size_t)(P.nb + 1) * 4);
     P.off_bsum = put((size_t)(P.nb / kScanChunk + 1) * 8);
-    P.off_sorted = put((size_t)pairs * 16);
+    P.off_sorted = put((size_t)items * kTile * 16);
     P.off_items = put((size_t)items * 16);
     P.off_nitems = put(16);
     P.off_partial = put((size_t)P.lv * pairs * D * 4);
@@ -770,6 +911,21 @@ hipError_t launch_count(const TP &a, int l, int32_t NP, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Blocks for a persistent launch over `blocks` blocks' worth of items: as many
+// as fit on the device at once (at most `blocks`).
+hipError_t persistent_grid(const void *kern, size_t smem, unsigned blocks, unsigned &grid) {
+    int dev = 0, cus = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && smem > 64 * 1024)
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, smem);
+    if (e != hipSuccess) return e;
+    const int64_t fit = (int64_t)std::max(per, 1) * std::max(cus, 1);
+    grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, fit));
+    return hipSuccess;
+}
+
 template <int D, int KC>
 hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_ctx, const Plan &P,
                     int32_t maxc, hipStream_t s) {
@@ -794,12 +950,20 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
         const int64_t pairs = rows * (int64_t)std::min(a.k + 1, (int)NP);
         const int64_t items = pairs / kTile + nb + 1;
         const unsigned ib = (unsigned)((items + 3) / 4);
+        const size_t crot_bytes = (size_t)a.b * crot_stride(D) * sizeof(float2);
         if (l == 0) {
-            hipLaunchKernelGGL((tp_attend<D, KC>), dim3(ib), dim3(256), 0, s, tv, a, NP);
+            const size_t sm = crot_bytes + (size_t)4 * kTile * (32 * KC + 1) * sizeof(float);
+            unsigned grid;
+            if ((e = persistent_grid((const void *)tp_attend<D, KC>, sm, ib, grid)) != hipSuccess) return e;
+            hipLaunchKernelGGL((tp_attend<D, KC>), dim3(grid), dim3(256), sm, s, tv, a, NP);
         } else {
-            hipLaunchKernelGGL(tp_score<D>, dim3(ib), dim3(256), 0, s, tv, a, l, NP);
+            unsigned grid;
+            if ((e = persistent_grid((const void *)tp_score<D, KC>, crot_bytes, ib, grid)) != hipSuccess)
+                return e;
+            hipLaunchKernelGGL((tp_score<D, KC>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
             if ((e = launch_select(a, dbg, l, maxc, smw, s)) != hipSuccess) return e;
-            hipLaunchKernelGGL((tp_pv<D, KC>), dim3(ib), dim3(256), 0, s, tv, a, l, NP);
+            if ((e = persistent_grid((const void *)tp_pv<D, KC>, 0, ib, grid)) != hipSuccess) return e;
+            hipLaunchKernelGGL((tp_pv<D, KC>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
