@@ -91,12 +91,18 @@ struct RowLevel {
     int64_t part;    // the partial parent's node id (N_{l+1})
 };
 
+// x / y for 0 <= x < 2^31 and y >= 1 in 32-bit arithmetic (64-bit division is a long
+// emulated sequence on the GPU); rows, contexts and node ids all stay below 2^31.
+__device__ __forceinline__ uint32_t div32(int64_t x, int64_t y) {
+    return y > x ? 0u : (uint32_t)x / (uint32_t)y;
+}
+
 __device__ __forceinline__ RowLevel row_level(const TP &a, int64_t row, int l) {
-    const int64_t n = a.ctx_base + (row / a.Hq) * a.ctx_step;
-    const int64_t up = n / a.pw[l + 1];
+    const int64_t n = a.ctx_base + (int64_t)div32(row, a.Hq) * a.ctx_step;
+    const int64_t up = div32(n, a.pw[l + 1]);
     RowLevel r;
     r.m = a.mk[l & 1][row];
-    r.o = (int32_t)(n / a.pw[l] - (int64_t)a.b * up);
+    r.o = (int32_t)((int64_t)div32(n, a.pw[l]) - (int64_t)a.b * up);
     r.part = up;
     return r;
 }
@@ -107,7 +113,8 @@ __device__ __forceinline__ int64_t parent_of(const TP &a, int64_t row, int l, in
 }
 
 __device__ __forceinline__ int64_t head_row(const TP &a, int g, int64_t t) {
-    return (t / a.G) * a.Hq + (int64_t)g * a.G + (t % a.G);
+    const uint32_t q = div32(t, a.G);
+    return (int64_t)q * a.Hq + (int64_t)g * a.G + (t - (int64_t)q * a.G);
 }
 
 // keys or values of level l (tokens at l = 0) of KV head g
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(256) void tp_scatter(TP a, DebugView dbg, int l, in
         const RowLevel rl = row_level(a, row, l);
         const int32_t np = rl.m + (rl.o > 0 ? 1 : 0);
         const int32_t n = rl.m * a.b + rl.o;
-        const int64_t g = (row % a.Hq) / a.G;
+        const int64_t g = div32(row - (int64_t)div32(row, a.Hq) * a.Hq, a.G);
         a.nplev[row * a.lv + l] = np;
         if (dbg.n_keys) dbg.n_keys[row] += n;
         for (int r = 0; r < np; ++r) {
@@ -382,9 +389,10 @@ __device__ __forceinline__ void for_items(const TP &a, int32_t NP, int lane, F &
             pn = a.sorted[next * kTile + i16];
         }
         Item it;
-        it.g = rec.x / NP;
-        it.p = rec.x % NP;
-        it.cnt = rec.z;
+        const int32_t bkt = __builtin_amdgcn_readfirstlane(rec.x);   // uniform over the wave
+        it.g = bkt / NP;
+        it.p = bkt % NP;
+        it.cnt = __builtin_amdgcn_readfirstlane(rec.z);
         it.pr = pr;
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -650,28 +658,19 @@ __global__ __launch_bounds__(256) void tp_score(TreeView tv, TP a, int l, int32_
 // the next level's parents; kept candidates' logits become -inf so the P.V
 // pass skips them.
 template <int KT>
-__global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int smem_wave) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + w;
-    if (row >= a.rows) return;
-    unsigned char *base = smem + w * smem_wave;
-    unsigned char *scratch = base;                                             // 16-aligned
-    float *outv = reinterpret_cast<float *>(base + sel::kScratchBytes);        // [4]
-    int32_t *kept = reinterpret_cast<int32_t *>(base + sel::kScratchBytes + 16);
-    float *zl = reinterpret_cast<float *>(base + sel::kScratchBytes + 16 + ((a.k * 4 + 15) & ~15));
-    uint8_t *flag = reinterpret_cast<uint8_t *>(zl + a.zs);
-
-    const RowLevel rl = row_level(a, row, l);
+__device__ __forceinline__ void select_row(const TP &a, const DebugView &dbg, int l, int64_t row, int lane,
+                                           unsigned char *scratch, float *outv, int32_t *kept,
+                                           int32_t *parl, uint8_t *flag) {
+    RowLevel rl = row_level(a, row, l);
+    rl.m = __builtin_amdgcn_readfirstlane(rl.m);        // uniform over the wave (one row)
     const int32_t n = rl.m * a.b + rl.o;
     const int32_t mm = min(a.k, n);
     if (lane == 0) a.mk[(l + 1) & 1][row] = mm;
     if (n == 0) return;
     float *zr = a.z + row * a.zs;
-    for (int i = lane; i < n; i += 64) {
-        zl[i] = zr[i];
-        flag[i] = 0;
-    }
+    const int32_t *par = a.par[l & 1] + row * a.k;
+    for (int r = lane; r < rl.m; r += 64) parl[r] = par[r];
+    for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<uint32_t *>(flag + i) = 0u;
     __threadfence_block();
     sel::Cands cd;
     cd.n = n;
@@ -679,7 +678,7 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
     cd.b = a.b;
     cd.top = 0;
     cd.orphan0 = (int32_t)(rl.part * a.b);
-    sel::select<KT>(zl, flag, kept, mm, cd, a.par[l & 1] + row * a.k, lane, scratch, outv);
+    sel::select<KT>(zr, flag, kept, mm, cd, parl, lane, scratch, outv);
     int32_t *pn = a.par[(l + 1) & 1] + row * a.k;
     for (int r = lane; r < mm; r += 64) pn[r] = kept[r];
     if (dbg.selected)
@@ -687,6 +686,21 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
     if (dbg.kth_gap && lane == 0) dbg.kth_gap[row * a.n_levels + (l - 1)] = outv[1] - outv[2];
     for (int i = lane; i < n; i += 64)
         if (flag[i]) zr[i] = -INFINITY;
+}
+
+template <int KT>
+__global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int smem_wave) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kq = (a.k * 4 + 15) & ~15;
+    unsigned char *base = smem + w * smem_wave;
+    unsigned char *scratch = base;                                             // 16-aligned
+    float *outv = reinterpret_cast<float *>(base + sel::kScratchBytes);        // [4]
+    int32_t *kept = reinterpret_cast<int32_t *>(base + sel::kScratchBytes + 16);
+    int32_t *parl = reinterpret_cast<int32_t *>(base + sel::kScratchBytes + 16 + kq);
+    uint8_t *flag = base + sel::kScratchBytes + 16 + 2 * kq;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < a.rows; row += (int64_t)gridDim.x * 4)
+        select_row<KT>(a, dbg, l, row, lane, scratch, outv, kept, parl, flag);
 }
 
 // -------------------------------------------------------------------- pv --
@@ -788,12 +802,9 @@ __global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) 
 // ----------------------------------------------------------------- final --
 // Merges every pair state (m, l, acc) of a row: with M the largest m,
 // out = sum exp(m - M) acc / sum exp(m - M) l.  One thread per (row, 4 dimensions).
-__global__ __launch_bounds__(256) void tp_final(TP a) {
-    const int D4 = a.D / 4;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = t / D4;
-    const int j = (int)(t % D4);
-    if (row >= a.rows) return;
+__device__ __forceinline__ void final_one(const TP &a, int64_t t, int D4) {
+    const int64_t row = div32(t, D4);
+    const int j = (int)(t - row * D4);
     const int64_t pslice = a.rows_cap * (a.k + 1);
     float M = -INFINITY;
     for (int l = 0; l <= a.top; ++l) {
@@ -824,6 +835,13 @@ __global__ __launch_bounds__(256) void tp_final(TP a) {
         Vec<bf16_t, 4>::store(static_cast<bf16_t *>(a.out) + row * a.D + 4 * j, o);
     else
         Vec<float, 4>::store(static_cast<float *>(a.out) + row * a.D + 4 * j, o);
+}
+
+__global__ __launch_bounds__(256) void tp_final(TP a) {
+    const int D4 = a.D / 4;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.rows * D4;
+         t += (int64_t)gridDim.x * blockDim.x)
+        final_one(a, t, D4);
 }
 
 // ------------------------------------------------------------------ host --
@@ -874,19 +892,31 @@ int64_t pass_rows(int64_t rows, int32_t Hq) {
 }
 
 size_t select_smem_wave(int32_t zs, int32_t k) {
-    return up256((size_t)sel::kScratchBytes + 16 + ((k * 4 + 15) & ~15) + (size_t)zs * 5);
+    return up256((size_t)sel::kScratchBytes + 16 + 2 * (size_t)((k * 4 + 15) & ~15) + (size_t)zs);
+}
+
+// Blocks for a persistent launch over `blocks` blocks' worth of items: as many
+// as fit on the device at once (at most `blocks`).
+hipError_t persistent_grid(const void *kern, size_t smem, unsigned blocks, unsigned &grid) {
+    int dev = 0, cus = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && smem > 64 * 1024)
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, smem);
+    if (e != hipSuccess) return e;
+    const int64_t fit = (int64_t)std::max(per, 1) * std::max(cus, 1);
+    grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, fit));
+    return hipSuccess;
 }
 
 template <int KT>
 hipError_t launch_select_t(const TP &a, const DebugView &dbg, int l, int smw, hipStream_t s) {
-    const int64_t blocks = (a.rows + 3) / 4;
     const size_t smem = (size_t)smw * 4;
-    if (smem > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void *)tp_select<KT>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(tp_select<KT>, dim3((unsigned)blocks), dim3(256), smem, s, a, dbg, l, smw);
+    unsigned grid;
+    const hipError_t e = persistent_grid((const void *)tp_select<KT>, smem, (unsigned)((a.rows + 3) / 4), grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tp_select<KT>, dim3(grid), dim3(256), smem, s, a, dbg, l, smw);
     return hipGetLastError();
 }
 
@@ -909,21 +939,6 @@ hipError_t launch_count(const TP &a, int l, int32_t NP, hipStream_t s) {
                            dim3(1024), (size_t)kRange * 4, s, a, l, NP, 1);
     }
     return hipGetLastError();
-}
-
-// Blocks for a persistent launch over `blocks` blocks' worth of items: as many
-// as fit on the device at once (at most `blocks`).
-hipError_t persistent_grid(const void *kern, size_t smem, unsigned blocks, unsigned &grid) {
-    int dev = 0, cus = 0, per = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess && smem > 64 * 1024)
-        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, smem);
-    if (e != hipSuccess) return e;
-    const int64_t fit = (int64_t)std::max(per, 1) * std::max(cus, 1);
-    grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, fit));
-    return hipSuccess;
 }
 
 template <int D, int KC>
@@ -967,7 +982,13 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(tp_final, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, s, a);
+    {
+        unsigned grid;
+        if ((e = persistent_grid((const void *)tp_final, 0, (unsigned)((rows * (D / 4) + 255) / 256), grid)) !=
+            hipSuccess)
+            return e;
+        hipLaunchKernelGGL(tp_final, dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

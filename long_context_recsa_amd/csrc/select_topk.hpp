@@ -17,10 +17,11 @@
 //   4. each survivor is ranked exactly against the others (larger key
 //      first, then lower index), reading them back 8 at a time by LDS
 //      broadcast; rank < m keeps it, and the kept ones are ordered by index.
-// Levels of at most 5 * 64 candidates instead find the m-th largest key by a
-// 32-step bisection with ballots over register-resident keys, which is faster
-// there; so do levels too wide for registers and the rare filter that lets
-// more than 128 candidates through (many equal logits).
+// Levels of at most 5 * 64 candidates instead find the threshold by bisection
+// with ballots over register-resident keys, which is faster there (it stops as
+// soon as exactly m keys lie above it); levels too wide for registers and the
+// rare filter that lets more than 128 candidates through (many equal logits)
+// use a 32-step bisection over the keys in LDS.
 #pragma once
 
 #include <math.h>
@@ -167,41 +168,59 @@ __device__ __noinline__ void select_bisect(const float *z, uint8_t *flag, int32_
 // calling wave on return.
 // Bisection for the m-th largest key with the keys in registers (narrow levels:
 // 32 ballot rounds over KT registers beat the filter's LDS round trips there).
-template <int KT>
-__device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag, int32_t *kept,
-                                                   int32_t m, Cands cd, const int32_t *parents,
-                                                   int lane, float *out) {
-    const int32_t n = cd.n;
-    uint32_t kk[KT];
-    uint32_t lmax = 0;
-    #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        const int32_t i = lane + 64 * t;
-        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;
-        lmax = max(lmax, kk[t]);
-    }
+// The largest threshold T with at least m of the keys (NT registers per lane;
+// unused slots 0) >= T, bit by bit from the top.  Once exactly m keys are >= the
+// trial threshold, every threshold in that gap keeps the same m keys: stop there.
+template <int NT>
+__device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m) {
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t trial = T | (1u << bit);
         int c = 0;
         #pragma unroll
-        for (int t = 0; t < KT; ++t) c += __popcll(__ballot(kk[t] >= trial));
-        if (c >= m) T = trial;
+        for (int t = 0; t < NT; ++t) c += __popcll(__ballot(kk[t] >= trial));
+        if (c >= m) {
+            T = trial;
+            if (c == m) break;
+        }
     }
-    int gt = 0, eq = 0;
-    #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        gt += __popcll(__ballot(kk[t] > T));
-        eq += __popcll(__ballot(kk[t] == T));
-    }
-    int need = m - gt;
-    int32_t pos = 0;
-    uint32_t below = 0;
+    return T;
+}
+
+template <int KT>
+__device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag, int32_t *kept,
+                                                   int32_t m, Cands cd, const int32_t *parents,
+                                                   int lane, float *out) {
+    // wave-uniform counts in scalar registers (they may come from a vector load)
+    const int32_t n = __builtin_amdgcn_readfirstlane(cd.n);
+    m = __builtin_amdgcn_readfirstlane(m);
+    const int nT = (n + 63) >> 6;                       // registers that hold keys
+    uint32_t kk[KT];
+    uint32_t lmax = 0;
     #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int32_t i = lane + 64 * t;
-        if (i < n && kk[t] < T) below = max(below, kk[t]);
-        const uint64_t e = __ballot(kk[t] == T);
+        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;      // valid keys are > 0
+        lmax = max(lmax, kk[t]);
+    }
+    uint32_t T = 0;
+    if (nT == 1)
+        T = bisect_threshold<1>(kk, m);
+    else
+        T = bisect_threshold<KT>(kk, m);
+    // kept: every key > T, then keys == T in ascending index until m are kept
+    int gt = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t)
+        if (t < nT) gt += __popcll(__ballot(kk[t] > T));
+    int need = m - gt;
+    int32_t pos = 0;
+    uint32_t kmin = 0xFFFFFFFFu, below = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        if (t >= nT) break;
+        const int32_t i = lane + 64 * t;
+        const uint64_t e = __ballot(i < n && kk[t] == T);
         const bool f = (i < n) && ((kk[t] > T) || (kk[t] == T && __popcll(e & lanes_below(lane)) < need));
         const int ce = __popcll(e);
         need -= ce < need ? ce : need;
@@ -209,15 +228,19 @@ __device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag
         if (f) {
             kept[pos + __popcll(mask & lanes_below(lane))] = node_id(i, cd, parents);
             flag[i] = 1;
+            kmin = min(kmin, kk[t]);
+        } else if (i < n) {
+            below = max(below, kk[t]);
         }
         pos += __popcll(mask);
     }
     const uint32_t kmax = wave_umax(lmax);
-    const uint32_t kn = (gt + eq > m) ? T : wave_umax(below);
+    kmin = wave_umin(kmin);
+    below = wave_umax(below);
     if (lane == 0) {
         out[0] = from_ordered(kmax);
-        out[1] = from_ordered(T);
-        out[2] = (n > m) ? from_ordered(kn) : NAN;
+        out[1] = from_ordered(kmin);
+        out[2] = (n > m) ? from_ordered(below) : NAN;
     }
 }
 
