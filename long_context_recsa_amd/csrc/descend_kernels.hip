@@ -127,8 +127,8 @@ template <typename T, int D, int NW, int CB>
 __device__ __forceinline__ void fused_pass(
     sel::Cands A, const int32_t *parA, const float *zA, const uint8_t *flagA, bool maskA,
     const T *vA, sel::Cands S, const int32_t *parS, const T *kS, float *zS, uint8_t *flagS,
-    const float *U, const float2 *rope, int32_t maxc, int32_t kmax, int slot, int sub, float scale,
-    float M, float &lsum, float *acc_a, float *acc_b) {
+    const T *vS, const float *U, const float2 *rope, int32_t maxc, int32_t kmax, int slot, int sub,
+    float scale, float &M, float &lsum, float *acc_a, float *acc_b) {
     constexpr int H2 = D / 2, PP = D / 32, NSLOT = NW * 4;
     constexpr uint32_t ROWB = D * sizeof(T);
     constexpr float kLog2e = 1.4426950408889634f;
@@ -138,7 +138,10 @@ __device__ __forceinline__ void fused_pass(
     const int j0 = sub * PP;
     const char *vAb = reinterpret_cast<const char *>(vA) + j0 * sizeof(T);
     const char *kSb = reinterpret_cast<const char *>(kS) + j0 * sizeof(T);
-    const float Ml2 = M * kLog2e;
+    // vS: the S candidates are tokens, entries as soon as they are scored; their values
+    // come in with their keys and join this slot's softmax online (M is then per slot)
+    const bool online = vS != nullptr;
+    const char *vSb = reinterpret_cast<const char *>(online ? vS : kS) + j0 * sizeof(T);
     for (int32_t c = slot; c < b; c += NSLOT) {
         float cr[PP], sr[PP];
         if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, cr, sr);
@@ -152,11 +155,18 @@ __device__ __forceinline__ void fused_pass(
                 const int32_t ic = i < maxc ? i : maxc - 1;
                 const int32_t rc = r < kmax ? r : kmax - 1;
                 const bool okA = (i < A.n) && !(maskA && flagA[ic]);
-                ea[t] = okA ? zA[ic] * kLog2e - Ml2 : -INFINITY;
+                ea[t] = okA ? zA[ic] * kLog2e : -INFINITY;
                 offA[t] = okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u;
                 offS[t] = (i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u;
             }
-            Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB];
+            Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
+            if (online) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    sa[t].load(reinterpret_cast<const T *>(vSb + offS[t]));
+                    sb[t].load(reinterpret_cast<const T *>(vSb + offS[t] + H2 * sizeof(T)));
+                }
+            }
             if (A.n > 0) {
                 #pragma unroll
                 for (int t = 0; t < CB; ++t) {
@@ -172,9 +182,10 @@ __device__ __forceinline__ void fused_pass(
                 }
             }
             if (A.n > 0) {
+                const float Ml2 = M * kLog2e;
                 #pragma unroll
                 for (int t = 0; t < CB; ++t) {
-                    const float pz = __builtin_amdgcn_exp2f(ea[t]);    // 0 for -inf
+                    const float pz = __builtin_amdgcn_exp2f(ea[t] - Ml2);    // 0 for -inf
                     float fa[PP], fb[PP];
                     va[t].get(fa);
                     vb[t].get(fb);
@@ -205,7 +216,25 @@ __device__ __forceinline__ void fused_pass(
                         dot += ua[p] * ra + ub[p] * rb;
                     }
                     dot = row_sum16(dot);
-                    if (sub == 15 && i < S.n) {
+                    if (online) {
+                        // the logit to all 16 lanes of the slot, then an online softmax step
+                        const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
+                        if (i < S.n) {
+                            const float Mn = fmaxf(M, z);
+                            const float sc = __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+                            const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
+                            float fa2[PP], fb2[PP];
+                            sa[t].get(fa2);
+                            sb[t].get(fb2);
+                            lsum = lsum * sc + pz;
+                            #pragma unroll
+                            for (int p = 0; p < PP; ++p) {
+                                acc_a[p] = acc_a[p] * sc + pz * fa2[p];
+                                acc_b[p] = acc_b[p] * sc + pz * fb2[p];
+                            }
+                            M = Mn;
+                        }
+                    } else if (sub == 15 && i < S.n) {
                         zS[i] = scale * dot;
                         flagS[i] = 0;
                     }
@@ -230,7 +259,8 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     float *U = zbuf + 2 * maxc;                                           // [nrank][D]
     float *red = U + (size_t)nrank * D;                                   // [NW][D]
     float *red_l = red + NW * D;                                          // [NW]
-    float *misc = red_l + NW;                                             // [4]
+    float *red_m = red_l + NW;                                            // [NW]
+    float *misc = red_m + NW;                                             // [4]
     unsigned char *scratch = reinterpret_cast<unsigned char *>(misc + 4); // selection scratch
     int32_t *kept = reinterpret_cast<int32_t *>(scratch + sel::kScratchBytes);  // [2][k]
     uint8_t *flagbuf = reinterpret_cast<uint8_t *>(kept + 2 * a.k);       // [2][maxc]
@@ -300,14 +330,19 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
                              : static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
         build_ranks(cA.n, 0);
         __syncthreads();
+        // with no level above the tokens, the top candidates are tokens: entries at once
         fused_pass<T, D, NW, CB>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
-                                 zbuf + (H & 1) * maxc, flagbuf + (H & 1) * maxc, U, rope, maxc,
-                                 a.k, slot, sub, a.scale, M, lsum, acc_a, acc_b);
+                                 zbuf + (H & 1) * maxc, flagbuf + (H & 1) * maxc,
+                                 H == 0 ? vcache : nullptr, U, rope, maxc, a.k, slot, sub, a.scale, M,
+                                 lsum, acc_a, acc_b);
         keys_scored += cA.n;
     }
 
+    // Levels H..1: select level l, then one pass over level l's entries and level l-1's
+    // candidates.  At l = 1 those are tokens, which join the softmax as they are scored,
+    // so the tokens' keys and values come in one round trip.
     int64_t pw = pwH;
-    for (int l = H; l >= 0; --l, pw /= b) {
+    for (int l = H; l >= 1; --l, pw /= b) {
         __syncthreads();
         float *zA = zbuf + (l & 1) * maxc;
         uint8_t *flagA = flagbuf + (l & 1) * maxc;
@@ -359,13 +394,27 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
                   : l > 1 ? static_cast<const T *>(tv.key[l - 1]) + (int64_t)g * tv.node_cap[l - 1] * D
                           : vA;
         fused_pass<T, D, NW, CB>(cA, parentsA, zA, flagA, l > 0, vA, cS, keptA, kS,
-                                 zbuf + ((l + 1) & 1) * maxc, flagbuf + ((l + 1) & 1) * maxc, U,
-                                 rope, maxc, a.k, slot, sub, a.scale, M, lsum, acc_a, acc_b);
+                                 zbuf + ((l + 1) & 1) * maxc, flagbuf + ((l + 1) & 1) * maxc,
+                                 l == 1 ? vcache : nullptr, U, rope, maxc, a.k, slot, sub, a.scale, M,
+                                 lsum, acc_a, acc_b);
         keys_scored += cS.n;
         cA = cS;
     }
 
-    // combine the slots: four lane groups by shuffles, the waves through LDS
+    // combine the slots: each has its own running max after the tokens; rescale to the
+    // largest, then add the four lane groups by shuffles and the waves through LDS
+    {
+        float mw = fmaxf(M, __shfl_xor(M, 16));
+        mw = fmaxf(mw, __shfl_xor(mw, 32));
+        if (lane == 0) red_m[wave] = mw;
+        __syncthreads();
+        float mf = red_m[0];
+        for (int w = 1; w < NW; ++w) mf = fmaxf(mf, red_m[w]);
+        const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - mf) * kLog2e);
+        lsum *= sc;
+        #pragma unroll
+        for (int p = 0; p < PP; ++p) { acc_a[p] *= sc; acc_b[p] *= sc; }
+    }
     #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
         lsum += __shfl_xor(lsum, off);
@@ -414,7 +463,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
 template <int NW>
 size_t descend_smem(int32_t maxc, int32_t k, int32_t b, int D) {
     const size_t nrank = ((size_t)maxc + b - 1) / b;
-    return sizeof(float) * (2 * (size_t)maxc + nrank * D + (size_t)NW * D + NW + 4) +
+    return sizeof(float) * (2 * (size_t)maxc + nrank * D + (size_t)NW * D + 2 * NW + 4) +
            sel::kScratchBytes + sizeof(int32_t) * 2 * (size_t)k + 2 * (size_t)maxc;
 }
 
