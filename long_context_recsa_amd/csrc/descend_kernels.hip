@@ -282,6 +282,25 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     int64_t pwH = 1;
     while (n_ctx / (pwH * b) >= 1) { pwH *= b; ++H; }
 
+    // The top level (H >= 1) has fewer than b nodes, all of them candidates at rank 0:
+    // with at most 64 of them, their keys and child-offset rotations are loaded now,
+    // alongside the query, instead of after the query's rotation is built.
+    constexpr int CT = NSLOT >= 64 ? 1 : 64 / NSLOT;
+    sel::Cands cA = level_cands(n_ctx, pwH, b, true, 0);
+    const bool top_early = H >= 1 && cA.n <= CT * NSLOT;
+    Raw<T, PP> tka[CT], tkb[CT];
+    float tc[CT][PP], ts[CT][PP];
+    if (top_early) {
+        const T *kH = static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
+        #pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int32_t c = slot + t * NSLOT;
+            const int32_t cc = c < cA.n ? c : 0;
+            tka[t].load(kH + (int64_t)cc * D + j0);
+            tkb[t].load(kH + (int64_t)cc * D + H2 + j0);
+            load_cs<PP>(rope + (int64_t)cc * H2 + j0, tc[t], ts[t]);
+        }
+    }
     float qa[PP], qb[PP];
     {
         const T *qp = static_cast<const T *>(a.q) + row * D;
@@ -322,19 +341,45 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     int64_t keys_scored = 0;
 
     // ---- top level: score all of its candidates -------------------------------------
-    sel::Cands cA = level_cands(n_ctx, pwH, b, true, 0);
     {
-        sel::Cands none = cA;
-        none.n = 0;
-        const T *kH = H == 0 ? kcache
-                             : static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
         build_ranks(cA.n, 0);
         __syncthreads();
-        // with no level above the tokens, the top candidates are tokens: entries at once
-        fused_pass<T, D, NW, CB>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
-                                 zbuf + (H & 1) * maxc, flagbuf + (H & 1) * maxc,
-                                 H == 0 ? vcache : nullptr, U, rope, maxc, a.k, slot, sub, a.scale, M,
-                                 lsum, acc_a, acc_b);
+        if (top_early) {
+            float ua[PP], ub[PP];
+            Vec<float, PP>::load(U + j0, ua);
+            Vec<float, PP>::load(U + H2 + j0, ub);
+            float *zH = zbuf + (H & 1) * maxc;
+            uint8_t *fH = flagbuf + (H & 1) * maxc;
+            #pragma unroll
+            for (int t = 0; t < CT; ++t) {
+                const int32_t c = slot + t * NSLOT;
+                float fa[PP], fb[PP];
+                tka[t].get(fa);
+                tkb[t].get(fb);
+                float dot = 0.f;
+                #pragma unroll
+                for (int p = 0; p < PP; ++p) {
+                    const float ra = fa[p] * tc[t][p] - fb[p] * ts[t][p];
+                    const float rb = fb[p] * tc[t][p] + fa[p] * ts[t][p];
+                    dot += ua[p] * ra + ub[p] * rb;
+                }
+                dot = row_sum16(dot);
+                if (sub == 15 && c < cA.n) {
+                    zH[c] = a.scale * dot;
+                    fH[c] = 0;
+                }
+            }
+        } else {
+            sel::Cands none = cA;
+            none.n = 0;
+            const T *kH = H == 0 ? kcache
+                                 : static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
+            // with no level above the tokens, the top candidates are tokens: entries at once
+            fused_pass<T, D, NW, CB>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
+                                     zbuf + (H & 1) * maxc, flagbuf + (H & 1) * maxc,
+                                     H == 0 ? vcache : nullptr, U, rope, maxc, a.k, slot, sub, a.scale,
+                                     M, lsum, acc_a, acc_b);
+        }
         keys_scored += cA.n;
     }
 
