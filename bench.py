@@ -111,7 +111,7 @@ def algorithmic(w, B):
                 decode_entries_per_row=kd + vd)
 
 
-def cpu_baseline(w, B, seconds=15.0):
+def cpu_baseline(w, B, seconds=15.0, queries=None):
     """The oracle (never tuned) on the host: tree over one KV head, then decode
     rows of that head until about `seconds` have passed."""
     from threadpoolctl import threadpool_limits
@@ -121,7 +121,7 @@ def cpu_baseline(w, B, seconds=15.0):
     with threadpool_limits(1):
         K, V = synth.gen_kv(w, 0, w.L, heads=[0])
         W = synth.pool_w(w)[:1]
-        Q = synth.decode_queries(w, B)
+        Q = synth.decode_queries(w, B) if queries is None else queries
         t0 = time.perf_counter()
         tree = O.build_tree(K, V, W, w.b, w.dtype, w.pool_scale, w.L)
         t_build = time.perf_counter() - t0
@@ -141,6 +141,88 @@ def cpu_baseline(w, B, seconds=15.0):
         "sample": f"{rows} decode rows (query x head) of KV head 0 at L={w.L}, single thread, "
                   f"after building that head's tree in {t_build:.1f} s; queries/s = rows/s / {w.n_q}",
     }
+
+
+def run_serve(args, name):
+    """A serving batch: independent sequences (own caches and trees) at ragged lengths,
+    one decode query each, in one call.  Step = that call."""
+    import torch
+
+    import long_context_recsa_amd as R
+    import synth
+    from long_context_recsa_amd.layer import decode_multi
+
+    seqs, Q = synth.serve_batch(name)
+    w0 = seqs[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cap = max(w.L for w in seqs)
+    p = R.make_params(w0.n_kv, w0.n_q, w0.d, w0.b, w0.k, cap, store=w0.dtype, out="f32",
+                      rope_base=w0.rope_base, softmax_scale=w0.softmax_scale,
+                      pool_scale=w0.pool_scale)
+
+    def dev_store(x):
+        bits = synth.storage_bits(x, w0.dtype)
+        if w0.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t_setup = time.perf_counter()
+    layers = []
+    for w in seqs:
+        K, V = synth.gen_kv(w, 0, w.L)
+        layer = R.RecsaLayer(p, dev)
+        for g in range(w.n_kv):
+            layer.k_cache[g, :w.L].copy_(dev_store(K[g]))
+            layer.v_cache[g, :w.L].copy_(dev_store(V[g]))
+        layer.pool_w.copy_(torch.from_numpy(synth.pool_w(w)))
+        layer.build(w.L)
+        layers.append(layer)
+        del K, V
+    q = dev_store(Q)
+    out = torch.empty((len(seqs), w0.n_q, w0.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(R.recsa_multi_workspace_bytes(len(seqs)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    for _ in range(args.warmup):
+        decode_multi(layers, q, out=out, ws=ws)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        decode_multi(layers, q, out=out, ws=ws)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    row_b = w0.d * (2 if w0.dtype == "bf16" else 4)
+    nbytes = sum(w.n_q * sum(row_entries(w.L, w.b, w.k)) * row_b for w in seqs)
+    ach = nbytes / ms / 1e6
+    tr = measured_traffic(name, "decode")
+    res = {
+        "metric": f"decode queries/s, {len(seqs)} independent sequences at ragged lengths "
+                  f"{min(w.L for w in seqs)}..{cap}, one query each",
+        "value": len(seqs) / (ms / 1e3), "unit": "decode queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "storage": w0.dtype, "n_seq": len(seqs),
+                   "lengths": [w.L for w in seqs], "n_kv_heads": w0.n_kv, "n_q_heads": w0.n_q,
+                   "head_dim": w0.d, "b": w0.b, "k": w0.k},
+        "ms": {"decode": ms},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None if tr is None else tr["fetch"] + tr["write"]},
+        "setup_s": t_setup,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(seqs[0], 1, args.cpu_seconds, queries=Q[:1])
+        res["cpu_baseline"]["sample"] += " (sequence 0 of the batch)"
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -175,6 +257,8 @@ def main():
     import long_context_recsa_amd as R
     import synth
 
+    if args.workload in synth.SERVE_BATCHES:
+        return run_serve(args, args.workload)
     w = synth.WORKLOADS[args.workload]
     B = args.batch or w.max_batch
     dev = torch.device("cuda:0")

@@ -104,8 +104,12 @@ RECSA_API recsa_status recsa_tree_layout(const recsa_params *p, int32_t level, s
  * (min(capacity, k*b + b - 1)); RoPE positions run 0..this value. */
 RECSA_API int64_t recsa_max_candidates(const recsa_params *p);
 
-/* Workspace bytes recsa_decode/recsa_prefill need for `max_rows` rows (0 today:
- * every per-row intermediate lives in LDS).  `ws` may be NULL when this is 0. */
+/* Workspace bytes recsa_decode/recsa_prefill need for `max_rows` rows (queries x
+ * query heads): 0 for decode and for calls that run one workgroup per row; a
+ * bf16-storage prefill of at least 4096 rows with fanout <= 128 runs
+ * parent-major (rows grouped by the parents they keep) and needs this much
+ * device memory, 256-byte aligned, passed as `ws`.  `ws` may be NULL when this
+ * is 0.  0 on invalid params. */
 RECSA_API size_t recsa_workspace_bytes(const recsa_params *p, int64_t max_rows);
 
 /* Build the tree over the first `length` tokens already stored in
@@ -141,11 +145,27 @@ RECSA_API recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc
                           int32_t batch, void *out, const recsa_debug *dbg, void *ws,
                           void *stream);
 
+/* Workspace bytes recsa_decode_multi needs for n_seq sequences (device memory). */
+RECSA_API size_t recsa_multi_workspace_bytes(int32_t n_seq);
+
+/* Decode for n_seq sequences at once (a serving batch): sequence i has its own
+ * cache and tree, described by descs[i] (host array, same params for all,
+ * each with length >= 1; read before the call returns), and one query
+ * q[i][n_q_heads][head_dim] at its own position descs[i].length, with the
+ * same per-level rule as recsa_decode.  out[i][n_q_heads][head_dim].  `ws`:
+ * recsa_multi_workspace_bytes(n_seq) bytes of device memory, 16-byte aligned,
+ * which the call fills with the sequence table on `stream`.  `dbg` may be
+ * NULL (rows are i * n_q_heads + h). */
+RECSA_API recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs,
+                                int32_t n_seq, const void *q, void *out, const recsa_debug *dbg,
+                                void *ws, void *stream);
+
 /* Causal prefill of the last n_q tokens of the tree (append them first):
  * q[n_q][n_q_heads][head_dim]; query j sits at token L0 + j, L0 = length - n_q,
  * and attends to tokens [0, L0 + j] through the tree of that prefix (complete
  * nodes only), with the same per-level rule as recsa_decode.
- * out[n_q][n_q_heads][head_dim].  `dbg` may be NULL. */
+ * out[n_q][n_q_heads][head_dim].  `ws`: see recsa_workspace_bytes(p, n_q * n_q_heads)
+ * (RECSA_ERR_INVALID_ARG when it is needed and NULL).  `dbg` may be NULL. */
 RECSA_API recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
                            int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
                            void *stream);

@@ -20,7 +20,8 @@ RECSA_FP32, RECSA_BF16 = 0, 1
 EXPORTED = (
     "recsa_num_levels", "recsa_tree_bytes", "recsa_tree_layout", "recsa_max_candidates",
     "recsa_workspace_bytes", "recsa_build_tree", "recsa_append", "recsa_decode",
-    "recsa_prefill", "recsa_status_string", "recsa_last_error",
+    "recsa_prefill", "recsa_status_string", "recsa_last_error", "recsa_multi_workspace_bytes",
+    "recsa_decode_multi",
 )
 
 
@@ -82,6 +83,8 @@ def load_library():
         "recsa_prefill": (i32, [P, D, v, i64, v, G, v, v]),
         "recsa_status_string": (ctypes.c_char_p, [i32]),
         "recsa_last_error": (ctypes.c_char_p, []),
+        "recsa_multi_workspace_bytes": (ctypes.c_size_t, [i32]),
+        "recsa_decode_multi": (i32, [P, D, i32, v, v, G, v, v]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -141,6 +144,17 @@ def recsa_prefill(p, desc, q_ptr, n_q, out_ptr, dbg=None, ws=None, stream=None) 
     _check(load_library().recsa_prefill(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q,
                                         out_ptr, ctypes.byref(dbg) if dbg is not None else None,
                                         ws, stream))
+
+
+def recsa_multi_workspace_bytes(n_seq: int) -> int:
+    return load_library().recsa_multi_workspace_bytes(n_seq)
+
+
+def recsa_decode_multi(p, descs, n_seq, q_ptr, out_ptr, dbg=None, ws=None, stream=None) -> None:
+    """descs: a ctypes array of n_seq recsa_tree_desc."""
+    _check(load_library().recsa_decode_multi(ctypes.byref(p), descs, n_seq, q_ptr, out_ptr,
+                                             ctypes.byref(dbg) if dbg is not None else None,
+                                             ws, stream))
 
 
 def make_params(n_kv_heads, n_q_heads, head_dim, fanout_b, budget_k, capacity,

@@ -269,7 +269,25 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     const int64_t qi = row / a.Hq;
     const int h = (int)(row - qi * a.Hq);
     const int g = h / a.G;
-    const int64_t n_ctx = a.ctx_base + qi * a.ctx_step;
+    int64_t n_ctx = a.ctx_base + qi * a.ctx_step;
+    // multi-sequence decode: this query's sequence, as byte offsets from sequence 0's buffers
+    int64_t dk = 0, dv = 0, dt = 0;
+    if (a.seqs != nullptr) {
+        const SeqEntry e = a.seqs[qi], e0 = a.seqs[0];
+        n_ctx = e.length;
+        dk = static_cast<const char *>(e.k_cache) - static_cast<const char *>(e0.k_cache);
+        dv = static_cast<const char *>(e.v_cache) - static_cast<const char *>(e0.v_cache);
+        dt = static_cast<const char *>(e.tree) - static_cast<const char *>(e0.tree);
+    }
+    // level l's keys / values of KV head g (l >= 1), in this query's tree
+    auto lkey = [&](int l) {
+        return reinterpret_cast<const T *>(static_cast<const char *>(tv.key[l]) + dt) +
+               (int64_t)g * tv.node_cap[l] * D;
+    };
+    auto lval = [&](int l) {
+        return reinterpret_cast<const T *>(static_cast<const char *>(tv.val[l]) + dt) +
+               (int64_t)g * tv.node_cap[l] * D;
+    };
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 4, sub = lane & 15;
     const int slot = wave * 4 + grp;
@@ -291,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     Raw<T, PP> tka[CT], tkb[CT];
     float tc[CT][PP], ts[CT][PP];
     if (top_early) {
-        const T *kH = static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
+        const T *kH = lkey(H);
         #pragma unroll
         for (int t = 0; t < CT; ++t) {
             const int32_t c = slot + t * NSLOT;
@@ -315,8 +333,10 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         }
     }
 
-    const T *kcache = static_cast<const T *>(tv.k_cache) + (int64_t)g * tv.cap * D;
-    const T *vcache = static_cast<const T *>(tv.v_cache) + (int64_t)g * tv.cap * D;
+    const T *kcache = reinterpret_cast<const T *>(static_cast<const char *>(tv.k_cache) + dk) +
+                      (int64_t)g * tv.cap * D;
+    const T *vcache = reinterpret_cast<const T *>(static_cast<const char *>(tv.v_cache) + dv) +
+                      (int64_t)g * tv.cap * D;
 
     // U[r] = R((n - r*b) theta) q for the ranks r < ceil(n / b) of a level with n
     // candidates; slots from first_slot on share the ranks.
@@ -372,8 +392,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         } else {
             sel::Cands none = cA;
             none.n = 0;
-            const T *kH = H == 0 ? kcache
-                                 : static_cast<const T *>(tv.key[H]) + (int64_t)g * tv.node_cap[H] * D;
+            const T *kH = H == 0 ? kcache : lkey(H);
             // with no level above the tokens, the top candidates are tokens: entries at once
             fused_pass<T, D, NW, CB>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
                                      zbuf + (H & 1) * maxc, flagbuf + (H & 1) * maxc,
@@ -433,11 +452,8 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         #pragma unroll
         for (int p = 0; p < PP; ++p) { acc_a[p] *= corr; acc_b[p] *= corr; }
         M = Mn;
-        const T *vA = l == 0 ? vcache
-                             : static_cast<const T *>(tv.val[l]) + (int64_t)g * tv.node_cap[l] * D;
-        const T *kS = l == 1 ? kcache
-                  : l > 1 ? static_cast<const T *>(tv.key[l - 1]) + (int64_t)g * tv.node_cap[l - 1] * D
-                          : vA;
+        const T *vA = l == 0 ? vcache : lval(l);
+        const T *kS = l == 1 ? kcache : l > 1 ? lkey(l - 1) : vA;
         fused_pass<T, D, NW, CB>(cA, parentsA, zA, flagA, l > 0, vA, cS, keptA, kS,
                                  zbuf + ((l + 1) & 1) * maxc, flagbuf + ((l + 1) & 1) * maxc,
                                  l == 1 ? vcache : nullptr, U, rope, maxc, a.k, slot, sub, a.scale, M,

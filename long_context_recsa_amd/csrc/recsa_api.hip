@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "recsa_internal.hpp"
 
 namespace recsa {
@@ -349,6 +351,69 @@ recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, co
         return fail(RECSA_ERR_INVALID_ARG, "decode needs at least one cached token");
     return run_descend(p, desc, q, batch, desc ? desc->length : 0, 0, out, dbg, false, nullptr,
                        static_cast<hipStream_t>(stream));
+}
+
+size_t recsa_multi_workspace_bytes(int32_t n_seq) {
+    return n_seq > 0 ? align_up((size_t)n_seq * sizeof(SeqEntry)) : 0;
+}
+
+recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs, int32_t n_seq,
+                                const void *q, void *out, const recsa_debug *dbg, void *ws,
+                                void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if (descs == nullptr || n_seq < 1)
+        return fail(RECSA_ERR_INVALID_ARG, "need at least one sequence descriptor");
+    for (int32_t i = 0; i < n_seq; ++i) {
+        if ((st = check_desc(p, &descs[i])) != RECSA_OK) return st;
+        if (descs[i].length < 1)
+            return fail(RECSA_ERR_INVALID_ARG, "sequence %d has no cached token", (int)i);
+    }
+    if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (ws == nullptr || !aligned(ws, 16))
+        return fail(RECSA_ERR_INVALID_ARG,
+                    "a 16-byte aligned workspace of recsa_multi_workspace_bytes(%d) bytes is needed",
+                    (int)n_seq);
+    if ((int64_t)n_seq * p->n_q_heads > 0x7FFFFFFF)
+        return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // the sequence table, copied into the workspace on the caller's stream (a pageable
+    // source is staged before the copy call returns)
+    thread_local std::vector<SeqEntry> table;
+    table.resize((size_t)n_seq);
+    for (int32_t i = 0; i < n_seq; ++i)
+        table[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
+    hipError_t e = hipMemcpyAsync(ws, table.data(), (size_t)n_seq * sizeof(SeqEntry),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "sequence table copy");
+    const TreeView tv = make_view(p, &descs[0], L);
+    DescendArgs a{};
+    a.q = q;
+    a.out = out;
+    a.rows = (int64_t)n_seq * p->n_q_heads;
+    a.Hq = p->n_q_heads;
+    a.G = p->n_q_heads / p->n_kv_heads;
+    a.ctx_base = 0;
+    a.ctx_step = 0;
+    a.b = p->fanout_b;
+    a.k = p->budget_k;
+    a.max_cand = (int32_t)L.max_cand;
+    a.scale = p->softmax_scale;
+    a.out_bf16 = p->out_dtype == RECSA_BF16;
+    a.seqs = static_cast<const SeqEntry *>(ws);
+    DebugView dv{};
+    if (dbg != nullptr) {
+        dv.selected = dbg->selected;
+        dv.kth_gap = dbg->kth_gap;
+        dv.n_keys = dbg->n_keys;
+    }
+    e = launch_descend(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "descend launch");
+    return RECSA_OK;
 }
 
 recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,

@@ -7,8 +7,9 @@ import ctypes
 import torch
 
 from . import (RECSA_BF16, recsa_append, recsa_build_tree, recsa_debug, recsa_decode,
-               recsa_max_candidates, recsa_num_levels, recsa_params, recsa_prefill,
-               recsa_tree_bytes, recsa_tree_desc, recsa_tree_layout, recsa_workspace_bytes)
+               recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
+               recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
+               recsa_tree_layout, recsa_workspace_bytes)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -117,3 +118,22 @@ class RecsaLayer:
         keys = self.tree[ko:ko + n * esz].view(self.store).view(shape)
         vals = self.tree[vo:vo + n * esz].view(self.store).view(shape)
         return keys, vals
+
+
+def decode_multi(layers, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None):
+    """One decode step for a batch of sequences: layers[i] (same params, own cache and
+    tree) answers query q[i] at its own length.  q: [n][n_q_heads][head_dim]."""
+    first = layers[0]
+    n = len(layers)
+    shape = (n, first.p.n_q_heads, first.p.head_dim)
+    first._check_dev(q, shape, first.store)
+    if out is None:
+        out = torch.empty(shape, dtype=first.out_dtype, device=first.device)
+    descs = (recsa_tree_desc * n)(*[l.desc for l in layers])
+    nbytes = recsa_multi_workspace_bytes(n)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=first.device)
+    d, dbg = first._debug(n * first.p.n_q_heads, debug)
+    recsa_decode_multi(first.p, descs, n, _ptr(q), _ptr(out), dbg, _ptr(ws), first.stream())
+    return (out, d) if debug else out

@@ -27,7 +27,7 @@ import numpy as np
 SLAB = 65536
 
 # tensor ids in the seed sequence
-T_K, T_V, T_Q, T_W, T_NEEDLE, T_DRIFT, T_QPREFILL = 0, 1, 2, 3, 4, 5, 6
+T_K, T_V, T_Q, T_W, T_NEEDLE, T_DRIFT, T_QPREFILL, T_SERVE = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -81,6 +81,28 @@ WORKLOADS = {
                             dtype="bf16", decode_batches=(1, 32), needles=64,
                             needle_recipe="pooler"),
 }
+
+
+# Serving batches: independent sequences, each with its own cache and tree at its
+# own (ragged) length, one decode query per sequence; layer shape and tree
+# parameters of the named workload, plain N(0,1) keys and values.
+SERVE_BATCHES = {
+    "qwen3_4b_serve16": dict(base="qwen3_4b_131k", n_seq=16, lmin=8192, lmax=40960),
+}
+
+
+def serve_batch(name: str):
+    """(per-sequence workloads, queries [n_seq][n_q][d]) of a serving batch."""
+    spec = SERVE_BATCHES[name]
+    base = WORKLOADS[spec["base"]]
+    r = _gen(base.cfg_id, T_SERVE, 0, 0)
+    lengths = r.integers(spec["lmin"], spec["lmax"] + 1, size=spec["n_seq"])
+    seqs = [dataclasses.replace(base, name=f"{name}_{i}", cfg_id=1000 + 16 * base.cfg_id + i,
+                                L=int(L), prefill_n=0, decode_batches=(1,), needles=0,
+                                needle_recipe="")
+            for i, L in enumerate(lengths)]
+    q = r.standard_normal((spec["n_seq"], base.n_q, base.d), dtype=np.float32)
+    return seqs, to_storage(q, base.dtype)
 
 
 def scaled(w: Workload, L: int, prefill_n: int | None = None, **kw) -> Workload:

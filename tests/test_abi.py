@@ -130,3 +130,27 @@ def test_params_struct_layout():
     assert R.recsa_params.rope_base.offset == 32
     assert R.recsa_params.capacity.offset == 48
     assert ctypes.sizeof(R.recsa_tree_desc) == 40
+
+
+def test_multi_decode_validates_before_any_hip_call():
+    p = _p(capacity=1000)
+    fake = 1 << 20
+    assert R.recsa_multi_workspace_bytes(0) == 0
+    assert R.recsa_multi_workspace_bytes(5) >= 5 * 32
+    good = (R.recsa_tree_desc * 2)(R.recsa_tree_desc(fake, fake, fake, fake, 10),
+                                   R.recsa_tree_desc(fake, fake, fake, fake, 20))
+    empty = (R.recsa_tree_desc * 2)(R.recsa_tree_desc(fake, fake, fake, fake, 10),
+                                    R.recsa_tree_desc(fake, fake, fake, fake, 0))
+    over = (R.recsa_tree_desc * 1)(R.recsa_tree_desc(fake, fake, fake, fake, 1001))
+    cases = [
+        (lambda: R.recsa_decode_multi(p, None, 2, fake, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi(p, good, 0, fake, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi(p, empty, 2, fake, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi(p, over, 1, fake, fake, ws=fake), R.RECSA_ERR_CAPACITY),
+        (lambda: R.recsa_decode_multi(p, good, 2, fake, fake, ws=None), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi(p, good, 2, None, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
+    ]
+    for i, (fn, status) in enumerate(cases):
+        with pytest.raises(R.RecsaError) as e:
+            fn()
+        assert e.value.status == status, (i, str(e.value))
