@@ -181,7 +181,8 @@ def run_serve(args, name):
         del K, V
     q = dev_store(Q)
     out = torch.empty((len(seqs), w0.n_q, w0.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(R.recsa_multi_workspace_bytes(len(seqs)), dtype=torch.uint8, device=dev)
+    nws = R.recsa_multi_workspace_bytes(len(seqs))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 

@@ -145,7 +145,8 @@ RECSA_API recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc
                           int32_t batch, void *out, const recsa_debug *dbg, void *ws,
                           void *stream);
 
-/* Workspace bytes recsa_decode_multi needs for n_seq sequences (device memory). */
+/* Workspace bytes recsa_decode_multi needs for n_seq sequences (device memory):
+ * 0 for up to 32 sequences, whose table travels with the launch. */
 RECSA_API size_t recsa_multi_workspace_bytes(int32_t n_seq);
 
 /* Decode for n_seq sequences at once (a serving batch): sequence i has its own
@@ -154,8 +155,8 @@ RECSA_API size_t recsa_multi_workspace_bytes(int32_t n_seq);
  * q[i][n_q_heads][head_dim] at its own position descs[i].length, with the
  * same per-level rule as recsa_decode.  out[i][n_q_heads][head_dim].  `ws`:
  * recsa_multi_workspace_bytes(n_seq) bytes of device memory, 16-byte aligned,
- * which the call fills with the sequence table on `stream`.  `dbg` may be
- * NULL (rows are i * n_q_heads + h). */
+ * which the call fills with the sequence table on `stream` (may be NULL when
+ * that is 0).  `dbg` may be NULL (rows are i * n_q_heads + h). */
 RECSA_API recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs,
                                 int32_t n_seq, const void *q, void *out, const recsa_debug *dbg,
                                 void *ws, void *stream);

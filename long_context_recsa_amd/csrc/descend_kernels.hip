@@ -272,8 +272,9 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     int64_t n_ctx = a.ctx_base + qi * a.ctx_step;
     // multi-sequence decode: this query's sequence, as byte offsets from sequence 0's buffers
     int64_t dk = 0, dv = 0, dt = 0;
-    if (a.seqs != nullptr) {
-        const SeqEntry e = a.seqs[qi], e0 = a.seqs[0];
+    if (a.seqs != nullptr || a.n_inline > 0) {
+        const SeqEntry e = a.n_inline > 0 ? a.seq_inline[qi] : a.seqs[qi];
+        const SeqEntry e0 = a.n_inline > 0 ? a.seq_inline[0] : a.seqs[0];
         n_ctx = e.length;
         dk = static_cast<const char *>(e.k_cache) - static_cast<const char *>(e0.k_cache);
         dv = static_cast<const char *>(e.v_cache) - static_cast<const char *>(e0.v_cache);

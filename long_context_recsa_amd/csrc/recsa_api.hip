@@ -354,7 +354,7 @@ recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, co
 }
 
 size_t recsa_multi_workspace_bytes(int32_t n_seq) {
-    return n_seq > 0 ? align_up((size_t)n_seq * sizeof(SeqEntry)) : 0;
+    return n_seq > kInlineSeqs ? align_up((size_t)n_seq * sizeof(SeqEntry)) : 0;
 }
 
 recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs, int32_t n_seq,
@@ -374,24 +374,32 @@ recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *de
     if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
     if (!aligned(q, 16) || !aligned(out, 16))
         return fail(RECSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-    if (ws == nullptr || !aligned(ws, 16))
+    if (n_seq > kInlineSeqs && (ws == nullptr || !aligned(ws, 16)))
         return fail(RECSA_ERR_INVALID_ARG,
                     "a 16-byte aligned workspace of recsa_multi_workspace_bytes(%d) bytes is needed",
                     (int)n_seq);
     if ((int64_t)n_seq * p->n_q_heads > 0x7FFFFFFF)
         return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    // the sequence table, copied into the workspace on the caller's stream (a pageable
-    // source is staged before the copy call returns)
-    thread_local std::vector<SeqEntry> table;
-    table.resize((size_t)n_seq);
-    for (int32_t i = 0; i < n_seq; ++i)
-        table[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
-    hipError_t e = hipMemcpyAsync(ws, table.data(), (size_t)n_seq * sizeof(SeqEntry),
-                                  hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "sequence table copy");
-    const TreeView tv = make_view(p, &descs[0], L);
     DescendArgs a{};
+    hipError_t e = hipSuccess;
+    if (n_seq <= kInlineSeqs) {
+        // the sequence table travels in the kernel arguments
+        a.n_inline = n_seq;
+        for (int32_t i = 0; i < n_seq; ++i)
+            a.seq_inline[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
+    } else {
+        // copied into the workspace on the caller's stream (a pageable source is staged
+        // before the copy call returns)
+        thread_local std::vector<SeqEntry> table;
+        table.resize((size_t)n_seq);
+        for (int32_t i = 0; i < n_seq; ++i)
+            table[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
+        e = hipMemcpyAsync(ws, table.data(), (size_t)n_seq * sizeof(SeqEntry), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "sequence table copy");
+        a.seqs = static_cast<const SeqEntry *>(ws);
+    }
+    const TreeView tv = make_view(p, &descs[0], L);
     a.q = q;
     a.out = out;
     a.rows = (int64_t)n_seq * p->n_q_heads;
@@ -404,7 +412,6 @@ recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *de
     a.max_cand = (int32_t)L.max_cand;
     a.scale = p->softmax_scale;
     a.out_bf16 = p->out_dtype == RECSA_BF16;
-    a.seqs = static_cast<const SeqEntry *>(ws);
     DebugView dv{};
     if (dbg != nullptr) {
         dv.selected = dbg->selected;

@@ -125,6 +125,8 @@ hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t
                         int32_t level, int64_t n0, int64_t n1, const float *pool_w,
                         float pool_scale, hipStream_t s);
 
+constexpr int kInlineSeqs = 32;    // sequences whose table travels in the kernel arguments
+
 // One sequence of a multi-sequence decode: its cache, its tree (same layout as the
 // others') and its length.
 struct SeqEntry {
@@ -145,9 +147,12 @@ struct DescendArgs {
     int32_t max_cand;          // largest candidate count of any level
     float scale;
     int32_t out_bf16;
-    // multi-sequence decode (else null): query i reads sequence i, at n_ctx = its length;
-    // the TreeView describes sequence 0 and the others are found by byte offsets from it
+    // multi-sequence decode: query i reads sequence i, at n_ctx = its length; the
+    // TreeView describes sequence 0 and the others are found by byte offsets from it.
+    // The table is inline for up to kInlineSeqs sequences, else in device memory.
     const SeqEntry *seqs;
+    int32_t n_inline;
+    SeqEntry seq_inline[kInlineSeqs];
 };
 
 hipError_t launch_descend(const TreeView &tv, recsa_dtype st, int32_t D, const DescendArgs &a,

@@ -132,8 +132,9 @@ def decode_multi(layers, q: torch.Tensor, debug: bool = False, out: torch.Tensor
         out = torch.empty(shape, dtype=first.out_dtype, device=first.device)
     descs = (recsa_tree_desc * n)(*[l.desc for l in layers])
     nbytes = recsa_multi_workspace_bytes(n)
-    if ws is None or ws.numel() < nbytes:
+    if nbytes and (ws is None or ws.numel() < nbytes):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=first.device)
     d, dbg = first._debug(n * first.p.n_q_heads, debug)
-    recsa_decode_multi(first.p, descs, n, _ptr(q), _ptr(out), dbg, _ptr(ws), first.stream())
+    recsa_decode_multi(first.p, descs, n, _ptr(q), _ptr(out), dbg, _ptr(ws) if nbytes else None,
+                       first.stream())
     return (out, d) if debug else out

@@ -136,7 +136,8 @@ def test_multi_decode_validates_before_any_hip_call():
     p = _p(capacity=1000)
     fake = 1 << 20
     assert R.recsa_multi_workspace_bytes(0) == 0
-    assert R.recsa_multi_workspace_bytes(5) >= 5 * 32
+    assert R.recsa_multi_workspace_bytes(32) == 0        # the table travels with the launch
+    assert R.recsa_multi_workspace_bytes(33) >= 33 * 32
     good = (R.recsa_tree_desc * 2)(R.recsa_tree_desc(fake, fake, fake, fake, 10),
                                    R.recsa_tree_desc(fake, fake, fake, fake, 20))
     empty = (R.recsa_tree_desc * 2)(R.recsa_tree_desc(fake, fake, fake, fake, 10),
@@ -147,7 +148,8 @@ def test_multi_decode_validates_before_any_hip_call():
         (lambda: R.recsa_decode_multi(p, good, 0, fake, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
         (lambda: R.recsa_decode_multi(p, empty, 2, fake, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
         (lambda: R.recsa_decode_multi(p, over, 1, fake, fake, ws=fake), R.RECSA_ERR_CAPACITY),
-        (lambda: R.recsa_decode_multi(p, good, 2, fake, fake, ws=None), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi(p, (R.recsa_tree_desc * 33)(*([good[0]] * 33)), 33, fake, fake,
+                                      ws=None), R.RECSA_ERR_INVALID_ARG),
         (lambda: R.recsa_decode_multi(p, good, 2, None, fake, ws=fake), R.RECSA_ERR_INVALID_ARG),
     ]
     for i, (fn, status) in enumerate(cases):

@@ -97,3 +97,30 @@ def test_serve16_sampled():
                                w.rope_base, w.softmax_scale, out[i:i + 1], sub, G, w.dtype,
                                all_out_rms=rms, head_of=lambda h: 0)
             _say(f"seq {i} L={w.L} head {g}", rep)
+
+
+def test_decode_multi_device_table():
+    """More sequences than travel with the launch (34 > 32): the table goes through
+    the workspace; every sequence equals its single-sequence decode, three against
+    the oracle."""
+    base = synth.WORKLOADS["tiny_f32_4k"]
+    rng = np.random.default_rng(8)
+    lengths = [int(x) for x in rng.integers(20, 4097, size=34)]
+    _say(f"case multi device table lengths={lengths}")
+    seqs = _sequences(base, lengths)
+    Q = synth.to_storage(rng.standard_normal((34, base.n_q, base.d)).astype(np.float32), "f32")
+    layers = [s[4] for s in seqs]
+    out, dbg = decode_multi(layers, P.to_device(Q, "f32"), debug=True)
+    torch.cuda.synchronize()
+    for i, (w, K, V, W, layer) in enumerate(seqs):
+        single = layer.decode(P.to_device(Q[i:i + 1], "f32"))
+        torch.cuda.synchronize()
+        assert torch.equal(single[0], out[i]), f"sequence {i}: batch and single decode differ"
+    for i in (0, 17, 33):
+        w, K, V, W, _ = seqs[i]
+        tree = P.head_tree(K, V, W, 0, w, w.L)
+        sub = {k: v[i:i + 1] for k, v in dbg.items()}
+        rep = P.check_rows(tree, Q[i:i + 1].astype(np.float64), [(0, 0)], lambda j: w.L, w.k,
+                           w.rope_base, w.softmax_scale, out[i:i + 1], sub, 1, "f32",
+                           head_of=lambda h: 0)
+        _say(f"seq {i} L={w.L}", rep)
