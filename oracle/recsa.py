@@ -294,6 +294,100 @@ def decode(tree: Tree, Q: np.ndarray, k: int, base: float, scale: float,
     return out, res
 
 
+# ----------------------------------------------------------------------------
+# variant: one selection shared by the query heads of a KV group
+# ----------------------------------------------------------------------------
+# Prior art, not the RecSA pages' rule: the MiniMax Sparse Attention abstract (on
+# the search-results page for "coarse attention block") selects its top-k once
+# per GQA group.  The pages do not say how a group's heads combine into one
+# score; the reading taken here is the plainest one that keeps each head's
+# softmax intact:
+#   * the group's score of a candidate is the sum of its G heads' logits (by
+#     linearity of RoPE and the inner product, the logit of the summed query);
+#   * equal scores go to the lower candidate index, as per head;
+#   * every head keeps its own logits for its own softmax over the shared
+#     entry set, and its own output.
+@dataclasses.dataclass
+class GroupResult:
+    out: np.ndarray         # [G][d], one output per head of the group
+    levels: list            # LevelTrace over the group score, top level first
+    head_z: list            # per level (same order): logits [G][n_candidates]
+
+    def selected_nodes(self, level: int) -> np.ndarray:
+        for t in self.levels:
+            if t.level == level:
+                return t.cand[t.sel_pos]
+        return np.zeros(0, np.int64)
+
+
+def descend_group(tree: Tree, Qg: np.ndarray, g: int, n_ctx: int, k: int, base: float,
+                  scale: float) -> GroupResult:
+    """Query rows Qg[G][d] of the heads that read KV head g, with one shared
+    selection per level.  The levels, candidates, entries and RoPE positions
+    are those of `descend`; only the selection score differs (the sum of the
+    heads' logits), and each head's entries carry its own logits."""
+    b = tree.b
+    N = level_sizes(n_ctx, b)
+    H = len(N) - 1
+    Qg = np.asarray(Qg, dtype=F64)
+    G = Qg.shape[0]
+    cand = np.arange(N[H], dtype=np.int64)
+    traces, head_z = [], []
+    ez = [[] for _ in range(G)]
+    ev = []
+    for l in range(H, -1, -1):
+        n = len(cand)
+        kr = rope(tree.keys[l][g][cand], np.arange(n), base)
+        z = np.stack([scale * (kr @ rope(Qg[h], n, base)) for h in range(G)])   # [G][n]
+        head_z.append(z)
+        if l == 0:
+            traces.append(LevelTrace(0, cand, z.sum(axis=0), np.zeros(0, np.int64), float("nan")))
+            for h in range(G):
+                ez[h].append(z[h])
+            ev.append(tree.vals[0][g][cand])
+            break
+        s = z.sum(axis=0)
+        m = min(k, n)
+        order = np.lexsort((np.arange(n), -s))
+        gap = float(s[order[m - 1]] - s[order[m]]) if n > m else float("nan")
+        sel = np.sort(order[:m])
+        traces.append(LevelTrace(l, cand, s, sel, gap))
+        keep = np.ones(n, bool)
+        keep[sel] = False
+        for h in range(G):
+            ez[h].append(z[h][keep])
+        ev.append(tree.vals[l][g][cand[keep]])
+        children = (cand[sel][:, None] * b + np.arange(b)).reshape(-1)
+        orphans = np.arange(b * N[l], N[l - 1], dtype=np.int64)
+        cand = np.concatenate([children, orphans])
+    v_all = np.concatenate(ev)
+    out = np.zeros((G, v_all.shape[1]))
+    for h in range(G):
+        z_all = np.concatenate(ez[h])
+        e = np.exp(z_all - z_all.max())
+        out[h] = (e @ v_all) / e.sum()
+    return GroupResult(out, traces, head_z)
+
+
+def decode_group(tree: Tree, Q: np.ndarray, k: int, base: float, scale: float,
+                 n_ctx: int | None = None, groups=None) -> tuple[np.ndarray, dict]:
+    """Decode queries Q[B][n_q][d] with one selection per (query, KV group):
+    query heads g*G .. g*G + G - 1 share it.  Returns out[B][n_q][d] (heads of
+    groups not listed stay nan) and the per-(query, group) results."""
+    Q = np.asarray(Q, F64)
+    B, nq, d = Q.shape
+    G = nq // tree.n_kv
+    n_ctx = tree.length if n_ctx is None else n_ctx
+    groups = [(i, g) for i in range(B) for g in range(tree.n_kv)] if groups is None else groups
+    out = np.full((B, nq, d), np.nan)
+    res = {}
+    for (i, g) in groups:
+        r = descend_group(tree, Q[i, g * G:(g + 1) * G], g, n_ctx, k, base, scale)
+        out[i, g * G:(g + 1) * G] = r.out
+        res[(i, g)] = r
+    return out, res
+
+
 def prefill(tree: Tree, Q: np.ndarray, k: int, base: float, scale: float,
             rows=None, force=None) -> tuple[np.ndarray, dict]:
     """Causal chunk: Q[n][n_q][d] are the queries of the last n tokens of the

@@ -346,3 +346,73 @@ def test_generator_slabs_independent():
     K2, V2 = synth.gen_kv(w, 65000, 70000, heads=[3])
     assert np.array_equal(K[0, 65000:], K2[0]) and np.array_equal(V[0, 65000:], V2[0])
     assert np.array_equal(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(K)), K)
+
+
+# -------------------------------------------- group-shared selection variant --
+@pytest.mark.parametrize("L,b,k,d", CASES[:6])
+def test_group_selection_is_the_summed_query_brute_force(L, b, k, d):
+    """The group score is the sum of the heads' logits.  RoPE and the inner
+    product are linear in q, so the shared selection must be the one the
+    brute-force enumeration makes for the single query q_1 + ... + q_G."""
+    r, K, V, w = _rand_inputs(2000 + L, L, d, scale_w=3.0)
+    base, ps, s = 10000.0, 1 / math.sqrt(d), 1 / math.sqrt(d)
+    tree = O.build_tree(K, V, w, b, "f32", ps, L)
+    bk, bv = BF.build(K[0].tolist(), V[0].tolist(), w[0].tolist(), b, ps, L)
+    for t in range(3):
+        Qg = r.standard_normal((4, d)) * 2.0
+        n_ctx = int(r.integers(1, L + 1)) if t else L
+        res = O.descend_group(tree, Qg, 0, n_ctx, k, base, s)
+        _, sels, _ = BF.row(bk, bv, Qg.sum(axis=0).tolist(), n_ctx, b, k, base, s)
+        if any(np.isfinite(lt.gap) and lt.gap < 1e-9 for lt in res.levels):
+            continue
+        for lev, nodes in sels.items():
+            assert list(res.selected_nodes(lev)) == nodes
+
+
+@pytest.mark.parametrize("L,b,k", [(300, 3, 2), (1000, 4, 3), (4096, 16, 4)])
+def test_group_heads_are_per_head_descents_on_the_shared_selection(L, b, k):
+    """Each head's output is the per-head mixed softmax with the selection
+    replaced by the group's (the per-head oracle replays a given selection)."""
+    d = 8
+    r, K, V, w = _rand_inputs(L + 5, L, d, n_kv=2)
+    tree = O.build_tree(K, V, w, b, "f32", 0.4, L)
+    for g in range(2):
+        Qg = r.standard_normal((3, d)) * 1.5
+        n_ctx = L - 7 * g
+        res = O.descend_group(tree, Qg, g, n_ctx, k, 1e4, 0.35)
+        force = {t.level: t.cand[t.sel_pos] for t in res.levels if t.level > 0}
+        for h in range(3):
+            ref = O.descend(tree, Qg[h], g, n_ctx, k, 1e4, 0.35, force=force)
+            np.testing.assert_allclose(res.out[h], ref.out, rtol=0, atol=1e-12)
+            # the heads' logits are their own, not the group score
+            for lt, z in zip(ref.levels, res.head_z):
+                np.testing.assert_allclose(z[h], lt.z, rtol=0, atol=1e-12)
+
+
+def test_group_of_one_and_identical_heads_reduce_to_per_head():
+    w = synth.WORKLOADS["tiny_f32_4k"]
+    K, V = synth.gen_kv(w)
+    tree = O.build_tree(K, V, synth.pool_w(w), w.b, "f32", w.pool_scale, w.L)
+    Q = synth.decode_queries(w, 4)
+    for i in range(4):
+        q = Q[i, 0]
+        ref = O.descend(tree, q, 0, w.L, w.k, w.rope_base, w.softmax_scale)
+        one = O.descend_group(tree, q[None], 0, w.L, w.k, w.rope_base, w.softmax_scale)
+        same = O.descend_group(tree, np.stack([q] * 4), 0, w.L, w.k, w.rope_base,
+                               w.softmax_scale)
+        for res in (one, same):
+            for lev in range(1, len(ref.levels)):
+                assert list(res.selected_nodes(lev)) == list(ref.selected_nodes(lev))
+            np.testing.assert_allclose(res.out, np.stack([ref.out] * len(res.out)), atol=1e-12)
+
+
+def test_group_k_covers_everything_is_dense_per_head():
+    """With k >= every candidate count nothing is summarized: every head's
+    output is its own dense causal attention, whatever the group shares."""
+    r, K, V, w = _rand_inputs(11, 1023, 8)
+    tree = O.build_tree(K, V, w, 32, "f32", 0.3, 1023)
+    Qg = r.standard_normal((4, 8))
+    res = O.descend_group(tree, Qg, 0, 1023, 32, 1e4, 0.35)
+    for h in range(4):
+        np.testing.assert_allclose(res.out[h], _sdpa_dense(Qg[h], K[0], V[0], 1023, 1e4, 0.35),
+                                   atol=1e-10)
