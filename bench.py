@@ -1,9 +1,10 @@
 """Benchmark of the RecSA hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-build the tree over the L cached tokens, decode a batch at length L, append
-the prefill chunk (growing the tree) and run the causal prefill of that
-chunk.  Each call is timed with HIP events on the stream it is launched on.
+build the tree over the L cached tokens, decode a batch at length L (per
+query head, then again with one selection per KV group), append the prefill
+chunk (growing the tree) and run the causal prefill of that chunk.  Each call
+is timed with HIP events on the stream it is launched on.
 
 Prints one JSON line: value = decode queries/s; prefill tokens/s, tree-build
 bandwidth and the roofline fractions of every kernel ride along.
@@ -90,6 +91,9 @@ def algorithmic(w, B):
     kd, vd = row_entries(w.L, w.b, w.k)
     decode_bytes = B * w.n_q * (kd + vd) * row_b
     decode_flops = B * w.n_q * (kd + vd) * 2 * w.d
+    # one selection per (query, KV group): each group row reads its keys and values once
+    # for its G heads
+    grouped_bytes = B * w.n_kv * (kd + vd) * row_b
     pk = pv = 0
     for j in range(w.prefill_n):
         a, c = row_entries(w.L + j + 1, w.b, w.k)
@@ -106,6 +110,7 @@ def algorithmic(w, B):
     new_nodes = sum(Nt[l] - (N[l] if l < len(N) else 0) for l in range(1, len(Nt)))
     append_bytes = 2 * 2 * w.n_kv * w.prefill_n * row_b + 2 * w.n_kv * new_nodes * row_b
     return dict(build=build_bytes, decode=decode_bytes, decode_flops=decode_flops,
+                decode_grouped=grouped_bytes,
                 prefill=prefill_bytes, prefill_flops=prefill_flops, append=append_bytes,
                 prefill_read_once=prefill_read_once,
                 decode_entries_per_row=kd + vd)
@@ -291,11 +296,12 @@ def main():
         q_pre = dev_store(Qp)
         out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
     out_dec = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
+    out_grp = torch.empty_like(out_dec)
     del K, V
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
-    ops = ["build", "decode"] + (["append", "prefill"] if w.prefill_n else [])
+    ops = ["build", "decode", "decode_grouped"] + (["append", "prefill"] if w.prefill_n else [])
     ev = {o: [] for o in ops}
 
     def step(record):
@@ -309,6 +315,8 @@ def main():
         mark("build")
         layer.decode(q_dec, out=out_dec)
         mark("decode")
+        layer.decode_grouped(q_dec, out=out_grp)
+        mark("decode_grouped")
         if w.prefill_n:
             layer.append(k_new, v_new)
             mark("append")
@@ -336,6 +344,9 @@ def main():
                           "achieved": alg["build"] / ms["build"] / 1e6, "unit": "GB/s"}
     kern["decode"] = {"bound": "hbm", "bytes": alg["decode"], "ms": ms["decode"],
                       "achieved": alg["decode"] / ms["decode"] / 1e6, "unit": "GB/s"}
+    kern["decode_grouped"] = {"bound": "hbm", "bytes": alg["decode_grouped"], "ms": ms["decode_grouped"],
+                              "achieved": alg["decode_grouped"] / ms["decode_grouped"] / 1e6,
+                              "unit": "GB/s"}
     if w.prefill_n:
         # the chunk's rows share parents, so the HBM floor is reading every reachable K/V row,
         # tree node and query once and writing the output; the bytes the rows would gather
@@ -373,6 +384,7 @@ def main():
                    "n_q_heads": w.n_q,
                    "head_dim": w.d, "b": w.b, "k": w.k, "decode_batch": B,
                    "prefill_chunk": w.prefill_n},
+        "grouped_decode_queries_per_s": B / (ms["decode_grouped"] / 1e3),
         "prefill_tokens_per_s": (w.prefill_n / ((ms["append"] + ms["prefill"]) / 1e3)
                                  if w.prefill_n else None),
         "ms": ms,

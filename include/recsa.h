@@ -145,6 +145,25 @@ RECSA_API recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc
                           int32_t batch, void *out, const recsa_debug *dbg, void *ws,
                           void *stream);
 
+/* Decode with one selection per (query, KV group) instead of per query head:
+ * the G = n_q_heads / n_kv_heads heads h = g*G .. g*G + G - 1 that read KV
+ * head g descend together.  Per level the group's score of a candidate is the
+ * sum of the G heads' logits z_i (the logit of the summed query, since RoPE
+ * and the inner product are linear); the min(k, n) best by that score are
+ * kept (equal scores: lower candidate index), for all G heads.  Each head's
+ * softmax runs over the shared entries with its own logits, so each key and
+ * value row is read once per group rather than once per head.  This is a
+ * variant, not the RecSA rule (which selects per head): per-group top-k is
+ * the selection of MiniMax Sparse Attention (its abstract, on the search-results
+ * page for "coarse attention block"); summing the heads' logits is this
+ * library's reading of how a group scores.  q, out, ws, stream: as in
+ * recsa_decode.  `dbg` rows are i * n_kv_heads + g, and kth_gap is that of
+ * the group score.  G must be 1, 2, 4 or 8 (RECSA_ERR_UNSUPPORTED otherwise);
+ * with G = 1 the result is recsa_decode's. */
+RECSA_API recsa_status recsa_decode_grouped(const recsa_params *p, const recsa_tree_desc *desc,
+                                  const void *q, int32_t batch, void *out,
+                                  const recsa_debug *dbg, void *ws, void *stream);
+
 /* Workspace bytes recsa_decode_multi needs for n_seq sequences (device memory):
  * 0 for up to 32 sequences, whose table travels with the launch. */
 RECSA_API size_t recsa_multi_workspace_bytes(int32_t n_seq);

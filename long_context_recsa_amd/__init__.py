@@ -21,7 +21,7 @@ EXPORTED = (
     "recsa_num_levels", "recsa_tree_bytes", "recsa_tree_layout", "recsa_max_candidates",
     "recsa_workspace_bytes", "recsa_build_tree", "recsa_append", "recsa_decode",
     "recsa_prefill", "recsa_status_string", "recsa_last_error", "recsa_multi_workspace_bytes",
-    "recsa_decode_multi",
+    "recsa_decode_multi", "recsa_decode_grouped",
 )
 
 
@@ -85,6 +85,7 @@ def load_library():
         "recsa_last_error": (ctypes.c_char_p, []),
         "recsa_multi_workspace_bytes": (ctypes.c_size_t, [i32]),
         "recsa_decode_multi": (i32, [P, D, i32, v, v, G, v, v]),
+        "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -138,6 +139,12 @@ def recsa_decode(p, desc, q_ptr, batch, out_ptr, dbg=None, ws=None, stream=None)
     _check(load_library().recsa_decode(ctypes.byref(p), ctypes.byref(desc), q_ptr, batch,
                                        out_ptr, ctypes.byref(dbg) if dbg is not None else None,
                                        ws, stream))
+
+
+def recsa_decode_grouped(p, desc, q_ptr, batch, out_ptr, dbg=None, ws=None, stream=None) -> None:
+    _check(load_library().recsa_decode_grouped(ctypes.byref(p), ctypes.byref(desc), q_ptr, batch,
+                                               out_ptr, ctypes.byref(dbg) if dbg is not None else None,
+                                               ws, stream))
 
 
 def recsa_prefill(p, desc, q_ptr, n_q, out_ptr, dbg=None, ws=None, stream=None) -> None:

@@ -1,0 +1,672 @@
+// Level-wise descent with candidate-index RoPE and the mixed softmax, for
+// decode and (row by row) for causal prefill, on gfx950: the kernel templates,
+// instantiated by descend_kernels.hip (one head per row) and descend_grouped_*.hip
+// (a KV group's heads per row, sharing one selection).
+//
+// RecSA, abstract: each level above the tokens keeps at most k candidates;
+// the summaries of the candidates not kept share one softmax with the exact
+// tokens; each entry's RoPE position is its index among its level's
+// candidates.  The query's position at a level is that level's candidate
+// count n.
+//
+// Position split.  Below the top, candidate i of a level is child c of the
+// r-th kept parent (i = r*b + c), or orphan c after the m kept parents'
+// children (i = m*b + c); either way c = node mod b.  With rotate-half RoPE
+//     <rope(q, n), rope(key, i)> = <R((n - r*b) theta) q, R(c theta) key>,
+// so a row needs one rotated query per rank r (at most k + 1 per level, built
+// once per level into LDS) and each key is rotated only by its child offset c.
+// The top level has fewer than b candidates, so r = 0 and c = i there.
+//
+// Work split.  One workgroup owns one row (a query and a query head).  A
+// 16-lane group (a "slot", one DPP row) handles one candidate at a time; a
+// lane holds D/32 RoPE pairs (i, i + D/2), so rotations stay inside a lane and
+// a key row is two contiguous half-row loads per slot.  Slot s owns the child
+// offsets c = s, s + NSLOT, ... and, for each, the ranks r = 0, 1, ...: only
+// one child-offset rotation is live at a time and no candidate index needs a
+// division.  Once level l's kept set is known, one pass issues the value loads
+// of level l's entries and the key loads of level l-1's candidates together
+// (CB ranks per slot, branch-free, 32-bit offsets from uniform bases), folds
+// the values into the running softmax and scores the keys: a row pays one
+// dependent round trip per level.  The running max is shared by all slots,
+// so their partial softmax states add up at the end without rescaling.
+//
+// Selection runs on wave 0 (see select_topk.hpp) while the other waves build
+// the next level's rotated queries.
+#pragma once
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "recsa_internal.hpp"
+#include "select_topk.hpp"
+
+namespace recsa {
+namespace descend {
+
+
+constexpr int kMaxCandidates = 4096;   // the LDS selection handles up to 64 logits per lane
+
+// PP elements of T as loaded (bf16 stays packed two per register until use).
+template <typename T, int PP> struct Raw;
+template <int PP> struct Raw<bf16_t, PP> {
+    uint32_t w[PP / 2];
+    __device__ __forceinline__ void load(const bf16_t *p) {
+        if constexpr (PP == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else {
+            #pragma unroll
+            for (int i = 0; i < PP / 2; i += 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(p + 2 * i);
+                w[i] = v.x; w[i + 1] = v.y;
+            }
+        }
+    }
+    __device__ __forceinline__ void get(float *out) const {
+        #pragma unroll
+        for (int i = 0; i < PP / 2; ++i) {
+            out[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            out[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+};
+template <int PP> struct Raw<float, PP> {
+    float w[PP];
+    __device__ __forceinline__ void load(const float *p) { Vec<float, PP>::load(p, w); }
+    __device__ __forceinline__ void get(float *out) const {
+        #pragma unroll
+        for (int i = 0; i < PP; ++i) out[i] = w[i];
+    }
+};
+
+// PP consecutive (cos, sin) pairs of one table row (PP * 8 bytes, 16-byte aligned).
+template <int PP>
+__device__ __forceinline__ void load_cs(const float2 *p, float *c, float *s) {
+    #pragma unroll
+    for (int q = 0; q < PP; q += 2) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + q);
+        c[q] = v.x; s[q] = v.y; c[q + 1] = v.z; s[q + 1] = v.w;
+    }
+}
+
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));
+    return v;   // the 16-lane row sum, in the row's lane 15
+}
+
+// Candidates of level l of a row over n_ctx tokens (pw = b^l), below a level that
+// kept `kept_above` nodes.
+__device__ __forceinline__ sel::Cands level_cands(int64_t n_ctx, int64_t pw, int32_t b, bool top,
+                                                  int32_t kept_above) {
+    sel::Cands c;
+    const int64_t Nl = n_ctx / pw;
+    c.b = b;
+    c.top = top;
+    if (top) {
+        c.n = (int32_t)Nl;
+        c.nchild = 0;
+        c.orphan0 = 0;
+    } else {
+        const int64_t Nup = n_ctx / (pw * b);
+        c.nchild = b * kept_above;
+        c.orphan0 = (int32_t)(Nup * b);
+        c.n = c.nchild + (int32_t)(Nl - Nup * b);
+    }
+    return c;
+}
+
+// Node id of candidate i = r*b + c (c < b).
+__device__ __forceinline__ uint32_t node_rc(int32_t i, int32_t r, int32_t c, const sel::Cands &cd,
+                                            const int32_t *parents) {
+    if (cd.top) return (uint32_t)i;
+    return i < cd.nchild ? (uint32_t)(parents[r] * cd.b + c) : (uint32_t)(cd.orphan0 + (i - cd.nchild));
+}
+
+// One pass over this slot's candidates of two levels: entries of level A (values,
+// logits zA, kept ones flagged when maskA) fold into the running softmax, and the
+// candidates of level S are scored into zS.  Either level may be empty.
+//
+// GS query heads share the pass (GS > 1: one selection per KV group).  Head j's logits
+// are row j of zA / zS (rows zstride apart) and its rotated queries start at U + j * ustride;
+// each value or key row is loaded once for all GS heads.  With GS > 1 the group score
+// (the sum of the heads' logits) goes to gS for the selection, and lane 15 of each slot
+// keeps, in smax, the largest logit per head that it scored.
+template <typename T, int D, int NW, int CB, int GS>
+__device__ __forceinline__ void fused_pass(
+    sel::Cands A, const int32_t *parA, const float *zA, const uint8_t *flagA, bool maskA,
+    const T *vA, sel::Cands S, const int32_t *parS, const T *kS, float *zS, float *gS,
+    uint8_t *flagS, const T *vS, const float *U, int32_t ustride, const float2 *rope,
+    int32_t maxc, int32_t zstride, int32_t kmax, int slot, int sub, float scale, float (&M)[GS],
+    float (&lsum)[GS], float (&acc_a)[GS][D / 32], float (&acc_b)[GS][D / 32],
+    float (&smax)[GS]) {
+    constexpr int H2 = D / 2, PP = D / 32, NSLOT = NW * 4;
+    constexpr uint32_t ROWB = D * sizeof(T);
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int32_t b = A.n > 0 ? A.b : S.b;
+    const int32_t nmax = A.n > S.n ? A.n : S.n;
+    const int32_t R = (nmax + b - 1) / b;
+    const int j0 = sub * PP;
+    const char *vAb = reinterpret_cast<const char *>(vA) + j0 * sizeof(T);
+    const char *kSb = reinterpret_cast<const char *>(kS) + j0 * sizeof(T);
+    // vS: the S candidates are tokens, entries as soon as they are scored; their values
+    // come in with their keys and join this slot's softmax online (M is then per slot)
+    const bool online = vS != nullptr;
+    const char *vSb = reinterpret_cast<const char *>(online ? vS : kS) + j0 * sizeof(T);
+    for (int32_t c = slot; c < b; c += NSLOT) {
+        float cr[PP], sr[PP];
+        if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, cr, sr);
+        for (int32_t r0 = 0; r0 < R; r0 += CB) {
+            uint32_t offA[CB], offS[CB];
+            float ea[CB][GS];
+            #pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                const int32_t r = r0 + t;
+                const int32_t i = r * b + c;
+                const int32_t ic = i < maxc ? i : maxc - 1;
+                const int32_t rc = r < kmax ? r : kmax - 1;
+                const bool okA = (i < A.n) && !(maskA && flagA[ic]);
+                #pragma unroll
+                for (int j = 0; j < GS; ++j) ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
+                offA[t] = okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u;
+                offS[t] = (i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u;
+            }
+            Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
+            if (online) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    sa[t].load(reinterpret_cast<const T *>(vSb + offS[t]));
+                    sb[t].load(reinterpret_cast<const T *>(vSb + offS[t] + H2 * sizeof(T)));
+                }
+            }
+            if (A.n > 0) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    va[t].load(reinterpret_cast<const T *>(vAb + offA[t]));
+                    vb[t].load(reinterpret_cast<const T *>(vAb + offA[t] + H2 * sizeof(T)));
+                }
+            }
+            if (S.n > 0) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    ka[t].load(reinterpret_cast<const T *>(kSb + offS[t]));
+                    kb[t].load(reinterpret_cast<const T *>(kSb + offS[t] + H2 * sizeof(T)));
+                }
+            }
+            if (A.n > 0) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    float fa[PP], fb[PP];
+                    va[t].get(fa);
+                    vb[t].get(fb);
+                    #pragma unroll
+                    for (int j = 0; j < GS; ++j) {
+                        const float pz = __builtin_amdgcn_exp2f(ea[t][j] - M[j] * kLog2e);  // 0 for -inf
+                        lsum[j] += pz;
+                        #pragma unroll
+                        for (int p = 0; p < PP; ++p) {
+                            acc_a[j][p] += pz * fa[p];
+                            acc_b[j][p] += pz * fb[p];
+                        }
+                    }
+                }
+            }
+            if (S.n > 0) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    const int32_t r = r0 + t;
+                    const int32_t i = r * b + c;
+                    const int32_t ru = (i < S.n) ? r : 0;
+                    float fa[PP], fb[PP], ra[PP], rb[PP];
+                    ka[t].get(fa);
+                    kb[t].get(fb);
+                    #pragma unroll
+                    for (int p = 0; p < PP; ++p) {
+                        ra[p] = fa[p] * cr[p] - fb[p] * sr[p];
+                        rb[p] = fb[p] * cr[p] + fa[p] * sr[p];
+                    }
+                    float fa2[PP], fb2[PP];
+                    if (online) {
+                        sa[t].get(fa2);
+                        sb[t].get(fb2);
+                    }
+                    float gsum = 0.f;
+                    #pragma unroll
+                    for (int j = 0; j < GS; ++j) {
+                        float ua[PP], ub[PP];
+                        const float *Uj = U + (size_t)j * ustride + (size_t)ru * D;
+                        Vec<float, PP>::load(Uj + j0, ua);
+                        Vec<float, PP>::load(Uj + H2 + j0, ub);
+                        float dot = 0.f;
+                        #pragma unroll
+                        for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
+                        dot = row_sum16(dot);
+                        if (online) {
+                            // the logit to all 16 lanes of the slot, then an online softmax step
+                            const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
+                            if (i < S.n) {
+                                const float Mn = fmaxf(M[j], z);
+                                const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
+                                const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
+                                lsum[j] = lsum[j] * sc + pz;
+                                #pragma unroll
+                                for (int p = 0; p < PP; ++p) {
+                                    acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
+                                    acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
+                                }
+                                M[j] = Mn;
+                            }
+                        } else if (sub == 15 && i < S.n) {
+                            const float z = scale * dot;
+                            zS[j * zstride + i] = z;
+                            if constexpr (GS > 1) {
+                                gsum += z;
+                                smax[j] = fmaxf(smax[j], z);
+                            }
+                        }
+                    }
+                    if (!online && sub == 15 && i < S.n) {
+                        if constexpr (GS > 1) gS[i] = gsum;
+                        flagS[i] = 0;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int NW, int GS>
+struct Smem {
+    // logit rows per buffer: one per head, then (GS > 1) the group score
+    static constexpr int NZ = GS == 1 ? 1 : GS + 1;
+    // logit rows are padded to a multiple of 4 floats, so every array after them is 16-byte aligned
+    __host__ __device__ static int32_t zstride(int32_t maxc) { return (maxc + 3) & ~3; }
+    static size_t bytes(int32_t maxc, int32_t k, int32_t b, int D) {
+        const size_t nrank = ((size_t)maxc + b - 1) / b;
+        const size_t floats = 2 * NZ * (size_t)zstride(maxc) + GS * nrank * D + (size_t)NW * GS * D +
+                              2 * (size_t)NW * GS + (GS > 1 ? 2 * (size_t)NW * GS + (size_t)GS * D : 0) + 4;
+        return sizeof(float) * floats + sel::kScratchBytes + sizeof(int32_t) * 2 * (size_t)k +
+               2 * (size_t)maxc;
+    }
+};
+
+// One row is one query and GS query heads of one KV head: GS = 1 (every head selects
+// for itself) or GS = G (the group's heads share one selection per level).
+template <typename T, int D, int NW, int CB, int KT, int GS>
+__global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendArgs a,
+                                                          DebugView dbg) {
+    constexpr int H2 = D / 2;
+    constexpr int PP = D / 32;
+    constexpr int NSLOT = NW * 4;
+    constexpr int NZ = Smem<NW, GS>::NZ;
+    constexpr float kLog2e = 1.4426950408889634f;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int32_t maxc = a.max_cand;
+    const int32_t b = a.b;
+    const int32_t nrank = (maxc + b - 1) / b;
+    const int32_t mz = Smem<NW, GS>::zstride(maxc);
+    float *zbuf = reinterpret_cast<float *>(smem);                        // [2][NZ][mz]
+    float *U = zbuf + 2 * NZ * mz;                                        // [GS][nrank][D]
+    float *red = U + (size_t)GS * nrank * D;                              // [NW][GS][D]
+    float *red_l = red + NW * GS * D;                                     // [NW][GS]
+    float *red_m = red_l + NW * GS;                                       // [NW][GS]
+    float *lmax = red_m + NW * GS;                    // GS > 1: [2][NW][GS] level maxima
+    float *qs = lmax + (GS > 1 ? 2 * NW * GS : 0);    // GS > 1: [GS][D] the queries
+    float *misc = qs + (GS > 1 ? GS * D : 0);                             // [4]
+    unsigned char *scratch = reinterpret_cast<unsigned char *>(misc + 4); // selection scratch
+    int32_t *kept = reinterpret_cast<int32_t *>(scratch + sel::kScratchBytes);  // [2][k]
+    uint8_t *flagbuf = reinterpret_cast<uint8_t *>(kept + 2 * a.k);       // [2][maxc]
+    // head j's logits and the selection score of buffer `buf`
+    auto zrow = [&](int buf, int j) { return zbuf + (size_t)(buf * NZ + j) * mz; };
+    auto zsel = [&](int buf) { return zbuf + (size_t)(buf * NZ + (GS == 1 ? 0 : GS)) * mz; };
+
+    const int64_t row = blockIdx.x;
+    const int32_t rows_per_q = a.Hq / GS;
+    const int64_t qi = row / rows_per_q;
+    const int h0 = (int)(row - qi * rows_per_q) * GS;     // first query head of the row
+    const int g = h0 / a.G;
+    int64_t n_ctx = a.ctx_base + qi * a.ctx_step;
+    // multi-sequence decode: this query's sequence, as byte offsets from sequence 0's buffers
+    int64_t dk = 0, dv = 0, dt = 0;
+    if (a.seqs != nullptr || a.n_inline > 0) {
+        const SeqEntry e = a.n_inline > 0 ? a.seq_inline[qi] : a.seqs[qi];
+        const SeqEntry e0 = a.n_inline > 0 ? a.seq_inline[0] : a.seqs[0];
+        n_ctx = e.length;
+        dk = static_cast<const char *>(e.k_cache) - static_cast<const char *>(e0.k_cache);
+        dv = static_cast<const char *>(e.v_cache) - static_cast<const char *>(e0.v_cache);
+        dt = static_cast<const char *>(e.tree) - static_cast<const char *>(e0.tree);
+    }
+    // level l's keys / values of KV head g (l >= 1), in this query's tree
+    auto lkey = [&](int l) {
+        return reinterpret_cast<const T *>(static_cast<const char *>(tv.key[l]) + dt) +
+               (int64_t)g * tv.node_cap[l] * D;
+    };
+    auto lval = [&](int l) {
+        return reinterpret_cast<const T *>(static_cast<const char *>(tv.val[l]) + dt) +
+               (int64_t)g * tv.node_cap[l] * D;
+    };
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, sub = lane & 15;
+    const int slot = wave * 4 + grp;
+    const int j0 = sub * PP;
+    const int nlev = tv.n_levels;
+    const float2 *rope = tv.rope;
+
+    // levels above the tokens for this row: H = max{l : n_ctx / b^l >= 1}
+    int H = 0;
+    int64_t pwH = 1;
+    while (n_ctx / (pwH * b) >= 1) { pwH *= b; ++H; }
+
+    // The top level (H >= 1) has fewer than b nodes, all of them candidates at rank 0:
+    // with at most 64 of them, their keys and child-offset rotations are loaded now,
+    // alongside the query, instead of after the query's rotation is built.
+    constexpr int CT = NSLOT >= 64 ? 1 : 64 / NSLOT;
+    sel::Cands cA = level_cands(n_ctx, pwH, b, true, 0);
+    const bool top_early = H >= 1 && cA.n <= CT * NSLOT;
+    Raw<T, PP> tka[CT], tkb[CT];
+    float tc[CT][PP], ts[CT][PP];
+    if (top_early) {
+        const T *kH = lkey(H);
+        #pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int32_t c = slot + t * NSLOT;
+            const int32_t cc = c < cA.n ? c : 0;
+            tka[t].load(kH + (int64_t)cc * D + j0);
+            tkb[t].load(kH + (int64_t)cc * D + H2 + j0);
+            load_cs<PP>(rope + (int64_t)cc * H2 + j0, tc[t], ts[t]);
+        }
+    }
+    // the row's queries: in registers for one head, in LDS for a group
+    float qa[PP], qb[PP];
+    const T *qrow = static_cast<const T *>(a.q) + (qi * a.Hq + h0) * D;
+    if constexpr (GS == 1) {
+        Vec<T, PP>::load(qrow + j0, qa);
+        Vec<T, PP>::load(qrow + H2 + j0, qb);
+    } else {
+        for (int e = threadIdx.x * 2; e < GS * D; e += NW * 64 * 2) {
+            float v[2];
+            Vec<T, 2>::load(qrow + e, v);
+            qs[e] = v[0];
+            qs[e + 1] = v[1];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        for (int l = H + 1; l <= nlev; ++l) {
+            if (dbg.selected != nullptr)
+                for (int t = 0; t < a.k; ++t) dbg.selected[(row * nlev + l - 1) * a.k + t] = -1;
+            if (dbg.kth_gap != nullptr) dbg.kth_gap[row * nlev + l - 1] = NAN;
+        }
+    }
+
+    const T *kcache = reinterpret_cast<const T *>(static_cast<const char *>(tv.k_cache) + dk) +
+                      (int64_t)g * tv.cap * D;
+    const T *vcache = reinterpret_cast<const T *>(static_cast<const char *>(tv.v_cache) + dv) +
+                      (int64_t)g * tv.cap * D;
+
+    // U[j][r] = R((n - r*b) theta) q_j for the ranks r < ceil(n / b) of a level with n
+    // candidates; slots from first_slot on share the (head, rank) pairs.
+    const int32_t ustride = nrank * D;
+    auto build_ranks = [&](int32_t n, int first_slot) {
+        const int32_t R = (n + b - 1) / b;
+        for (int32_t x = slot - first_slot; x < GS * R; x += NSLOT - first_slot) {
+            const int j = GS == 1 ? 0 : x / R;
+            const int32_t r = x - j * R;
+            float c[PP], s[PP], ua[PP], ub[PP], xa[PP], xb[PP];
+            if constexpr (GS == 1) {
+                #pragma unroll
+                for (int p = 0; p < PP; ++p) { xa[p] = qa[p]; xb[p] = qb[p]; }
+            } else {
+                Vec<float, PP>::load(qs + j * D + j0, xa);
+                Vec<float, PP>::load(qs + j * D + H2 + j0, xb);
+            }
+            load_cs<PP>(rope + (int64_t)(n - r * b) * H2 + j0, c, s);
+            #pragma unroll
+            for (int p = 0; p < PP; ++p) {
+                ua[p] = xa[p] * c[p] - xb[p] * s[p];
+                ub[p] = xb[p] * c[p] + xa[p] * s[p];
+            }
+            Vec<float, PP>::store(U + (size_t)j * ustride + (size_t)r * D + j0, ua);
+            Vec<float, PP>::store(U + (size_t)j * ustride + (size_t)r * D + H2 + j0, ub);
+        }
+    };
+    // GS > 1: the per-head maxima a pass found (lane 15 of each slot) go to lmax[buf]
+    auto publish_max = [&](float (&smax)[GS], int buf) {
+        if constexpr (GS > 1) {
+            #pragma unroll
+            for (int j = 0; j < GS; ++j) {
+                float v = fmaxf(smax[j], __shfl_xor(smax[j], 16));
+                v = fmaxf(v, __shfl_xor(v, 32));
+                if (lane == 15) lmax[(buf * NW + wave) * GS + j] = v;
+                smax[j] = -INFINITY;
+            }
+        }
+    };
+
+    float M[GS], lsum[GS], acc_a[GS][PP], acc_b[GS][PP], smax[GS];
+    #pragma unroll
+    for (int j = 0; j < GS; ++j) {
+        M[j] = -INFINITY;
+        lsum[j] = 0.f;
+        smax[j] = -INFINITY;
+        #pragma unroll
+        for (int p = 0; p < PP; ++p) { acc_a[j][p] = 0.f; acc_b[j][p] = 0.f; }
+    }
+    int64_t keys_scored = 0;
+
+    // ---- top level: score all of its candidates -------------------------------------
+    {
+        build_ranks(cA.n, 0);
+        __syncthreads();
+        if (top_early) {
+            const int buf = H & 1;
+            uint8_t *fH = flagbuf + buf * maxc;
+            #pragma unroll
+            for (int t = 0; t < CT; ++t) {
+                const int32_t c = slot + t * NSLOT;
+                float fa[PP], fb[PP], ra[PP], rb[PP];
+                tka[t].get(fa);
+                tkb[t].get(fb);
+                #pragma unroll
+                for (int p = 0; p < PP; ++p) {
+                    ra[p] = fa[p] * tc[t][p] - fb[p] * ts[t][p];
+                    rb[p] = fb[p] * tc[t][p] + fa[p] * ts[t][p];
+                }
+                float gsum = 0.f;
+                #pragma unroll
+                for (int j = 0; j < GS; ++j) {
+                    float ua[PP], ub[PP];
+                    Vec<float, PP>::load(U + (size_t)j * ustride + j0, ua);
+                    Vec<float, PP>::load(U + (size_t)j * ustride + H2 + j0, ub);
+                    float dot = 0.f;
+                    #pragma unroll
+                    for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
+                    dot = row_sum16(dot);
+                    if (sub == 15 && c < cA.n) {
+                        const float z = a.scale * dot;
+                        zrow(buf, j)[c] = z;
+                        gsum += z;
+                        smax[j] = fmaxf(smax[j], z);
+                    }
+                }
+                if (sub == 15 && c < cA.n) {
+                    if constexpr (GS > 1) zsel(buf)[c] = gsum;
+                    fH[c] = 0;
+                }
+            }
+            publish_max(smax, buf);
+        } else {
+            sel::Cands none = cA;
+            none.n = 0;
+            const T *kH = H == 0 ? kcache : lkey(H);
+            const int buf = H & 1;
+            // with no level above the tokens, the top candidates are tokens: entries at once
+            fused_pass<T, D, NW, CB, GS>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
+                                         zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
+                                         H == 0 ? vcache : nullptr, U, ustride, rope, maxc, mz, a.k, slot,
+                                         sub, a.scale, M, lsum, acc_a, acc_b, smax);
+            if (H > 0) publish_max(smax, buf);
+        }
+        keys_scored += cA.n;
+    }
+
+    // Levels H..1: select level l, then one pass over level l's entries and level l-1's
+    // candidates.  At l = 1 those are tokens, which join the softmax as they are scored,
+    // so the tokens' keys and values come in one round trip.
+    int64_t pw = pwH;
+    for (int l = H; l >= 1; --l, pw /= b) {
+        __syncthreads();
+        const int bufA = l & 1, bufS = (l + 1) & 1;
+        uint8_t *flagA = flagbuf + bufA * maxc;
+        const int32_t mA = a.k < cA.n ? a.k : cA.n;
+        const int32_t *parentsA = kept + bufS * a.k;
+        int32_t *keptA = kept + bufA * a.k;
+        const sel::Cands cS = level_cands(n_ctx, pw / b, b, false, mA);
+        // ---- selection at level l (wave 0); the other waves build level l-1's ranks -----
+        if (wave == 0) {
+            const float *zA = zsel(bufA);
+            if constexpr (KT > 0) {
+                if (cA.n <= 64 * KT)
+                    sel::select<KT>(zA, flagA, keptA, mA, cA, parentsA, lane, scratch, misc);
+                else
+                    sel::select<0>(zA, flagA, keptA, mA, cA, parentsA, lane, scratch, misc);
+            } else {
+                sel::select<0>(zA, flagA, keptA, mA, cA, parentsA, lane, scratch, misc);
+            }
+            if (lane == 0 && dbg.kth_gap != nullptr)
+                dbg.kth_gap[row * nlev + l - 1] = misc[1] - misc[2];
+            if (dbg.selected != nullptr) {
+                int32_t *ds = dbg.selected + (row * nlev + l - 1) * a.k;
+                for (int q = lane; q < a.k; q += 64) ds[q] = q < mA ? keptA[q] : -1;
+            }
+        } else {
+            build_ranks(cS.n, 4);
+        }
+        __syncthreads();
+
+        // ---- fused pass: entries of level l, candidates of level l-1 ---------------------
+        // the running max moves to the largest logit of level l (per head)
+        #pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            float lm;
+            if constexpr (GS == 1) {
+                lm = misc[0];
+            } else {
+                lm = lmax[(bufA * NW) * GS + j];
+                for (int w = 1; w < NW; ++w) lm = fmaxf(lm, lmax[(bufA * NW + w) * GS + j]);
+            }
+            const float Mn = fmaxf(M[j], lm);
+            const float corr = (M[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
+            lsum[j] *= corr;
+            #pragma unroll
+            for (int p = 0; p < PP; ++p) { acc_a[j][p] *= corr; acc_b[j][p] *= corr; }
+            M[j] = Mn;
+        }
+        const T *vA = lval(l);
+        const T *kS = l == 1 ? kcache : lkey(l - 1);
+        fused_pass<T, D, NW, CB, GS>(cA, parentsA, zrow(bufA, 0), flagA, true, vA, cS, keptA, kS,
+                                     zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
+                                     l == 1 ? vcache : nullptr, U, ustride, rope, maxc, mz, a.k, slot, sub,
+                                     a.scale, M, lsum, acc_a, acc_b, smax);
+        if (l > 1) publish_max(smax, bufS);
+        keys_scored += cS.n;
+        cA = cS;
+    }
+
+    // combine the slots, per head: each slot has its own running max after the tokens;
+    // rescale to the largest, then add the four lane groups by shuffles and the waves
+    // through LDS
+    #pragma unroll
+    for (int j = 0; j < GS; ++j) {
+        float mw = fmaxf(M[j], __shfl_xor(M[j], 16));
+        mw = fmaxf(mw, __shfl_xor(mw, 32));
+        if (lane == 0) red_m[wave * GS + j] = mw;
+    }
+    __syncthreads();
+    #pragma unroll
+    for (int j = 0; j < GS; ++j) {
+        float mf = red_m[j];
+        for (int w = 1; w < NW; ++w) mf = fmaxf(mf, red_m[w * GS + j]);
+        const float sc = (M[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M[j] - mf) * kLog2e);
+        lsum[j] *= sc;
+        #pragma unroll
+        for (int p = 0; p < PP; ++p) { acc_a[j][p] *= sc; acc_b[j][p] *= sc; }
+        #pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            lsum[j] += __shfl_xor(lsum[j], off);
+            #pragma unroll
+            for (int p = 0; p < PP; ++p) {
+                acc_a[j][p] += __shfl_xor(acc_a[j][p], off);
+                acc_b[j][p] += __shfl_xor(acc_b[j][p], off);
+            }
+        }
+        if (grp == 0) {
+            float *rw = red + (size_t)(wave * GS + j) * D;
+            #pragma unroll
+            for (int p = 0; p < PP; ++p) {
+                rw[j0 + p] = acc_a[j][p];
+                rw[H2 + j0 + p] = acc_b[j][p];
+            }
+            if (sub == 0) red_l[wave * GS + j] = lsum[j];
+        }
+    }
+    __syncthreads();
+    // head j's output: slot j (and j + NSLOT, ...) adds the waves' partial sums
+    for (int j = slot; j < GS; j += NSLOT) {
+        float oa[PP], ob[PP], L = 0.f;
+        #pragma unroll
+        for (int p = 0; p < PP; ++p) { oa[p] = 0.f; ob[p] = 0.f; }
+        for (int w = 0; w < NW; ++w) {
+            const float *rw = red + (size_t)(w * GS + j) * D;
+            L += red_l[w * GS + j];
+            #pragma unroll
+            for (int p = 0; p < PP; ++p) {
+                oa[p] += rw[j0 + p];
+                ob[p] += rw[H2 + j0 + p];
+            }
+        }
+        #pragma unroll
+        for (int p = 0; p < PP; ++p) { oa[p] /= L; ob[p] /= L; }
+        const int64_t orow = qi * a.Hq + h0 + j;
+        if (a.out_bf16) {
+            bf16_t *o = static_cast<bf16_t *>(a.out) + orow * D;
+            Vec<bf16_t, PP>::store(o + j0, oa);
+            Vec<bf16_t, PP>::store(o + H2 + j0, ob);
+        } else {
+            float *o = static_cast<float *>(a.out) + orow * D;
+            Vec<float, PP>::store(o + j0, oa);
+            Vec<float, PP>::store(o + H2 + j0, ob);
+        }
+    }
+    if (threadIdx.x == 0 && dbg.n_keys != nullptr) dbg.n_keys[row] = (int32_t)keys_scored;
+}
+
+template <typename T, int D, int NW, int CB, int KT, int GS>
+hipError_t launch_descend_t(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
+                            hipStream_t s) {
+    const size_t smem = Smem<NW, GS>::bytes(a.max_cand, a.k, a.b, D);
+    if (smem > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)descend_kernel<T, D, NW, CB, KT, GS>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((descend_kernel<T, D, NW, CB, KT, GS>), dim3((unsigned)(a.rows / GS)),
+                       dim3(NW * 64), smem, s, tv, a, dbg);
+    return hipGetLastError();
+}
+
+// Logits per lane the selection keeps in registers, from the widest level.
+template <typename T, int D, int NW, int CB, int GS>
+hipError_t launch_kt(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
+                     hipStream_t s) {
+    const int32_t n = a.max_cand;
+    if (n <= 64 * 2) return launch_descend_t<T, D, NW, CB, 2, GS>(tv, a, dbg, s);
+    if (n <= 64 * 5) return launch_descend_t<T, D, NW, CB, 5, GS>(tv, a, dbg, s);
+    if (n <= 64 * 9) return launch_descend_t<T, D, NW, CB, 9, GS>(tv, a, dbg, s);
+    if (n <= 64 * 17) return launch_descend_t<T, D, NW, CB, 17, GS>(tv, a, dbg, s);
+    return launch_descend_t<T, D, NW, CB, 0, GS>(tv, a, dbg, s);
+}
+
+}  // namespace descend
+}  // namespace recsa

@@ -12,7 +12,7 @@
 #include "recsa_internal.hpp"
 
 namespace recsa {
-size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D);
+size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D, int32_t gs);
 int32_t descend_max_candidates();
 size_t tiled_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
                              int32_t maxc, int64_t capacity, int32_t n_levels);
@@ -148,7 +148,7 @@ recsa_status check_limits(const recsa_params *p, const Layout &L) {
                     "a level can hold %lld candidates (min(capacity, k*b + b - 1)); at most %d "
                     "are supported",
                     (long long)L.max_cand, descend_max_candidates());
-    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->fanout_b, p->head_dim) > kMaxLds)
+    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->fanout_b, p->head_dim, 1) > kMaxLds)
         return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
     return RECSA_OK;
 }
@@ -206,11 +206,21 @@ recsa_status grow_levels(const recsa_params *p, const recsa_tree_desc *d, const 
 
 recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const void *q,
                          int64_t n_queries, int64_t ctx_base, int32_t ctx_step, void *out,
-                         const recsa_debug *dbg, bool tiled, void *ws, hipStream_t s) {
+                         const recsa_debug *dbg, bool tiled, void *ws, hipStream_t s,
+                         bool group_shared = false) {
     recsa_status st = check_params(p);
     if (st != RECSA_OK) return st;
     const Layout L = make_layout(p);
     if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    const int32_t G = p->n_q_heads / p->n_kv_heads;
+    const int32_t gs = group_shared ? G : 1;
+    if (gs != 1 && gs != 2 && gs != 4 && gs != 8)
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "a shared selection is built for groups of 1, 2, 4 or 8 query heads (got %d)",
+                    (int)G);
+    if (descend_lds_bytes((int32_t)L.max_cand, p->budget_k, p->fanout_b, p->head_dim, gs) > kMaxLds)
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "budget_k and fanout_b need more LDS than a CU has for %d heads per row", (int)gs);
     if ((st = check_desc(p, d)) != RECSA_OK) return st;
     if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
     if (!aligned(q, 16) || !aligned(out, 16))
@@ -223,7 +233,8 @@ recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const 
     a.out = out;
     a.rows = rows;
     a.Hq = p->n_q_heads;
-    a.G = p->n_q_heads / p->n_kv_heads;
+    a.G = G;
+    a.gs = gs;
     a.ctx_base = ctx_base;
     a.ctx_step = ctx_step;
     a.b = p->fanout_b;
@@ -353,6 +364,17 @@ recsa_status recsa_decode(const recsa_params *p, const recsa_tree_desc *desc, co
                        static_cast<hipStream_t>(stream));
 }
 
+recsa_status recsa_decode_grouped(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                                  int32_t batch, void *out, const recsa_debug *dbg, void *ws,
+                                  void *stream) {
+    (void)ws;
+    if (batch < 1) return fail(RECSA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (desc != nullptr && desc->length < 1)
+        return fail(RECSA_ERR_INVALID_ARG, "decode needs at least one cached token");
+    return run_descend(p, desc, q, batch, desc ? desc->length : 0, 0, out, dbg, false, nullptr,
+                       static_cast<hipStream_t>(stream), true);
+}
+
 size_t recsa_multi_workspace_bytes(int32_t n_seq) {
     return n_seq > kInlineSeqs ? align_up((size_t)n_seq * sizeof(SeqEntry)) : 0;
 }
@@ -405,6 +427,7 @@ recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *de
     a.rows = (int64_t)n_seq * p->n_q_heads;
     a.Hq = p->n_q_heads;
     a.G = p->n_q_heads / p->n_kv_heads;
+    a.gs = 1;
     a.ctx_base = 0;
     a.ctx_step = 0;
     a.b = p->fanout_b;

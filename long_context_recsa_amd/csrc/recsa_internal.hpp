@@ -141,6 +141,7 @@ struct DescendArgs {
     void *out;                 // same shape, out dtype
     int64_t rows;              // queries * Hq
     int32_t Hq, G;             // query heads, query heads per KV head
+    int32_t gs;                // query heads per row: 1, or G when a group shares its selection
     int64_t ctx_base;          // n_ctx of query 0
     int32_t ctx_step;          // n_ctx of query i = ctx_base + i * ctx_step
     int32_t b, k;
@@ -157,5 +158,10 @@ struct DescendArgs {
 
 hipError_t launch_descend(const TreeView &tv, recsa_dtype st, int32_t D, const DescendArgs &a,
                           const DebugView &dbg, hipStream_t s);
+// a.gs > 1: one selection per (query, KV group), by storage type
+hipError_t launch_descend_grouped_bf16(const TreeView &tv, int32_t D, const DescendArgs &a,
+                                       const DebugView &dbg, hipStream_t s);
+hipError_t launch_descend_grouped_f32(const TreeView &tv, int32_t D, const DescendArgs &a,
+                                      const DebugView &dbg, hipStream_t s);
 
 }  // namespace recsa

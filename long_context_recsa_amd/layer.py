@@ -7,7 +7,7 @@ import ctypes
 import torch
 
 from . import (RECSA_BF16, recsa_append, recsa_build_tree, recsa_debug, recsa_decode,
-               recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
+               recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
                recsa_tree_layout, recsa_workspace_bytes)
 
@@ -95,6 +95,17 @@ class RecsaLayer:
             out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
         d, dbg = self._debug(B * self.p.n_q_heads, debug)
         recsa_decode(self.p, self.desc, _ptr(q), B, _ptr(out), dbg, None, self.stream())
+        return (out, d) if debug else out
+
+    def decode_grouped(self, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+        """Decode with one selection per (query, KV group); debug rows are i * n_kv + g."""
+        B = q.shape[0]
+        shape = (B, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        if out is None:
+            out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
+        d, dbg = self._debug(B * self.p.n_kv_heads, debug)
+        recsa_decode_grouped(self.p, self.desc, _ptr(q), B, _ptr(out), dbg, None, self.stream())
         return (out, d) if debug else out
 
     def prefill(self, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):

@@ -321,11 +321,12 @@ class GroupResult:
 
 
 def descend_group(tree: Tree, Qg: np.ndarray, g: int, n_ctx: int, k: int, base: float,
-                  scale: float) -> GroupResult:
+                  scale: float, force: dict | None = None) -> GroupResult:
     """Query rows Qg[G][d] of the heads that read KV head g, with one shared
     selection per level.  The levels, candidates, entries and RoPE positions
     are those of `descend`; only the selection score differs (the sum of the
-    heads' logits), and each head's entries carry its own logits."""
+    heads' logits), and each head's entries carry its own logits.  `force`
+    maps level -> node ids to select instead, as in `descend`."""
     b = tree.b
     N = level_sizes(n_ctx, b)
     H = len(N) - 1
@@ -350,7 +351,12 @@ def descend_group(tree: Tree, Qg: np.ndarray, g: int, n_ctx: int, k: int, base: 
         m = min(k, n)
         order = np.lexsort((np.arange(n), -s))
         gap = float(s[order[m - 1]] - s[order[m]]) if n > m else float("nan")
-        sel = np.sort(order[:m])
+        if force is not None and l in force:
+            sel = np.searchsorted(cand, np.asarray(force[l], np.int64))
+            if len(sel) != m or np.any(cand[np.minimum(sel, n - 1)] != np.asarray(force[l])):
+                raise ValueError(f"forced selection at level {l} is not a candidate set")
+        else:
+            sel = np.sort(order[:m])
         traces.append(LevelTrace(l, cand, s, sel, gap))
         keep = np.ones(n, bool)
         keep[sel] = False

@@ -156,3 +156,28 @@ def test_multi_decode_validates_before_any_hip_call():
         with pytest.raises(R.RecsaError) as e:
             fn()
         assert e.value.status == status, (i, str(e.value))
+
+
+def test_grouped_decode_validates_before_any_hip_call():
+    fake = 1 << 20
+    d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
+    cases = [
+        # groups of 3 heads: the shared selection is built for 1, 2, 4 or 8
+        (lambda: R.recsa_decode_grouped(_p(n_kv_heads=4, n_q_heads=12, capacity=1000), d, fake, 1, fake),
+         R.RECSA_ERR_UNSUPPORTED),
+        (lambda: R.recsa_decode_grouped(_p(n_kv_heads=1, n_q_heads=16, capacity=1000), d, fake, 1, fake),
+         R.RECSA_ERR_UNSUPPORTED),
+        (lambda: R.recsa_decode_grouped(_p(capacity=1000), R.recsa_tree_desc(fake, fake, fake, fake, 0),
+                                        fake, 1, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_grouped(_p(capacity=1000), d, fake, 0, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_grouped(_p(capacity=1000), d, None, 1, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_grouped(_p(capacity=1000), d, fake, 1, fake + 8), R.RECSA_ERR_INVALID_ARG),
+        # k = 64, b = 64 at G = 8: the group's logits and rotated queries exceed a CU's LDS
+        (lambda: R.recsa_decode_grouped(_p(n_kv_heads=1, n_q_heads=8, fanout_b=64, budget_k=63,
+                                           capacity=1 << 20), d, fake, 1, fake),
+         R.RECSA_ERR_UNSUPPORTED),
+    ]
+    for i, (fn, status) in enumerate(cases):
+        with pytest.raises(R.RecsaError) as e:
+            fn()
+        assert e.value.status == status, (i, str(e.value))

@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: 524K tokens (decode batch 16, append + prefill of 4096),
+benchmark times: 524K tokens (decode batch 16, per head and with one selection
+per KV group, append + prefill of 4096),
 1M tokens with block drift (decode batch 4, append + prefill of 8192) and 2M
 tokens (decode batch 1 and 32, pooler needles that the descent must reach).
 Rows are sampled; the oracle builds the trees of the sampled KV heads only."""
@@ -47,6 +48,7 @@ def test_full_decode_and_prefill(name):
     Qp = synth.prefill_queries(w)
     layer = _layer_at(w, K, V, W, w.L, Lt)
     out_d, dbg_d = layer.decode(P.to_device(Qd, w.dtype), debug=True)
+    out_g, dbg_g = layer.decode_grouped(P.to_device(Qd, w.dtype), debug=True)
     layer.append(P.to_device(np.ascontiguousarray(K[:, w.L:].transpose(1, 0, 2)), w.dtype),
                  P.to_device(np.ascontiguousarray(V[:, w.L:].transpose(1, 0, 2)), w.dtype))
     out_p, dbg_p = layer.prefill(P.to_device(Qp, w.dtype), debug=True)
@@ -59,6 +61,11 @@ def test_full_decode_and_prefill(name):
     rows_d = [(i, h) for i in range(B) for h in range(w.n_q) if h // G in heads]
     rep = _check(w, out_d, dbg_d, Qd, rows_d, lambda i: w.L, trees, rms_d)
     _say("decode", rep)
+    rms_g = float(np.sqrt(np.mean(P.to_host(out_g) ** 2)))
+    rep = P.check_groups(trees, Qd.astype(np.float64), [(i, g) for i in range(B) for g in heads],
+                         lambda i: w.L, w.k, w.rope_base, w.softmax_scale, out_g, dbg_g, w.n_kv,
+                         w.dtype, all_out_rms=rms_g)
+    _say("grouped decode", rep)
     qs = sorted(set(rng.choice(w.prefill_n, 12, replace=False).tolist()) | {0, w.prefill_n - 1})
     rows_p = [(j, h) for j in qs for h in range(w.n_q) if h // G in heads]
     rms_p = float(np.sqrt(np.mean(P.to_host(out_p) ** 2)))
