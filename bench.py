@@ -29,11 +29,24 @@ CSRC = os.path.join(ROOT, "long_context_recsa_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_{workload}.md")
 
 
-def sources_digest():
-    """sha256 over the kernel sources; HBM counters taken from an older build do not apply."""
+# Sources each library call's kernels are built from (with the shared headers and the
+# host-side launch code); HBM counters taken with other versions of them do not apply.
+OP_SOURCES = {
+    "tree_build": ["tree_kernels.hip"],
+    "append": ["tree_kernels.hip"],
+    "decode": ["descend_impl.hpp", "descend_kernels.hip", "select_topk.hpp"],
+    "decode_grouped": ["descend_impl.hpp", "descend_grouped_bf16.hip", "descend_grouped_f32.hip",
+                       "select_topk.hpp"],
+    "prefill": ["prefill_tiled.hip", "select_topk.hpp"],
+}
+COMMON_SOURCES = ["recsa_internal.hpp", "recsa_api.hip"]
+
+
+def sources_digest(op):
+    """sha256 over the kernel sources of one library call."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in sorted(OP_SOURCES[op] + COMMON_SOURCES):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -46,7 +59,7 @@ def measured_traffic(workload, kernel):
     path = COUNTERS.format(workload=workload)
     if not os.path.exists(path):
         return None
-    digest = sources_digest()
+    digest = sources_digest(kernel) if kernel in OP_SOURCES else None
     with open(path) as fh:
         for line in fh:
             parts = line.strip().strip("`").split()
@@ -358,8 +371,10 @@ def main():
                            "mfma_frac": alg["prefill_flops"] / ms["prefill"] / 1e9 / BF16_PEAK_TFLOPS}
         kern["append"] = {"bound": "hbm", "bytes": alg["append"], "ms": ms["append"],
                           "achieved": alg["append"] / ms["append"] / 1e6, "unit": "GB/s"}
-    for v in kern.values():
+    for name_, v in kern.items():
         v["frac"] = v["achieved"] / HBM_PEAK_GBS
+        t_ = measured_traffic(w.name, name_)
+        v["traffic"] = None if t_ is None else t_["fetch"] + t_["write"]
     dom = max(kern, key=lambda n: kern[n]["ms"])
     tr = measured_traffic(w.name, dom)
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": kern[dom]["achieved"],

@@ -24,10 +24,10 @@ hipError_t dispatch_grouped(const TreeView &tv, const DescendArgs &a, const Debu
             return launch_kt<bf16_t, D, 8, 4, 2>(tv, a, dbg, s);
         case 4:
             if (nw == 4) return launch_kt<bf16_t, D, 4, 4, 4>(tv, a, dbg, s);
-            return launch_kt<bf16_t, D, 8, 2, 4>(tv, a, dbg, s);
+            return launch_kt<bf16_t, D, 8, 4, 4>(tv, a, dbg, s);
         case 8:
             if (nw == 4) return launch_kt<bf16_t, D, 4, 2, 8>(tv, a, dbg, s);
-            return launch_kt<bf16_t, D, 8, 1, 8>(tv, a, dbg, s);
+            return launch_kt<bf16_t, D, 8, 2, 8>(tv, a, dbg, s);
         default:
             return hipErrorInvalidValue;
     }

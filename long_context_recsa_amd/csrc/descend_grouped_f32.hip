@@ -9,7 +9,8 @@ using namespace descend;
 
 // Launch shape: 8 waves per row by default (a group's row carries G heads' work, and
 // there are G times fewer rows than with one head per row); RECSA_DESCEND_SHAPE="4,x"
-// selects 4 waves (for tuning sweeps).
+// selects 4 waves (for tuning sweeps).  fp32 rows take twice the registers of bf16
+// ones, so fewer ranks per slot are in flight than in the bf16 variant.
 template <int D>
 hipError_t dispatch_grouped(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
                             hipStream_t s) {

@@ -96,6 +96,13 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;   // the 16-lane row sum, in the row's lane 15
 }
 
+// A wave-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Candidates of level l of a row over n_ctx tokens (pw = b^l), below a level that
 // kept `kept_above` nodes.
 __device__ __forceinline__ sel::Cands level_cands(int64_t n_ctx, int64_t pw, int32_t b, bool top,
@@ -148,12 +155,15 @@ __device__ __forceinline__ void fused_pass(
     const int32_t nmax = A.n > S.n ? A.n : S.n;
     const int32_t R = (nmax + b - 1) / b;
     const int j0 = sub * PP;
-    const char *vAb = reinterpret_cast<const char *>(vA) + j0 * sizeof(T);
-    const char *kSb = reinterpret_cast<const char *>(kS) + j0 * sizeof(T);
+    // uniform bases with the lane's slice in the 32-bit offsets: the loads can take a
+    // scalar base and one offset register each
+    const uint32_t j0b = (uint32_t)(j0 * sizeof(T));
+    const char *vAb = reinterpret_cast<const char *>(vA);
+    const char *kSb = reinterpret_cast<const char *>(kS);
     // vS: the S candidates are tokens, entries as soon as they are scored; their values
     // come in with their keys and join this slot's softmax online (M is then per slot)
     const bool online = vS != nullptr;
-    const char *vSb = reinterpret_cast<const char *>(online ? vS : kS) + j0 * sizeof(T);
+    const char *vSb = reinterpret_cast<const char *>(online ? vS : kS);
     for (int32_t c = slot; c < b; c += NSLOT) {
         float cr[PP], sr[PP];
         if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, cr, sr);
@@ -169,8 +179,8 @@ __device__ __forceinline__ void fused_pass(
                 const bool okA = (i < A.n) && !(maskA && flagA[ic]);
                 #pragma unroll
                 for (int j = 0; j < GS; ++j) ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
-                offA[t] = okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u;
-                offS[t] = (i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u;
+                offA[t] = (okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u) + j0b;
+                offS[t] = ((i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u) + j0b;
             }
             Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
             if (online) {
@@ -336,6 +346,11 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         dk = static_cast<const char *>(e.k_cache) - static_cast<const char *>(e0.k_cache);
         dv = static_cast<const char *>(e.v_cache) - static_cast<const char *>(e0.v_cache);
         dt = static_cast<const char *>(e.tree) - static_cast<const char *>(e0.tree);
+        // the same for every lane: keep them (and the bases built from them) scalar
+        dk = uniform64(dk);
+        dv = uniform64(dv);
+        dt = uniform64(dt);
+        n_ctx = uniform64(n_ctx);
     }
     // level l's keys / values of KV head g (l >= 1), in this query's tree
     auto lkey = [&](int l) {
