@@ -361,7 +361,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         return reinterpret_cast<const T *>(static_cast<const char *>(tv.val[l]) + dt) +
                (int64_t)g * tv.node_cap[l] * D;
     };
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int grp = lane >> 4, sub = lane & 15;
     const int slot = wave * 4 + grp;
     const int j0 = sub * PP;

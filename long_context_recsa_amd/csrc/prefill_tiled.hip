@@ -160,7 +160,7 @@ __device__ __forceinline__ void load_cs(const float2 *p, float *c, float *s) {
 // Exclusive scan of (x, y) over a 256-thread block; `total` gets the block sums.
 __device__ __forceinline__ int2 block_scan(int2 v, int2 &total) {
     __shared__ int2 wsum[4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_id();
     int2 inc = v;
     #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -376,7 +376,7 @@ template <typename F>
 __device__ __forceinline__ void for_items(const TP &a, int32_t NP, int lane, F &&body) {
     const int64_t n = *a.n_items;
     const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
-    int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
     if (item >= n) return;
     const int i16 = lane & 15, grp = lane >> 4;
     int4 rec = a.items[item];
@@ -390,8 +390,9 @@ __device__ __forceinline__ void for_items(const TP &a, int32_t NP, int lane, F &
         }
         Item it;
         const int32_t bkt = __builtin_amdgcn_readfirstlane(rec.x);   // uniform over the wave
-        it.g = bkt / NP;
-        it.p = bkt % NP;
+        // (the division runs on the vector unit; bring the uniform results back to scalars)
+        it.g = __builtin_amdgcn_readfirstlane(bkt / NP);
+        it.p = __builtin_amdgcn_readfirstlane(bkt % NP);
         it.cnt = __builtin_amdgcn_readfirstlane(rec.z);
         it.pr = pr;
         #pragma unroll
@@ -489,15 +490,19 @@ __device__ __forceinline__ void load_keys(const bf16_t *keys, int64_t c0, int64_
                                           int lane, KRaw<D> &r) {
     constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
     const int i16 = lane & 15, grp = lane >> 4;
+    // a uniform base (the parent's first child, or the last node when it has none) and
+    // 32-bit byte offsets: the loads take a scalar base; lanes past the children read
+    // the base row
+    const char *kb = reinterpret_cast<const char *>(keys + (c0 < nexist ? c0 : nexist - 1) * D);
     #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int c = 32 * kk + 16 * t + i16;
         const bool ok = c < b && c0 + c < nexist;
-        const bf16_t *kp = keys + (ok ? c0 + c : 0) * D + grp * PG;
+        const uint32_t off = ((ok ? (uint32_t)c * D : 0u) + grp * PG) * (uint32_t)sizeof(bf16_t);
         #pragma unroll
         for (int pc = 0; pc < KS1; ++pc) {
-            r.k[t][2 * pc] = *reinterpret_cast<const uint4 *>(kp + 8 * pc);
-            r.k[t][2 * pc + 1] = *reinterpret_cast<const uint4 *>(kp + H + 8 * pc);
+            r.k[t][2 * pc] = *reinterpret_cast<const uint4 *>(kb + off + 16 * pc);
+            r.k[t][2 * pc + 1] = *reinterpret_cast<const uint4 *>(kb + off + 2 * H + 16 * pc);
         }
     }
 }
@@ -542,11 +547,13 @@ __device__ __forceinline__ void load_values(const bf16_t *vals, int64_t c0, int6
                                             int lane, VRaw<D> &r) {
     constexpr int NT = D / 16;
     const int i16 = lane & 15, grp = lane >> 4;
+    const char *vb = reinterpret_cast<const char *>(vals + (c0 < nexist ? c0 : nexist - 1) * D);
     #pragma unroll
     for (int v = 0; v < 8; ++v) {
         const int c = 32 * kk + 8 * grp + v;
         const bool ok = c < b && c0 + c < nexist;
-        const bf16_t *vp = vals + (ok ? c0 + c : 0) * D + NT * i16;
+        const bf16_t *vp = reinterpret_cast<const bf16_t *>(
+            vb + ((ok ? (uint32_t)c * D : 0u) + NT * i16) * (uint32_t)sizeof(bf16_t));
         uint4 x;
         if constexpr (NT == 8) {
             x = *reinterpret_cast<const uint4 *>(vp);
@@ -554,7 +561,7 @@ __device__ __forceinline__ void load_values(const bf16_t *vals, int64_t c0, int6
             const uint2 y = *reinterpret_cast<const uint2 *>(vp);
             x = make_uint4(y.x, y.y, 0u, 0u);
         }
-        r.v[v] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+        r.v[v] = x;     // a missing child's P weight is 0, and its row here is the base row's
     }
 }
 
@@ -691,7 +698,7 @@ __device__ __forceinline__ void select_row(const TP &a, const DebugView &dbg, in
 template <int KT>
 __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int smem_wave) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = wave_id(), lane = threadIdx.x & 63;
     const int kq = (a.k * 4 + 15) & ~15;
     unsigned char *base = smem + w * smem_wave;
     unsigned char *scratch = base;                                             // 16-aligned
@@ -750,7 +757,7 @@ __global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) 
     extern __shared__ __align__(16) unsigned char smem[];
     float2 *crot = reinterpret_cast<float2 *>(smem);
     load_crot(tv, a.b, D, crot);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int i16 = lane & 15, grp = lane >> 4;
     constexpr int ZS = 32 * KC + 1;
     float *zw = reinterpret_cast<float *>(smem + (size_t)a.b * crot_stride(D) * sizeof(float2)) +

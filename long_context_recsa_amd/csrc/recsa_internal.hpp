@@ -32,6 +32,13 @@ struct DebugView {
     int32_t *n_keys;     // [rows]
 };
 
+// Index of the calling wave in its workgroup, as a scalar: the compiler does not treat
+// threadIdx.x / 64 as wave-uniform by itself, and branches and addresses built from
+// it would otherwise run on the vector unit under exec masks.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---- storage conversions ---------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
     int64_t n0, int64_t n1) {
     constexpr int E = D / 16;                       // elements of a row per lane
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int grp = lane >> 4, sub = lane & 15;
     const int g = blockIdx.y;
     const int64_t node = n0 + (int64_t)blockIdx.x * kNodesPerBlock + wave;
