@@ -60,6 +60,8 @@ F64 = np.float64
 def round_store(x: np.ndarray, store: str) -> np.ndarray:
     """Round float64 values to the summary storage format, returned as float64."""
     x = np.ascontiguousarray(x, dtype=F64)
+    if store == "f64":          # no rounding (gradient checks by finite differences)
+        return x
     if store == "f32":
         return x.astype(np.float32).astype(F64)
     if store != "bf16":
@@ -427,6 +429,97 @@ def prefill_sequential(K, V, w, b, store, pool_scale, L0, Q, k, base, scale):
         for h in range(nq):
             out[j, h] = descend(tree, Q[j, h], h // G, L0 + j + 1, k, base, scale).out
     return out
+
+
+# ----------------------------------------------------------------------------
+# backward through the mixed softmax, the selection held fixed
+# ----------------------------------------------------------------------------
+# The pages train RecSA end to end from a Qwen3-4B initialisation (abstract,
+# sentence on evaluation), which needs the gradient of the attention output with
+# respect to the query, the token keys and values and the pooler.  The pages give
+# no formula; the readings taken here:
+#   * the kept sets are held fixed: selection is piecewise constant in its
+#     inputs, so only the softmax entries carry gradient;
+#   * rounding a summary to the storage format passes the gradient through
+#     unchanged;
+#   * a summary key depends on its stored children's keys and on w through the
+#     pooler, and a summary value is the mean of its subtree's token values, so
+#     gradients reaching summaries flow down the tree to the tokens and to w.
+# With z = s <rope(q, n), rope(key, i)> = s q . R_(i-n) key (rotations compose):
+#   dz/dq = s rope(key, i - n),   dz/dkey = s rope(q, n - i).
+def backward_row(tree: Tree, q: np.ndarray, g: int, n_ctx: int, k: int, base: float, scale: float,
+                 dout: np.ndarray, gk: list, gv: list, force: dict | None = None) -> np.ndarray:
+    """Gradient of <dout, out> for one query row of KV head g.  Adds the
+    gradients of its entries' keys and values into gk[l][g], gv[l][g] (level 0:
+    tokens) and returns d/dq."""
+    q = np.asarray(q, F64)
+    dout = np.asarray(dout, F64)
+    res = descend(tree, q, g, n_ctx, k, base, scale, force=force)
+    p = np.exp(res.entry_z - res.entry_z.max())
+    p /= p.sum()
+    D = float(dout @ res.out)
+    dq = np.zeros_like(q)
+    e = 0
+    for lt in res.levels:
+        n = len(lt.cand)
+        keep = np.ones(n, bool)
+        keep[lt.sel_pos] = False
+        for i in np.nonzero(keep)[0]:
+            node = int(lt.cand[i])
+            key = tree.keys[lt.level][g][node]
+            val = tree.vals[lt.level][g][node]
+            dz = p[e] * (float(dout @ val) - D)
+            dq += dz * scale * rope(key, i - n, base)
+            gk[lt.level][g][node] += dz * scale * rope(q, n - i, base)
+            gv[lt.level][g][node] += p[e] * dout
+            e += 1
+    assert e == len(p)
+    return dq
+
+
+def backward_tree(tree: Tree, gk: list, gv: list) -> np.ndarray:
+    """Push the summaries' gradients down the tree, top level first: a node's
+    value is the mean of its b children's (its subtree's tokens), and its key is
+    the pooler over its b stored children's keys.  Leaves token gradients in
+    gk[0], gv[0] and returns d/dw [n_kv][d]."""
+    b = tree.b
+    dw = np.zeros_like(tree.w)
+    for l in range(len(tree.keys) - 1, 0, -1):
+        for g in range(tree.n_kv):
+            w = tree.w[g]
+            for j in range(len(tree.keys[l][g])):
+                x = tree.keys[l - 1][g][j * b:(j + 1) * b]          # the stored children
+                a = tree.pool_scale * (x @ w)
+                alpha = np.exp(a - a.max())
+                alpha /= alpha.sum()
+                gkey = gk[l][g][j]
+                dalpha = x @ gkey
+                da = alpha * (dalpha - alpha @ dalpha)
+                gk[l - 1][g][j * b:(j + 1) * b] += np.outer(alpha, gkey) + tree.pool_scale * np.outer(da, w)
+                dw[g] += tree.pool_scale * (da @ x)
+                gv[l - 1][g][j * b:(j + 1) * b] += gv[l][g][j] / b
+    return dw
+
+
+def backward(tree: Tree, Q: np.ndarray, dO: np.ndarray, k: int, base: float, scale: float,
+             causal: bool = False, rows=None, force=None) -> dict:
+    """Gradients of sum <dO, out> for decode queries Q[n][n_q][d] at the tree's
+    length (causal=False) or for the causal chunk of the last n tokens
+    (causal=True, query j at n_ctx = length - n + j + 1).  Returns dict with
+    dq [n][n_q][d], dk and dv [n_kv][length][d] and dw [n_kv][d]."""
+    Q = np.asarray(Q, F64)
+    n, nq, d = Q.shape
+    G = nq // tree.n_kv
+    gk = [[np.zeros_like(a) for a in lev] for lev in tree.keys]
+    gv = [[np.zeros_like(a) for a in lev] for lev in tree.vals]
+    dq = np.zeros((n, nq, d))
+    rows = [(i, h) for i in range(n) for h in range(nq)] if rows is None else rows
+    for (i, h) in rows:
+        n_ctx = tree.length - n + i + 1 if causal else tree.length
+        f = None if force is None else force.get((i, h))
+        dq[i, h] = backward_row(tree, Q[i, h], h // G, n_ctx, k, base, scale, dO[i, h], gk, gv, f)
+    dw = backward_tree(tree, gk, gv)
+    return {"dq": dq, "dk": np.stack(gk[0]), "dv": np.stack(gv[0]), "dw": dw}
 
 
 # ----------------------------------------------------------------------------
