@@ -190,6 +190,35 @@ RECSA_API recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_des
                            int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
                            void *stream);
 
+/* Workspace bytes recsa_backward needs (device memory, 256-byte aligned): fp32
+ * gradients of every level's summary keys and values.  0 on invalid params. */
+RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p);
+
+/* Backward of the attention output with the selection held fixed (the method
+ * is trained end to end: abstract, sentence on evaluation).  For the rows of
+ * recsa_decode (causal = 0: n_q queries at position desc->length) or of
+ * recsa_prefill (causal = 1: the last n_q tokens' queries, causal), given
+ * d_out = dL/d out [n_q][n_q_heads][head_dim] fp32, computes with the kept
+ * sets of the forward rule held fixed (selection is piecewise constant; only
+ * the softmax entries carry gradient):
+ *   d_q [n_q][n_q_heads][head_dim] fp32, written;
+ *   d_k, d_v [n_kv_heads][capacity][head_dim] fp32, ADDED TO for tokens
+ *     [0, length): entries' direct gradients plus those reaching summaries,
+ *     pushed down the tree (a summary value is its subtree's mean; a summary
+ *     key is the pooler over its stored children's keys);
+ *   d_w [n_kv_heads][head_dim] fp32, ADDED TO: the pooler vectors' gradient.
+ * Rounding a summary to store_dtype passes the gradient through unchanged.
+ * Entry logits, softmax and the selection are recomputed as in the forward.
+ * Sums over rows use fp32 atomics, so low-order bits depend on their order.
+ * q: as the forward's, store_dtype.  ws: recsa_backward_workspace_bytes(p)
+ * bytes, 256-byte aligned, cleared by the call (may be NULL when that is 0,
+ * i.e. capacity < fanout_b).  dbg (may be NULL): selected
+ * and kth_gap as recsa_decode reports them (n_keys is not written). */
+RECSA_API recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                            int64_t n_q, int32_t causal, const float *d_out, float *d_q,
+                            float *d_k, float *d_v, float *d_w, const recsa_debug *dbg, void *ws,
+                            void *stream);
+
 /* Static name of a status code. */
 RECSA_API const char *recsa_status_string(recsa_status s);
 

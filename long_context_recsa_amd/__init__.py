@@ -21,7 +21,8 @@ EXPORTED = (
     "recsa_num_levels", "recsa_tree_bytes", "recsa_tree_layout", "recsa_max_candidates",
     "recsa_workspace_bytes", "recsa_build_tree", "recsa_append", "recsa_decode",
     "recsa_prefill", "recsa_status_string", "recsa_last_error", "recsa_multi_workspace_bytes",
-    "recsa_decode_multi", "recsa_decode_grouped",
+    "recsa_decode_multi", "recsa_decode_grouped", "recsa_backward_workspace_bytes",
+    "recsa_backward",
 )
 
 
@@ -86,6 +87,8 @@ def load_library():
         "recsa_multi_workspace_bytes": (ctypes.c_size_t, [i32]),
         "recsa_decode_multi": (i32, [P, D, i32, v, v, G, v, v]),
         "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
+        "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P]),
+        "recsa_backward": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -151,6 +154,17 @@ def recsa_prefill(p, desc, q_ptr, n_q, out_ptr, dbg=None, ws=None, stream=None) 
     _check(load_library().recsa_prefill(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q,
                                         out_ptr, ctypes.byref(dbg) if dbg is not None else None,
                                         ws, stream))
+
+
+def recsa_backward_workspace_bytes(p) -> int:
+    return load_library().recsa_backward_workspace_bytes(ctypes.byref(p))
+
+
+def recsa_backward(p, desc, q_ptr, n_q, causal, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr, dbg=None,
+                   ws=None, stream=None) -> None:
+    _check(load_library().recsa_backward(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q, int(causal),
+                                         dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr,
+                                         ctypes.byref(dbg) if dbg is not None else None, ws, stream))
 
 
 def recsa_multi_workspace_bytes(n_seq: int) -> int:

@@ -458,6 +458,107 @@ recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, c
                        static_cast<hipStream_t>(stream));
 }
 
+size_t recsa_backward_workspace_bytes(const recsa_params *p) {
+    if (check_params(p) != RECSA_OK) return 0;
+    const Layout L = make_layout(p);
+    size_t total = 0;
+    for (int l = 1; l <= L.n_levels; ++l)
+        total += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+    return total;
+}
+
+recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                            int64_t n_q, int32_t causal, const float *d_out, float *d_q, float *d_k,
+                            float *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if ((st = check_desc(p, desc)) != RECSA_OK) return st;
+    if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "the backward needs at least one cached token");
+    if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
+    if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (causal && n_q > desc->length)
+        return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld)", (long long)n_q,
+                    (long long)desc->length);
+    const void *ptrs[] = {q, d_out, d_q, d_k, d_v, d_w};
+    for (const void *ptr : ptrs) {
+        if (ptr == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q, d_k, d_v and d_w must be non-NULL");
+        if (!aligned(ptr, 16)) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q, d_k, d_v and d_w must be 16-byte aligned");
+    }
+    const size_t ws_bytes = recsa_backward_workspace_bytes(p);
+    if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
+        return fail(RECSA_ERR_INVALID_ARG,
+                    "the backward needs a 256-byte aligned workspace of recsa_backward_workspace_bytes() bytes");
+    const int64_t rows = n_q * p->n_q_heads;
+    if (rows > 0x7FFFFFFF) return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    if (backward_rows_lds_bytes((int32_t)L.max_cand, p->budget_k, L.n_levels, p->head_dim) > kMaxLds)
+        return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const TreeView tv = make_view(p, desc, L);
+    BwdArgs a{};
+    a.q = q;
+    a.dout = d_out;
+    a.dq = d_q;
+    a.dk = d_k;
+    a.dv = d_v;
+    char *w = static_cast<char *>(ws);
+    for (int l = 1; l <= L.n_levels; ++l) {
+        const size_t bytes = align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+        a.gk[l] = reinterpret_cast<float *>(w);
+        a.gv[l] = reinterpret_cast<float *>(w + bytes);
+        w += 2 * bytes;
+    }
+    a.rows = rows;
+    a.Hq = p->n_q_heads;
+    a.G = p->n_q_heads / p->n_kv_heads;
+    a.ctx_base = causal ? desc->length - n_q + 1 : desc->length;
+    a.ctx_step = causal ? 1 : 0;
+    a.b = p->fanout_b;
+    a.k = p->budget_k;
+    a.max_cand = (int32_t)L.max_cand;
+    a.scale = p->softmax_scale;
+    DebugView dv{};
+    if (dbg != nullptr) {
+        dv.selected = dbg->selected;
+        dv.kth_gap = dbg->kth_gap;
+        dv.n_keys = nullptr;
+    }
+    hipError_t e = launch_fill_zero(ws, ws_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
+    e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "backward rows launch");
+    // summaries' gradients down the tree, top level first
+    int64_t pw = 1;
+    int top = 0;
+    for (int l = 1; l <= L.n_levels; ++l) {
+        pw *= p->fanout_b;
+        if (desc->length / pw < 1) break;
+        top = l;
+    }
+    for (int l = top; l >= 1; --l) {
+        int64_t pl = 1;
+        for (int i = 0; i < l; ++i) pl *= p->fanout_b;
+        BwdTreeArgs t{};
+        t.level = l;
+        t.Hkv = p->n_kv_heads;
+        t.nodes = desc->length / pl;
+        t.b = p->fanout_b;
+        t.pool_scale = p->pool_scale;
+        t.pool_w = desc->pool_w;
+        t.gk = a.gk[l];
+        t.gv = a.gv[l];
+        t.gk_child = l >= 2 ? a.gk[l - 1] : nullptr;
+        t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
+        t.dk = d_k;
+        t.dv = d_v;
+        t.dw = d_w;
+        e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
+        if (e != hipSuccess) return hip_fail(e, "backward tree launch");
+    }
+    return RECSA_OK;
+}
+
 const char *recsa_status_string(recsa_status s) {
     switch (s) {
         case RECSA_OK: return "RECSA_OK";

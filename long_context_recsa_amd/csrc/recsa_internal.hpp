@@ -165,6 +165,43 @@ struct DescendArgs {
 
 hipError_t launch_descend(const TreeView &tv, recsa_dtype st, int32_t D, const DescendArgs &a,
                           const DebugView &dbg, hipStream_t s);
+
+// ---- backward (selection held fixed) -------------------------------------------
+struct BwdArgs {
+    const void *q;             // [rows / Hq][Hq][D] store type
+    const float *dout;         // same shape, fp32
+    float *dq;                 // same shape, fp32 (written)
+    float *dk, *dv;            // [Hkv][cap][D] fp32 (added to)
+    float *gk[kMaxLevels + 1]; // gk[l], gv[l]: [Hkv][node_cap[l]][D] fp32 summary gradients (l >= 1)
+    float *gv[kMaxLevels + 1];
+    int64_t rows;              // queries * Hq
+    int32_t Hq, G;
+    int64_t ctx_base;          // n_ctx of query 0
+    int32_t ctx_step;          // n_ctx of query i = ctx_base + i * ctx_step
+    int32_t b, k;
+    int32_t max_cand;
+    float scale;
+};
+
+struct BwdTreeArgs {
+    int32_t level;             // the nodes' level (>= 1); children are level - 1
+    int32_t Hkv;
+    int64_t nodes;             // complete nodes of that level
+    int32_t b;
+    float pool_scale;
+    const float *pool_w;       // [Hkv][D]
+    const float *gk, *gv;      // the level's gradients
+    float *gk_child, *gv_child;  // level - 1's (level >= 2)
+    float *dk, *dv;            // token gradients (level 1)
+    float *dw;                 // [Hkv][D] (added to)
+};
+
+size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, const BwdArgs &a,
+                                const DebugView &dbg, hipStream_t s);
+hipError_t launch_backward_tree(const TreeView &tv, recsa_dtype st, int32_t D, const BwdTreeArgs &t,
+                                hipStream_t s);
 // a.gs > 1: one selection per (query, KV group), by storage type
 hipError_t launch_descend_grouped_bf16(const TreeView &tv, int32_t D, const DescendArgs &a,
                                        const DebugView &dbg, hipStream_t s);

@@ -6,8 +6,8 @@ import ctypes
 
 import torch
 
-from . import (RECSA_BF16, recsa_append, recsa_build_tree, recsa_debug, recsa_decode,
-               recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
+from . import (RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
+               recsa_build_tree, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
                recsa_tree_layout, recsa_workspace_bytes)
 
@@ -39,6 +39,7 @@ class RecsaLayer:
         self.desc = recsa_tree_desc(self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                                     self.tree.data_ptr(), self.pool_w.data_ptr(), 0)
         self._ws = None
+        self._bws = None
 
     def workspace(self, rows: int):
         """Device scratch for a call over `rows` rows, as the library sizes it (kept and
@@ -118,6 +119,32 @@ class RecsaLayer:
         ws = self.workspace(n * self.p.n_q_heads)
         recsa_prefill(self.p, self.desc, _ptr(q), n, _ptr(out), dbg, ws, self.stream())
         return (out, d) if debug else out
+
+    def backward(self, q: torch.Tensor, dout: torch.Tensor, causal: bool = False, debug: bool = False,
+                 grads: dict | None = None):
+        """Gradients of <dout, out> with the selection held fixed, for the rows of
+        decode(q) (causal=False) or prefill(q) (causal=True).  Returns a dict with
+        dq [n][Hq][D] and dk, dv [Hkv][capacity][D], dw [Hkv][D] (fp32); pass
+        `grads` (such a dict) to add dk, dv, dw into existing tensors."""
+        n = q.shape[0]
+        shape = (n, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        self._check_dev(dout, shape, torch.float32)
+        Hkv, D, cap = self.p.n_kv_heads, self.p.head_dim, self.p.capacity
+        if grads is None:
+            grads = {"dk": torch.zeros((Hkv, cap, D), dtype=torch.float32, device=self.device),
+                     "dv": torch.zeros((Hkv, cap, D), dtype=torch.float32, device=self.device),
+                     "dw": torch.zeros((Hkv, D), dtype=torch.float32, device=self.device)}
+        grads["dq"] = torch.empty(shape, dtype=torch.float32, device=self.device)
+        nbytes = recsa_backward_workspace_bytes(self.p)
+        if nbytes and (self._bws is None or self._bws.numel() < nbytes):
+            self._bws = None
+            self._bws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        d, dbg = self._debug(n * self.p.n_q_heads, debug)
+        recsa_backward(self.p, self.desc, _ptr(q), n, causal, _ptr(dout), _ptr(grads["dq"]),
+                       _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dw"]), dbg,
+                       _ptr(self._bws) if nbytes else None, self.stream())
+        return (grads, d) if debug else grads
 
     # ---- inspection -------------------------------------------------------------
     def level(self, l: int):

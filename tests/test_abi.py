@@ -181,3 +181,33 @@ def test_grouped_decode_validates_before_any_hip_call():
         with pytest.raises(R.RecsaError) as e:
             fn()
         assert e.value.status == status, (i, str(e.value))
+
+
+def test_backward_validates_before_any_hip_call():
+    p = _p(capacity=1000)
+    fake = 1 << 20
+    d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
+    assert R.recsa_backward_workspace_bytes(p) >= 2 * 8 * (1000 // 32) * 128 * 4
+    ws = fake
+    ok = dict(q_ptr=fake, n_q=2, causal=0, dout_ptr=fake, dq_ptr=fake, dk_ptr=fake, dv_ptr=fake,
+              dw_ptr=fake, ws=ws)
+    cases = [
+        (dict(n_q=0), R.RECSA_ERR_INVALID_ARG),
+        (dict(causal=2), R.RECSA_ERR_INVALID_ARG),
+        (dict(causal=1, n_q=11), R.RECSA_ERR_INVALID_ARG),       # more queries than tokens
+        (dict(dout_ptr=None), R.RECSA_ERR_INVALID_ARG),
+        (dict(dk_ptr=fake + 4), R.RECSA_ERR_INVALID_ARG),
+        (dict(dw_ptr=None), R.RECSA_ERR_INVALID_ARG),
+        (dict(ws=None), R.RECSA_ERR_INVALID_ARG),
+        (dict(ws=fake + 128), R.RECSA_ERR_INVALID_ARG),
+    ]
+    for i, (kw, status) in enumerate(cases):
+        args = dict(ok, **kw)
+        with pytest.raises(R.RecsaError) as e:
+            R.recsa_backward(p, d, args["q_ptr"], args["n_q"], args["causal"], args["dout_ptr"],
+                             args["dq_ptr"], args["dk_ptr"], args["dv_ptr"], args["dw_ptr"], ws=args["ws"])
+        assert e.value.status == status, (i, str(e.value))
+    with pytest.raises(R.RecsaError) as e:
+        R.recsa_backward(p, R.recsa_tree_desc(fake, fake, fake, fake, 0), fake, 1, 0, fake, fake, fake,
+                         fake, fake, ws=ws)
+    assert e.value.status == R.RECSA_ERR_INVALID_ARG

@@ -1,0 +1,101 @@
+"""GPU parity of the backward pass (selection held fixed) against the oracle's
+backward on the same seeded inputs: the GPU's selections are checked against
+the oracle's (near-ties replayed), then dq, token dk and dv, and dw are compared
+with the oracle run on the GPU's selections.  Tolerance: 1e-5 of the largest
+magnitude of each gradient for fp32 storage (fp32 sums over up to a few thousand
+entries and, for dk/dv/dw, over the rows that share a node, in atomic order),
+2e-2 x RMS for bf16 storage, as for outputs."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import recsa as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+CASES = [
+    # (workload, L, n_kv, n_q, n rows, causal, overrides)
+    ("tiny_f32_4k", 4096, 1, 1, 3, False, {}),
+    ("tiny_f32_4k", 4229, 2, 4, 2, False, {}),                 # GQA, ragged tail and orphans
+    ("tiny_f32_4k", 3001, 1, 2, 24, True, {"b": 5, "k": 3}),   # causal chunk, odd fanout
+    ("tiny_f32_4k", 10, 1, 2, 4, True, {}),                    # L < b: tokens only, dw = 0
+    ("tiny_f32_4k", 300, 1, 2, 2, False, {"dtype": "bf16"}),
+    ("qwen3_4b_131k", 20000, 8, 32, 2, False, {}),             # the Qwen3-4B layer shape, bf16
+    ("qwen3_4b_131k", 9000, 8, 32, 3, True, {}),
+]
+
+
+def _tol(ref, dtype):
+    if dtype == "f32":
+        return 1e-5 * max(1.0, float(np.abs(ref).max()))
+    return 2e-2 * float(np.sqrt(np.mean(ref ** 2))) + 1e-12
+
+
+@pytest.mark.parametrize("name,L,n_kv,n_q,n,causal,kw", CASES)
+def test_backward(name, L, n_kv, n_q, n, causal, kw):
+    _say(f"case backward {name} L={L} n_kv={n_kv} n_q={n_q} n={n} causal={causal} {kw}")
+    w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=0, n_kv=n_kv, n_q=n_q, **kw)
+    K, V = synth.gen_kv(w, 0, L)
+    W = synth.pool_w(w)
+    layer = P.make_layer(w, capacity=L)
+    P.load_cache(layer, K, V, W, L, w.dtype)
+    layer.build(L)
+    rng = np.random.default_rng(L + n)
+    Q = synth.to_storage(rng.standard_normal((n, n_q, w.d)).astype(np.float32), w.dtype)
+    dO = rng.standard_normal((n, n_q, w.d)).astype(np.float32)
+    grads, dbg = layer.backward(P.to_device(Q, w.dtype), torch.from_numpy(dO).cuda(), causal=causal,
+                                debug=True)
+    torch.cuda.synchronize()
+    sel = dbg["selected"].cpu().numpy()
+    G = n_q // n_kv
+    # selections: GPU vs oracle (near-ties excused), then the oracle on the GPU's selections
+    force = {}
+    for i in range(n):
+        n_ctx = L - n + i + 1 if causal else L
+        for h in range(n_q):
+            g = h // G
+            tree_g = P.head_tree(K, V, W, g, w, L)
+            P.check_row(tree_g, Q[i, h].astype(np.float64), 0, n_ctx, w.k, w.rope_base, w.softmax_scale,
+                        sel[i * n_q + h])
+            N = O.level_sizes(n_ctx, w.b)
+            force[(i, h)] = {l: sel[i * n_q + h, l - 1][sel[i * n_q + h, l - 1] >= 0]
+                             for l in range(1, len(N))}
+    tree = O.build_tree(K[:, :L], V[:, :L], W, w.b, w.dtype, w.pool_scale, L)
+    ref = O.backward(tree, Q.astype(np.float64), dO.astype(np.float64), w.k, w.rope_base, w.softmax_scale,
+                     causal=causal, force=force)
+    got = {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    rep = {}
+    for key in ("dq", "dk", "dv", "dw"):
+        g_ = got[key] if key in ("dq", "dw") else got[key][:, :L]
+        err = float(np.abs(g_ - ref[key]).max())
+        tol = _tol(ref[key], w.dtype)
+        rep[key] = (err, tol)
+        assert err <= tol, f"{key}: max abs error {err:.3g} > {tol:.3g}"
+    # tokens past the length keep their gradients untouched
+    assert np.all(got["dk"][:, L:] == 0) and np.all(got["dv"][:, L:] == 0)
+    _say("backward", {k: f"{e:.2e}/{t:.2e}" for k, (e, t) in rep.items()})
+
+
+def test_backward_adds_into_given_gradients():
+    w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], 2000, prefill_n=0, n_q=2)
+    K, V = synth.gen_kv(w, 0, 2000)
+    W = synth.pool_w(w)
+    layer = P.make_layer(w, capacity=2000)
+    P.load_cache(layer, K, V, W, 2000, "f32")
+    layer.build(2000)
+    rng = np.random.default_rng(9)
+    q = torch.from_numpy(rng.standard_normal((2, 2, w.d)).astype(np.float32)).cuda()
+    dO = torch.from_numpy(rng.standard_normal((2, 2, w.d)).astype(np.float32)).cuda()
+    once = layer.backward(q, dO)
+    twice = layer.backward(q, dO, grads={k: once[k].clone() for k in ("dk", "dv", "dw")})
+    torch.cuda.synchronize()
+    for k in ("dk", "dv", "dw"):
+        torch.testing.assert_close(twice[k], 2 * once[k], rtol=1e-5, atol=1e-6)
+    assert torch.equal(twice["dq"], once["dq"])
