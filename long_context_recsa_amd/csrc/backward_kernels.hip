@@ -320,11 +320,14 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
     }
 }
 
-// One wave per node of level l: the node's key and value gradients to its b
-// children (level l - 1, or the tokens) and to dw.
+// Per node of level l, one wave: the node's key and value gradients to its b
+// children (level l - 1, or the tokens) and to dw.  A 16-lane group takes
+// children grp, grp + 4, ...; each lane holds D/16 contiguous elements of a row.
+// Children go four per group at a time, their loads issued together.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     constexpr int NE = D / 16;              // contiguous elements per lane
+    constexpr int CB = 4;                   // children per group in flight
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int grp = lane >> 4, sub = lane & 15;
@@ -332,11 +335,43 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     const int32_t b = t.b;
     float *sa = reinterpret_cast<float *>(smem) + (size_t)wave * 2 * b;    // [b] pooler logits, then alpha
     float *sd = sa + b;                                                   // [b] <g, x_c>, then da_c
-    const int64_t widx = (int64_t)blockIdx.x * 4 + wave;
-    if (widx >= (int64_t)t.Hkv * t.nodes) return;
+    const int l = t.level;
+    // persistent waves, each over a contiguous range of (head, node): dw stays in
+    // registers while the head does not change (one set of atomics per head and wave,
+    // not per node, which would serialize on dw's few addresses)
+    const int64_t total = (int64_t)t.Hkv * t.nodes;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t chunk = (total + nwaves - 1) / nwaves;
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wave) * chunk;
+    const int64_t w1 = w0 + chunk < total ? w0 + chunk : total;
+    float dw[NE];
+    #pragma unroll
+    for (int e = 0; e < NE; ++e) dw[e] = 0.f;
+    int gcur = w0 < w1 ? (int)(w0 / t.nodes) : 0;
+    auto flush = [&](int gg) {
+        float v[NE];
+        #pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            v[e] = dw[e];
+            v[e] += __shfl_xor(v[e], 16);
+            v[e] += __shfl_xor(v[e], 32);
+            dw[e] = 0.f;
+        }
+        bool nz = false;
+        #pragma unroll
+        for (int e = 0; e < NE; ++e) nz = nz || v[e] != 0.f;
+        if (grp == 0 && nz) {
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) atomicAdd(t.dw + (int64_t)gg * D + e0 + e, v[e]);
+        }
+    };
+    for (int64_t widx = w0; widx < w1; ++widx) {
     const int g = (int)(widx / t.nodes);
     const int64_t j = widx - (int64_t)g * t.nodes;
-    const int l = t.level;
+    if (g != gcur) {
+        flush(gcur);
+        gcur = g;
+    }
     const float *gkp = t.gk + ((int64_t)g * tv.node_cap[l] + j) * D + e0;
     const float *gvp = t.gv + ((int64_t)g * tv.node_cap[l] + j) * D + e0;
     float gk[NE], gv[NE], w[NE];
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     bool any = false;
     #pragma unroll
     for (int u = 0; u < NE; ++u) any = any || gk[u] != 0.f || gv[u] != 0.f;
-    if (__ballot(any) == 0) return;         // no row read this node
+    if (__ballot(any) == 0) continue;       // no row read this node
 
     // the children: stored keys of level l - 1 (tokens at l = 1) and their gradients
     const int64_t c0 = j * b;
@@ -356,20 +391,30 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
                        : t.gk_child + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
     float *cv = l == 1 ? t.dv + ((int64_t)g * tv.cap + c0) * D
                        : t.gv_child + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
-    for (int32_t c = grp; c < b; c += 4) {
-        float x[NE];
-        Vec<T, NE>::load(xk + (int64_t)c * D + e0, x);
-        float pa = 0.f, pd = 0.f;
+    // child of this group's batch slot u (clamped to the last child; the result is then unused)
+    auto child = [&](int32_t cb, int u) {
+        const int32_t c = cb + grp + 4 * u;
+        return c < b ? c : b - 1;
+    };
+    for (int32_t cb = 0; cb < b; cb += 4 * CB) {
+        float x[CB][NE];
         #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            pa += w[u] * x[u];
-            pd += gk[u] * x[u];
-        }
-        pa = row_sum16(pa);
-        pd = row_sum16(pd);
-        if (sub == 15) {
-            sa[c] = t.pool_scale * pa;
-            sd[c] = pd;
+        for (int u = 0; u < CB; ++u) Vec<T, NE>::load(xk + (int64_t)child(cb, u) * D + e0, x[u]);
+        #pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            float pa = 0.f, pd = 0.f;
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                pa += w[e] * x[u][e];
+                pd += gk[e] * x[u][e];
+            }
+            pa = row_sum16(pa);
+            pd = row_sum16(pd);
+            const int32_t c = cb + grp + 4 * u;
+            if (sub == 15 && c < b) {
+                sa[c] = t.pool_scale * pa;
+                sd[c] = pd;
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -403,34 +448,36 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const float invb = 1.f / (float)b;
-    float dw[NE];
-    #pragma unroll
-    for (int u = 0; u < NE; ++u) dw[u] = 0.f;
-    for (int32_t c = grp; c < b; c += 4) {
-        float x[NE], ok[NE], ov[NE];
-        Vec<T, NE>::load(xk + (int64_t)c * D + e0, x);
-        float *ckr = ck + (int64_t)c * D + e0;
-        float *cvr = cv + (int64_t)c * D + e0;
-        Vec<float, NE>::load(ckr, ok);
-        Vec<float, NE>::load(cvr, ov);
-        const float al = sa[c], dac = t.pool_scale * sd[c];
+    for (int32_t cb = 0; cb < b; cb += 4 * CB) {
+        float x[CB][NE], ok[CB][NE], ov[CB][NE];
         #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-            ok[u] += al * gk[u] + dac * w[u];
-            ov[u] += gv[u] * invb;
-            dw[u] += dac * x[u];
+        for (int u = 0; u < CB; ++u) {
+            const int64_t c = child(cb, u);
+            Vec<T, NE>::load(xk + c * D + e0, x[u]);
+            Vec<float, NE>::load(ck + c * D + e0, ok[u]);
+            Vec<float, NE>::load(cv + c * D + e0, ov[u]);
         }
-        Vec<float, NE>::store(ckr, ok);
-        Vec<float, NE>::store(cvr, ov);
-    }
-    #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1)
         #pragma unroll
-        for (int u = 0; u < NE; ++u) dw[u] += __shfl_xor(dw[u], off);
-    if (grp == 0) {
-        #pragma unroll
-        for (int u = 0; u < NE; ++u) atomicAdd(t.dw + (int64_t)g * D + e0 + u, dw[u]);
+        for (int u = 0; u < CB; ++u) {
+            const int32_t c = cb + grp + 4 * u;
+            if (c >= b) continue;
+            const float al = sa[c], dac = t.pool_scale * sd[c];
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                ok[u][e] += al * gk[e] + dac * w[e];
+                ov[u][e] += gv[e] * invb;
+                dw[e] += dac * x[u][e];
+            }
+            Vec<float, NE>::store(ck + (int64_t)c * D + e0, ok[u]);
+            Vec<float, NE>::store(cv + (int64_t)c * D + e0, ov[u]);
+        }
     }
+    // the next node reuses sa / sd
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (w0 < w1) flush(gcur);
 }
 
 __global__ void fill_zero(uint4 *p, int64_t n16) {
@@ -452,10 +499,20 @@ hipError_t launch_rows_t(const TreeView &tv, const BwdArgs &a, const DebugView &
 
 template <typename T, int D>
 hipError_t launch_tree_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
-    const int64_t waves = (int64_t)t.Hkv * t.nodes;
-    if (waves == 0) return hipSuccess;
+    const int64_t nodes = (int64_t)t.Hkv * t.nodes;
+    if (nodes == 0) return hipSuccess;
     const size_t smem = sizeof(float) * 4 * 2 * (size_t)t.b;
-    hipLaunchKernelGGL((bwd_tree<T, D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), smem, s, tv, t);
+    // as many workgroups as are resident at once; each wave then walks its share of nodes
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree<T, D>, 256, smem);
+    if (e != hipSuccess) return e;
+    const int64_t want = (nodes + 3) / 4;
+    const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t blocks = want < cap ? want : cap;
+    hipLaunchKernelGGL((bwd_tree<T, D>), dim3((unsigned)blocks), dim3(256), smem, s, tv, t);
     return hipGetLastError();
 }
 
