@@ -2,9 +2,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 build the tree over the L cached tokens, decode a batch at length L (per
-query head, then again with one selection per KV group), append the prefill
-chunk (growing the tree) and run the causal prefill of that chunk.  Each call
-is timed with HIP events on the stream it is launched on.
+query head, then again with one selection per KV group), the backward of that
+decode batch (selection fixed; a synthetic output gradient), append the
+prefill chunk (growing the tree) and run the causal prefill of that chunk.
+Each call is timed with HIP events on the stream it is launched on.  The
+roofline line follows the forward calls.
 
 Prints one JSON line: value = decode queries/s; prefill tokens/s, tree-build
 bandwidth and the roofline fractions of every kernel ride along.
@@ -107,6 +109,12 @@ def algorithmic(w, B):
     # one selection per (query, KV group): each group row reads its keys and values once
     # for its G heads
     grouped_bytes = B * w.n_kv * (kd + vd) * row_b
+    # backward of the decode batch, its per-row part: every row reads its keys and values
+    # twice (the descent again, then the entry walk) and adds a key and a value gradient
+    # (fp32) per entry.  The tree pass after it (the touched nodes' children read, their
+    # fp32 gradients updated) is in the call's time but not in these bytes.
+    bwd_bytes = 2 * B * w.n_q * (kd + vd) * row_b + B * w.n_q * vd * 2 * w.d * 4
+    bwd_atomics = B * w.n_q * vd * 2 * w.d
     pk = pv = 0
     for j in range(w.prefill_n):
         a, c = row_entries(w.L + j + 1, w.b, w.k)
@@ -123,7 +131,7 @@ def algorithmic(w, B):
     new_nodes = sum(Nt[l] - (N[l] if l < len(N) else 0) for l in range(1, len(Nt)))
     append_bytes = 2 * 2 * w.n_kv * w.prefill_n * row_b + 2 * w.n_kv * new_nodes * row_b
     return dict(build=build_bytes, decode=decode_bytes, decode_flops=decode_flops,
-                decode_grouped=grouped_bytes,
+                decode_grouped=grouped_bytes, backward=bwd_bytes, backward_atomics=bwd_atomics,
                 prefill=prefill_bytes, prefill_flops=prefill_flops, append=append_bytes,
                 prefill_read_once=prefill_read_once,
                 decode_entries_per_row=kd + vd)
@@ -310,11 +318,17 @@ def main():
         out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
     out_dec = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
     out_grp = torch.empty_like(out_dec)
+    # backward of the decode batch: the output gradient is synthetic, the token and pooler
+    # gradients accumulate over steps (the call adds into them)
+    d_out = torch.from_numpy(np.random.default_rng(5).standard_normal((B, w.n_q, w.d)).astype(np.float32)).to(dev)
+    grads = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
+             "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
+             "dw": torch.zeros((w.n_kv, w.d), dtype=torch.float32, device=dev)}
     del K, V
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
-    ops = ["build", "decode", "decode_grouped"] + (["append", "prefill"] if w.prefill_n else [])
+    ops = ["build", "decode", "decode_grouped", "backward"] + (["append", "prefill"] if w.prefill_n else [])
     ev = {o: [] for o in ops}
 
     def step(record):
@@ -330,6 +344,8 @@ def main():
         mark("decode")
         layer.decode_grouped(q_dec, out=out_grp)
         mark("decode_grouped")
+        layer.backward(q_dec, d_out, grads=grads)
+        mark("backward")
         if w.prefill_n:
             layer.append(k_new, v_new)
             mark("append")
@@ -357,6 +373,10 @@ def main():
                           "achieved": alg["build"] / ms["build"] / 1e6, "unit": "GB/s"}
     kern["decode"] = {"bound": "hbm", "bytes": alg["decode"], "ms": ms["decode"],
                       "achieved": alg["decode"] / ms["decode"] / 1e6, "unit": "GB/s"}
+    kern["backward"] = {"bound": "atomics", "bytes": alg["backward"], "ms": ms["backward"],
+                        "achieved": alg["backward"] / ms["backward"] / 1e6, "unit": "GB/s",
+                        "atomic_adds": alg["backward_atomics"],
+                        "atomic_adds_per_s": alg["backward_atomics"] / ms["backward"] * 1e3}
     kern["decode_grouped"] = {"bound": "hbm", "bytes": alg["decode_grouped"], "ms": ms["decode_grouped"],
                               "achieved": alg["decode_grouped"] / ms["decode_grouped"] / 1e6,
                               "unit": "GB/s"}
@@ -375,7 +395,8 @@ def main():
         v["frac"] = v["achieved"] / HBM_PEAK_GBS
         t_ = measured_traffic(w.name, name_)
         v["traffic"] = None if t_ is None else t_["fetch"] + t_["write"]
-    dom = max(kern, key=lambda n: kern[n]["ms"])
+    # the roofline line follows the forward path; the backward rides along in `kernels`
+    dom = max((n for n in kern if n != "backward"), key=lambda n: kern[n]["ms"])
     tr = measured_traffic(w.name, dom)
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": kern[dom]["achieved"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac"],
