@@ -523,6 +523,40 @@ def backward(tree: Tree, Q: np.ndarray, dO: np.ndarray, k: int, base: float, sca
 
 
 # ----------------------------------------------------------------------------
+# pooler distillation from dense attention
+# ----------------------------------------------------------------------------
+# The pages distill the per-layer pooler from dense attention (abstract, sentence
+# on the pooler) and give no objective.  Reading: on a set of training queries at
+# the cache's length, the pooler vectors w are fitted so that RecSA's output
+# matches dense attention's output,
+#   loss = (1 / rows) sum_rows || out_recsa(q) - out_dense(q) ||^2,
+# its gradient in w taken with the selection held fixed (the backward above) and
+# the tree rebuilt from the new w after each step; the optimizer is SGD with
+# momentum: vel <- mu vel + dloss/dw, w <- w - lr vel.
+def distill_loss(tree: Tree, Q: np.ndarray, teacher: np.ndarray, k: int, base: float,
+                 scale: float, force=None) -> tuple[float, dict]:
+    """Loss of the decode queries Q[B][n_q][d] against teacher outputs, and the
+    gradients (backward's dict, dw included) of that loss."""
+    Q = np.asarray(Q, F64)
+    out, _ = decode(tree, Q, k, base, scale,
+                    force=None if force is None else force)
+    rows = Q.shape[0] * Q.shape[1]
+    diff = out - np.asarray(teacher, F64)
+    loss = float((diff ** 2).sum() / rows)
+    grads = backward(tree, Q, 2.0 * diff / rows, k, base, scale, force=force)
+    return loss, grads
+
+
+def distill_step(K, V, w, b, store, pool_scale, L, Q, teacher, k, base, scale, lr, mu, vel):
+    """One step: build the tree from w, the loss and dloss/dw, then the update.
+    Returns (loss before the step, new w, new velocity)."""
+    tree = build_tree(K, V, w, b, store, pool_scale, L)
+    loss, grads = distill_loss(tree, Q, teacher, k, base, scale)
+    vel = mu * np.asarray(vel, F64) + grads["dw"]
+    return loss, np.asarray(w, F64) - lr * vel, vel
+
+
+# ----------------------------------------------------------------------------
 # dense causal attention (the comparison point of the pages' speed claim)
 # ----------------------------------------------------------------------------
 def dense(q: np.ndarray, K: np.ndarray, V: np.ndarray, n: int, base: float, scale: float):

@@ -1,0 +1,76 @@
+"""Pins of the oracle's pooler distillation (fit w so that RecSA's output
+matches dense attention's): the loss gradient in w against central finite
+differences through the tree rebuild, a zero loss where RecSA is dense
+attention, and descent of the loss under small steps."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import recsa as O
+
+
+def _setup(seed, L, d, n_kv, nq, B, wscale=2.0):
+    r = np.random.default_rng(seed)
+    K = r.standard_normal((n_kv, L, d))
+    V = r.standard_normal((n_kv, L, d))
+    w = r.standard_normal((n_kv, d)) * wscale / math.sqrt(d)
+    Q = r.standard_normal((B, nq, d)) * 1.5
+    return K, V, w, Q
+
+
+def _teacher(K, V, Q, L, base, s):
+    B, nq, d = Q.shape
+    G = nq // K.shape[0]
+    return np.stack([np.stack([O.dense(Q[i, h], K[h // G], V[h // G], L, base, s) for h in range(nq)])
+                     for i in range(B)])
+
+
+@pytest.mark.parametrize("L,b,k", [(47, 3, 2), (70, 4, 2)])
+def test_distill_gradient_matches_finite_differences(L, b, k):
+    d, base, s, ps = 4, 1e4, 0.6, 0.7
+    K, V, w, Q = _setup(L, L, d, 1, 2, 2)
+    T = _teacher(K, V, Q, L, base, s)
+    tree = O.build_tree(K, V, w, b, "f64", ps, L)
+    force = {}
+    for i in range(2):
+        for h in range(2):
+            r = O.descend(tree, Q[i, h], 0, L, k, base, s)
+            assert all(not np.isfinite(t.gap) or t.gap > 1e-6 for t in r.levels)
+            force[(i, h)] = {t.level: t.cand[t.sel_pos] for t in r.levels if t.level > 0}
+    loss, g = O.distill_loss(tree, Q, T, k, base, s, force=force)
+    assert loss > 0
+    h = 1e-6
+    for idx in np.ndindex(w.shape):
+        wp, wm = w.copy(), w.copy()
+        wp[idx] += h
+        wm[idx] -= h
+        lp, _ = O.distill_loss(O.build_tree(K, V, wp, b, "f64", ps, L), Q, T, k, base, s, force=force)
+        lm, _ = O.distill_loss(O.build_tree(K, V, wm, b, "f64", ps, L), Q, T, k, base, s, force=force)
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - g["dw"][idx]) <= 1e-6 * (1 + abs(fd)), (idx, fd, g["dw"][idx])
+
+
+def test_distill_loss_is_zero_where_recsa_is_dense():
+    L, d, b = 200, 8, 16
+    K, V, w, Q = _setup(3, L, d, 1, 2, 2)
+    T = _teacher(K, V, Q, L, 1e4, 0.35)
+    loss, g = O.distill_loss(O.build_tree(K, V, w, b, "f32", 0.5, L), Q, T, L, 1e4, 0.35)
+    assert loss < 1e-20 and np.all(np.abs(g["dw"]) < 1e-15)
+
+
+def test_distill_small_steps_descend():
+    """Gradient steps with a small rate lower the loss (tiny workload shape)."""
+    w0 = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], 1024, n_q=2)
+    K, V = synth.gen_kv(w0)
+    W = synth.pool_w(w0) * 8.0
+    Q = synth.decode_queries(w0, 4)
+    T = _teacher(K, V, Q, w0.L, w0.rope_base, w0.softmax_scale)
+    vel = np.zeros_like(W)
+    losses = []
+    for _ in range(4):
+        loss, W, vel = O.distill_step(K, V, W, w0.b, "f64", w0.pool_scale, w0.L, Q, T, w0.k,
+                                      w0.rope_base, w0.softmax_scale, lr=0.5, mu=0.0, vel=vel)
+        losses.append(loss)
+    assert all(b_ < a_ for a_, b_ in zip(losses, losses[1:])), losses
