@@ -205,7 +205,8 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p);
  *   d_k, d_v [n_kv_heads][capacity][head_dim] fp32, ADDED TO for tokens
  *     [0, length): entries' direct gradients plus those reaching summaries,
  *     pushed down the tree (a summary value is its subtree's mean; a summary
- *     key is the pooler over its stored children's keys);
+ *     key is the pooler over its stored children's keys); both NULL to skip
+ *     the token gradients (d_w and d_q are still computed);
  *   d_w [n_kv_heads][head_dim] fp32, ADDED TO: the pooler vectors' gradient.
  * Rounding a summary to store_dtype passes the gradient through unchanged.
  * Entry logits, softmax and the selection are recomputed as in the forward.
@@ -218,6 +219,41 @@ RECSA_API recsa_status recsa_backward(const recsa_params *p, const recsa_tree_de
                             int64_t n_q, int32_t causal, const float *d_out, float *d_q,
                             float *d_k, float *d_v, float *d_w, const recsa_debug *dbg, void *ws,
                             void *stream);
+
+/* Workspace bytes recsa_dense_decode needs for `batch` queries (device
+ * memory): per-span partial softmax states.  0 on invalid arguments. */
+RECSA_API size_t recsa_dense_workspace_bytes(const recsa_params *p, int32_t batch);
+
+/* Dense causal attention of decode queries (the pooler distillation's teacher;
+ * abstract, sentence on the pooler): out[i][h] = softmax over tokens t <
+ * desc->length of softmax_scale * <rope(q, length), rope(K_t, t)>, applied to V
+ * (no tree).  q as recsa_decode's; out [batch][n_q_heads][head_dim] out_dtype.
+ * ws: recsa_dense_workspace_bytes(p, batch) bytes, 16-byte aligned. */
+RECSA_API recsa_status recsa_dense_decode(const recsa_params *p, const recsa_tree_desc *desc,
+                                const void *q, int32_t batch, void *out, void *ws, void *stream);
+
+/* Workspace bytes recsa_distill_step needs for `batch` queries (device memory,
+ * 256-byte aligned).  0 on invalid arguments. */
+RECSA_API size_t recsa_distill_workspace_bytes(const recsa_params *p, int32_t batch);
+
+/* One step of the pooler's distillation from dense attention (abstract,
+ * sentence on the pooler; the objective is this library's reading): with the
+ * decode queries q[batch][n_q_heads][head_dim] (store_dtype, at position
+ * desc->length) and their dense outputs `teacher` (fp32, e.g. from
+ * recsa_dense_decode with out_dtype fp32),
+ *   loss = (1 / (batch * n_q_heads)) * sum ||recsa_decode(q) - teacher||^2,
+ * written to *loss (device fp32), then dloss/dw with the selection held fixed
+ * (as recsa_backward), then SGD with momentum on the pooler vectors,
+ *   velocity <- momentum * velocity + dloss/dw,  pool_w <- pool_w - lr * velocity,
+ * then the tree is built again from the new pool_w.  pool_w must be
+ * desc->pool_w ([n_kv_heads][head_dim] fp32, updated in place); velocity has
+ * its shape (fp32, the caller zeroes it before the first step).  ws:
+ * recsa_distill_workspace_bytes(p, batch) bytes, 256-byte aligned.  The loss is
+ * the one before the update. */
+RECSA_API recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, float *pool_w,
+                                const void *q, int32_t batch, const float *teacher, float lr,
+                                float momentum, float *velocity, float *loss, void *ws,
+                                void *stream);
 
 /* Static name of a status code. */
 RECSA_API const char *recsa_status_string(recsa_status s);

@@ -22,7 +22,8 @@ EXPORTED = (
     "recsa_workspace_bytes", "recsa_build_tree", "recsa_append", "recsa_decode",
     "recsa_prefill", "recsa_status_string", "recsa_last_error", "recsa_multi_workspace_bytes",
     "recsa_decode_multi", "recsa_decode_grouped", "recsa_backward_workspace_bytes",
-    "recsa_backward",
+    "recsa_backward", "recsa_dense_workspace_bytes", "recsa_dense_decode",
+    "recsa_distill_workspace_bytes", "recsa_distill_step",
 )
 
 
@@ -89,6 +90,10 @@ def load_library():
         "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
         "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P]),
         "recsa_backward": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
+        "recsa_dense_workspace_bytes": (ctypes.c_size_t, [P, i32]),
+        "recsa_dense_decode": (i32, [P, D, v, i32, v, v, v]),
+        "recsa_distill_workspace_bytes": (ctypes.c_size_t, [P, i32]),
+        "recsa_distill_step": (i32, [P, D, v, v, i32, v, ctypes.c_float, ctypes.c_float, v, v, v, v]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -165,6 +170,25 @@ def recsa_backward(p, desc, q_ptr, n_q, causal, dout_ptr, dq_ptr, dk_ptr, dv_ptr
     _check(load_library().recsa_backward(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q, int(causal),
                                          dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr,
                                          ctypes.byref(dbg) if dbg is not None else None, ws, stream))
+
+
+def recsa_dense_workspace_bytes(p, batch: int) -> int:
+    return load_library().recsa_dense_workspace_bytes(ctypes.byref(p), batch)
+
+
+def recsa_dense_decode(p, desc, q_ptr, batch, out_ptr, ws, stream=None) -> None:
+    _check(load_library().recsa_dense_decode(ctypes.byref(p), ctypes.byref(desc), q_ptr, batch, out_ptr,
+                                             ws, stream))
+
+
+def recsa_distill_workspace_bytes(p, batch: int) -> int:
+    return load_library().recsa_distill_workspace_bytes(ctypes.byref(p), batch)
+
+
+def recsa_distill_step(p, desc, w_ptr, q_ptr, batch, teacher_ptr, lr, momentum, vel_ptr, loss_ptr, ws,
+                       stream=None) -> None:
+    _check(load_library().recsa_distill_step(ctypes.byref(p), ctypes.byref(desc), w_ptr, q_ptr, batch,
+                                             teacher_ptr, lr, momentum, vel_ptr, loss_ptr, ws, stream))
 
 
 def recsa_multi_workspace_bytes(n_seq: int) -> int:

@@ -281,17 +281,23 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
                 const float dp = slot_sum(t);
                 const float pe = __builtin_amdgcn_exp2f((zi - Mg) * kLog2e) * invL;
                 const float dz = pe * (dp - Dv) * a.scale;
-                float *gk = gk_row(l, node);
-                float *gv = gv_row(l, node);
                 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
-                    // dq += s dz R_(i-n) key;  dkey = s dz R_(n-i) q;  dv = p dO
+                    // dq += s dz R_(i-n) key
                     dqa[p] += dz * (ka[p] * c[p] + kb[p] * s[p]);
                     dqb[p] += dz * (kb[p] * c[p] - ka[p] * s[p]);
-                    atomicAdd(gk + j0 + p, dz * (qa[p] * c[p] - qb[p] * s[p]));
-                    atomicAdd(gk + H2 + j0 + p, dz * (qb[p] * c[p] + qa[p] * s[p]));
-                    atomicAdd(gv + j0 + p, pe * da[p]);
-                    atomicAdd(gv + H2 + j0 + p, pe * db[p]);
+                }
+                if (l >= 1 || a.dk != nullptr) {    // token gradients may be skipped
+                    float *gk = gk_row(l, node);
+                    float *gv = gv_row(l, node);
+                    #pragma unroll
+                    for (int p = 0; p < PP; ++p) {
+                        // dkey = s dz R_(n-i) q;  dv = p dO
+                        atomicAdd(gk + j0 + p, dz * (qa[p] * c[p] - qb[p] * s[p]));
+                        atomicAdd(gk + H2 + j0 + p, dz * (qb[p] * c[p] + qa[p] * s[p]));
+                        atomicAdd(gv + j0 + p, pe * da[p]);
+                        atomicAdd(gv + H2 + j0 + p, pe * db[p]);
+                    }
                 }
             }
             m_above = l >= 1 ? (K < cd.n ? K : cd.n) : 0;
@@ -448,14 +454,17 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const float invb = 1.f / (float)b;
+    const bool child_grads = l >= 2 || t.dk != nullptr;     // token gradients may be skipped
     for (int32_t cb = 0; cb < b; cb += 4 * CB) {
         float x[CB][NE], ok[CB][NE], ov[CB][NE];
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
             const int64_t c = child(cb, u);
             Vec<T, NE>::load(xk + c * D + e0, x[u]);
-            Vec<float, NE>::load(ck + c * D + e0, ok[u]);
-            Vec<float, NE>::load(cv + c * D + e0, ov[u]);
+            if (child_grads) {
+                Vec<float, NE>::load(ck + c * D + e0, ok[u]);
+                Vec<float, NE>::load(cv + c * D + e0, ov[u]);
+            }
         }
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
@@ -463,13 +472,16 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
             if (c >= b) continue;
             const float al = sa[c], dac = t.pool_scale * sd[c];
             #pragma unroll
-            for (int e = 0; e < NE; ++e) {
-                ok[u][e] += al * gk[e] + dac * w[e];
-                ov[u][e] += gv[e] * invb;
-                dw[e] += dac * x[u][e];
+            for (int e = 0; e < NE; ++e) dw[e] += dac * x[u][e];
+            if (child_grads) {
+                #pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    ok[u][e] += al * gk[e] + dac * w[e];
+                    ov[u][e] += gv[e] * invb;
+                }
+                Vec<float, NE>::store(ck + (int64_t)c * D + e0, ok[u]);
+                Vec<float, NE>::store(cv + (int64_t)c * D + e0, ov[u]);
             }
-            Vec<float, NE>::store(ck + (int64_t)c * D + e0, ok[u]);
-            Vec<float, NE>::store(cv + (int64_t)c * D + e0, ov[u]);
         }
     }
     // the next node reuses sa / sd

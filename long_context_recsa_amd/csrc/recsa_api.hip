@@ -267,6 +267,102 @@ recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const 
     return RECSA_OK;
 }
 
+recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                          int64_t n_q, int32_t causal, const float *d_out, float *d_q, float *d_k,
+                          float *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if ((st = check_desc(p, desc)) != RECSA_OK) return st;
+    if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "the backward needs at least one cached token");
+    if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
+    if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (causal && n_q > desc->length)
+        return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld)", (long long)n_q,
+                    (long long)desc->length);
+    const void *ptrs[] = {q, d_out, d_q, d_w};
+    for (const void *ptr : ptrs) {
+        if (ptr == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q and d_w must be non-NULL");
+        if (!aligned(ptr, 16)) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q and d_w must be 16-byte aligned");
+    }
+    if ((d_k == nullptr) != (d_v == nullptr))
+        return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must both be given or both be NULL");
+    if (!aligned(d_k, 16) || !aligned(d_v, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must be 16-byte aligned");
+    const size_t ws_bytes = recsa_backward_workspace_bytes(p);
+    if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
+        return fail(RECSA_ERR_INVALID_ARG,
+                    "the backward needs a 256-byte aligned workspace of recsa_backward_workspace_bytes() bytes");
+    const int64_t rows = n_q * p->n_q_heads;
+    if (rows > 0x7FFFFFFF) return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    if (backward_rows_lds_bytes((int32_t)L.max_cand, p->budget_k, L.n_levels, p->head_dim) > kMaxLds)
+        return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const TreeView tv = make_view(p, desc, L);
+    BwdArgs a{};
+    a.q = q;
+    a.dout = d_out;
+    a.dq = d_q;
+    a.dk = d_k;
+    a.dv = d_v;
+    char *w = static_cast<char *>(ws);
+    for (int l = 1; l <= L.n_levels; ++l) {
+        const size_t bytes = align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+        a.gk[l] = reinterpret_cast<float *>(w);
+        a.gv[l] = reinterpret_cast<float *>(w + bytes);
+        w += 2 * bytes;
+    }
+    a.rows = rows;
+    a.Hq = p->n_q_heads;
+    a.G = p->n_q_heads / p->n_kv_heads;
+    a.ctx_base = causal ? desc->length - n_q + 1 : desc->length;
+    a.ctx_step = causal ? 1 : 0;
+    a.b = p->fanout_b;
+    a.k = p->budget_k;
+    a.max_cand = (int32_t)L.max_cand;
+    a.scale = p->softmax_scale;
+    DebugView dv{};
+    if (dbg != nullptr) {
+        dv.selected = dbg->selected;
+        dv.kth_gap = dbg->kth_gap;
+        dv.n_keys = nullptr;
+    }
+    hipError_t e = launch_fill_zero(ws, ws_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
+    e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "backward rows launch");
+    // summaries' gradients down the tree, top level first
+    int64_t pw = 1;
+    int top = 0;
+    for (int l = 1; l <= L.n_levels; ++l) {
+        pw *= p->fanout_b;
+        if (desc->length / pw < 1) break;
+        top = l;
+    }
+    for (int l = top; l >= 1; --l) {
+        int64_t pl = 1;
+        for (int i = 0; i < l; ++i) pl *= p->fanout_b;
+        BwdTreeArgs t{};
+        t.level = l;
+        t.Hkv = p->n_kv_heads;
+        t.nodes = desc->length / pl;
+        t.b = p->fanout_b;
+        t.pool_scale = p->pool_scale;
+        t.pool_w = desc->pool_w;
+        t.gk = a.gk[l];
+        t.gv = a.gv[l];
+        t.gk_child = l >= 2 ? a.gk[l - 1] : nullptr;
+        t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
+        t.dk = d_k;
+        t.dv = d_v;
+        t.dw = d_w;
+        e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
+        if (e != hipSuccess) return hip_fail(e, "backward tree launch");
+    }
+    return RECSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -470,93 +566,101 @@ size_t recsa_backward_workspace_bytes(const recsa_params *p) {
 recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
                             int64_t n_q, int32_t causal, const float *d_out, float *d_q, float *d_k,
                             float *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
+    return run_backward(p, desc, q, n_q, causal, d_out, d_q, d_k, d_v, d_w, dbg, ws, stream);
+}
+
+size_t recsa_dense_workspace_bytes(const recsa_params *p, int32_t batch) {
+    if (check_params(p) != RECSA_OK || batch < 1) return 0;
+    // at most 1024 spans whatever the length
+    return align_up((size_t)p->n_kv_heads * 1024 * (size_t)batch * (size_t)(p->n_q_heads / p->n_kv_heads) *
+                    (size_t)(p->head_dim + 2) * sizeof(float));
+}
+
+recsa_status recsa_dense_decode(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                                int32_t batch, void *out, void *ws, void *stream) {
     recsa_status st = check_params(p);
     if (st != RECSA_OK) return st;
-    const Layout L = make_layout(p);
-    if ((st = check_limits(p, L)) != RECSA_OK) return st;
     if ((st = check_desc(p, desc)) != RECSA_OK) return st;
-    if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "the backward needs at least one cached token");
-    if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
-    if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (causal && n_q > desc->length)
-        return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld)", (long long)n_q,
-                    (long long)desc->length);
-    const void *ptrs[] = {q, d_out, d_q, d_k, d_v, d_w};
-    for (const void *ptr : ptrs) {
-        if (ptr == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q, d_k, d_v and d_w must be non-NULL");
-        if (!aligned(ptr, 16)) return fail(RECSA_ERR_INVALID_ARG, "q, d_out, d_q, d_k, d_v and d_w must be 16-byte aligned");
-    }
-    const size_t ws_bytes = recsa_backward_workspace_bytes(p);
-    if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
-        return fail(RECSA_ERR_INVALID_ARG,
-                    "the backward needs a 256-byte aligned workspace of recsa_backward_workspace_bytes() bytes");
-    const int64_t rows = n_q * p->n_q_heads;
-    if (rows > 0x7FFFFFFF) return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
-    if (backward_rows_lds_bytes((int32_t)L.max_cand, p->budget_k, L.n_levels, p->head_dim) > kMaxLds)
-        return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const TreeView tv = make_view(p, desc, L);
-    BwdArgs a{};
+    if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "dense attention needs at least one cached token");
+    if (batch < 1) return fail(RECSA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (q == nullptr || out == nullptr || ws == nullptr)
+        return fail(RECSA_ERR_INVALID_ARG, "q, out and ws must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(ws, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "q, out and ws must be 16-byte aligned");
+    DenseArgs a{};
     a.q = q;
-    a.dout = d_out;
-    a.dq = d_q;
-    a.dk = d_k;
-    a.dv = d_v;
-    char *w = static_cast<char *>(ws);
-    for (int l = 1; l <= L.n_levels; ++l) {
-        const size_t bytes = align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
-        a.gk[l] = reinterpret_cast<float *>(w);
-        a.gv[l] = reinterpret_cast<float *>(w + bytes);
-        w += 2 * bytes;
-    }
-    a.rows = rows;
+    a.out = out;
+    a.out_bf16 = p->out_dtype == RECSA_BF16;
+    a.part = static_cast<float *>(ws);
+    a.k_cache = desc->k_cache;
+    a.v_cache = desc->v_cache;
+    a.cap = p->capacity;
+    a.B = batch;
     a.Hq = p->n_q_heads;
+    a.Hkv = p->n_kv_heads;
     a.G = p->n_q_heads / p->n_kv_heads;
-    a.ctx_base = causal ? desc->length - n_q + 1 : desc->length;
-    a.ctx_step = causal ? 1 : 0;
-    a.b = p->fanout_b;
-    a.k = p->budget_k;
-    a.max_cand = (int32_t)L.max_cand;
+    a.length = desc->length;
+    a.span = dense_span(desc->length);
+    a.nspan = (int32_t)((desc->length + a.span - 1) / a.span);
+    a.base = p->rope_base;
     a.scale = p->softmax_scale;
-    DebugView dv{};
-    if (dbg != nullptr) {
-        dv.selected = dbg->selected;
-        dv.kth_gap = dbg->kth_gap;
-        dv.n_keys = nullptr;
-    }
-    hipError_t e = launch_fill_zero(ws, ws_bytes, s);
-    if (e != hipSuccess) return hip_fail(e, "workspace clear");
-    e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
-    if (e != hipSuccess) return hip_fail(e, "backward rows launch");
-    // summaries' gradients down the tree, top level first
-    int64_t pw = 1;
-    int top = 0;
-    for (int l = 1; l <= L.n_levels; ++l) {
-        pw *= p->fanout_b;
-        if (desc->length / pw < 1) break;
-        top = l;
-    }
-    for (int l = top; l >= 1; --l) {
-        int64_t pl = 1;
-        for (int i = 0; i < l; ++i) pl *= p->fanout_b;
-        BwdTreeArgs t{};
-        t.level = l;
-        t.Hkv = p->n_kv_heads;
-        t.nodes = desc->length / pl;
-        t.b = p->fanout_b;
-        t.pool_scale = p->pool_scale;
-        t.pool_w = desc->pool_w;
-        t.gk = a.gk[l];
-        t.gv = a.gv[l];
-        t.gk_child = l >= 2 ? a.gk[l - 1] : nullptr;
-        t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
-        t.dk = d_k;
-        t.dv = d_v;
-        t.dw = d_w;
-        e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
-        if (e != hipSuccess) return hip_fail(e, "backward tree launch");
-    }
+    hipError_t e = launch_dense((recsa_dtype)p->store_dtype, p->head_dim, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dense attention launch");
     return RECSA_OK;
+}
+
+size_t recsa_distill_workspace_bytes(const recsa_params *p, int32_t batch) {
+    if (check_params(p) != RECSA_OK || batch < 1) return 0;
+    const size_t rowsD = (size_t)batch * p->n_q_heads * p->head_dim * sizeof(float);
+    return 3 * align_up(rowsD) + align_up((size_t)p->n_kv_heads * p->head_dim * sizeof(float)) +
+           recsa_backward_workspace_bytes(p);
+}
+
+recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, float *pool_w,
+                                const void *q, int32_t batch, const float *teacher, float lr,
+                                float momentum, float *velocity, float *loss, void *ws, void *stream) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    if ((st = check_desc(p, desc)) != RECSA_OK) return st;
+    if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "distillation needs at least one cached token");
+    if (batch < 1) return fail(RECSA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (pool_w == nullptr || pool_w != desc->pool_w)
+        return fail(RECSA_ERR_INVALID_ARG, "pool_w must be the tree descriptor's pooler vectors");
+    const void *ptrs[] = {q, teacher, velocity, loss, ws};
+    for (const void *ptr : ptrs) {
+        if (ptr == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q, teacher, velocity, loss and ws must be non-NULL");
+    }
+    if (!aligned(q, 16) || !aligned(teacher, 16) || !aligned(velocity, 16) || !aligned(ws, 256))
+        return fail(RECSA_ERR_INVALID_ARG,
+                    "q, teacher and velocity must be 16-byte aligned and ws 256-byte aligned");
+    if (!(lr >= 0.f) || !(momentum >= 0.f && momentum < 1.f))
+        return fail(RECSA_ERR_INVALID_ARG, "lr must be >= 0 and momentum in [0, 1)");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = (int64_t)batch * p->n_q_heads;
+    const size_t rowsD = (size_t)rows * p->head_dim * sizeof(float);
+    char *w = static_cast<char *>(ws);
+    float *out = reinterpret_cast<float *>(w);
+    float *dout = reinterpret_cast<float *>(w + align_up(rowsD));
+    float *dq = reinterpret_cast<float *>(w + 2 * align_up(rowsD));
+    float *dw = reinterpret_cast<float *>(w + 3 * align_up(rowsD));
+    void *bws = w + 3 * align_up(rowsD) + align_up((size_t)p->n_kv_heads * p->head_dim * sizeof(float));
+    // the student: RecSA decode with fp32 output
+    recsa_params pf = *p;
+    pf.out_dtype = RECSA_FP32;
+    if ((st = run_descend(&pf, desc, q, batch, desc->length, 0, out, nullptr, false, nullptr, s)) != RECSA_OK)
+        return st;
+    hipError_t e = launch_distill_loss(out, teacher, dout, loss, (int64_t)rows * p->head_dim, rows, s);
+    if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
+    e = launch_fill_zero(dw, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
+    if (e != hipSuccess) return hip_fail(e, "gradient clear");
+    // dloss/dw with the selection fixed; the token gradients are not needed
+    if ((st = run_backward(p, desc, q, batch, 0, dout, dq, nullptr, nullptr, dw, nullptr, bws, stream)) !=
+        RECSA_OK)
+        return st;
+    e = launch_distill_update(pool_w, velocity, dw, (int64_t)p->n_kv_heads * p->head_dim, lr, momentum, s);
+    if (e != hipSuccess) return hip_fail(e, "pooler update launch");
+    // every summary key depends on w: build the tree again
+    return recsa_build_tree(p, desc, desc->length, stream);
 }
 
 const char *recsa_status_string(recsa_status s) {

@@ -196,6 +196,29 @@ struct BwdTreeArgs {
     float *dw;                 // [Hkv][D] (added to)
 };
 
+// ---- dense attention (the distillation teacher) ---------------------------------
+struct DenseArgs {
+    const void *q;             // [B][Hq][D] store type, at position `length`
+    void *out;                 // [B][Hq][D] out type
+    int32_t out_bf16;
+    float *part;               // [Hkv][nspan][B * G][D + 2] per-span (acc, max, sum)
+    const void *k_cache, *v_cache;
+    int64_t cap;
+    int32_t B, Hq, Hkv, G;
+    int64_t length;
+    int64_t span;              // tokens per span
+    int32_t nspan;
+    double base;
+    float scale;
+};
+int64_t dense_span(int64_t length);
+hipError_t launch_dense(recsa_dtype st, int32_t D, const DenseArgs &a, hipStream_t s);
+
+hipError_t launch_distill_loss(const float *out, const float *teacher, float *dout, float *loss,
+                               int64_t n, int64_t rows, hipStream_t s);
+hipError_t launch_distill_update(float *w, float *vel, const float *dw, int64_t n, float lr, float mu,
+                                 hipStream_t s);
+
 size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, const BwdArgs &a,

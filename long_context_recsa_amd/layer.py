@@ -7,7 +7,8 @@ import ctypes
 import torch
 
 from . import (RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
-               recsa_build_tree, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
+               recsa_build_tree, recsa_dense_decode, recsa_dense_workspace_bytes, recsa_distill_step,
+               recsa_distill_workspace_bytes, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
                recsa_tree_layout, recsa_workspace_bytes)
 
@@ -145,6 +146,32 @@ class RecsaLayer:
                        _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dw"]), dbg,
                        _ptr(self._bws) if nbytes else None, self.stream())
         return (grads, d) if debug else grads
+
+    def dense_decode(self, q: torch.Tensor, out: torch.Tensor | None = None):
+        """Dense causal attention of decode queries at the cache's length (no tree)."""
+        B = q.shape[0]
+        shape = (B, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        if out is None:
+            out = torch.empty(shape, dtype=self.out_dtype, device=self.device)
+        ws = torch.empty(recsa_dense_workspace_bytes(self.p, B), dtype=torch.uint8, device=self.device)
+        recsa_dense_decode(self.p, self.desc, _ptr(q), B, _ptr(out), _ptr(ws), self.stream())
+        return out
+
+    def distill_step(self, q: torch.Tensor, teacher: torch.Tensor, lr: float, momentum: float,
+                     velocity: torch.Tensor, loss: torch.Tensor, ws: torch.Tensor | None = None):
+        """One pooler distillation step (updates pool_w and velocity, rebuilds the tree);
+        the loss before the step goes to `loss` (one fp32 element on the device)."""
+        B = q.shape[0]
+        shape = (B, self.p.n_q_heads, self.p.head_dim)
+        self._check_dev(q, shape, self.store)
+        self._check_dev(teacher, shape, torch.float32)
+        self._check_dev(velocity, (self.p.n_kv_heads, self.p.head_dim), torch.float32)
+        if ws is None:
+            ws = torch.empty(recsa_distill_workspace_bytes(self.p, B), dtype=torch.uint8, device=self.device)
+        recsa_distill_step(self.p, self.desc, _ptr(self.pool_w), _ptr(q), B, _ptr(teacher), lr, momentum,
+                           _ptr(velocity), _ptr(loss), _ptr(ws), self.stream())
+        return loss
 
     # ---- inspection -------------------------------------------------------------
     def level(self, l: int):

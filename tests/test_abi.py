@@ -211,3 +211,36 @@ def test_backward_validates_before_any_hip_call():
         R.recsa_backward(p, R.recsa_tree_desc(fake, fake, fake, fake, 0), fake, 1, 0, fake, fake, fake,
                          fake, fake, ws=ws)
     assert e.value.status == R.RECSA_ERR_INVALID_ARG
+
+
+def test_dense_and_distill_validate_before_any_hip_call():
+    p = _p(capacity=1000)
+    fake = 1 << 20
+    d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
+    assert R.recsa_dense_workspace_bytes(p, 2) >= 8 * 1024 * 2 * 4 * 130 * 4
+    assert R.recsa_distill_workspace_bytes(p, 2) > R.recsa_backward_workspace_bytes(p)
+    assert R.recsa_dense_workspace_bytes(p, 0) == 0 and R.recsa_distill_workspace_bytes(p, 0) == 0
+    cases = [
+        (lambda: R.recsa_dense_decode(p, R.recsa_tree_desc(fake, fake, fake, fake, 0), fake, 1, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_dense_decode(p, d, fake, 0, fake, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_dense_decode(p, d, fake, 1, fake, None), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_dense_decode(p, d, fake + 2, 1, fake, fake), R.RECSA_ERR_INVALID_ARG),
+        # pool_w must be the descriptor's
+        (lambda: R.recsa_distill_step(p, d, fake + 4096, fake, 1, fake, 0.1, 0.9, fake, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_distill_step(p, d, fake, fake, 1, fake, 0.1, 1.0, fake, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_distill_step(p, d, fake, fake, 1, fake, -0.1, 0.9, fake, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_distill_step(p, d, fake, fake, 1, None, 0.1, 0.9, fake, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_distill_step(p, d, fake, fake, 1, fake, 0.1, 0.9, fake, fake, fake + 16),
+         R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_distill_step(p, d, fake, fake, 0, fake, 0.1, 0.9, fake, fake, fake),
+         R.RECSA_ERR_INVALID_ARG),
+    ]
+    for i, (fn, status) in enumerate(cases):
+        with pytest.raises(R.RecsaError) as e:
+            fn()
+        assert e.value.status == status, (i, str(e.value))
