@@ -252,6 +252,82 @@ def run_serve(args, name):
     print(json.dumps(res), flush=True)
 
 
+def run_distill(args, name):
+    """Pooler distillation from dense attention on a workload's cache: B training
+    queries at the cache's length, their dense outputs once (the teacher), then
+    distillation steps (student decode, loss, dloss/dw with the selection fixed,
+    SGD with momentum, tree rebuild).  Step = one recsa_distill_step."""
+    import torch
+
+    import long_context_recsa_amd as R
+    import synth
+
+    w = synth.WORKLOADS[name]
+    B = args.batch or w.max_batch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, V = synth.gen_kv(w, 0, w.L)
+    W = synth.pool_w(w)
+    Q = synth.decode_queries(w, B)
+
+    def dev_store(x):
+        bits = synth.storage_bits(x, w.dtype)
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    p = R.make_params(w.n_kv, w.n_q, w.d, w.b, w.k, w.L, store=w.dtype, out="f32",
+                      rope_base=w.rope_base, softmax_scale=w.softmax_scale, pool_scale=w.pool_scale)
+    layer = R.RecsaLayer(p, dev)
+    for g in range(w.n_kv):
+        layer.k_cache[g].copy_(dev_store(K[g]))
+        layer.v_cache[g].copy_(dev_store(V[g]))
+    layer.pool_w.copy_(torch.from_numpy(W))
+    layer.build(w.L)
+    del K, V
+    q = dev_store(Q)
+    teacher = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    layer.dense_decode(q, out=teacher)
+    a.record()
+    layer.dense_decode(q, out=teacher)
+    b.record()
+    torch.cuda.synchronize()
+    t_teacher = a.elapsed_time(b)
+    vel = torch.zeros_like(layer.pool_w)
+    n = args.warmup + args.steps
+    losses = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = torch.empty(R.recsa_distill_workspace_bytes(p, B), dtype=torch.uint8, device=dev)
+    lr, mu = args.lr, 0.9
+    for i in range(args.warmup):
+        layer.distill_step(q, teacher, lr, mu, vel, losses[i:i + 1], ws)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.distill_step(q, teacher, lr, mu, vel, losses[i:i + 1], ws)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    lv = losses.cpu().numpy().tolist()
+    res = {
+        "metric": "pooler distillation steps/s (decode + loss + dw + update + tree rebuild per step)",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "storage": w.dtype, "L": w.L, "n_kv_heads": w.n_kv,
+                   "n_q_heads": w.n_q, "head_dim": w.d, "b": w.b, "k": w.k, "train_queries": B,
+                   "lr": lr, "momentum": mu},
+        "ms": {"distill_step": ms, "teacher_dense_decode": t_teacher},
+        "loss_first": lv[0], "loss_last": lv[-1], "losses": lv,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +337,9 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--distill", action="store_true",
+                    help="time pooler distillation steps on the workload instead of the hot path")
+    ap.add_argument("--lr", type=float, default=1000.0, help="distillation learning rate")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
@@ -286,6 +365,8 @@ def main():
 
     if args.workload in synth.SERVE_BATCHES:
         return run_serve(args, args.workload)
+    if args.distill:
+        return run_distill(args, args.workload)
     w = synth.WORKLOADS[args.workload]
     B = args.batch or w.max_batch
     dev = torch.device("cuda:0")
