@@ -187,22 +187,28 @@ __device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m) 
     return T;
 }
 
+// The ordered keys of candidates lane, lane + 64, ... of z[0..n) (0 past n: valid
+// keys are > 0).
 template <int KT>
-__device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag, int32_t *kept,
+__device__ __forceinline__ void load_keys(const float *z, int32_t n, int lane, uint32_t (&kk)[KT]) {
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int32_t i = lane + 64 * t;
+        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;
+    }
+}
+
+template <int KT>
+__device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uint8_t *flag, int32_t *kept,
                                                    int32_t m, Cands cd, const int32_t *parents,
                                                    int lane, float *out) {
     // wave-uniform counts in scalar registers (they may come from a vector load)
     const int32_t n = __builtin_amdgcn_readfirstlane(cd.n);
     m = __builtin_amdgcn_readfirstlane(m);
     const int nT = (n + 63) >> 6;                       // registers that hold keys
-    uint32_t kk[KT];
     uint32_t lmax = 0;
     #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        const int32_t i = lane + 64 * t;
-        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;      // valid keys are > 0
-        lmax = max(lmax, kk[t]);
-    }
+    for (int t = 0; t < KT; ++t) lmax = max(lmax, kk[t]);
     uint32_t T = 0;
     if (nT == 1)
         T = bisect_threshold<1>(kk, m);
@@ -244,30 +250,25 @@ __device__ __forceinline__ void select_bisect_regs(const float *z, uint8_t *flag
     }
 }
 
+// The selection with the keys already in registers (KT > 0, from load_keys); z is
+// read again only by the rare fallback of the wide filter.
 template <int KT>
-__device__ __forceinline__ void select(const float *z, uint8_t *flag, int32_t *kept, int32_t m,
-                                       Cands cd, const int32_t *parents, int lane,
-                                       unsigned char *scratch, float *out) {
-    if constexpr (KT == 0) {
-        select_bisect(z, flag, kept, m, cd, parents, lane, out);
-        __threadfence_block();
-        return;
-    } else if constexpr (KT <= 5) {
-        select_bisect_regs<KT>(z, flag, kept, m, cd, parents, lane, out);
+__device__ __forceinline__ void select_from_keys(const uint32_t (&kk)[KT], const float *z, uint8_t *flag,
+                                                 int32_t *kept, int32_t m, Cands cd,
+                                                 const int32_t *parents, int lane,
+                                                 unsigned char *scratch, float *out) {
+    static_assert(KT > 0, "register keys");
+    if constexpr (KT <= 5) {
+        select_bisect_regs<KT>(kk, flag, kept, m, cd, parents, lane, out);
         __threadfence_block();
         return;
     } else {
         const int32_t n = cd.n;
         uint2 *list = reinterpret_cast<uint2 *>(scratch);                 // [128] (key, index)
         uint32_t *keep = reinterpret_cast<uint32_t *>(scratch + 128 * 8);  // [128]
-        uint32_t kk[KT];
         uint32_t lmax = 0;
         #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int32_t i = lane + 64 * t;
-            kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;    // valid keys are > 0
-            lmax = max(lmax, kk[t]);
-        }
+        for (int t = 0; t < KT; ++t) lmax = max(lmax, kk[t]);
         uint32_t gmax;
         if (m <= 4) gmax = group_umax<16>(lmax);
         else if (m <= 8) gmax = group_umax<8>(lmax);
@@ -360,6 +361,20 @@ __device__ __forceinline__ void select(const float *z, uint8_t *flag, int32_t *k
             flag[e1.y] = 1;
         }
         __threadfence_block();
+    }
+}
+
+template <int KT>
+__device__ __forceinline__ void select(const float *z, uint8_t *flag, int32_t *kept, int32_t m,
+                                       Cands cd, const int32_t *parents, int lane,
+                                       unsigned char *scratch, float *out) {
+    if constexpr (KT == 0) {
+        select_bisect(z, flag, kept, m, cd, parents, lane, out);
+        __threadfence_block();
+    } else {
+        uint32_t kk[KT];
+        load_keys<KT>(z, cd.n, lane, kk);
+        select_from_keys<KT>(kk, z, flag, kept, m, cd, parents, lane, scratch, out);
     }
 }
 
