@@ -40,6 +40,7 @@ OP_SOURCES = {
     "decode_grouped": ["descend_impl.hpp", "descend_grouped_bf16.hip", "descend_grouped_f32.hip",
                        "select_topk.hpp"],
     "prefill": ["prefill_tiled.hip", "select_topk.hpp"],
+    "backward": ["backward_kernels.hip", "select_topk.hpp"],
 }
 COMMON_SOURCES = ["recsa_internal.hpp", "recsa_api.hip"]
 
