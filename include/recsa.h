@@ -190,9 +190,12 @@ RECSA_API recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_des
                            int64_t n_q, void *out, const recsa_debug *dbg, void *ws,
                            void *stream);
 
-/* Workspace bytes recsa_backward needs (device memory, 256-byte aligned): fp32
- * gradients of every level's summary keys and values.  0 on invalid params. */
-RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p);
+/* Workspace bytes recsa_backward needs for up to `max_rows` rows (n_q *
+ * n_q_heads; device memory, 256-byte aligned): fp32 gradients of every level's
+ * summary keys and values, and, for bf16 storage and at least 4096 rows (fanout
+ * <= 128), the parent-major path's buffers: the forward's buckets, its output,
+ * selections and per-row softmax statistics.  0 on invalid params. */
+RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t max_rows);
 
 /* Backward of the attention output with the selection held fixed (the method
  * is trained end to end: abstract, sentence on evaluation).  For the rows of
@@ -211,9 +214,11 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p);
  * Rounding a summary to store_dtype passes the gradient through unchanged.
  * Entry logits, softmax and the selection are recomputed as in the forward.
  * Sums over rows use fp32 atomics, so low-order bits depend on their order.
- * q: as the forward's, store_dtype.  ws: recsa_backward_workspace_bytes(p)
- * bytes, 256-byte aligned, cleared by the call (may be NULL when that is 0,
- * i.e. capacity < fanout_b).  dbg (may be NULL): selected
+ * bf16 storage with at least 4096 rows runs parent-major (as recsa_prefill
+ * does): pairs (row, parent) are grouped by parent and each group's children
+ * take one summed gradient per group rather than one per row.
+ * q: as the forward's, store_dtype.  ws: recsa_backward_workspace_bytes(p,
+ * n_q * n_q_heads) bytes, 256-byte aligned (may be NULL when that is 0).  dbg (may be NULL): selected
  * and kth_gap as recsa_decode reports them (n_keys is not written). */
 RECSA_API recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
                             int64_t n_q, int32_t causal, const float *d_out, float *d_q,

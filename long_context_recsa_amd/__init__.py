@@ -88,7 +88,7 @@ def load_library():
         "recsa_multi_workspace_bytes": (ctypes.c_size_t, [i32]),
         "recsa_decode_multi": (i32, [P, D, i32, v, v, G, v, v]),
         "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
-        "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P]),
+        "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P, i64]),
         "recsa_backward": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
         "recsa_dense_workspace_bytes": (ctypes.c_size_t, [P, i32]),
         "recsa_dense_decode": (i32, [P, D, v, i32, v, v, v]),
@@ -161,8 +161,8 @@ def recsa_prefill(p, desc, q_ptr, n_q, out_ptr, dbg=None, ws=None, stream=None) 
                                         ws, stream))
 
 
-def recsa_backward_workspace_bytes(p) -> int:
-    return load_library().recsa_backward_workspace_bytes(ctypes.byref(p))
+def recsa_backward_workspace_bytes(p, max_rows: int) -> int:
+    return load_library().recsa_backward_workspace_bytes(ctypes.byref(p), max_rows)
 
 
 def recsa_backward(p, desc, q_ptr, n_q, causal, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr, dbg=None,

@@ -83,6 +83,21 @@ struct TP {
     float *partial;            // [lv][rows_cap][k+1][D]: sum of exp(z - m) v per pair
     float2 *pml;               // [lv][rows_cap][k+1]: (m, sum of exp(z - m)) per pair
     int32_t *nplev;            // [rows][lv]: pairs at each level
+    float2 *rowml;             // [rows] (max, sum) of each row's softmax, when not null (backward)
+};
+
+// The backward's inputs and outputs for one pass of rows.
+struct TB {
+    const float *dout;         // [rows][D] fp32
+    float *dq;                 // [rows][D] fp32, added to
+    float *dk, *dv;            // [Hkv][cap][D] fp32 token gradients, added to
+    float *gk[kMaxLevels + 1]; // [Hkv][node_cap][D] fp32 summary gradients (l >= 1), added to
+    float *gv[kMaxLevels + 1];
+    const float2 *rowml;       // [rows] (max, sum) from the forward
+    const float *rowD;         // [rows] <dO, out>
+    const int32_t *sel;        // [rows][n_levels][k] kept nodes by level, -1 padded
+    int64_t cap;               // token capacity (row stride of a head in dk, dv)
+    int64_t node_cap[kMaxLevels + 1];
 };
 
 struct RowLevel {
@@ -806,6 +821,288 @@ __global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) 
     });
 }
 
+// ------------------------------------------------------------- backward --
+// Gradients of <dO, out> with the selection of the forward held fixed, per
+// (KV head, parent) item of up to 16 pairs: the pairs' logits against the
+// parent's children (score_tile) and dp = <dO, v> (dot_tile) on MFMA; then per
+// chunk of 32 children, with p = e^(z - M) / L (0 for kept or missing
+// children) and dz = s p (dp - D):
+//   dV_c += sum_pairs p dO,  dK_c += R(-c) sum_pairs dz U  (U = R(n - r b) q),
+//   dq += R(-(n - r b)) sum_c dz R(c) k_c,
+// summed over the item's pairs in registers first, so each (child, dim) takes
+// one atomic add per item rather than one per pair.  In that phase lane j holds
+// the RoPE pair (j, j + D/2) of every pair of the item and the wave walks the
+// children, so each atomic instruction covers consecutive dimensions of one
+// child (two cache lines) instead of one dimension of 64 children.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// <dO, v> of pairs 4*grp + v against child 32*kk + 16*t + L%16: values in the keys'
+// k-slot layout (bf16, exact as the B operand), dO split into bf16 hi + lo.
+template <int D>
+__device__ __forceinline__ f32x4 dot_tile(const KRaw<D> &r, int t, const bf16x8 *dh, const bf16x8 *dl) {
+    constexpr int KS1 = D / 64;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int pc = 0; pc < KS1; ++pc) {
+        const bf16x8 v1 = __builtin_bit_cast(bf16x8, r.k[t][2 * pc]);
+        const bf16x8 v2 = __builtin_bit_cast(bf16x8, r.k[t][2 * pc + 1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dh[pc], v1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dl[pc], v1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dh[pc + KS1], v2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dl[pc + KS1], v2, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <int D>
+__host__ __device__ constexpr size_t tb_wave_lds() {
+    return (size_t)2 * kTile * D * 4 + (size_t)32 * D * 2 + (size_t)2 * 32 * kTile * 4 + (size_t)kTile * 4 * 4;
+}
+
+template <int D, int KC>
+__global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, int32_t NP) {
+    constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
+    constexpr int SUB = 64 / H;                  // children per step of the wave (1 at D = 128, 2 at D = 64)
+    extern __shared__ __align__(16) unsigned char smem[];
+    float2 *crot = reinterpret_cast<float2 *>(smem);
+    load_crot(tv, a.b, D, crot);
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int j = lane % H, sb = lane / H;       // the lane's RoPE pair (j, j + H) and child sub-step
+    unsigned char *wb = smem + (size_t)a.b * crot_stride(D) * sizeof(float2) + (size_t)wv * tb_wave_lds<D>();
+    float *U = reinterpret_cast<float *>(wb);                         // [16][D] rotated queries
+    float *dO = U + kTile * D;                                        // [16][D]
+    uint16_t *Kb = reinterpret_cast<uint16_t *>(dO + kTile * D);      // [32][D] the chunk's keys (bf16)
+    float *Pt = reinterpret_cast<float *>(Kb + 32 * D);               // [32 children][16 pairs]
+    float *dZt = Pt + 32 * kTile;                                     // [32][16]
+    uint32_t *kmask = reinterpret_cast<uint32_t *>(dZt + 32 * kTile); // [16][4] kept children bits
+    const int64_t nexist = a.length / a.pw[l];
+    const int32_t b = a.b;
+    const bool grads_here = l > 0 || t.dk != nullptr;
+    for_items(a, NP, lane, [&](const Item &it) {
+        const bf16_t *keys = level_rows(tv, false, l, it.g, D);
+        const bf16_t *vals = level_rows(tv, true, l, it.g, D);
+        const int64_t c0 = it.p * b;
+        wave_sync();                        // the previous item's LDS reads are done
+        // queries rotated to their rank position (the score's A operand, and fp32 to LDS)
+        QRaw<D> qr;
+        load_query<D>(tv, a, it, lane, qr);
+        bf16x8 ah[D / 32], al[D / 32];
+        query_operands<D>(qr, it, lane, ah, al);
+        #pragma unroll
+        for (int pc = 0; pc < KS1; ++pc) {
+            float x1[8], x2[8];
+            unpack8(qr.q[2 * pc], x1);
+            unpack8(qr.q[2 * pc + 1], x2);
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 cs = qr.cs[4 * pc + u];
+                U[i16 * D + grp * PG + 8 * pc + 2 * u] = x1[2 * u] * cs.x - x2[2 * u] * cs.y;
+                U[i16 * D + H + grp * PG + 8 * pc + 2 * u] = x2[2 * u] * cs.x + x1[2 * u] * cs.y;
+                U[i16 * D + grp * PG + 8 * pc + 2 * u + 1] = x1[2 * u + 1] * cs.z - x2[2 * u + 1] * cs.w;
+                U[i16 * D + H + grp * PG + 8 * pc + 2 * u + 1] = x2[2 * u + 1] * cs.z + x1[2 * u + 1] * cs.w;
+            }
+        }
+        // dO of the pairs: to LDS, and split into the A operand of <dO, v>
+        bf16x8 dh[D / 32], dl[D / 32];
+        {
+            const float live = i16 < it.cnt ? 1.f : 0.f;
+            const float *dp = t.dout + (int64_t)it.pr.x * D;
+            #pragma unroll
+            for (int pc = 0; pc < KS1; ++pc) {
+                float x1[8], x2[8];
+                #pragma unroll
+                for (int v = 0; v < 8; v += 4) {
+                    const float4 y1 = *reinterpret_cast<const float4 *>(dp + grp * PG + 8 * pc + v);
+                    const float4 y2 = *reinterpret_cast<const float4 *>(dp + H + grp * PG + 8 * pc + v);
+                    x1[v] = live * y1.x; x1[v + 1] = live * y1.y; x1[v + 2] = live * y1.z; x1[v + 3] = live * y1.w;
+                    x2[v] = live * y2.x; x2[v + 1] = live * y2.y; x2[v + 2] = live * y2.z; x2[v + 3] = live * y2.w;
+                }
+                #pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    dO[i16 * D + grp * PG + 8 * pc + v] = x1[v];
+                    dO[i16 * D + H + grp * PG + 8 * pc + v] = x2[v];
+                }
+                split8(x1, dh[pc], dl[pc]);
+                split8(x2, dh[pc + KS1], dl[pc + KS1]);
+            }
+        }
+        // children of the parent that a pair's row kept at this level (they are not entries)
+        if (grp == 0) {
+            uint32_t m4[4] = {0u, 0u, 0u, 0u};
+            if (l >= 1 && i16 < it.cnt) {
+                const int32_t *ks = t.sel + ((int64_t)it.pr.x * a.n_levels + (l - 1)) * a.k;
+                for (int r = 0; r < a.k; ++r) {
+                    const int32_t id = ks[r];
+                    const int64_t c = (int64_t)id - c0;
+                    if (id >= 0 && c >= 0 && c < b) m4[c >> 5] |= 1u << (c & 31);
+                }
+            }
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) kmask[i16 * 4 + u] = m4[u];
+        }
+        // per D-row pair (4*grp + v): the row's softmax statistics
+        float Mv[4], Lv[4], Dv[4];
+        #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const bool ok = 4 * grp + v < it.cnt;
+            const float2 ml = ok ? t.rowml[it.orow[v]] : make_float2(0.f, 1.f);
+            Mv[v] = ml.x;
+            Lv[v] = 1.f / ml.y;
+            Dv[v] = ok ? t.rowD[it.orow[v]] : 0.f;
+        }
+        wave_sync();
+        // dq of every pair of the item in the children's frame, dimensions (j, j + H)
+        float dq1[kTile], dq2[kTile];
+        #pragma unroll
+        for (int pr = 0; pr < kTile; ++pr) { dq1[pr] = 0.f; dq2[pr] = 0.f; }
+        for (int kk = 0; kk < KC; ++kk) {
+            KRaw<D> kr, vr;
+            load_keys<D>(keys, c0, nexist, b, kk, lane, kr);
+            load_keys<D>(vals, c0, nexist, b, kk, lane, vr);
+            // the chunk's keys to LDS (bf16), for dq
+            #pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                #pragma unroll
+                for (int pc = 0; pc < KS1; ++pc) {
+                    *reinterpret_cast<uint4 *>(Kb + (16 * tt + i16) * D + grp * PG + 8 * pc) = kr.k[tt][2 * pc];
+                    *reinterpret_cast<uint4 *>(Kb + (16 * tt + i16) * D + H + grp * PG + 8 * pc) = kr.k[tt][2 * pc + 1];
+                }
+            // p and dz of pairs 4*grp .. 4*grp + 3 against child 32*kk + cc, to [cc][pair]
+            #pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const f32x4 zt = score_tile<D>(kr, tt, crot, c0, nexist, b, kk, lane, ah, al);
+                const f32x4 pt = dot_tile<D>(vr, tt, dh, dl);
+                const int cc = 16 * tt + i16;
+                const int c = 32 * kk + cc;
+                float pe4[4], dz4[4];
+                #pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int pr = 4 * grp + v;
+                    const bool kept = (kmask[pr * 4 + (c >> 5)] >> (c & 31)) & 1u;
+                    const bool ok = pr < it.cnt && c < it.onc[v] && !kept;
+                    pe4[v] = ok ? __expf(a.scale * zt[v] - Mv[v]) * Lv[v] : 0.f;
+                    dz4[v] = a.scale * pe4[v] * (pt[v] - Dv[v]);
+                }
+                *reinterpret_cast<float4 *>(Pt + cc * kTile + 4 * grp) = make_float4(pe4[0], pe4[1], pe4[2], pe4[3]);
+                *reinterpret_cast<float4 *>(dZt + cc * kTile + 4 * grp) = make_float4(dz4[0], dz4[1], dz4[2], dz4[3]);
+            }
+            wave_sync();
+            // per child: dV, dK (one atomic add per dimension) and its share of dq
+            {
+                float u1[kTile], u2[kTile], o1[kTile], o2[kTile];
+                #pragma unroll
+                for (int pr = 0; pr < kTile; ++pr) {
+                    u1[pr] = U[pr * D + j];
+                    u2[pr] = U[pr * D + H + j];
+                    o1[pr] = dO[pr * D + j];
+                    o2[pr] = dO[pr * D + H + j];
+                }
+                const int nc = b - 32 * kk < 32 ? b - 32 * kk : 32;      // children in this chunk
+                for (int s0 = 0; s0 < nc; s0 += SUB) {
+                    const int cc = s0 + sb;
+                    const bool inb = cc < nc;
+                    const int ccl = inb ? cc : 0;
+                    const int c = 32 * kk + ccl;
+                    float pv[kTile], dz[kTile];
+                    #pragma unroll
+                    for (int q4 = 0; q4 < kTile / 4; ++q4) {
+                        const float4 x = *reinterpret_cast<const float4 *>(Pt + ccl * kTile + 4 * q4);
+                        const float4 y = *reinterpret_cast<const float4 *>(dZt + ccl * kTile + 4 * q4);
+                        pv[4 * q4] = x.x; pv[4 * q4 + 1] = x.y; pv[4 * q4 + 2] = x.z; pv[4 * q4 + 3] = x.w;
+                        dz[4 * q4] = y.x; dz[4 * q4 + 1] = y.y; dz[4 * q4 + 2] = y.z; dz[4 * q4 + 3] = y.w;
+                    }
+                    bool any = false;
+                    #pragma unroll
+                    for (int pr = 0; pr < kTile; ++pr) {
+                        if (!inb) { pv[pr] = 0.f; dz[pr] = 0.f; }
+                        any = any || pv[pr] != 0.f || dz[pr] != 0.f;
+                    }
+                    float v1 = 0.f, v2 = 0.f, k1 = 0.f, k2 = 0.f;
+                    #pragma unroll
+                    for (int pr = 0; pr < kTile; ++pr) {
+                        v1 += pv[pr] * o1[pr];
+                        v2 += pv[pr] * o2[pr];
+                        k1 += dz[pr] * u1[pr];
+                        k2 += dz[pr] * u2[pr];
+                    }
+                    const float2 cs = crot[c * crot_stride(D) + j];         // (cos, sin) of c theta_j
+                    if (any && grads_here && c0 + c < nexist) {
+                        float *gk = l == 0 ? t.dk + ((int64_t)it.g * t.cap + c0 + c) * D
+                                           : t.gk[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
+                        float *gv = l == 0 ? t.dv + ((int64_t)it.g * t.cap + c0 + c) * D
+                                           : t.gv[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
+                        atomicAdd(gv + j, v1);
+                        atomicAdd(gv + H + j, v2);
+                        atomicAdd(gk + j, k1 * cs.x + k2 * cs.y);             // R(-c theta)
+                        atomicAdd(gk + H + j, k2 * cs.x - k1 * cs.y);
+                    }
+                    const float x1 = bf16_to_f32(Kb[ccl * D + j]), x2 = bf16_to_f32(Kb[ccl * D + H + j]);
+                    const float r1 = x1 * cs.x - x2 * cs.y, r2 = x2 * cs.x + x1 * cs.y;   // R(c theta) k_c
+                    #pragma unroll
+                    for (int pr = 0; pr < kTile; ++pr) {
+                        dq1[pr] += dz[pr] * r1;
+                        dq2[pr] += dz[pr] * r2;
+                    }
+                }
+            }
+            wave_sync();                    // the next chunk rewrites Kb, Pt and dZt
+        }
+        // dq += R(-(n - r b) theta) of the sums, pair by pair
+        if (SUB == 2) {
+            #pragma unroll
+            for (int pr = 0; pr < kTile; ++pr) {
+                dq1[pr] += __shfl_xor(dq1[pr], 32);
+                dq2[pr] += __shfl_xor(dq2[pr], 32);
+            }
+        }
+        #pragma unroll
+        for (int pr = 0; pr < kTile; ++pr) {
+            if (pr < it.cnt) {
+                const int row = __builtin_amdgcn_readlane(it.pr.x, pr);
+                const int pos = __builtin_amdgcn_readlane(it.pr.z, pr);
+                if (sb == 0) {
+                    const float2 r = tv.rope[(int64_t)pos * H + j];
+                    float *dq = t.dq + (int64_t)row * D;
+                    atomicAdd(dq + j, dq1[pr] * r.x + dq2[pr] * r.y);
+                    atomicAdd(dq + H + j, dq2[pr] * r.x - dq1[pr] * r.y);
+                }
+            }
+        }
+    });
+}
+
+// The kept nodes of level l + 1 (the parents of level l) from the forward's record.
+__global__ void tb_parents(TP a, const int32_t *sel, int l) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.rows) return;
+    int32_t m = 0;
+    if (l < a.top) {
+        const int32_t *ks = sel + (row * a.n_levels + l) * a.k;
+        for (int r = 0; r < a.k; ++r) {
+            const int32_t id = ks[r];
+            if (id >= 0) a.par[l & 1][row * a.k + m++] = id;
+        }
+    }
+    a.mk[l & 1][row] = m;
+}
+
+// <dO, out> per row.
+__global__ void tb_rowdot(const float *dout, const float *out, float *rowD, int64_t rows, int D) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    float v = 0.f;
+    for (int j = lane; j < D; j += 64) v += dout[row * D + j] * out[row * D + j];
+    #pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) rowD[row] = v;
+}
+
 // ----------------------------------------------------------------- final --
 // Merges every pair state (m, l, acc) of a row: with M the largest m,
 // out = sum exp(m - M) acc / sum exp(m - M) l.  One thread per (row, 4 dimensions).
@@ -837,6 +1134,7 @@ __device__ __forceinline__ void final_one(const TP &a, int64_t t, int D4) {
         }
     }
     const float inv = 1.f / L;
+    if (a.rowml != nullptr && j == 0) a.rowml[row] = make_float2(M, L);
     const float o[4] = {v.x * inv, v.y * inv, v.z * inv, v.w * inv};
     if (a.out_bf16)
         Vec<bf16_t, 4>::store(static_cast<bf16_t *>(a.out) + row * a.D + 4 * j, o);
@@ -948,6 +1246,20 @@ hipError_t launch_count(const TP &a, int l, int32_t NP, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The pairs of level l grouped by (KV head, parent) into items of up to 16.
+hipError_t bucket_level(const TP &a, const DebugView &dbg, int l, int32_t NP, hipStream_t s) {
+    const int64_t nb = (int64_t)a.Hkv * NP;
+    const int64_t nchunks = (nb + kScanChunk - 1) / kScanChunk;
+    hipError_t e;
+    if ((e = launch_count(a, l, NP, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tp_scan_sums, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+    hipLaunchKernelGGL(tp_scan_chunks, dim3(1), dim3(256), 0, s, a, nb, nchunks);
+    hipLaunchKernelGGL(tp_scan_write, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+    hipLaunchKernelGGL(tp_scatter, dim3((unsigned)((a.rows + nb + 255) / 256)), dim3(256), 0, s, a, dbg, l, NP,
+                       nb);
+    return hipGetLastError();
+}
+
 template <int D, int KC>
 hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_ctx, const Plan &P,
                     int32_t maxc, hipStream_t s) {
@@ -962,13 +1274,7 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
     for (int l = a.top; l >= 0; --l) {
         const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
         const int64_t nb = (int64_t)a.Hkv * NP;
-        const int64_t nchunks = (nb + kScanChunk - 1) / kScanChunk;
-        if ((e = launch_count(a, l, NP, s)) != hipSuccess) return e;
-        hipLaunchKernelGGL(tp_scan_sums, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
-        hipLaunchKernelGGL(tp_scan_chunks, dim3(1), dim3(256), 0, s, a, nb, nchunks);
-        hipLaunchKernelGGL(tp_scan_write, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
-        hipLaunchKernelGGL(tp_scatter, dim3((unsigned)((rows + nb + 255) / 256)), dim3(256), 0, s, a, dbg, l,
-                           NP, nb);
+        if ((e = bucket_level(a, dbg, l, NP, s)) != hipSuccess) return e;
         const int64_t pairs = rows * (int64_t)std::min(a.k + 1, (int)NP);
         const int64_t items = pairs / kTile + nb + 1;
         const unsigned ib = (unsigned)((items + 3) / 4);
@@ -999,6 +1305,58 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
     return hipGetLastError();
 }
 
+}  // namespace
+
+size_t tiled_backward_lds_bytes(int32_t D, int32_t b) {
+    return (size_t)b * crot_stride(D) * sizeof(float2) +
+           4 * (D == 128 ? tb_wave_lds<128>() : tb_wave_lds<64>());
+}
+
+namespace {
+
+// Backward of one pass of rows: the forward (recording the selections and each row's
+// softmax statistics), <dO, out>, then per level the same buckets and tb_item.
+template <int D, int KC>
+hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, int64_t max_ctx, const Plan &P,
+                             int32_t maxc, hipStream_t s) {
+    DebugView fd{};
+    fd.selected = const_cast<int32_t *>(t.sel);
+    a.out = out;
+    a.out_bf16 = 0;
+    hipError_t e = run_pass<D, KC>(tv, a, fd, max_ctx, P, maxc, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tb_rowdot, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, t.dout, out,
+                       const_cast<float *>(t.rowD), a.rows, D);
+    const DebugView none{};
+    const size_t lds = tiled_backward_lds_bytes(D, a.b);
+    for (int l = a.top; l >= 0; --l) {
+        const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
+        const int64_t nb = (int64_t)a.Hkv * NP;
+        hipLaunchKernelGGL(tb_parents, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, s, a, t.sel, l);
+        if ((e = bucket_level(a, none, l, NP, s)) != hipSuccess) return e;
+        const int64_t pairs = a.rows * (int64_t)std::min(a.k + 1, (int)NP);
+        const int64_t items = pairs / kTile + nb + 1;
+        unsigned grid;
+        if ((e = persistent_grid((const void *)tb_item<D, KC>, lds, (unsigned)((items + 3) / 4), grid)) !=
+            hipSuccess)
+            return e;
+        hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, t, l, NP);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int D>
+hipError_t run_backward_pass_d(const TreeView &tv, const TP &a, const TB &t, float *out, int64_t max_ctx,
+                               const Plan &P, int32_t maxc, hipStream_t s) {
+    switch ((a.b + 31) / 32) {
+        case 1: return run_backward_pass<D, 1>(tv, a, t, out, max_ctx, P, maxc, s);
+        case 2: return run_backward_pass<D, 2>(tv, a, t, out, max_ctx, P, maxc, s);
+        case 3: return run_backward_pass<D, 3>(tv, a, t, out, max_ctx, P, maxc, s);
+        default: return run_backward_pass<D, 4>(tv, a, t, out, max_ctx, P, maxc, s);
+    }
+}
+
 template <int D>
 hipError_t run_pass_d(const TreeView &tv, const TP &a, const DebugView &dbg, int64_t max_ctx,
                       const Plan &P, int32_t maxc, hipStream_t s) {
@@ -1023,11 +1381,10 @@ size_t tiled_select_lds_bytes(int32_t maxc, int32_t k) {
     return 4 * select_smem_wave((maxc + 3) / 4 * 4, k);
 }
 
-hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
-                                int64_t length, int64_t capacity, const DebugView &dbg, void *ws,
-                                hipStream_t s) {
-    const int64_t per = pass_rows(da.rows, da.Hq);
-    const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
+namespace {
+
+TP make_tp(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv, int64_t length, const Plan &P,
+           void *ws) {
     unsigned char *w = static_cast<unsigned char *>(ws);
     TP a{};
     a.Hq = da.Hq;
@@ -1060,21 +1417,101 @@ hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs
     a.partial = reinterpret_cast<float *>(w + P.off_partial);
     a.pml = reinterpret_cast<float2 *>(w + P.off_pml);
     a.nplev = reinterpret_cast<int32_t *>(w + P.off_nplev);
-    const size_t esz_q = 2, esz_o = da.out_bf16 ? 2 : 4;
+    return a;
+}
+
+// The pass's first row r0 onwards: queries, context lengths and the level powers.
+int64_t set_pass(TP &a, const DescendArgs &da, int64_t r0, int64_t rows, int32_t D) {
+    const int64_t q0 = r0 / da.Hq;
+    a.rows = rows;
+    a.q = reinterpret_cast<const bf16_t *>(static_cast<const unsigned char *>(da.q) + r0 * D * 2);
+    a.ctx_base = da.ctx_base + q0 * da.ctx_step;
+    const int64_t max_ctx = a.ctx_base + (rows / da.Hq - 1) * da.ctx_step;
+    a.top = 0;
+    a.pw[0] = 1;
+    for (int l = 1; l < kMaxLevels + 2; ++l) {
+        a.pw[l] = a.pw[l - 1] <= max_ctx ? a.pw[l - 1] * da.b : a.pw[l - 1];
+        if (a.pw[l] <= max_ctx && a.pw[l] > a.pw[l - 1]) a.top = l;
+    }
+    return max_ctx;
+}
+
+// The backward's own buffers after the forward's plan: out [rows][D] fp32, the
+// selections [rows][n_levels][k], (max, sum) and <dO, out> per row.
+struct BwdPlan {
+    size_t off_out, off_sel, off_ml, off_rowD, total;
+};
+
+BwdPlan make_bwd_plan(const Plan &P, int32_t D, int32_t k, int32_t n_levels) {
+    BwdPlan B{};
+    size_t o = P.total;
+    auto put = [&](size_t bytes) { const size_t at = o; o = up256(o + bytes); return at; };
+    B.off_out = put((size_t)P.rows * D * 4);
+    B.off_sel = put((size_t)P.rows * (n_levels > 0 ? n_levels : 1) * k * 4);
+    B.off_ml = put((size_t)P.rows * 8);
+    B.off_rowD = put((size_t)P.rows * 4);
+    B.total = o;
+    return B;
+}
+
+}  // namespace
+
+size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
+                                      int32_t maxc, int64_t capacity, int32_t n_levels) {
+    const Plan P = make_plan(pass_rows(rows, Hq), Hkv, D, b, k, maxc, capacity, n_levels);
+    return make_bwd_plan(P, D, k, n_levels).total;
+}
+
+hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
+                                 int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
+                                 void *ws, hipStream_t s) {
+    const int64_t per = pass_rows(da.rows, da.Hq);
+    const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
+    const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels);
+    unsigned char *w = static_cast<unsigned char *>(ws);
+    TP a = make_tp(tv, D, da, Hkv, length, P, ws);
+    a.rowml = reinterpret_cast<float2 *>(w + B.off_ml);
+    float *out = reinterpret_cast<float *>(w + B.off_out);
+    TB t{};
+    t.dk = ba.dk;
+    t.dv = ba.dv;
+    for (int l = 0; l <= kMaxLevels; ++l) {
+        t.gk[l] = ba.gk[l];
+        t.gv[l] = ba.gv[l];
+        t.node_cap[l] = tv.node_cap[l];
+    }
+    t.cap = tv.cap;
+    t.rowml = a.rowml;
+    t.rowD = reinterpret_cast<const float *>(w + B.off_rowD);
+    t.sel = reinterpret_cast<const int32_t *>(w + B.off_sel);
     for (int64_t r0 = 0; r0 < da.rows; r0 += per) {
         const int64_t rows = std::min(per, da.rows - r0);
-        const int64_t q0 = r0 / da.Hq;
-        a.rows = rows;
-        a.q = reinterpret_cast<const bf16_t *>(static_cast<const unsigned char *>(da.q) + r0 * D * esz_q);
-        a.out = static_cast<unsigned char *>(da.out) + r0 * D * esz_o;
-        a.ctx_base = da.ctx_base + q0 * da.ctx_step;
-        const int64_t max_ctx = a.ctx_base + (rows / da.Hq - 1) * da.ctx_step;
-        a.top = 0;
-        a.pw[0] = 1;
-        for (int l = 1; l < kMaxLevels + 2; ++l) {
-            a.pw[l] = a.pw[l - 1] <= max_ctx ? a.pw[l - 1] * da.b : a.pw[l - 1];
-            if (a.pw[l] <= max_ctx && a.pw[l] > a.pw[l - 1]) a.top = l;
+        const int64_t max_ctx = set_pass(a, da, r0, rows, D);
+        t.dout = ba.dout + r0 * D;
+        t.dq = ba.dq + r0 * D;
+        const hipError_t e = D == 128 ? run_backward_pass_d<128>(tv, a, t, out, max_ctx, P, da.max_cand, s)
+                                      : run_backward_pass_d<64>(tv, a, t, out, max_ctx, P, da.max_cand, s);
+        if (e != hipSuccess) return e;
+        if (dbg_selected != nullptr && tv.n_levels > 0) {
+            const hipError_t c = hipMemcpyAsync(dbg_selected + r0 * tv.n_levels * da.k, t.sel,
+                                                (size_t)rows * tv.n_levels * da.k * 4, hipMemcpyDeviceToDevice, s);
+            if (c != hipSuccess) return c;
         }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_prefill_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
+                                int64_t length, int64_t capacity, const DebugView &dbg, void *ws,
+                                hipStream_t s) {
+    const int64_t per = pass_rows(da.rows, da.Hq);
+    const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
+    TP a = make_tp(tv, D, da, Hkv, length, P, ws);
+    const size_t esz_o = da.out_bf16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < da.rows; r0 += per) {
+        const int64_t rows = std::min(per, da.rows - r0);
+        const int64_t max_ctx = set_pass(a, da, r0, rows, D);
+        a.out = static_cast<unsigned char *>(da.out) + r0 * D * esz_o;
         DebugView d = dbg;
         if (d.selected) d.selected += r0 * tv.n_levels * da.k;
         if (d.kth_gap) d.kth_gap += r0 * tv.n_levels;

@@ -64,6 +64,17 @@ bool use_tiled(const recsa_params *p, int64_t rows) {
     return rows >= kTiledMinRows;
 }
 
+// The backward's parent-major path: the same conditions as the forward's, its own switch.
+bool use_tiled_backward(const recsa_params *p, int64_t rows) {
+    if (p->store_dtype != RECSA_BF16 || p->fanout_b > tiled_max_fanout()) return false;
+    if (tiled_backward_lds_bytes(p->head_dim, p->fanout_b) > kMaxLds) return false;
+    if (const char *e = getenv("RECSA_BACKWARD_PATH")) {
+        if (strcmp(e, "rowwise") == 0) return false;
+        if (strcmp(e, "tiled") == 0) return true;
+    }
+    return rows >= kTiledMinRows;
+}
+
 struct Layout {
     int32_t n_levels = 0;
     int64_t node_cap[kMaxLevels + 1] = {};
@@ -290,7 +301,8 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must both be given or both be NULL");
     if (!aligned(d_k, 16) || !aligned(d_v, 16))
         return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must be 16-byte aligned");
-    const size_t ws_bytes = recsa_backward_workspace_bytes(p);
+    const int64_t rows_all = n_q * p->n_q_heads;
+    const size_t ws_bytes = recsa_backward_workspace_bytes(p, rows_all);
     if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
         return fail(RECSA_ERR_INVALID_ARG,
                     "the backward needs a 256-byte aligned workspace of recsa_backward_workspace_bytes() bytes");
@@ -328,10 +340,36 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         dv.kth_gap = dbg->kth_gap;
         dv.n_keys = nullptr;
     }
-    hipError_t e = launch_fill_zero(ws, ws_bytes, s);
+    size_t grad_bytes = 0;
+    for (int l = 1; l <= L.n_levels; ++l)
+        grad_bytes += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+    hipError_t e = launch_fill_zero(ws, grad_bytes, s);
     if (e != hipSuccess) return hip_fail(e, "workspace clear");
-    e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
-    if (e != hipSuccess) return hip_fail(e, "backward rows launch");
+    if (use_tiled_backward(p, rows)) {
+        // parent-major: dq is a sum over items
+        e = launch_fill_zero(d_q, (size_t)rows * p->head_dim * sizeof(float), s);
+        if (e != hipSuccess) return hip_fail(e, "gradient clear");
+        DescendArgs da{};
+        da.q = q;
+        da.out = nullptr;
+        da.rows = rows;
+        da.Hq = p->n_q_heads;
+        da.G = a.G;
+        da.gs = 1;
+        da.ctx_base = a.ctx_base;
+        da.ctx_step = a.ctx_step;
+        da.b = a.b;
+        da.k = a.k;
+        da.max_cand = a.max_cand;
+        da.scale = a.scale;
+        e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a,
+                                  dbg != nullptr ? dbg->selected : nullptr, static_cast<char *>(ws) + grad_bytes,
+                                  s);
+        if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
+    } else {
+        e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+        if (e != hipSuccess) return hip_fail(e, "backward rows launch");
+    }
     // summaries' gradients down the tree, top level first
     int64_t pw = 1;
     int top = 0;
@@ -554,12 +592,15 @@ recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, c
                        static_cast<hipStream_t>(stream));
 }
 
-size_t recsa_backward_workspace_bytes(const recsa_params *p) {
-    if (check_params(p) != RECSA_OK) return 0;
+size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t max_rows) {
+    if (check_params(p) != RECSA_OK || max_rows < 0) return 0;
     const Layout L = make_layout(p);
     size_t total = 0;
     for (int l = 1; l <= L.n_levels; ++l)
         total += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+    if (use_tiled_backward(p, max_rows))
+        total += tiled_backward_workspace_bytes(max_rows, p->n_q_heads, p->n_kv_heads, p->head_dim, p->fanout_b,
+                                                p->budget_k, (int32_t)L.max_cand, p->capacity, L.n_levels);
     return total;
 }
 
@@ -613,7 +654,7 @@ size_t recsa_distill_workspace_bytes(const recsa_params *p, int32_t batch) {
     if (check_params(p) != RECSA_OK || batch < 1) return 0;
     const size_t rowsD = (size_t)batch * p->n_q_heads * p->head_dim * sizeof(float);
     return 3 * align_up(rowsD) + align_up((size_t)p->n_kv_heads * p->head_dim * sizeof(float)) +
-           recsa_backward_workspace_bytes(p);
+           recsa_backward_workspace_bytes(p, (int64_t)batch * p->n_q_heads);
 }
 
 recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, float *pool_w,

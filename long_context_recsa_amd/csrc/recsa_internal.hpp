@@ -220,6 +220,15 @@ hipError_t launch_distill_update(float *w, float *vel, const float *dw, int64_t 
                                  hipStream_t s);
 
 size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D);
+// parent-major backward (bf16 storage, many rows): the forward again, then per level
+// the pairs bucketed by parent and one item kernel; summary gradients to ba.gk / ba.gv
+// LDS of the parent-major backward's item kernel (per workgroup of four waves).
+size_t tiled_backward_lds_bytes(int32_t D, int32_t b);
+size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
+                                      int32_t maxc, int64_t capacity, int32_t n_levels);
+hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
+                                 int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
+                                 void *ws, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, const BwdArgs &a,
                                 const DebugView &dbg, hipStream_t s);

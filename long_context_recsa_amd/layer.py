@@ -137,7 +137,7 @@ class RecsaLayer:
                      "dv": torch.zeros((Hkv, cap, D), dtype=torch.float32, device=self.device),
                      "dw": torch.zeros((Hkv, D), dtype=torch.float32, device=self.device)}
         grads["dq"] = torch.empty(shape, dtype=torch.float32, device=self.device)
-        nbytes = recsa_backward_workspace_bytes(self.p)
+        nbytes = recsa_backward_workspace_bytes(self.p, n * self.p.n_q_heads)
         if nbytes and (self._bws is None or self._bws.numel() < nbytes):
             self._bws = None
             self._bws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)

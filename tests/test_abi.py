@@ -187,7 +187,9 @@ def test_backward_validates_before_any_hip_call():
     p = _p(capacity=1000)
     fake = 1 << 20
     d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
-    assert R.recsa_backward_workspace_bytes(p) >= 2 * 8 * (1000 // 32) * 128 * 4
+    assert R.recsa_backward_workspace_bytes(p, 64) >= 2 * 8 * (1000 // 32) * 128 * 4
+    # bf16 storage and >= 4096 rows: the parent-major path's buffers come on top
+    assert R.recsa_backward_workspace_bytes(p, 4096) > R.recsa_backward_workspace_bytes(p, 64)
     ws = fake
     ok = dict(q_ptr=fake, n_q=2, causal=0, dout_ptr=fake, dq_ptr=fake, dk_ptr=fake, dv_ptr=fake,
               dw_ptr=fake, ws=ws)
@@ -218,7 +220,7 @@ def test_dense_and_distill_validate_before_any_hip_call():
     fake = 1 << 20
     d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
     assert R.recsa_dense_workspace_bytes(p, 2) >= 8 * 1024 * 2 * 4 * 130 * 4
-    assert R.recsa_distill_workspace_bytes(p, 2) > R.recsa_backward_workspace_bytes(p)
+    assert R.recsa_distill_workspace_bytes(p, 2) > R.recsa_backward_workspace_bytes(p, 2 * 32)
     assert R.recsa_dense_workspace_bytes(p, 0) == 0 and R.recsa_distill_workspace_bytes(p, 0) == 0
     cases = [
         (lambda: R.recsa_dense_decode(p, R.recsa_tree_desc(fake, fake, fake, fake, 0), fake, 1, fake, fake),

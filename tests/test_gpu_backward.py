@@ -31,6 +31,20 @@ CASES = [
     ("qwen3_4b_131k", 9000, 8, 32, 3, True, {}),
 ]
 
+# The parent-major backward (bf16 storage; the library takes it for large row counts),
+# forced on small cases: buckets of one parent spanning several items, odd fanouts,
+# fanouts of one to four 32-child chunks, L < b.
+TILED_CASES = [
+    ("tiny_f32_4k", 300, 1, 2, 2, False, {"dtype": "bf16"}),
+    ("tiny_f32_4k", 10, 1, 2, 4, True, {"dtype": "bf16"}),
+    ("tiny_f32_4k", 3001, 1, 2, 24, True, {"b": 5, "k": 3, "dtype": "bf16"}),
+    ("tiny_f32_4k", 4229, 2, 4, 40, True, {"dtype": "bf16"}),
+    ("tiny_f32_4k", 3000, 1, 2, 8, True, {"b": 100, "k": 3, "dtype": "bf16"}),
+    ("tiny_f32_4k", 5000, 1, 3, 6, False, {"b": 40, "k": 5, "dtype": "bf16"}),
+    ("qwen3_4b_131k", 20000, 8, 32, 2, False, {}),
+    ("qwen3_4b_131k", 9000, 8, 32, 3, True, {}),
+]
+
 
 def _tol(ref, dtype):
     if dtype == "f32":
@@ -39,8 +53,20 @@ def _tol(ref, dtype):
 
 
 @pytest.mark.parametrize("name,L,n_kv,n_q,n,causal,kw", CASES)
-def test_backward(name, L, n_kv, n_q, n, causal, kw):
+def test_backward(name, L, n_kv, n_q, n, causal, kw, monkeypatch):
+    monkeypatch.setenv("RECSA_BACKWARD_PATH", "rowwise")
     _say(f"case backward {name} L={L} n_kv={n_kv} n_q={n_q} n={n} causal={causal} {kw}")
+    _run(name, L, n_kv, n_q, n, causal, kw)
+
+
+@pytest.mark.parametrize("name,L,n_kv,n_q,n,causal,kw", TILED_CASES)
+def test_backward_tiled(name, L, n_kv, n_q, n, causal, kw, monkeypatch):
+    monkeypatch.setenv("RECSA_BACKWARD_PATH", "tiled")
+    _say(f"case backward tiled {name} L={L} n_kv={n_kv} n_q={n_q} n={n} causal={causal} {kw}")
+    _run(name, L, n_kv, n_q, n, causal, kw)
+
+
+def _run(name, L, n_kv, n_q, n, causal, kw):
     w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=0, n_kv=n_kv, n_q=n_q, **kw)
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
@@ -57,11 +83,12 @@ def test_backward(name, L, n_kv, n_q, n, causal, kw):
     G = n_q // n_kv
     # selections: GPU vs oracle (near-ties excused), then the oracle on the GPU's selections
     force = {}
+    trees = [P.head_tree(K, V, W, g, w, L) for g in range(n_kv)]
     for i in range(n):
         n_ctx = L - n + i + 1 if causal else L
         for h in range(n_q):
             g = h // G
-            tree_g = P.head_tree(K, V, W, g, w, L)
+            tree_g = trees[g]
             P.check_row(tree_g, Q[i, h].astype(np.float64), 0, n_ctx, w.k, w.rope_base, w.softmax_scale,
                         sel[i * n_q + h])
             N = O.level_sizes(n_ctx, w.b)
