@@ -40,7 +40,7 @@ OP_SOURCES = {
     "decode_grouped": ["descend_impl.hpp", "descend_grouped_bf16.hip", "descend_grouped_f32.hip",
                        "select_topk.hpp"],
     "prefill": ["prefill_tiled.hip", "select_topk.hpp"],
-    "backward": ["backward_kernels.hip", "select_topk.hpp"],
+    "backward": ["backward_kernels.hip", "prefill_tiled.hip", "select_topk.hpp"],
 }
 COMMON_SOURCES = ["recsa_internal.hpp", "recsa_api.hip"]
 
@@ -329,6 +329,68 @@ def run_distill(args, name):
     print(json.dumps(res), flush=True)
 
 
+def run_backward_chunk(args, name, n):
+    """Backward of a causal chunk at the end of a workload's cache (training-shaped):
+    the last n tokens' queries attend causally over the tree built on the L cached
+    tokens; a synthetic output gradient; the selection of the forward held fixed.
+    Step = one recsa_backward (dq written, dk, dv, dw added to)."""
+    import torch
+
+    import long_context_recsa_amd as R
+    import synth
+
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, V = synth.gen_kv(w, 0, w.L)
+    W = synth.pool_w(w)
+
+    def dev_store(x):
+        bits = synth.storage_bits(x, w.dtype)
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    p = R.make_params(w.n_kv, w.n_q, w.d, w.b, w.k, w.L, store=w.dtype, out="f32",
+                      rope_base=w.rope_base, softmax_scale=w.softmax_scale, pool_scale=w.pool_scale)
+    layer = R.RecsaLayer(p, dev)
+    for g in range(w.n_kv):
+        layer.k_cache[g].copy_(dev_store(K[g]))
+        layer.v_cache[g].copy_(dev_store(V[g]))
+    layer.pool_w.copy_(torch.from_numpy(W))
+    layer.build(w.L)
+    del K, V
+    rng = np.random.default_rng(2024)
+    q = dev_store(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32))
+    dO = torch.from_numpy(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)).to(dev)
+    grads = layer.backward(q, dO, causal=True)
+    for _ in range(max(args.warmup - 1, 0)):
+        layer.backward(q, dO, causal=True, grads=grads)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.backward(q, dO, causal=True, grads=grads)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    res = {
+        "metric": "causal-chunk backward query tokens/s (dq, dk, dv, dw; selection fixed)",
+        "value": n / (ms * 1e-3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "storage": w.dtype, "L": w.L, "n_kv_heads": w.n_kv,
+                   "n_q_heads": w.n_q, "head_dim": w.d, "b": w.b, "k": w.k, "chunk": n,
+                   "rows": n * w.n_q, "path": os.environ.get("RECSA_BACKWARD_PATH", "default")},
+        "ms": {"backward": ms},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +403,8 @@ def main():
     ap.add_argument("--distill", action="store_true",
                     help="time pooler distillation steps on the workload instead of the hot path")
     ap.add_argument("--lr", type=float, default=1000.0, help="distillation learning rate")
+    ap.add_argument("--backward-chunk", type=int, default=0, metavar="N",
+                    help="time the backward of a causal chunk of N queries at the workload's length")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
@@ -368,6 +432,8 @@ def main():
         return run_serve(args, args.workload)
     if args.distill:
         return run_distill(args, args.workload)
+    if args.backward_chunk:
+        return run_backward_chunk(args, args.workload, args.backward_chunk)
     w = synth.WORKLOADS[args.workload]
     B = args.batch or w.max_batch
     dev = torch.device("cuda:0")

@@ -192,9 +192,10 @@ RECSA_API recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_des
 
 /* Workspace bytes recsa_backward needs for up to `max_rows` rows (n_q *
  * n_q_heads; device memory, 256-byte aligned): fp32 gradients of every level's
- * summary keys and values, and, for bf16 storage and at least 4096 rows (fanout
- * <= 128), the parent-major path's buffers: the forward's buckets, its output,
- * selections and per-row softmax statistics.  0 on invalid params. */
+ * summary keys and values, and, for bf16 storage and at least 256 rows (fanout
+ * <= 128, and the item kernel's LDS within a CU's), the parent-major path's
+ * buffers: the forward's buckets, its output, selections and per-row softmax
+ * statistics.  0 on invalid params. */
 RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t max_rows);
 
 /* Backward of the attention output with the selection held fixed (the method
@@ -214,9 +215,13 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t m
  * Rounding a summary to store_dtype passes the gradient through unchanged.
  * Entry logits, softmax and the selection are recomputed as in the forward.
  * Sums over rows use fp32 atomics, so low-order bits depend on their order.
- * bf16 storage with at least 4096 rows runs parent-major (as recsa_prefill
- * does): pairs (row, parent) are grouped by parent and each group's children
- * take one summed gradient per group rather than one per row.
+ * bf16 storage with at least 256 rows runs parent-major (as recsa_prefill
+ * does): the forward again, recording the selections and each row's softmax
+ * statistics, then per level the pairs (row, parent) grouped by parent, each
+ * group of up to 16 pairs adding one summed gradient per child rather than one
+ * per row.  Its entry logits come from the prefill's split-bf16 products (about
+ * 16 significant bits), so a row whose k-th and (k+1)-th logits lie closer than
+ * that may keep another candidate than the row-wise path keeps.
  * q: as the forward's, store_dtype.  ws: recsa_backward_workspace_bytes(p,
  * n_q * n_q_heads) bytes, 256-byte aligned (may be NULL when that is 0).  dbg (may be NULL): selected
  * and kth_gap as recsa_decode reports them (n_keys is not written). */

@@ -1317,10 +1317,11 @@ namespace {
 // Backward of one pass of rows: the forward (recording the selections and each row's
 // softmax statistics), <dO, out>, then per level the same buckets and tb_item.
 template <int D, int KC>
-hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, int64_t max_ctx, const Plan &P,
-                             int32_t maxc, hipStream_t s) {
+hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *kth_gap, int64_t max_ctx,
+                             const Plan &P, int32_t maxc, hipStream_t s) {
     DebugView fd{};
     fd.selected = const_cast<int32_t *>(t.sel);
+    fd.kth_gap = kth_gap;
     a.out = out;
     a.out_bf16 = 0;
     hipError_t e = run_pass<D, KC>(tv, a, fd, max_ctx, P, maxc, s);
@@ -1347,13 +1348,13 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, int64_t
 }
 
 template <int D>
-hipError_t run_backward_pass_d(const TreeView &tv, const TP &a, const TB &t, float *out, int64_t max_ctx,
-                               const Plan &P, int32_t maxc, hipStream_t s) {
+hipError_t run_backward_pass_d(const TreeView &tv, const TP &a, const TB &t, float *out, float *kth_gap,
+                               int64_t max_ctx, const Plan &P, int32_t maxc, hipStream_t s) {
     switch ((a.b + 31) / 32) {
-        case 1: return run_backward_pass<D, 1>(tv, a, t, out, max_ctx, P, maxc, s);
-        case 2: return run_backward_pass<D, 2>(tv, a, t, out, max_ctx, P, maxc, s);
-        case 3: return run_backward_pass<D, 3>(tv, a, t, out, max_ctx, P, maxc, s);
-        default: return run_backward_pass<D, 4>(tv, a, t, out, max_ctx, P, maxc, s);
+        case 1: return run_backward_pass<D, 1>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
+        case 2: return run_backward_pass<D, 2>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
+        case 3: return run_backward_pass<D, 3>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
+        default: return run_backward_pass<D, 4>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
     }
 }
 
@@ -1464,7 +1465,7 @@ size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int
 
 hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                  int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
-                                 void *ws, hipStream_t s) {
+                                 float *dbg_kth_gap, void *ws, hipStream_t s) {
     const int64_t per = pass_rows(da.rows, da.Hq);
     const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
     const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels);
@@ -1489,8 +1490,9 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
         const int64_t max_ctx = set_pass(a, da, r0, rows, D);
         t.dout = ba.dout + r0 * D;
         t.dq = ba.dq + r0 * D;
-        const hipError_t e = D == 128 ? run_backward_pass_d<128>(tv, a, t, out, max_ctx, P, da.max_cand, s)
-                                      : run_backward_pass_d<64>(tv, a, t, out, max_ctx, P, da.max_cand, s);
+        float *kth = dbg_kth_gap != nullptr ? dbg_kth_gap + r0 * tv.n_levels : nullptr;
+        const hipError_t e = D == 128 ? run_backward_pass_d<128>(tv, a, t, out, kth, max_ctx, P, da.max_cand, s)
+                                      : run_backward_pass_d<64>(tv, a, t, out, kth, max_ctx, P, da.max_cand, s);
         if (e != hipSuccess) return e;
         if (dbg_selected != nullptr && tv.n_levels > 0) {
             const hipError_t c = hipMemcpyAsync(dbg_selected + r0 * tv.n_levels * da.k, t.sel,

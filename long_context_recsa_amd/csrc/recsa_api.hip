@@ -64,7 +64,13 @@ bool use_tiled(const recsa_params *p, int64_t rows) {
     return rows >= kTiledMinRows;
 }
 
-// The backward's parent-major path: the same conditions as the forward's, its own switch.
+// The backward's parent-major path: the same storage and fanout conditions as the
+// forward's, its own switch and threshold.  It runs the forward again with its bucket
+// set-up (a fixed ~0.2 ms at 524K tokens), so the row-wise backward stays faster up to
+// about 128 rows; from 256 rows on the parent-major one is (1.6-2x at 1024 rows, 19x
+// at 131072 rows, 524K tokens, Qwen3-4B layer).
+constexpr int64_t kTiledBackwardMinRows = 256;
+
 bool use_tiled_backward(const recsa_params *p, int64_t rows) {
     if (p->store_dtype != RECSA_BF16 || p->fanout_b > tiled_max_fanout()) return false;
     if (tiled_backward_lds_bytes(p->head_dim, p->fanout_b) > kMaxLds) return false;
@@ -72,7 +78,7 @@ bool use_tiled_backward(const recsa_params *p, int64_t rows) {
         if (strcmp(e, "rowwise") == 0) return false;
         if (strcmp(e, "tiled") == 0) return true;
     }
-    return rows >= kTiledMinRows;
+    return rows >= kTiledBackwardMinRows;
 }
 
 struct Layout {
@@ -363,8 +369,8 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         da.max_cand = a.max_cand;
         da.scale = a.scale;
         e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a,
-                                  dbg != nullptr ? dbg->selected : nullptr, static_cast<char *>(ws) + grad_bytes,
-                                  s);
+                                  dbg != nullptr ? dbg->selected : nullptr, dbg != nullptr ? dbg->kth_gap : nullptr,
+                                  static_cast<char *>(ws) + grad_bytes, s);
         if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
     } else {
         e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);

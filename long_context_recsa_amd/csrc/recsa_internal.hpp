@@ -228,6 +228,7 @@ size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int
                                       int32_t maxc, int64_t capacity, int32_t n_levels);
 hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                  int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
+                                 float *dbg_kth_gap,
                                  void *ws, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, const BwdArgs &a,

@@ -66,6 +66,13 @@ def test_backward_tiled(name, L, n_kv, n_q, n, causal, kw, monkeypatch):
     _run(name, L, n_kv, n_q, n, causal, kw)
 
 
+def test_backward_default_path(monkeypatch):
+    """256 rows of a causal chunk: the library's own choice (the parent-major path)."""
+    monkeypatch.delenv("RECSA_BACKWARD_PATH", raising=False)
+    _say("case backward default path qwen3_4b_131k L=9000 n=8 causal")
+    _run("qwen3_4b_131k", 9000, 8, 32, 8, True, {})
+
+
 def _run(name, L, n_kv, n_q, n, causal, kw):
     w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=0, n_kv=n_kv, n_q=n_q, **kw)
     K, V = synth.gen_kv(w, 0, L)
@@ -126,3 +133,79 @@ def test_backward_adds_into_given_gradients():
     for k in ("dk", "dv", "dw"):
         torch.testing.assert_close(twice[k], 2 * once[k], rtol=1e-5, atol=1e-6)
     assert torch.equal(twice["dq"], once["dq"])
+
+
+def test_backward_tiled_full_131k(monkeypatch):
+    """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 64
+    queries (2048 rows): the parent-major backward against the row-wise one (itself
+    pinned to the oracle above).  Rows whose selections differ between the two (a
+    near-tie under the parent-major forward's split-bf16 logits) get dO = 0, which
+    removes them from every gradient on both paths; all four gradients must then
+    agree to the bf16 bar.  Sampled rows' dq is also checked against the oracle on
+    the GPU's selections."""
+    w = synth.WORKLOADS["qwen3_4b_131k"]
+    L, n = w.L, 64
+    _say(f"case backward tiled vs rowwise qwen3_4b_131k L={L} n={n} causal")
+    K, V = synth.gen_kv(w, 0, L)
+    W = synth.pool_w(w)
+    layer = P.make_layer(w, capacity=L)
+    P.load_cache(layer, K, V, W, L, w.dtype)
+    layer.build(L)
+    rng = np.random.default_rng(11)
+    Q = synth.to_storage(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32), w.dtype)
+    q = P.to_device(Q, w.dtype)
+    dO = torch.from_numpy(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)).cuda()
+
+    def run(path, d):
+        monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
+        g, dbg = layer.backward(q, d, causal=True, debug=True)
+        torch.cuda.synchronize()
+        return g, dbg
+
+    gt, dt = run("tiled", dO)
+    gr, dr = run("rowwise", dO)
+    bad = (dt["selected"] != dr["selected"]).flatten(1).any(1)
+    _say(f"rows with another selection: {int(bad.sum())} of {bad.numel()}")
+    assert int(bad.sum()) <= 8, "too many rows select differently for near-ties alone"
+    dO2 = dO.clone().view(-1, w.d)
+    dO2[bad] = 0
+    dO2 = dO2.view_as(dO)
+    gt, dt = run("tiled", dO2)
+    gr, _ = run("rowwise", dO2)
+    rep = {}
+    for key in ("dq", "dk", "dv", "dw"):
+        x, y = gt[key].cpu().numpy().astype(np.float64), gr[key].cpu().numpy().astype(np.float64)
+        err = float(np.abs(x - y).max())
+        tol = _tol(y, "bf16")
+        rep[key] = f"{err:.2e}/{tol:.2e}"
+        assert err <= tol, f"{key}: parent-major vs row-wise {err:.3g} > {tol:.3g}"
+    _say("tiled vs rowwise", rep)
+    # sampled rows' dq against the oracle on the parent-major path's selections
+    sel = dt["selected"].cpu().numpy()
+    G = w.n_q // w.n_kv
+    dq_gpu = gt["dq"].cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
+    dOn = dO2.cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
+    trees = {}
+    refs, gots = [], []
+    for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, n * w.n_q - 1):
+        if bool(bad[r]):
+            continue
+        i, h = divmod(r, w.n_q)
+        g = h // G
+        if g not in trees:
+            trees[g] = P.head_tree(K, V, W, g, w, L)
+        tree = trees[g]
+        n_ctx = L - n + i + 1
+        P.check_row(tree, Q[i, h].astype(np.float64), 0, n_ctx, w.k, w.rope_base, w.softmax_scale, sel[r])
+        N = O.level_sizes(n_ctx, w.b)
+        force = {l: sel[r, l - 1][sel[r, l - 1] >= 0] for l in range(1, len(N))}
+        gk = [np.zeros(np.shape(tree.keys[l])) for l in range(len(tree.keys))]
+        gv = [np.zeros(np.shape(tree.vals[l])) for l in range(len(tree.vals))]
+        refs.append(O.backward_row(tree, Q[i, h].astype(np.float64), 0, n_ctx, w.k, w.rope_base,
+                                   w.softmax_scale, dOn[r], gk, gv, force=force))
+        gots.append(dq_gpu[r])
+    ref, got = np.array(refs), np.array(gots)
+    err = float(np.abs(got - ref).max())
+    tol = _tol(ref, "bf16")
+    assert err <= tol, f"sampled dq vs oracle {err:.3g} > {tol:.3g}"
+    _say(f"sampled dq vs oracle {err:.2e}/{tol:.2e} over {len(refs)} rows")
