@@ -860,7 +860,7 @@ __device__ __forceinline__ f32x4 dot_tile(const KRaw<D> &r, int t, const bf16x8 
 
 template <int D>
 __host__ __device__ constexpr size_t tb_wave_lds() {
-    return (size_t)2 * kTile * D * 4 + (size_t)32 * D * 2 + (size_t)2 * 32 * kTile * 4 + (size_t)kTile * 4 * 4;
+    return (size_t)32 * D * 2 + (size_t)2 * 32 * kTile * 4 + (size_t)kTile * 4 * 4;
 }
 
 template <int D, int KC>
@@ -874,9 +874,7 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
     const int i16 = lane & 15, grp = lane >> 4;
     const int j = lane % H, sb = lane / H;       // the lane's RoPE pair (j, j + H) and child sub-step
     unsigned char *wb = smem + (size_t)a.b * crot_stride(D) * sizeof(float2) + (size_t)wv * tb_wave_lds<D>();
-    float *U = reinterpret_cast<float *>(wb);                         // [16][D] rotated queries
-    float *dO = U + kTile * D;                                        // [16][D]
-    uint16_t *Kb = reinterpret_cast<uint16_t *>(dO + kTile * D);      // [32][D] the chunk's keys (bf16)
+    uint16_t *Kb = reinterpret_cast<uint16_t *>(wb);                  // [32][D] the chunk's keys (bf16)
     float *Pt = reinterpret_cast<float *>(Kb + 32 * D);               // [32 children][16 pairs]
     float *dZt = Pt + 32 * kTile;                                     // [32][16]
     uint32_t *kmask = reinterpret_cast<uint32_t *>(dZt + 32 * kTile); // [16][4] kept children bits
@@ -888,26 +886,12 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
         const bf16_t *vals = level_rows(tv, true, l, it.g, D);
         const int64_t c0 = it.p * b;
         wave_sync();                        // the previous item's LDS reads are done
-        // queries rotated to their rank position (the score's A operand, and fp32 to LDS)
+        // queries rotated to their rank position (the score's A operand)
         QRaw<D> qr;
         load_query<D>(tv, a, it, lane, qr);
         bf16x8 ah[D / 32], al[D / 32];
         query_operands<D>(qr, it, lane, ah, al);
-        #pragma unroll
-        for (int pc = 0; pc < KS1; ++pc) {
-            float x1[8], x2[8];
-            unpack8(qr.q[2 * pc], x1);
-            unpack8(qr.q[2 * pc + 1], x2);
-            #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float4 cs = qr.cs[4 * pc + u];
-                U[i16 * D + grp * PG + 8 * pc + 2 * u] = x1[2 * u] * cs.x - x2[2 * u] * cs.y;
-                U[i16 * D + H + grp * PG + 8 * pc + 2 * u] = x2[2 * u] * cs.x + x1[2 * u] * cs.y;
-                U[i16 * D + grp * PG + 8 * pc + 2 * u + 1] = x1[2 * u + 1] * cs.z - x2[2 * u + 1] * cs.w;
-                U[i16 * D + H + grp * PG + 8 * pc + 2 * u + 1] = x2[2 * u + 1] * cs.z + x1[2 * u + 1] * cs.w;
-            }
-        }
-        // dO of the pairs: to LDS, and split into the A operand of <dO, v>
+        // dO of the pairs split into the A operand of <dO, v>
         bf16x8 dh[D / 32], dl[D / 32];
         {
             const float live = i16 < it.cnt ? 1.f : 0.f;
@@ -921,11 +905,6 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                     const float4 y2 = *reinterpret_cast<const float4 *>(dp + H + grp * PG + 8 * pc + v);
                     x1[v] = live * y1.x; x1[v + 1] = live * y1.y; x1[v + 2] = live * y1.z; x1[v + 3] = live * y1.w;
                     x2[v] = live * y2.x; x2[v + 1] = live * y2.y; x2[v + 2] = live * y2.z; x2[v + 3] = live * y2.w;
-                }
-                #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    dO[i16 * D + grp * PG + 8 * pc + v] = x1[v];
-                    dO[i16 * D + H + grp * PG + 8 * pc + v] = x2[v];
                 }
                 split8(x1, dh[pc], dl[pc]);
                 split8(x2, dh[pc + KS1], dl[pc + KS1]);
@@ -994,13 +973,21 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
             wave_sync();
             // per child: dV, dK (one atomic add per dimension) and its share of dq
             {
+                // every pair's rotated query U = R((n - r b) theta) q and dO in dimensions
+                // (j, j + H), straight from memory (the same products as the score's operand)
                 float u1[kTile], u2[kTile], o1[kTile], o2[kTile];
                 #pragma unroll
                 for (int pr = 0; pr < kTile; ++pr) {
-                    u1[pr] = U[pr * D + j];
-                    u2[pr] = U[pr * D + H + j];
-                    o1[pr] = dO[pr * D + j];
-                    o2[pr] = dO[pr * D + H + j];
+                    const int row = __builtin_amdgcn_readlane(it.pr.x, pr);
+                    const int pos = __builtin_amdgcn_readlane(it.pr.z, pr);
+                    const bf16_t *qp = a.q + (int64_t)row * D;
+                    const float x1 = bf16_to_f32(qp[j]), x2 = bf16_to_f32(qp[H + j]);
+                    const float2 cs = tv.rope[(int64_t)pos * H + j];
+                    u1[pr] = x1 * cs.x - x2 * cs.y;
+                    u2[pr] = x2 * cs.x + x1 * cs.y;
+                    const bool live = pr < it.cnt;
+                    o1[pr] = live ? t.dout[(int64_t)row * D + j] : 0.f;
+                    o2[pr] = live ? t.dout[(int64_t)row * D + H + j] : 0.f;
                 }
                 const int nc = b - 32 * kk < 32 ? b - 32 * kk : 32;      // children in this chunk
                 for (int s0 = 0; s0 < nc; s0 += SUB) {
