@@ -188,8 +188,14 @@ def test_backward_validates_before_any_hip_call():
     fake = 1 << 20
     d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
     assert R.recsa_backward_workspace_bytes(p, 64) >= 2 * 8 * (1000 // 32) * 128 * 4
-    # bf16 storage and >= 4096 rows: the parent-major path's buffers come on top
-    assert R.recsa_backward_workspace_bytes(p, 4096) > R.recsa_backward_workspace_bytes(p, 64)
+    # bf16 storage and >= 256 rows: the parent-major path's buffers come on top
+    summaries = R.recsa_backward_workspace_bytes(p, 64)
+    assert R.recsa_backward_workspace_bytes(p, 255) == summaries
+    assert R.recsa_backward_workspace_bytes(p, 256) > summaries
+    assert R.recsa_backward_workspace_bytes(p, 4096) >= R.recsa_backward_workspace_bytes(p, 256)
+    # fp32 storage stays row-wise at any row count
+    pf = _p(capacity=1000, store="f32")
+    assert R.recsa_backward_workspace_bytes(pf, 4096) == R.recsa_backward_workspace_bytes(pf, 64)
     ws = fake
     ok = dict(q_ptr=fake, n_q=2, causal=0, dout_ptr=fake, dq_ptr=fake, dk_ptr=fake, dv_ptr=fake,
               dw_ptr=fake, ws=ws)
