@@ -167,14 +167,14 @@ __device__ __noinline__ void select_bisect(const float *z, uint8_t *flag, int32_
 // level max, m-th and (m+1)-th largest logit (NaN when n == m); visible to the
 // calling wave on return.
 // Bisection for the m-th largest key with the keys in registers (narrow levels:
-// 32 ballot rounds over KT registers beat the filter's LDS round trips there).
+// ballot rounds over KT registers beat the filter's LDS round trips there).
 // The largest threshold T with at least m of the keys (NT registers per lane;
-// unused slots 0) >= T, bit by bit from the top.  Once exactly m keys are >= the
-// trial threshold, every threshold in that gap keeps the same m keys: stop there.
+// unused slots 0) >= T, bit by bit from bit `top` down, starting from T (a value
+// with at least m keys >= it, zero below bit `top`).  Once exactly m keys are >=
+// the trial threshold, every threshold in that gap keeps the same m keys: stop there.
 template <int NT>
-__device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m) {
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+__device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m, uint32_t T, int top) {
+    for (int bit = top; bit >= 0; --bit) {
         const uint32_t trial = T | (1u << bit);
         int c = 0;
         #pragma unroll
@@ -209,11 +209,35 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
     uint32_t lmax = 0;
     #pragma unroll
     for (int t = 0; t < KT; ++t) lmax = max(lmax, kk[t]);
+    const uint32_t kmax = wave_umax(lmax);
+    // The m-th largest key K lies in [tau, kmax], with tau the smallest of the maxima
+    // of 64/G >= m lane groups (each group holds a key >= tau; a group without valid
+    // keys has maximum 0, and then tau = 0).  Every value in that range shares the
+    // bits above the highest bit where tau and kmax differ, so the bisection starts
+    // there: the threshold with those bits and zeros below has >= m keys above it.
     uint32_t T = 0;
-    if (nT == 1)
-        T = bisect_threshold<1>(kk, m);
+    int top = 31;
+    if (m <= 32) {
+        uint32_t gmax;
+        if (m <= 4) gmax = group_umax<16>(lmax);
+        else if (m <= 8) gmax = group_umax<8>(lmax);
+        else if (m <= 16) gmax = group_umax<4>(lmax);
+        else gmax = group_umax<2>(lmax);
+        const uint32_t tau = wave_umin(gmax);
+        const uint32_t d = tau ^ kmax;
+        top = d == 0u ? -1 : 31 - (int)__builtin_clz(d);
+        T = top < 0 ? kmax : (top == 31 ? 0u : kmax & ~((2u << top) - 1u));
+    }
+    if (nT <= 1)
+        T = bisect_threshold<1>(kk, m, T, top);
+    else if (nT <= 2 || KT <= 2)
+        T = bisect_threshold<(KT < 2 ? KT : 2)>(kk, m, T, top);
+    else if (nT <= 3 || KT <= 3)
+        T = bisect_threshold<(KT < 3 ? KT : 3)>(kk, m, T, top);
+    else if (nT <= 4 || KT <= 4)
+        T = bisect_threshold<(KT < 4 ? KT : 4)>(kk, m, T, top);
     else
-        T = bisect_threshold<KT>(kk, m);
+        T = bisect_threshold<KT>(kk, m, T, top);
     // kept: every key > T, then keys == T in ascending index until m are kept
     int gt = 0;
     #pragma unroll
@@ -240,7 +264,6 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
         }
         pos += __popcll(mask);
     }
-    const uint32_t kmax = wave_umax(lmax);
     kmin = wave_umin(kmin);
     below = wave_umax(below);
     if (lane == 0) {
