@@ -164,124 +164,147 @@ __device__ __forceinline__ void fused_pass(
     // come in with their keys and join this slot's softmax online (M is then per slot)
     const bool online = vS != nullptr;
     const char *vSb = reinterpret_cast<const char *>(online ? vS : kS);
-    for (int32_t c = slot; c < b; c += NSLOT) {
+    // The slot's batches: child offsets c = slot, slot + NSLOT, ... and for each the ranks
+    // in groups of CB, in that order, as one flat loop.  A batch issues all its loads,
+    // then folds them in.
+    struct Batch {
+        int32_t c, r0;
+        float ea[CB][GS];
         float cr[PP], sr[PP];
-        if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, cr, sr);
-        for (int32_t r0 = 0; r0 < R; r0 += CB) {
-            uint32_t offA[CB], offS[CB];
-            float ea[CB][GS];
+        Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
+    };
+    const int32_t nc = slot < b ? (b - slot + NSLOT - 1) / NSLOT : 0;
+    const int32_t nrb = (R + CB - 1) / CB;
+    const int32_t NB = nc * nrb;
+    auto issue = [&](Batch &B, int32_t ci, int32_t ri) __attribute__((always_inline)) {
+        B.c = slot + ci * NSLOT;
+        B.r0 = ri * CB;
+        const int32_t c = B.c;
+        if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, B.cr, B.sr);
+        uint32_t offA[CB], offS[CB];
+        #pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const int32_t r = B.r0 + t;
+            const int32_t i = r * b + c;
+            const int32_t ic = i < maxc ? i : maxc - 1;
+            const int32_t rc = r < kmax ? r : kmax - 1;
+            const bool okA = (i < A.n) && !(maskA && flagA[ic]);
+            #pragma unroll
+            for (int j = 0; j < GS; ++j) B.ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
+            offA[t] = (okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u) + j0b;
+            offS[t] = ((i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u) + j0b;
+        }
+        if (online) {
             #pragma unroll
             for (int t = 0; t < CB; ++t) {
-                const int32_t r = r0 + t;
-                const int32_t i = r * b + c;
-                const int32_t ic = i < maxc ? i : maxc - 1;
-                const int32_t rc = r < kmax ? r : kmax - 1;
-                const bool okA = (i < A.n) && !(maskA && flagA[ic]);
-                #pragma unroll
-                for (int j = 0; j < GS; ++j) ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
-                offA[t] = (okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u) + j0b;
-                offS[t] = ((i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u) + j0b;
+                B.sa[t].load(reinterpret_cast<const T *>(vSb + offS[t]));
+                B.sb[t].load(reinterpret_cast<const T *>(vSb + offS[t] + H2 * sizeof(T)));
             }
-            Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
-            if (online) {
-                #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    sa[t].load(reinterpret_cast<const T *>(vSb + offS[t]));
-                    sb[t].load(reinterpret_cast<const T *>(vSb + offS[t] + H2 * sizeof(T)));
-                }
+        }
+        if (A.n > 0) {
+            #pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                B.va[t].load(reinterpret_cast<const T *>(vAb + offA[t]));
+                B.vb[t].load(reinterpret_cast<const T *>(vAb + offA[t] + H2 * sizeof(T)));
             }
-            if (A.n > 0) {
-                #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    va[t].load(reinterpret_cast<const T *>(vAb + offA[t]));
-                    vb[t].load(reinterpret_cast<const T *>(vAb + offA[t] + H2 * sizeof(T)));
-                }
+        }
+        if (S.n > 0) {
+            #pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                B.ka[t].load(reinterpret_cast<const T *>(kSb + offS[t]));
+                B.kb[t].load(reinterpret_cast<const T *>(kSb + offS[t] + H2 * sizeof(T)));
             }
-            if (S.n > 0) {
+        }
+    };
+    auto consume = [&](const Batch &B) __attribute__((always_inline)) {
+        const int32_t c = B.c;
+        if (A.n > 0) {
+            #pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                float fa[PP], fb[PP];
+                B.va[t].get(fa);
+                B.vb[t].get(fb);
                 #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    ka[t].load(reinterpret_cast<const T *>(kSb + offS[t]));
-                    kb[t].load(reinterpret_cast<const T *>(kSb + offS[t] + H2 * sizeof(T)));
-                }
-            }
-            if (A.n > 0) {
-                #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    float fa[PP], fb[PP];
-                    va[t].get(fa);
-                    vb[t].get(fb);
-                    #pragma unroll
-                    for (int j = 0; j < GS; ++j) {
-                        const float pz = __builtin_amdgcn_exp2f(ea[t][j] - M[j] * kLog2e);  // 0 for -inf
-                        lsum[j] += pz;
-                        #pragma unroll
-                        for (int p = 0; p < PP; ++p) {
-                            acc_a[j][p] += pz * fa[p];
-                            acc_b[j][p] += pz * fb[p];
-                        }
-                    }
-                }
-            }
-            if (S.n > 0) {
-                #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    const int32_t r = r0 + t;
-                    const int32_t i = r * b + c;
-                    const int32_t ru = (i < S.n) ? r : 0;
-                    float fa[PP], fb[PP], ra[PP], rb[PP];
-                    ka[t].get(fa);
-                    kb[t].get(fb);
+                for (int j = 0; j < GS; ++j) {
+                    const float pz = __builtin_amdgcn_exp2f(B.ea[t][j] - M[j] * kLog2e);  // 0 for -inf
+                    lsum[j] += pz;
                     #pragma unroll
                     for (int p = 0; p < PP; ++p) {
-                        ra[p] = fa[p] * cr[p] - fb[p] * sr[p];
-                        rb[p] = fb[p] * cr[p] + fa[p] * sr[p];
-                    }
-                    float fa2[PP], fb2[PP];
-                    if (online) {
-                        sa[t].get(fa2);
-                        sb[t].get(fb2);
-                    }
-                    float gsum = 0.f;
-                    #pragma unroll
-                    for (int j = 0; j < GS; ++j) {
-                        float ua[PP], ub[PP];
-                        const float *Uj = U + (size_t)j * ustride + (size_t)ru * D;
-                        Vec<float, PP>::load(Uj + j0, ua);
-                        Vec<float, PP>::load(Uj + H2 + j0, ub);
-                        float dot = 0.f;
-                        #pragma unroll
-                        for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
-                        dot = row_sum16(dot);
-                        if (online) {
-                            // the logit to all 16 lanes of the slot, then an online softmax step
-                            const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
-                            if (i < S.n) {
-                                const float Mn = fmaxf(M[j], z);
-                                const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
-                                const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
-                                lsum[j] = lsum[j] * sc + pz;
-                                #pragma unroll
-                                for (int p = 0; p < PP; ++p) {
-                                    acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
-                                    acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
-                                }
-                                M[j] = Mn;
-                            }
-                        } else if (sub == 15 && i < S.n) {
-                            const float z = scale * dot;
-                            zS[j * zstride + i] = z;
-                            if constexpr (GS > 1) {
-                                gsum += z;
-                                smax[j] = fmaxf(smax[j], z);
-                            }
-                        }
-                    }
-                    if (!online && sub == 15 && i < S.n) {
-                        if constexpr (GS > 1) gS[i] = gsum;
-                        flagS[i] = 0;
+                        acc_a[j][p] += pz * fa[p];
+                        acc_b[j][p] += pz * fb[p];
                     }
                 }
             }
+        }
+        if (S.n > 0) {
+            #pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                const int32_t r = B.r0 + t;
+                const int32_t i = r * b + c;
+                const int32_t ru = (i < S.n) ? r : 0;
+                float fa[PP], fb[PP], ra[PP], rb[PP];
+                B.ka[t].get(fa);
+                B.kb[t].get(fb);
+                #pragma unroll
+                for (int p = 0; p < PP; ++p) {
+                    ra[p] = fa[p] * B.cr[p] - fb[p] * B.sr[p];
+                    rb[p] = fb[p] * B.cr[p] + fa[p] * B.sr[p];
+                }
+                float fa2[PP], fb2[PP];
+                if (online) {
+                    B.sa[t].get(fa2);
+                    B.sb[t].get(fb2);
+                }
+                float gsum = 0.f;
+                #pragma unroll
+                for (int j = 0; j < GS; ++j) {
+                    float ua[PP], ub[PP];
+                    const float *Uj = U + (size_t)j * ustride + (size_t)ru * D;
+                    Vec<float, PP>::load(Uj + j0, ua);
+                    Vec<float, PP>::load(Uj + H2 + j0, ub);
+                    float dot = 0.f;
+                    #pragma unroll
+                    for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
+                    dot = row_sum16(dot);
+                    if (online) {
+                        // the logit to all 16 lanes of the slot, then an online softmax step
+                        const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
+                        if (i < S.n) {
+                            const float Mn = fmaxf(M[j], z);
+                            const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
+                            const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
+                            lsum[j] = lsum[j] * sc + pz;
+                            #pragma unroll
+                            for (int p = 0; p < PP; ++p) {
+                                acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
+                                acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
+                            }
+                            M[j] = Mn;
+                        }
+                    } else if (sub == 15 && i < S.n) {
+                        const float z = scale * dot;
+                        zS[j * zstride + i] = z;
+                        if constexpr (GS > 1) {
+                            gsum += z;
+                            smax[j] = fmaxf(smax[j], z);
+                        }
+                    }
+                }
+                if (!online && sub == 15 && i < S.n) {
+                    if constexpr (GS > 1) gS[i] = gsum;
+                    flagS[i] = 0;
+                }
+            }
+        }
+    };
+    Batch B;
+    int32_t ci = 0, ri = 0;
+    for (int32_t k = 0; k < NB; ++k) {
+        issue(B, ci, ri);
+        consume(B);
+        if (++ri == nrb) {
+            ri = 0;
+            ++ci;
         }
     }
 }
