@@ -136,15 +136,16 @@ def test_backward_adds_into_given_gradients():
 
 
 def test_backward_tiled_full_131k(monkeypatch):
-    """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 64
-    queries (2048 rows): the parent-major backward against the row-wise one (itself
-    pinned to the oracle above).  Rows whose selections differ between the two (a
-    near-tie under the parent-major forward's split-bf16 logits) get dO = 0, which
-    removes them from every gradient on both paths; all four gradients must then
-    agree to the bf16 bar.  Sampled rows' dq is also checked against the oracle on
-    the GPU's selections."""
+    """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 4224
+    queries (135168 rows: the parent-major path's two passes of at most 131072 rows):
+    the parent-major backward against the row-wise one (itself pinned to the oracle
+    above).  Rows whose selections differ between the two (a near-tie under the
+    parent-major forward's split-bf16 logits) get dO = 0, which removes them from
+    every gradient on both paths; all four gradients must then agree to the bf16 bar.
+    Sampled rows' dq, in both passes, is also checked against the oracle on the GPU's
+    selections."""
     w = synth.WORKLOADS["qwen3_4b_131k"]
-    L, n = w.L, 64
+    L, n = w.L, 4224
     _say(f"case backward tiled vs rowwise qwen3_4b_131k L={L} n={n} causal")
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
@@ -166,7 +167,7 @@ def test_backward_tiled_full_131k(monkeypatch):
     gr, dr = run("rowwise", dO)
     bad = (dt["selected"] != dr["selected"]).flatten(1).any(1)
     _say(f"rows with another selection: {int(bad.sum())} of {bad.numel()}")
-    assert int(bad.sum()) <= 8, "too many rows select differently for near-ties alone"
+    assert int(bad.sum()) <= 32, "too many rows select differently for near-ties alone"
     dO2 = dO.clone().view(-1, w.d)
     dO2[bad] = 0
     dO2 = dO2.view_as(dO)
@@ -187,7 +188,7 @@ def test_backward_tiled_full_131k(monkeypatch):
     dOn = dO2.cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
     trees = {}
     refs, gots = [], []
-    for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, n * w.n_q - 1):
+    for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, 131072 + 5, n * w.n_q - 1):
         if bool(bad[r]):
             continue
         i, h = divmod(r, w.n_q)
