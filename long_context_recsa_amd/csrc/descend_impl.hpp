@@ -354,7 +354,23 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     auto zrow = [&](int buf, int j) { return zbuf + (size_t)(buf * NZ + j) * mz; };
     auto zsel = [&](int buf) { return zbuf + (size_t)(buf * NZ + (GS == 1 ? 0 : GS)) * mz; };
 
-    const int64_t row = blockIdx.x;
+    // Workgroups go to the 8 XCDs round robin (block index mod 8) and every XCD has its
+    // own L2.  One head per row: block x is the row of rank (x mod 8) * R/8 + x / 8 in
+    // KV-head-major order (KV head, query, head within the group), so each XCD takes a
+    // contiguous run of rows that read the same KV head's tree (at 8 KV heads, one head
+    // per XCD).  A group row (GS = G) already has its KV head at x mod 8.
+    int64_t row = blockIdx.x;
+    if constexpr (GS == 1) {
+        constexpr int kXcds = 8;
+        const int64_t R = gridDim.x;
+        if (R % kXcds == 0) {
+            const int64_t rp = (int64_t)(blockIdx.x % kXcds) * (R / kXcds) + blockIdx.x / kXcds;
+            const int64_t per_g = (R / a.Hq) * a.G;         // rows of one KV head
+            const int64_t gg = rp / per_g, rem = rp - gg * per_g;
+            const int64_t qq = rem / a.G;
+            row = qq * a.Hq + gg * a.G + (rem - qq * a.G);
+        }
+    }
     const int32_t rows_per_q = a.Hq / GS;
     const int64_t qi = row / rows_per_q;
     const int h0 = (int)(row - qi * rows_per_q) * GS;     // first query head of the row
