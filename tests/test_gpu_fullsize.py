@@ -75,7 +75,8 @@ def test_full_decode_and_prefill(name):
 
 def test_full_2m_needles():
     """2M tokens, b=64, k=16: decode B=32 and B=1; every pooler needle's matching
-    query reaches its needle token on the GPU, as on the oracle."""
+    query reaches its needle token on the GPU, as on the oracle; grouped decode at B=32
+    against the oracle's group selection on sampled rows."""
     w = synth.WORKLOADS["qwen3_4b_2m"]
     _say(f"case {w.name}: L={w.L}")
     K, V = synth.gen_kv(w, 0, w.L)
@@ -102,3 +103,11 @@ def test_full_2m_needles():
     rms = float(np.sqrt(np.mean(P.to_host(out32) ** 2)))
     rep = _check(w, out32, dbg, Q, rows, lambda i: w.L, trees, rms)
     _say("decode", rep, "needles reached", reached)
+    # one selection per (query, KV group) at the widest levels (k = 16, b = 64)
+    out_g, dbg_g = layer.decode_grouped(P.to_device(Q, w.dtype), debug=True)
+    torch.cuda.synchronize()
+    rms_g = float(np.sqrt(np.mean(P.to_host(out_g) ** 2)))
+    rep = P.check_groups(trees, Q.astype(np.float64), [(i, g) for i in (0, 7, 31) for g in heads],
+                         lambda i: w.L, w.k, w.rope_base, w.softmax_scale, out_g, dbg_g, w.n_kv,
+                         w.dtype, all_out_rms=rms_g)
+    _say("grouped decode", rep)
