@@ -231,7 +231,9 @@ RECSA_API recsa_status recsa_backward(const recsa_params *p, const recsa_tree_de
                             void *stream);
 
 /* Workspace bytes recsa_dense_decode needs for `batch` queries (device
- * memory): per-span partial softmax states.  0 on invalid arguments. */
+ * memory, 16-byte aligned): per-span partial softmax states and, for bf16
+ * storage, a table of 64 x head_dim/2 RoPE rotation increments the call fills.
+ * 0 on invalid arguments. */
 RECSA_API size_t recsa_dense_workspace_bytes(const recsa_params *p, int32_t batch);
 
 /* Dense causal attention of decode queries (the pooler distillation's teacher;

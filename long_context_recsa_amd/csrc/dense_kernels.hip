@@ -12,6 +12,14 @@
 // against a row, the wave updates that row's running (max, sum), and lane j
 // accumulates output dimensions j and j + 64.  A second kernel merges the spans'
 // (max, sum, acc) per row.
+//
+// bf16 storage takes dense_mfma instead: the same spans and per-span states, with a
+// wave per 16 query rows and q.K and P.V on bf16 MFMA (16x16x32, fp32 accumulate).
+// The rotated queries and keys are fp32, so each is split into a bf16 high and low
+// part and the logits take three products (about 16 significant bits); P is split
+// the same way against the values, which are exact in bf16.  Key rotations use
+// cos/sin of (t0 + tt) theta_j from the step's base angle t0 theta_j (double
+// precision) and a table of tt theta_j, tt < 64, by angle addition.
 #include <math.h>
 
 #include "recsa_internal.hpp"
@@ -136,36 +144,286 @@ __global__ __launch_bounds__(256) void dense_part(DenseArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void dense_merge(DenseArgs a) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void dense_merge(DenseArgs a) {
+    // one row per workgroup; wave w merges the spans w, w + 4, ... online (running max,
+    // rescaled sums), then the four partial states combine through LDS
+    constexpr int NV = D / 64;
+    __shared__ float wm[4], wl[4];
+    __shared__ float wo[4][D];
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int32_t rows_g = a.B * a.G;
     const int64_t rr = blockIdx.x;             // over Hkv * rows_g
     const int g = (int)(rr / rows_g);
     const int32_t rg = (int32_t)(rr - (int64_t)g * rows_g);
-    const int64_t qi = rg / a.G;
-    const int h = g * a.G + (int)(rg - qi * a.G);
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.nspan; ++sp) {
-        const float *src = a.part + (((int64_t)g * a.nspan + sp) * rows_g + rg) * (D + 2);
-        M = fmaxf(M, src[D]);
-    }
-    constexpr int NV = D / 64;
-    float o[NV] = {}, L = 0.f;
-    for (int sp = 0; sp < a.nspan; ++sp) {
+    float M = -INFINITY, L = 0.f, o[NV] = {};
+    for (int sp = wave; sp < a.nspan; sp += 4) {
         const float *src = a.part + (((int64_t)g * a.nspan + sp) * rows_g + rg) * (D + 2);
         const float ms = src[D];
-        const float w = ms == -INFINITY ? 0.f : expf(ms - M);
-        L += w * src[D + 1];
+        if (ms == -INFINITY) continue;
+        const float mn = fmaxf(M, ms);
+        const float cold = M == -INFINITY ? 0.f : expf(M - mn), cnew = expf(ms - mn);
+        L = L * cold + cnew * src[D + 1];
         #pragma unroll
-        for (int v = 0; v < NV; ++v) o[v] += w * src[lane + 64 * v];
+        for (int v = 0; v < NV; ++v) o[v] = o[v] * cold + cnew * src[lane + 64 * v];
+        M = mn;
     }
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = L;
+    }
+    #pragma unroll
+    for (int v = 0; v < NV; ++v) wo[wave][lane + 64 * v] = o[v];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, wm[w]);
+    float Lt = 0.f, ot[NV] = {};
+    for (int w = 0; w < 4; ++w) {
+        if (wm[w] == -INFINITY) continue;
+        const float c = expf(wm[w] - Mt);
+        Lt += c * wl[w];
+        #pragma unroll
+        for (int v = 0; v < NV; ++v) ot[v] += c * wo[w][lane + 64 * v];
+    }
+    const int64_t qi = rg / a.G;
+    const int h = g * a.G + (int)(rg - qi * a.G);
     const int64_t orow = (qi * a.Hq + h) * D;
     #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        const float x = o[v] / L;
+        const float x = ot[v] / Lt;
         if (a.out_bf16) static_cast<bf16_t *>(a.out)[orow + lane + 64 * v] = (bf16_t)f32_to_bf16(x);
         else static_cast<float *>(a.out)[orow + lane + 64 * v] = x;
     }
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// x ~ hi + lo with both parts bf16
+__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    #pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const __bf16 h = (__bf16)x[v];
+        hi[v] = h;
+        lo[v] = (__bf16)(x[v] - (float)h);
+    }
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// (cos, sin) of tt * theta_j for tt < kTok, row-major [tt][j], double precision angles.
+__global__ void dense_incr(float2 *incr, int D, double base) {
+    const int H = D / 2;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= kTok * H) return;
+    const int tt = e / H, j = e - tt * H;
+    const double ang = (double)tt * pow(base, -2.0 * (double)j / (double)D);
+    incr[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+constexpr int kMRows = 64;      // query rows per workgroup: 4 waves x 16
+
+// MFMA 16x16x32: lane L supplies A row L%16 and B column L%16 for the 8 k-slots of lane
+// group grp = L/16, and gets D rows 4*grp .. 4*grp + 3 of column L%16.
+template <int D>
+__global__ __launch_bounds__(256) void dense_mfma(DenseArgs a) {
+    constexpr int H = D / 2, KC = D / 32, NT = D / 16;
+    constexpr int KP = D + 8;             // padded key row (bf16)
+    constexpr int VP = kTok + 8;          // padded transposed value row (bf16)
+    constexpr int PS = kTok + 4;          // padded P row (fp32)
+    __shared__ __align__(16) __bf16 khi[kTok][KP];
+    __shared__ __align__(16) __bf16 klo[kTok][KP];
+    __shared__ __align__(16) uint16_t vt[D][VP];
+    __shared__ __align__(16) float pbuf[4][16][PS];
+    __shared__ float2 cs0[H];             // (cos, sin) of t0 theta_j for the step
+    __shared__ float2 csn[H];             // (cos, sin) of n theta_j
+    __shared__ double theta[H];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x, g = blockIdx.y;
+    const int32_t rows_g = a.B * a.G;
+    const int32_t r0 = blockIdx.z * kMRows;
+    const int64_t n = a.length;
+    const int64_t t_begin = (int64_t)split * a.span;
+    const int64_t t_end = t_begin + a.span < n ? t_begin + a.span : n;
+    const uint16_t *kc = static_cast<const uint16_t *>(a.k_cache) + (int64_t)g * a.cap * D;
+    const uint16_t *vc = static_cast<const uint16_t *>(a.v_cache) + (int64_t)g * a.cap * D;
+
+    for (int j = threadIdx.x; j < H; j += 256) {
+        theta[j] = pow(a.base, -2.0 * (double)j / (double)D);
+        const double ang = (double)n * theta[j];
+        csn[j] = make_float2((float)cos(ang), (float)sin(ang));
+    }
+    __syncthreads();
+    // this lane's query row (A row i16 of the wave's tile), rotated to position n
+    const int32_t rw = r0 + wave * 16 + i16;
+    const int32_t rg = rw < rows_g ? rw : rows_g - 1;
+    const int64_t qi = rg / a.G;
+    const int h = g * a.G + (int)(rg - qi * a.G);
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + (qi * a.Hq + h) * D;
+    bf16x8 ah[KC], al[KC];
+    #pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        float u[8];
+        #pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int d = 32 * c + 8 * grp + v;
+            const int j = d < H ? d : d - H;
+            const float2 cs = csn[j];
+            const float x1 = bf16_to_f32(qp[j]), x2 = bf16_to_f32(qp[j + H]);
+            u[v] = d < H ? x1 * cs.x - x2 * cs.y : x2 * cs.x + x1 * cs.y;
+        }
+        split8(u, ah[c], al[c]);
+    }
+    float m_r[4], l_r[4];
+    f32x4 acc[NT];
+    #pragma unroll
+    for (int v = 0; v < 4; ++v) { m_r[v] = -INFINITY; l_r[v] = 0.f; }
+    #pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTok) {
+        __syncthreads();            // the previous step's LDS reads are done
+        for (int j = threadIdx.x; j < H; j += 256) {
+            const double ang = (double)t0 * theta[j];
+            cs0[j] = make_float2((float)cos(ang), (float)sin(ang));
+        }
+        __syncthreads();
+        // keys rotated to their positions and split; values transposed
+        for (int e = threadIdx.x; e < kTok * (H / 4); e += 256) {
+            const int tt = e / (H / 4), j = (e - tt * (H / 4)) * 4;
+            const int64_t t = t0 + tt;
+            uint2 k1 = make_uint2(0u, 0u), k2 = k1, v1 = k1, v2 = k1;
+            if (t < t_end) {
+                k1 = *reinterpret_cast<const uint2 *>(kc + t * D + j);
+                k2 = *reinterpret_cast<const uint2 *>(kc + t * D + H + j);
+                v1 = *reinterpret_cast<const uint2 *>(vc + t * D + j);
+                v2 = *reinterpret_cast<const uint2 *>(vc + t * D + H + j);
+            }
+            const uint16_t ka[4] = {(uint16_t)(k1.x & 0xFFFFu), (uint16_t)(k1.x >> 16),
+                                    (uint16_t)(k1.y & 0xFFFFu), (uint16_t)(k1.y >> 16)};
+            const uint16_t kb[4] = {(uint16_t)(k2.x & 0xFFFFu), (uint16_t)(k2.x >> 16),
+                                    (uint16_t)(k2.y & 0xFFFFu), (uint16_t)(k2.y >> 16)};
+            const uint16_t va[4] = {(uint16_t)(v1.x & 0xFFFFu), (uint16_t)(v1.x >> 16),
+                                    (uint16_t)(v1.y & 0xFFFFu), (uint16_t)(v1.y >> 16)};
+            const uint16_t vb[4] = {(uint16_t)(v2.x & 0xFFFFu), (uint16_t)(v2.x >> 16),
+                                    (uint16_t)(v2.y & 0xFFFFu), (uint16_t)(v2.y >> 16)};
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float2 b0 = cs0[j + u], inc = a.incr[tt * H + j + u];
+                const float cn = b0.x * inc.x - b0.y * inc.y, sn = b0.y * inc.x + b0.x * inc.y;
+                const float x1 = bf16_to_f32(ka[u]), x2 = bf16_to_f32(kb[u]);
+                const float r1 = x1 * cn - x2 * sn, r2 = x2 * cn + x1 * sn;
+                const __bf16 h1 = (__bf16)r1, h2 = (__bf16)r2;
+                khi[tt][j + u] = h1;
+                klo[tt][j + u] = (__bf16)(r1 - (float)h1);
+                khi[tt][H + j + u] = h2;
+                klo[tt][H + j + u] = (__bf16)(r2 - (float)h2);
+                vt[j + u][tt] = va[u];
+                vt[H + j + u][tt] = vb[u];
+            }
+        }
+        __syncthreads();
+        // logits of the wave's 16 rows against the step's 64 tokens: 4 tiles of 16
+        f32x4 st[4];
+        #pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&khi[16 * nt + i16][32 * c + 8 * grp]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&klo[16 * nt + i16][32 * c + 8 * grp]);
+                c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c], bh, c4, 0, 0, 0);
+                c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c], bl, c4, 0, 0, 0);
+                c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c], bh, c4, 0, 0, 0);
+            }
+            st[nt] = c4;
+        }
+        // online softmax per row 4*grp + v; the row's 64 logits sit in the 16 lanes of
+        // the group, 4 per lane
+        #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float mx = -INFINITY;
+            #pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const float z = (t0 + 16 * nt + i16 < t_end) ? a.scale * st[nt][v] : -INFINITY;
+                st[nt][v] = z;
+                mx = fmaxf(mx, z);
+            }
+            #pragma unroll
+            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            const float mn = fmaxf(m_r[v], mx);          // finite: token t0 is in the span
+            const float corr = m_r[v] == -INFINITY ? 0.f : __expf(m_r[v] - mn);
+            float ps = 0.f;
+            #pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const float p = st[nt][v] == -INFINITY ? 0.f : __expf(st[nt][v] - mn);
+                st[nt][v] = p;
+                ps += p;
+            }
+            #pragma unroll
+            for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
+            l_r[v] = l_r[v] * corr + ps;
+            m_r[v] = mn;
+            #pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t][v] *= corr;
+        }
+        // P to the A operand's layout (row i16, 8 consecutive tokens) through LDS
+        #pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            #pragma unroll
+            for (int v = 0; v < 4; ++v) pbuf[wave][4 * grp + v][16 * nt + i16] = st[nt][v];
+        wave_sync();
+        #pragma unroll
+        for (int c = 0; c < kTok / 32; ++c) {
+            float pr[8];
+            const float4 p0 = *reinterpret_cast<const float4 *>(&pbuf[wave][i16][32 * c + 8 * grp]);
+            const float4 p1 = *reinterpret_cast<const float4 *>(&pbuf[wave][i16][32 * c + 8 * grp + 4]);
+            pr[0] = p0.x; pr[1] = p0.y; pr[2] = p0.z; pr[3] = p0.w;
+            pr[4] = p1.x; pr[5] = p1.y; pr[6] = p1.z; pr[7] = p1.w;
+            bf16x8 ph, pl;
+            split8(pr, ph, pl);
+            #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bf16x8 vv = *reinterpret_cast<const bf16x8 *>(&vt[16 * t + i16][32 * c + 8 * grp]);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, acc[t], 0, 0, 0);
+            }
+        }
+    }
+    // partial state of each row: [D] acc (dimension 16 t + i16 of row 4 grp + v), m, l
+    #pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int32_t rr = r0 + wave * 16 + 4 * grp + v;
+        if (rr < rows_g) {
+            float *dst = a.part + (((int64_t)g * a.nspan + split) * rows_g + rr) * (D + 2);
+            #pragma unroll
+            for (int t = 0; t < NT; ++t) dst[16 * t + i16] = acc[t][v];
+            if (i16 == 0) {
+                dst[D] = m_r[v];
+                dst[D + 1] = l_r[v];
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_mfma(const DenseArgs &a, hipStream_t s) {
+    const int32_t rows_g = a.B * a.G;
+    hipLaunchKernelGGL(dense_incr, dim3((unsigned)((kTok * D / 2 + 255) / 256)), dim3(256), 0, s, a.incr, D,
+                       a.base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)a.nspan, (unsigned)a.Hkv, (unsigned)((rows_g + kMRows - 1) / kMRows));
+    hipLaunchKernelGGL((dense_mfma<D>), grid, dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dense_merge<D>), dim3((unsigned)((int64_t)a.Hkv * rows_g)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -175,7 +433,7 @@ hipError_t launch_t(const DenseArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((dense_part<T, D>), grid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_merge<D>), dim3((unsigned)((int64_t)a.Hkv * rows_g)), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((dense_merge<D>), dim3((unsigned)((int64_t)a.Hkv * rows_g)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -190,7 +448,7 @@ int64_t dense_span(int64_t length) {
 
 hipError_t launch_dense(recsa_dtype st, int32_t D, const DenseArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.length <= 0) return hipSuccess;
-    if (st == RECSA_BF16) return D == 128 ? launch_t<bf16_t, 128>(a, s) : launch_t<bf16_t, 64>(a, s);
+    if (st == RECSA_BF16) return D == 128 ? launch_mfma<128>(a, s) : launch_mfma<64>(a, s);
     return D == 128 ? launch_t<float, 128>(a, s) : launch_t<float, 64>(a, s);
 }
 

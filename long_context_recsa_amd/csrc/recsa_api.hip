@@ -407,6 +407,12 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     return RECSA_OK;
 }
 
+// Per-span partial states of dense attention: at most 1024 spans whatever the length.
+size_t dense_part_bytes(const recsa_params *p, int32_t batch) {
+    return align_up((size_t)p->n_kv_heads * 1024 * (size_t)batch * (size_t)(p->n_q_heads / p->n_kv_heads) *
+                    (size_t)(p->head_dim + 2) * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -618,9 +624,7 @@ recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, 
 
 size_t recsa_dense_workspace_bytes(const recsa_params *p, int32_t batch) {
     if (check_params(p) != RECSA_OK || batch < 1) return 0;
-    // at most 1024 spans whatever the length
-    return align_up((size_t)p->n_kv_heads * 1024 * (size_t)batch * (size_t)(p->n_q_heads / p->n_kv_heads) *
-                    (size_t)(p->head_dim + 2) * sizeof(float));
+    return dense_part_bytes(p, batch) + align_up((size_t)64 * (p->head_dim / 2) * sizeof(float2));
 }
 
 recsa_status recsa_dense_decode(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
@@ -651,6 +655,7 @@ recsa_status recsa_dense_decode(const recsa_params *p, const recsa_tree_desc *de
     a.nspan = (int32_t)((desc->length + a.span - 1) / a.span);
     a.base = p->rope_base;
     a.scale = p->softmax_scale;
+    a.incr = reinterpret_cast<float2 *>(static_cast<char *>(ws) + dense_part_bytes(p, batch));
     hipError_t e = launch_dense((recsa_dtype)p->store_dtype, p->head_dim, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "dense attention launch");
     return RECSA_OK;

@@ -210,6 +210,7 @@ struct DenseArgs {
     int32_t nspan;
     double base;
     float scale;
+    float2 *incr;              // bf16 storage: [64][D/2] (cos, sin) of tt * theta_j, filled by the launch
 };
 int64_t dense_span(int64_t length);
 hipError_t launch_dense(recsa_dtype st, int32_t D, const DenseArgs &a, hipStream_t s);

@@ -33,6 +33,8 @@ def _layer(name, L, n_kv, n_q, kw=None, wscale=1.0):
     ("tiny_f32_4k", 3001, 2, 4, {"b": 5}),
     ("tiny_f32_4k", 37, 1, 1, {}),
     ("qwen3_4b_131k", 40961, 8, 32, {}),
+    ("tiny_f32_4k", 3001, 2, 4, {"dtype": "bf16"}),            # bf16 MFMA path at d = 64
+    ("qwen3_4b_131k", 5000, 1, 32, {}),                        # 96 rows per KV head: two row tiles
 ])
 def test_dense_decode(name, L, n_kv, n_q, kw):
     _say(f"case dense {name} L={L} n_kv={n_kv} n_q={n_q}")
