@@ -257,7 +257,9 @@ RECSA_API size_t recsa_distill_workspace_bytes(const recsa_params *p, int32_t ba
  * written to *loss (device fp32), then dloss/dw with the selection held fixed
  * (as recsa_backward), then SGD with momentum on the pooler vectors,
  *   velocity <- momentum * velocity + dloss/dw,  pool_w <- pool_w - lr * velocity,
- * then the tree is built again from the new pool_w.  pool_w must be
+ * then every summary key is pooled again from the new pool_w (the summary
+ * values, subtree means, do not depend on it and stay as built: the tree must
+ * have been built over the current cache).  pool_w must be
  * desc->pool_w ([n_kv_heads][head_dim] fp32, updated in place); velocity has
  * its shape (fp32, the caller zeroes it before the first step).  ws:
  * recsa_distill_workspace_bytes(p, batch) bytes, 256-byte aligned.  The loss is

@@ -203,9 +203,11 @@ TreeView make_view(const recsa_params *p, const recsa_tree_desc *d, const Layout
     return tv;
 }
 
-// Summarize every node that is complete at new_len and was not at old_len.
+// Summarize every node that is complete at new_len and was not at old_len (keys_only:
+// the summary keys alone, the means being those stored already).
 recsa_status grow_levels(const recsa_params *p, const recsa_tree_desc *d, const Layout &L,
-                         const TreeView &tv, int64_t old_len, int64_t new_len, hipStream_t s) {
+                         const TreeView &tv, int64_t old_len, int64_t new_len, hipStream_t s,
+                         bool keys_only = false) {
     int64_t pw = 1;
     for (int l = 1; l <= L.n_levels; ++l) {
         pw *= p->fanout_b;
@@ -214,7 +216,7 @@ recsa_status grow_levels(const recsa_params *p, const recsa_tree_desc *d, const 
         if (n1 > n0) {
             hipError_t e = launch_level(tv, (recsa_dtype)p->store_dtype, p->n_kv_heads,
                                         p->head_dim, p->fanout_b, l, n0, n1, d->pool_w,
-                                        p->pool_scale, s);
+                                        p->pool_scale, keys_only, s);
             if (e != hipSuccess) return hip_fail(e, "tree level launch");
         }
     }
@@ -711,8 +713,9 @@ recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, fl
         return st;
     e = launch_distill_update(pool_w, velocity, dw, (int64_t)p->n_kv_heads * p->head_dim, lr, momentum, s);
     if (e != hipSuccess) return hip_fail(e, "pooler update launch");
-    // every summary key depends on w: build the tree again
-    return recsa_build_tree(p, desc, desc->length, stream);
+    // every summary key depends on w, no mean does: pool the keys again, level by level
+    const Layout L = make_layout(p);
+    return grow_levels(p, desc, L, make_view(p, desc, L), 0, desc->length, s, true);
 }
 
 const char *recsa_status_string(recsa_status s) {

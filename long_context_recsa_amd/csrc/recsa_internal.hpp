@@ -130,7 +130,7 @@ hipError_t launch_scatter(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32
 // Summarize level-`level` nodes [n0, n1) of every KV head from level level-1.
 hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D, int32_t b,
                         int32_t level, int64_t n0, int64_t n1, const float *pool_w,
-                        float pool_scale, hipStream_t s);
+                        float pool_scale, bool keys_only, hipStream_t s);
 
 constexpr int kInlineSeqs = 32;    // sequences whose table travels in the kernel arguments
 

@@ -23,7 +23,9 @@ namespace {
 constexpr int kNodesPerBlock = 4;     // one wave per node
 constexpr int kRowsInFlight = 4;      // child rows per lane group loaded before use
 
-template <typename TK, typename TVC, typename TS, int D>
+// KO (keys only): the pooled keys alone, for a pooler vector that changed while the
+// cache did not (the means do not depend on it); child values are not read.
+template <typename TK, typename TVC, typename TS, int D, bool KO>
 __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
     const TK *__restrict__ child_key, int64_t child_key_stride,
     const TVC *__restrict__ child_val, int64_t child_val_stride,
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
             const int r = r0 + 4 * t;
             if (r < b) {
                 Vec<TK, E>::load(ck + (int64_t)r * D, kf[t]);
-                Vec<TVC, E>::load(cv + (int64_t)r * D, vf[t]);
+                if constexpr (!KO) Vec<TVC, E>::load(cv + (int64_t)r * D, vf[t]);
             }
         }
         #pragma unroll
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
                 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     acc[e] = acc[e] * c + p * kf[t][e];
-                    vacc[e] += vf[t][e];
+                    if constexpr (!KO) vacc[e] += vf[t][e];
                 }
                 m = mn;
             }
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
         for (int e = 0; e < E; ++e) {
             const float ao = __shfl_xor(acc[e], off);
             acc[e] = acc[e] * ca + ao * cb;
-            vacc[e] += __shfl_xor(vacc[e], off);
+            if constexpr (!KO) vacc[e] += __shfl_xor(vacc[e], off);
         }
         m = mn;
     }
@@ -108,25 +110,31 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
         }
         const int64_t o = (int64_t)g * out_stride + node * D + sub * E;
         Vec<TS, E>::store(out_key + o, key);
-        Vec<TS, E>::store(out_val + o, mean);
-        if (out_mean != nullptr) Vec<float, E>::store(out_mean + o, mean);
+        if constexpr (!KO) {
+            Vec<TS, E>::store(out_val + o, mean);
+            if (out_mean != nullptr) Vec<float, E>::store(out_mean + o, mean);
+        }
     }
 }
 
 template <typename TK, typename TVC, typename TS, int D>
 hipError_t launch_level_t(const TK *ck, int64_t cks, const TVC *cv, int64_t cvs, TS *ok, TS *ov,
                           float *om, int64_t os, int32_t Hkv, int32_t b, int64_t n0, int64_t n1,
-                          const float *pool_w, float pool_scale, hipStream_t s) {
+                          const float *pool_w, float pool_scale, bool keys_only, hipStream_t s) {
     const int64_t nodes = n1 - n0;
     dim3 grid((unsigned)((nodes + kNodesPerBlock - 1) / kNodesPerBlock), (unsigned)Hkv);
-    hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
-                       cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
+    if (keys_only)
+        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, true>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
+                           cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
+    else
+        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, false>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
+                           cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_level_d(const TreeView &tv, int32_t Hkv, int32_t b, int32_t level, int64_t n0,
-                          int64_t n1, const float *pool_w, float pool_scale, hipStream_t s) {
+                          int64_t n1, const float *pool_w, float pool_scale, bool ko, hipStream_t s) {
     T *ok = static_cast<T *>(tv.key[level]);
     T *ov = static_cast<T *>(tv.val[level]);
     float *om = tv.mean[level];
@@ -134,15 +142,15 @@ hipError_t launch_level_d(const TreeView &tv, int32_t Hkv, int32_t b, int32_t le
     if (level == 1) {
         return launch_level_t<T, T, T, D>(static_cast<const T *>(tv.k_cache), tv.cap * D,
                                           static_cast<const T *>(tv.v_cache), tv.cap * D, ok, ov,
-                                          om, os, Hkv, b, n0, n1, pool_w, pool_scale, s);
+                                          om, os, Hkv, b, n0, n1, pool_w, pool_scale, ko, s);
     }
     const T *ck = static_cast<const T *>(tv.key[level - 1]);
     const int64_t cs = tv.node_cap[level - 1] * D;
     if (tv.mean[level - 1] != nullptr)                   // bf16 storage: fp32 child means
         return launch_level_t<T, float, T, D>(ck, cs, tv.mean[level - 1], cs, ok, ov, om, os, Hkv,
-                                              b, n0, n1, pool_w, pool_scale, s);
+                                              b, n0, n1, pool_w, pool_scale, ko, s);
     return launch_level_t<T, T, T, D>(ck, cs, static_cast<const T *>(tv.val[level - 1]), cs, ok,
-                                      ov, om, os, Hkv, b, n0, n1, pool_w, pool_scale, s);
+                                      ov, om, os, Hkv, b, n0, n1, pool_w, pool_scale, ko, s);
 }
 
 // ---- scatter of token-major new rows into the head-major cache -------------
@@ -181,14 +189,15 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2 *__restrict__ ta
 
 hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D, int32_t b,
                         int32_t level, int64_t n0, int64_t n1, const float *pool_w,
-                        float pool_scale, hipStream_t s) {
+                        float pool_scale, bool keys_only, hipStream_t s) {
     if (n1 <= n0) return hipSuccess;
+    const bool ko = keys_only;
     if (st == RECSA_BF16) {
-        if (D == 128) return launch_level_d<bf16_t, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
-        return launch_level_d<bf16_t, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+        if (D == 128) return launch_level_d<bf16_t, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, ko, s);
+        return launch_level_d<bf16_t, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, ko, s);
     }
-    if (D == 128) return launch_level_d<float, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
-    return launch_level_d<float, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, s);
+    if (D == 128) return launch_level_d<float, 128>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, ko, s);
+    return launch_level_d<float, 64>(tv, Hkv, b, level, n0, n1, pool_w, pool_scale, ko, s);
 }
 
 hipError_t launch_scatter(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t D,
