@@ -327,7 +327,7 @@ def run_backward_chunk(args, name, n):
     """Backward of a causal chunk at the end of a workload's cache (training-shaped):
     the last n tokens' queries attend causally over the tree built on the L cached
     tokens; a synthetic output gradient; the selection of the forward held fixed.
-    Step = one recsa_backward (dq written, dk, dv, dw added to)."""
+    Step = one recsa_backward (dq, dk, dv, dw written)."""
     import torch
 
     import long_context_recsa_amd as R
@@ -460,8 +460,8 @@ def main():
         out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
     out_dec = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
     out_grp = torch.empty_like(out_dec)
-    # backward of the decode batch: the output gradient is synthetic, the token and pooler
-    # gradients accumulate over steps (the call adds into them)
+    # backward of the decode batch: the output gradient is synthetic; every step writes
+    # the same token and pooler gradient buffers
     d_out = torch.from_numpy(np.random.default_rng(5).standard_normal((B, w.n_q, w.d)).astype(np.float32)).to(dev)
     grads = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
              "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),

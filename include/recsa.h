@@ -206,12 +206,19 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t m
  * sets of the forward rule held fixed (selection is piecewise constant; only
  * the softmax entries carry gradient):
  *   d_q [n_q][n_q_heads][head_dim] fp32, written;
- *   d_k, d_v [n_kv_heads][capacity][head_dim] fp32, ADDED TO for tokens
- *     [0, length): entries' direct gradients plus those reaching summaries,
- *     pushed down the tree (a summary value is its subtree's mean; a summary
- *     key is the pooler over its stored children's keys); both NULL to skip
- *     the token gradients (d_w and d_q are still computed);
- *   d_w [n_kv_heads][head_dim] fp32, ADDED TO: the pooler vectors' gradient.
+ *   d_k, d_v [n_kv_heads][capacity][head_dim] fp32, WRITTEN for tokens
+ *     [0, length) (rows from length on are not touched): entries' direct
+ *     gradients plus those reaching summaries, pushed down the tree (a summary
+ *     value is its subtree's mean; a summary key is the pooler over its stored
+ *     children's keys); both NULL to skip the token gradients (d_w and d_q are
+ *     still computed);
+ *   d_w [n_kv_heads][head_dim] fp32, written: the pooler vectors' gradient.
+ * Nothing is added to what the buffers held: a caller accumulating over calls
+ * adds the results itself.  The summaries' gradients reach the tokens first
+ * (written, so the tokens' gradients are never read back), then the rows' own
+ * token entries are added with atomics; with more than one pass of rows on the
+ * parent-major path (over 131072 rows) the tokens' gradients are cleared
+ * first and added to instead.
  * Rounding a summary to store_dtype passes the gradient through unchanged.
  * Entry logits, softmax and the selection are recomputed as in the forward.
  * Sums over rows use fp32 atomics, so low-order bits depend on their order.

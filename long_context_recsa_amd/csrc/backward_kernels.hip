@@ -16,7 +16,9 @@
 // softmax that also carries sum e^(z-M) dp, so D needs no output vector),
 // then walks the entries a second time and adds dkey and dv to the token
 // gradients (dk, dv) or to the per-level summary gradients in the workspace,
-// with fp32 atomics: rows share entries.
+// with fp32 atomics: rows share entries.  Run in two phases (summaries and dq,
+// then the token entries alone) it lets the tree pass below write the token
+// gradients first, so they are never read back.
 //
 // bwd_tree: per level from the top down, one wave per node.  A node's value
 // is the mean of its b children's, so each child gets dv / b; its key is the
@@ -25,7 +27,10 @@
 // so with g = dkey: dx_c = alpha_c g + s_p da_c w and dw += s_p sum da_c x_c,
 // da_c = alpha_c (<g, x_c> - sum alpha <g, x>).  Children belong to one node,
 // so their gradients are read, added to and written without atomics; dw is
-// added with atomics.  Storage rounding of summaries passes gradients through.
+// added with atomics.  At level 1 with write_tokens the tokens' dk and dv are
+// written instead (the rows' own token entries are added afterwards), which
+// halves the traffic of the one pass that touches every token.  Storage
+// rounding of summaries passes gradients through.
 #include <math.h>
 
 #include "recsa_internal.hpp"
@@ -251,6 +256,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
     const float invL = 1.f / Lg;
 
     // ---- pass 2: every entry again; dq in registers, dkey and dv to memory ------------
+    // (phase 1 leaves out the token entries' dkey and dv, phase 2 does only those)
     float dqa[PP], dqb[PP];
     #pragma unroll
     for (int p = 0; p < PP; ++p) { dqa[p] = 0.f; dqb[p] = 0.f; }
@@ -261,6 +267,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
             const sel::Cands cd = level_cands(n_ctx, pw, b, l == H, m_above);
             const int32_t *parents = kept + (l + 1) * K;
             const uint8_t *fl = flags + (size_t)l * maxc;
+            if (a.phase == 2 && l >= 1) {
+                m_above = K < cd.n ? K : cd.n;
+                continue;
+            }
+            const bool grads = l >= 1 ? true : a.dk != nullptr && a.phase != 1;   // token gradients may be skipped
             float qna[PP], qnb[PP];
             rotate_q(cd.n, qna, qnb);
             for (int32_t i = slot; i < cd.n; i += kNSlot) {
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
                     dqa[p] += dz * (ka[p] * c[p] + kb[p] * s[p]);
                     dqb[p] += dz * (kb[p] * c[p] - ka[p] * s[p]);
                 }
-                if (l >= 1 || a.dk != nullptr) {    // token gradients may be skipped
+                if (grads) {
                     float *gk = gk_row(l, node);
                     float *gv = gv_row(l, node);
                     #pragma unroll
@@ -303,6 +314,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
             m_above = l >= 1 ? (K < cd.n ? K : cd.n) : 0;
         }
     }
+    if (a.phase == 2) return;           // dq was written by phase 1
     // dq: add the four slots of each wave, then the waves
     #pragma unroll
     for (int off = 16; off <= 32; off <<= 1)
@@ -326,6 +338,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_rows(TreeView tv, BwdArgs a, Deb
     }
 }
 
+// LDS of the per-wave pooler statistics (4 waves x [2][b] floats), 16-byte aligned.
+__host__ __device__ constexpr size_t tree_stats_bytes(int32_t b) {
+    return ((size_t)4 * 2 * b * sizeof(float) + 15) / 16 * 16;
+}
+
 // Per node of level l, one wave: the node's key and value gradients to its b
 // children (level l - 1, or the tokens) and to dw.  A 16-lane group takes
 // children grp, grp + 4, ...; each lane holds D/16 contiguous elements of a row.
@@ -341,7 +358,13 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     const int32_t b = t.b;
     float *sa = reinterpret_cast<float *>(smem) + (size_t)wave * 2 * b;    // [b] pooler logits, then alpha
     float *sd = sa + b;                                                   // [b] <g, x_c>, then da_c
+    // cache_keys: the children's key rows ([b][D] per wave), stored by the first pass
+    // and read by the second instead of a second read from memory
+    T *kc = reinterpret_cast<T *>(smem + tree_stats_bytes(b)) + (size_t)wave * b * D;
+    const bool cache = t.cache_keys != 0;
     const int l = t.level;
+    // level 1 with write_tokens: dk, dv are written (this is the first contribution to them)
+    const bool wr = l == 1 && t.write_tokens != 0 && t.dk != nullptr;
     // persistent waves, each over a contiguous range of (head, node): dw stays in
     // registers while the head does not change (one set of atomics per head and wave,
     // not per node, which would serialize on dw's few addresses)
@@ -387,10 +410,22 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     bool any = false;
     #pragma unroll
     for (int u = 0; u < NE; ++u) any = any || gk[u] != 0.f || gv[u] != 0.f;
-    if (__ballot(any) == 0) continue;       // no row read this node
+    const int64_t c0 = j * b;
+    if (__ballot(any) == 0) {               // no row read this node
+        if (wr) {                           // its tokens' gradients are still written: zero
+            float *ck0 = t.dk + ((int64_t)g * tv.cap + c0) * D, *cv0 = t.dv + ((int64_t)g * tv.cap + c0) * D;
+            float z[NE];
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) z[e] = 0.f;
+            for (int32_t c = grp; c < b; c += 4) {
+                Vec<float, NE>::store(ck0 + (int64_t)c * D + e0, z);
+                Vec<float, NE>::store(cv0 + (int64_t)c * D + e0, z);
+            }
+        }
+        continue;
+    }
 
     // the children: stored keys of level l - 1 (tokens at l = 1) and their gradients
-    const int64_t c0 = j * b;
     const T *xk = l == 1 ? static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + c0) * D
                          : static_cast<const T *>(tv.key[l - 1]) + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
     float *ck = l == 1 ? t.dk + ((int64_t)g * tv.cap + c0) * D
@@ -406,6 +441,10 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
         float x[CB][NE];
         #pragma unroll
         for (int u = 0; u < CB; ++u) Vec<T, NE>::load(xk + (int64_t)child(cb, u) * D + e0, x[u]);
+        if (cache) {
+            #pragma unroll
+            for (int u = 0; u < CB; ++u) Vec<T, NE>::store(kc + (int64_t)child(cb, u) * D + e0, x[u]);
+        }
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
             float pa = 0.f, pd = 0.f;
@@ -460,10 +499,14 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
         #pragma unroll
         for (int u = 0; u < CB; ++u) {
             const int64_t c = child(cb, u);
-            Vec<T, NE>::load(xk + c * D + e0, x[u]);
-            if (child_grads) {
+            if (cache) Vec<T, NE>::load(kc + c * D + e0, x[u]);
+            else Vec<T, NE>::load(xk + c * D + e0, x[u]);
+            if (child_grads && !wr) {
                 Vec<float, NE>::load(ck + c * D + e0, ok[u]);
                 Vec<float, NE>::load(cv + c * D + e0, ov[u]);
+            } else {
+                #pragma unroll
+                for (int e = 0; e < NE; ++e) { ok[u][e] = 0.f; ov[u][e] = 0.f; }
             }
         }
         #pragma unroll
@@ -497,6 +540,15 @@ __global__ void fill_zero(uint4 *p, int64_t n16) {
         p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// rows [r0, r1) of each head of a [H][cap][D] fp32 array, in float4s
+__global__ void zero_rows(float4 *p, int32_t H, int64_t cap4, int64_t r0_4, int64_t n4) {
+    const int64_t total = (int64_t)H * n4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t h = i / n4;
+        p[h * cap4 + r0_4 + (i - h * n4)] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_rows_t(const TreeView &tv, const BwdArgs &a, const DebugView &dbg, hipStream_t s) {
     const size_t smem = rows_smem<kNW>(a.max_cand, a.k, tv.n_levels, D);
@@ -510,10 +562,14 @@ hipError_t launch_rows_t(const TreeView &tv, const BwdArgs &a, const DebugView &
 }
 
 template <typename T, int D>
-hipError_t launch_tree_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
-    const int64_t nodes = (int64_t)t.Hkv * t.nodes;
+hipError_t launch_tree_t(const TreeView &tv, const BwdTreeArgs &targ, hipStream_t s) {
+    const int64_t nodes = (int64_t)targ.Hkv * targ.nodes;
     if (nodes == 0) return hipSuccess;
-    const size_t smem = sizeof(float) * 4 * 2 * (size_t)t.b;
+    // the key cache while it leaves room for two workgroups per CU
+    BwdTreeArgs t = targ;
+    const size_t cache_bytes = (size_t)4 * t.b * D * sizeof(T);
+    t.cache_keys = tree_stats_bytes(t.b) + cache_bytes <= 64 * 1024 ? 1 : 0;
+    const size_t smem = tree_stats_bytes(t.b) + (t.cache_keys ? cache_bytes : 0);
     // as many workgroups as are resident at once; each wave then walks its share of nodes
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -532,6 +588,16 @@ hipError_t launch_tree_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s
 
 size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D) {
     return rows_smem<kNW>(maxc, k, nlev, D);
+}
+
+hipError_t launch_zero_rows(float *p, int32_t Hkv, int64_t cap, int64_t r0, int64_t r1, int32_t D, hipStream_t s) {
+    if (p == nullptr || r1 <= r0 || Hkv < 1) return hipSuccess;
+    const int64_t n4 = (r1 - r0) * D / 4;
+    const int64_t total = (int64_t)Hkv * n4;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(zero_rows, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4 *>(p), Hkv, cap * D / 4, r0 * D / 4, n4);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {

@@ -90,7 +90,7 @@ struct TP {
 struct TB {
     const float *dout;         // [rows][D] fp32
     float *dq;                 // [rows][D] fp32, added to
-    float *dk, *dv;            // [Hkv][cap][D] fp32 token gradients, added to
+    float *dk, *dv;            // [Hkv][cap][D] fp32 token gradients, added to (NULL: skipped)
     float *gk[kMaxLevels + 1]; // [Hkv][node_cap][D] fp32 summary gradients (l >= 1), added to
     float *gv[kMaxLevels + 1];
     const float2 *rowml;       // [rows] (max, sum) from the forward
@@ -1303,21 +1303,26 @@ namespace {
 
 // Backward of one pass of rows: the forward (recording the selections and each row's
 // softmax statistics), <dO, out>, then per level the same buckets and tb_item.
+// Phase 1 stops before the token level, phase 2 runs only that level (after phase 1
+// of the same pass, whose selections and row statistics are still in the workspace).
 template <int D, int KC>
 hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *kth_gap, int64_t max_ctx,
-                             const Plan &P, int32_t maxc, hipStream_t s) {
-    DebugView fd{};
-    fd.selected = const_cast<int32_t *>(t.sel);
-    fd.kth_gap = kth_gap;
-    a.out = out;
-    a.out_bf16 = 0;
-    hipError_t e = run_pass<D, KC>(tv, a, fd, max_ctx, P, maxc, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(tb_rowdot, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, t.dout, out,
-                       const_cast<float *>(t.rowD), a.rows, D);
+                             const Plan &P, int32_t maxc, int32_t phase, hipStream_t s) {
+    hipError_t e;
+    if (phase != 2) {
+        DebugView fd{};
+        fd.selected = const_cast<int32_t *>(t.sel);
+        fd.kth_gap = kth_gap;
+        a.out = out;
+        a.out_bf16 = 0;
+        if ((e = run_pass<D, KC>(tv, a, fd, max_ctx, P, maxc, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL(tb_rowdot, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, t.dout, out,
+                           const_cast<float *>(t.rowD), a.rows, D);
+    }
     const DebugView none{};
     const size_t lds = tiled_backward_lds_bytes(D, a.b);
-    for (int l = a.top; l >= 0; --l) {
+    const int l_lo = phase == 1 ? 1 : 0;
+    for (int l = phase == 2 ? 0 : a.top; l >= l_lo; --l) {
         const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
         const int64_t nb = (int64_t)a.Hkv * NP;
         hipLaunchKernelGGL(tb_parents, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, s, a, t.sel, l);
@@ -1336,12 +1341,12 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
 
 template <int D>
 hipError_t run_backward_pass_d(const TreeView &tv, const TP &a, const TB &t, float *out, float *kth_gap,
-                               int64_t max_ctx, const Plan &P, int32_t maxc, hipStream_t s) {
+                               int64_t max_ctx, const Plan &P, int32_t maxc, int32_t phase, hipStream_t s) {
     switch ((a.b + 31) / 32) {
-        case 1: return run_backward_pass<D, 1>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
-        case 2: return run_backward_pass<D, 2>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
-        case 3: return run_backward_pass<D, 3>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
-        default: return run_backward_pass<D, 4>(tv, a, t, out, kth_gap, max_ctx, P, maxc, s);
+        case 1: return run_backward_pass<D, 1>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
+        case 2: return run_backward_pass<D, 2>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
+        case 3: return run_backward_pass<D, 3>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
+        default: return run_backward_pass<D, 4>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
     }
 }
 
@@ -1450,10 +1455,13 @@ size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int
     return make_bwd_plan(P, D, k, n_levels).total;
 }
 
+bool tiled_backward_one_pass(int64_t rows, int32_t Hq) { return pass_rows(rows, Hq) >= rows; }
+
 hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                  int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
-                                 float *dbg_kth_gap, void *ws, hipStream_t s) {
+                                 float *dbg_kth_gap, int32_t phase, void *ws, hipStream_t s) {
     const int64_t per = pass_rows(da.rows, da.Hq);
+    if (phase != 0 && per < da.rows) return hipErrorInvalidValue;      // phases need one pass
     const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
     const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels);
     unsigned char *w = static_cast<unsigned char *>(ws);
@@ -1478,10 +1486,11 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
         t.dout = ba.dout + r0 * D;
         t.dq = ba.dq + r0 * D;
         float *kth = dbg_kth_gap != nullptr ? dbg_kth_gap + r0 * tv.n_levels : nullptr;
-        const hipError_t e = D == 128 ? run_backward_pass_d<128>(tv, a, t, out, kth, max_ctx, P, da.max_cand, s)
-                                      : run_backward_pass_d<64>(tv, a, t, out, kth, max_ctx, P, da.max_cand, s);
+        const hipError_t e =
+            D == 128 ? run_backward_pass_d<128>(tv, a, t, out, kth, max_ctx, P, da.max_cand, phase, s)
+                     : run_backward_pass_d<64>(tv, a, t, out, kth, max_ctx, P, da.max_cand, phase, s);
         if (e != hipSuccess) return e;
-        if (dbg_selected != nullptr && tv.n_levels > 0) {
+        if (phase != 2 && dbg_selected != nullptr && tv.n_levels > 0) {
             const hipError_t c = hipMemcpyAsync(dbg_selected + r0 * tv.n_levels * da.k, t.sel,
                                                 (size_t)rows * tv.n_levels * da.k * 4, hipMemcpyDeviceToDevice, s);
             if (c != hipSuccess) return c;

@@ -352,12 +352,25 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     for (int l = 1; l <= L.n_levels; ++l)
         grad_bytes += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
     hipError_t e = launch_fill_zero(ws, grad_bytes, s);
+    if (e == hipSuccess) e = launch_fill_zero(d_w, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
     if (e != hipSuccess) return hip_fail(e, "workspace clear");
-    if (use_tiled_backward(p, rows)) {
+    // Every gradient is written.  Where the rows' token entries can be added after the
+    // tree pass (row-wise, in two phases; parent-major in one pass of rows), the tree
+    // pass's level 1 writes the tokens' dk, dv first and nothing reads them back;
+    // otherwise they are cleared and the tree pass adds to them.
+    const bool tiled = use_tiled_backward(p, rows);
+    const bool tokens = d_k != nullptr;
+    const bool split = tokens && (!tiled || tiled_backward_one_pass(rows, p->n_q_heads));
+    if (tokens && !split) {
+        e = launch_zero_rows(d_k, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
+        if (e == hipSuccess) e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient clear");
+    }
+    DescendArgs da{};
+    if (tiled) {
         // parent-major: dq is a sum over items
         e = launch_fill_zero(d_q, (size_t)rows * p->head_dim * sizeof(float), s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
-        DescendArgs da{};
         da.q = q;
         da.out = nullptr;
         da.rows = rows;
@@ -372,9 +385,10 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         da.scale = a.scale;
         e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a,
                                   dbg != nullptr ? dbg->selected : nullptr, dbg != nullptr ? dbg->kth_gap : nullptr,
-                                  static_cast<char *>(ws) + grad_bytes, s);
+                                  split ? 1 : 0, static_cast<char *>(ws) + grad_bytes, s);
         if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
     } else {
+        a.phase = split ? 1 : 0;
         e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
         if (e != hipSuccess) return hip_fail(e, "backward rows launch");
     }
@@ -402,9 +416,28 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
         t.dk = d_k;
         t.dv = d_v;
+        t.write_tokens = split ? 1 : 0;
         t.dw = d_w;
         e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
         if (e != hipSuccess) return hip_fail(e, "backward tree launch");
+    }
+    if (split) {
+        // tokens past the last complete level-1 node have no parent to write them
+        const int64_t under = desc->length / p->fanout_b * p->fanout_b;
+        e = launch_zero_rows(d_k, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
+        if (e == hipSuccess)
+            e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient clear");
+        // then the rows' own token entries
+        if (tiled) {
+            e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a, nullptr,
+                                      nullptr, 2, static_cast<char *>(ws) + grad_bytes, s);
+            if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
+        } else {
+            a.phase = 2;
+            e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, DebugView{}, s);
+            if (e != hipSuccess) return hip_fail(e, "backward rows launch");
+        }
     }
     return RECSA_OK;
 }
@@ -705,9 +738,7 @@ recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, fl
         return st;
     hipError_t e = launch_distill_loss(out, teacher, dout, loss, (int64_t)rows * p->head_dim, rows, s);
     if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
-    e = launch_fill_zero(dw, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
-    if (e != hipSuccess) return hip_fail(e, "gradient clear");
-    // dloss/dw with the selection fixed; the token gradients are not needed
+    // dloss/dw (written) with the selection fixed; the token gradients are not needed
     if ((st = run_backward(p, desc, q, batch, 0, dout, dq, nullptr, nullptr, dw, nullptr, bws, stream)) !=
         RECSA_OK)
         return st;

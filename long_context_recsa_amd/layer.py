@@ -126,7 +126,8 @@ class RecsaLayer:
         """Gradients of <dout, out> with the selection held fixed, for the rows of
         decode(q) (causal=False) or prefill(q) (causal=True).  Returns a dict with
         dq [n][Hq][D] and dk, dv [Hkv][capacity][D], dw [Hkv][D] (fp32); pass
-        `grads` (such a dict) to add dk, dv, dw into existing tensors."""
+        `grads` (such a dict) to have dk, dv, dw written into existing tensors (dk, dv
+        rows from the cache's length on are left as they are)."""
         n = q.shape[0]
         shape = (n, self.p.n_q_heads, self.p.head_dim)
         self._check_dev(q, shape, self.store)

@@ -117,22 +117,32 @@ def _run(name, L, n_kv, n_q, n, causal, kw):
     _say("backward", {k: f"{e:.2e}/{t:.2e}" for k, (e, t) in rep.items()})
 
 
-def test_backward_adds_into_given_gradients():
-    w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], 2000, prefill_n=0, n_q=2)
-    K, V = synth.gen_kv(w, 0, 2000)
+@pytest.mark.parametrize("path,dtype,nq", [("rowwise", "f32", 2), ("tiled", "bf16", 64)])
+def test_backward_overwrites_given_gradients(monkeypatch, path, dtype, nq):
+    """dk, dv (tokens [0, length)) and dw are written whatever the buffers held; rows
+    from the length on are left alone.  Row-wise (two phases around the tree pass) and
+    parent-major in one pass of rows (token level after the tree pass)."""
+    monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
+    L, cap = 2000, 2100
+    w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], L, prefill_n=0, n_q=2, dtype=dtype)
+    K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
-    layer = P.make_layer(w, capacity=2000)
-    P.load_cache(layer, K, V, W, 2000, "f32")
-    layer.build(2000)
+    layer = P.make_layer(w, capacity=cap)
+    P.load_cache(layer, K, V, W, L, w.dtype)
+    layer.build(L)
+    _say(f"case overwrite {path} {dtype} nq={nq}")
     rng = np.random.default_rng(9)
-    q = torch.from_numpy(rng.standard_normal((2, 2, w.d)).astype(np.float32)).cuda()
-    dO = torch.from_numpy(rng.standard_normal((2, 2, w.d)).astype(np.float32)).cuda()
+    q = P.to_device(synth.to_storage(rng.standard_normal((nq, 2, w.d)).astype(np.float32), w.dtype), w.dtype)
+    dO = torch.from_numpy(rng.standard_normal((nq, 2, w.d)).astype(np.float32)).cuda()
     once = layer.backward(q, dO)
-    twice = layer.backward(q, dO, grads={k: once[k].clone() for k in ("dk", "dv", "dw")})
+    junk = {k: torch.full_like(once[k], 7.5) for k in ("dk", "dv", "dw")}
+    twice = layer.backward(q, dO, grads=junk)
     torch.cuda.synchronize()
-    for k in ("dk", "dv", "dw"):
-        torch.testing.assert_close(twice[k], 2 * once[k], rtol=1e-5, atol=1e-6)
-    assert torch.equal(twice["dq"], once["dq"])
+    for k in ("dk", "dv"):
+        torch.testing.assert_close(twice[k][:, :L], once[k][:, :L], rtol=1e-5, atol=1e-6)
+        assert torch.all(twice[k][:, L:] == 7.5)
+    torch.testing.assert_close(twice["dw"], once["dw"], rtol=1e-5, atol=1e-6)
+    torch.testing.assert_close(twice["dq"], once["dq"], rtol=1e-5, atol=1e-6)
 
 
 def test_backward_tiled_full_131k(monkeypatch):
@@ -141,8 +151,8 @@ def test_backward_tiled_full_131k(monkeypatch):
     the parent-major backward against the row-wise one (itself pinned to the oracle
     above).  Rows whose selections differ between the two (a near-tie under the
     parent-major forward's split-bf16 logits) get dO = 0, which removes them from
-    every gradient on both paths; all four gradients must then agree to the bf16 bar.
-    Sampled rows' dq, in both passes, is also checked against the oracle on the GPU's
+    every gradient on both paths; all four gradients must then agree to the bf16 bar
+    (the parent-major run writes over buffers that held other values).  Sampled rows' dq, in both passes, is also checked against the oracle on the GPU's
     selections."""
     w = synth.WORKLOADS["qwen3_4b_131k"]
     L, n = w.L, 4224
@@ -157,9 +167,9 @@ def test_backward_tiled_full_131k(monkeypatch):
     q = P.to_device(Q, w.dtype)
     dO = torch.from_numpy(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)).cuda()
 
-    def run(path, d):
+    def run(path, d, grads=None):
         monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
-        g, dbg = layer.backward(q, d, causal=True, debug=True)
+        g, dbg = layer.backward(q, d, causal=True, debug=True, grads=grads)
         torch.cuda.synchronize()
         return g, dbg
 
@@ -171,7 +181,10 @@ def test_backward_tiled_full_131k(monkeypatch):
     dO2 = dO.clone().view(-1, w.d)
     dO2[bad] = 0
     dO2 = dO2.view_as(dO)
-    gt, dt = run("tiled", dO2)
+    # two passes of rows clear the token gradients first: start the parent-major run
+    # from buffers that hold something else
+    junk = {k: torch.full_like(gt[k], -3.25) for k in ("dk", "dv", "dw")}
+    gt, dt = run("tiled", dO2, junk)
     gr, _ = run("rowwise", dO2)
     rep = {}
     for key in ("dq", "dk", "dv", "dw"):
