@@ -47,6 +47,8 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 constexpr int kTile = 16;               // pairs per MFMA tile (the M side)
 constexpr int kMaxFanout = 128;         // children per parent the P.V tiles hold
 constexpr int kHistSplit = 4096;        // up to this many parents per head: one LDS count per 256 rows
+constexpr int kHistMax = 24576;         // ... and up to this many when a head has kHistRows rows or more
+constexpr int64_t kHistRows = 2048;
 constexpr int kRange = 2048;            // else: parents per counting block
 constexpr int kScanPer = 16;            // bucket sizes per thread in the scans
 constexpr int kScanChunk = kScanPer * 256;
@@ -218,8 +220,9 @@ __global__ void tp_init(TP a, DebugView dbg, int64_t nb) {
 }
 
 // Position of every pair of level l inside its (head, parent) bucket, and the
-// bucket sizes.  mode 0 (few parents): each block counts 256 rows of one head
-// in LDS, then adds to the global sizes (one atomic per parent and block).
+// bucket sizes.  mode 0 (few parents, or up to kHistMax over at least kHistRows
+// rows per head): each block counts 256 rows of one head in LDS, then adds to the
+// global sizes (one atomic per parent and block).
 // mode 1 (many parents): each block owns a range of kRange parents of one head,
 // counts the pairs of all of the head's rows that fall in it, and stores the
 // sizes of its range; no global atomics.
@@ -260,6 +263,7 @@ __global__ __launch_bounds__(1024) void tp_count(TP a, int l, int32_t NP, int mo
     int32_t *pp = a.pairpos + (row >= 0 ? row : 0) * (a.k + 1);
     for (int r = 0; r < np; ++r) pp[r] = atomicAdd(&hist[parent_of(a, row, l, r, rl)], 1);
     __syncthreads();
+    #pragma unroll 4
     for (int p = threadIdx.x; p < NP; p += blockDim.x) {
         const int32_t c = hist[p];
         if (c) hist[p] = atomicAdd(&a.counts[(int64_t)g * NP + p], c);
@@ -710,6 +714,69 @@ __device__ __forceinline__ void select_row(const TP &a, const DebugView &dbg, in
         if (flag[i]) zr[i] = -INFINITY;
 }
 
+// A row's inputs to the selection, loaded ahead: its kept-parent count, this lane's
+// parent (rank lane) and its logits lane, lane + 64, ... (the whole padded row; the
+// slots past the row's candidates are masked once their number is known).
+template <int KT>
+struct SelIn {
+    int32_t m, par;
+    float z[KT];
+};
+
+template <int KT>
+__device__ __forceinline__ void sel_fetch(const TP &a, int l, int64_t row, int lane, SelIn<KT> &f) {
+    f.m = a.mk[l & 1][row];
+    f.par = lane < a.k ? a.par[l & 1][row * a.k + lane] : 0;
+    const float *zr = a.z + row * a.zs;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int32_t i = lane + 64 * t;
+        f.z[t] = i < a.zs ? zr[i] : 0.f;
+    }
+}
+
+// select_row with its inputs already in registers (KT > 0)
+template <int KT>
+__device__ __forceinline__ void select_row_in(const TP &a, const DebugView &dbg, int l, int64_t row, int lane,
+                                              const SelIn<KT> &f, unsigned char *scratch, float *outv,
+                                              int32_t *kept, int32_t *parl, uint8_t *flag) {
+    const int64_t nctx = a.ctx_base + (int64_t)div32(row, a.Hq) * a.ctx_step;
+    const int64_t up = div32(nctx, a.pw[l + 1]);
+    RowLevel rl;
+    rl.m = __builtin_amdgcn_readfirstlane(f.m);
+    rl.o = (int32_t)((int64_t)div32(nctx, a.pw[l]) - (int64_t)a.b * up);
+    rl.part = up;
+    const int32_t n = rl.m * a.b + rl.o;
+    const int32_t mm = min(a.k, n);
+    if (lane == 0) a.mk[(l + 1) & 1][row] = mm;
+    if (n == 0) return;
+    float *zr = a.z + row * a.zs;
+    const int32_t *par = a.par[l & 1] + row * a.k;
+    for (int r = lane; r < rl.m; r += 64) parl[r] = r == lane ? f.par : par[r];
+    for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<uint32_t *>(flag + i) = 0u;
+    __threadfence_block();
+    sel::Cands cd;
+    cd.n = n;
+    cd.nchild = rl.m * a.b;
+    cd.b = a.b;
+    cd.top = 0;
+    cd.orphan0 = (int32_t)(rl.part * a.b);
+    uint32_t kk[KT];
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) kk[t] = lane + 64 * t < n ? sel::ordered_bits(f.z[t]) : 0u;
+    sel::select_from_keys<KT>(kk, zr, flag, kept, mm, cd, parl, lane, scratch, outv);
+    int32_t *pn = a.par[(l + 1) & 1] + row * a.k;
+    for (int r = lane; r < mm; r += 64) pn[r] = kept[r];
+    if (dbg.selected)
+        for (int r = lane; r < mm; r += 64) dbg.selected[(row * a.n_levels + (l - 1)) * a.k + r] = kept[r];
+    if (dbg.kth_gap && lane == 0) dbg.kth_gap[row * a.n_levels + (l - 1)] = outv[1] - outv[2];
+    for (int i = lane; i < n; i += 64)
+        if (flag[i]) zr[i] = -INFINITY;
+}
+
+// Persistent waves over rows; with the keys in registers (KT > 0) each wave loads the
+// next row's inputs before selecting the current row, so the loads' latency hides
+// behind the selection.
 template <int KT>
 __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int smem_wave) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -721,8 +788,23 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
     int32_t *kept = reinterpret_cast<int32_t *>(base + sel::kScratchBytes + 16);
     int32_t *parl = reinterpret_cast<int32_t *>(base + sel::kScratchBytes + 16 + kq);
     uint8_t *flag = base + sel::kScratchBytes + 16 + 2 * kq;
-    for (int64_t row = (int64_t)blockIdx.x * 4 + w; row < a.rows; row += (int64_t)gridDim.x * 4)
-        select_row<KT>(a, dbg, l, row, lane, scratch, outv, kept, parl, flag);
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    int64_t row = (int64_t)blockIdx.x * 4 + w;
+    if constexpr (KT == 0) {
+        for (; row < a.rows; row += stride) select_row<KT>(a, dbg, l, row, lane, scratch, outv, kept, parl, flag);
+    } else {
+        if (row >= a.rows) return;
+        SelIn<KT> cur, nxt;
+        sel_fetch<KT>(a, l, row, lane, cur);
+        for (;;) {
+            const int64_t next = row + stride;
+            if (next < a.rows) sel_fetch<KT>(a, l, next, lane, nxt);
+            select_row_in<KT>(a, dbg, l, row, lane, cur, scratch, outv, kept, parl, flag);
+            if (next >= a.rows) break;
+            row = next;
+            cur = nxt;
+        }
+    }
 }
 
 // -------------------------------------------------------------------- pv --
@@ -1223,7 +1305,14 @@ hipError_t launch_select(const TP &a, const DebugView &dbg, int l, int32_t maxc,
 
 hipError_t launch_count(const TP &a, int l, int32_t NP, hipStream_t s) {
     const int64_t per_head = a.rows / a.Hq * a.G;
-    if (NP <= kHistSplit) {
+    // a block clears and scans the whole histogram, which pays for itself only over
+    // enough rows; with few rows and many parents, blocks own ranges of parents instead
+    if (NP <= kHistSplit || (NP <= kHistMax && per_head >= kHistRows)) {
+        if ((size_t)NP * 4 > 64 * 1024) {
+            const hipError_t e =
+                hipFuncSetAttribute((const void *)tp_count, hipFuncAttributeMaxDynamicSharedMemorySize, NP * 4);
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(tp_count, dim3((unsigned)((per_head + 255) / 256), (unsigned)a.Hkv), dim3(256),
                            (size_t)NP * 4, s, a, l, NP, 0);
     } else {

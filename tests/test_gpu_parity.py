@@ -147,6 +147,9 @@ PREFILL_CASES = [
     # head_dim 64 in bf16, b = 16, k = 4, one head: 300 rows
     ("tiny_f32_4k", 4000, 300, {"dtype": "bf16"}),
     ("tiny_f32_4k", 4000, 96, {}),
+    # fanout 3 over 78K tokens: 26,067 token-level parents, past the LDS histogram's
+    # 24,576, so the parent-major path counts pairs per range of parents instead
+    ("tiny_f32_4k", 78000, 200, {"dtype": "bf16", "b": 3, "k": 4}),
 ]
 
 
