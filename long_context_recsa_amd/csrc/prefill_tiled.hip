@@ -845,6 +845,101 @@ __global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t N
     });
 }
 
+// Level l >= 1, fanout <= 32: the same per pair, over runs of kRun consecutive
+// items per wave.  A bucket's items are consecutive, so a run mostly shares one
+// parent: every item's logits are loaded at the run's start and the parent's
+// values once per parent, so a run waits on memory about twice instead of once
+// per item.
+constexpr int kRun = 4;
+
+__device__ __forceinline__ Item make_item(int4 rec, int4 pr, int32_t NP, int grp) {
+    Item it;
+    const int32_t bkt = __builtin_amdgcn_readfirstlane(rec.x);
+    it.g = __builtin_amdgcn_readfirstlane(bkt / NP);
+    it.p = __builtin_amdgcn_readfirstlane(bkt % NP);
+    it.cnt = __builtin_amdgcn_readfirstlane(rec.z);
+    it.pr = pr;
+    #pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        it.orow[v] = __shfl(pr.x, 4 * grp + v);
+        it.orank[v] = __shfl(pr.y, 4 * grp + v);
+        it.onc[v] = __shfl(pr.w, 4 * grp + v);
+    }
+    return it;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int32_t NP) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, i16 = lane & 15;
+    const int64_t nexist = a.length / a.pw[l];
+    float *slice = a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D;
+    const int64_t n = *a.n_items;
+    const int64_t nruns = (n + kRun - 1) / kRun;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    // each run's item records (bucket and pair count, uniform; this lane's pair)
+    struct Recs {
+        int32_t bkt[kRun], cnt[kRun];
+        int4 pr[kRun];
+    };
+    auto fetch = [&](int64_t run, Recs &r) {
+        const int64_t i0 = run * kRun;
+        #pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            const int64_t i = i0 + u < n ? i0 + u : i0;
+            const int4 rec = a.items[i];
+            r.bkt[u] = __builtin_amdgcn_readfirstlane(rec.x);
+            r.cnt[u] = __builtin_amdgcn_readfirstlane(rec.z);
+            r.pr[u] = a.sorted[i * kTile + i16];
+        }
+    };
+    int64_t run = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
+    if (run >= nruns) return;
+    Recs cur, nxt;
+    fetch(run, cur);
+    for (;;) {
+        const int64_t next = run + nw;
+        if (next < nruns) fetch(next, nxt);        // the next run's records, ahead of this run's loads
+        const int64_t i0 = run * kRun;
+        const int nit = (int)__builtin_amdgcn_readfirstlane((int32_t)min<int64_t>(kRun, n - i0));
+        const int32_t *bkt = cur.bkt, *cnt = cur.cnt;
+        const int4 *pr = cur.pr;
+        float w[kRun][1][8];
+        #pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            const int32_t nc = (u < nit && i16 < cnt[u]) ? pr[u].w : 0;
+            const float *zr = a.z + (int64_t)pr[u].x * a.zs + pr[u].y * a.b;
+            #pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int c = 8 * grp + v;
+                const float zz = zr[c < nc ? c : 0];
+                w[u][0][v] = c < nc ? zz : -INFINITY;
+            }
+        }
+        VRaw<D> vr;
+        int32_t held = -1;                  // the bucket whose values vr holds
+        #pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            if (u < nit) {
+                const Item it = make_item(make_int4(bkt[u], 0, cnt[u], 0), pr[u], NP, grp);
+                if (bkt[u] != held) {
+                    load_values<D>(level_rows(tv, true, l, it.g, D), it.p * a.b, nexist, a.b, 0, lane, vr);
+                    held = bkt[u];
+                }
+                pair_softmax<1>(a, it, l, lane, w[u]);
+                f32x4 acc[D / 16];
+                #pragma unroll
+                for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pv_accumulate<D>(vr, w[u][0], acc);
+                pv_store<D>(a, it, lane, acc, slice);
+            }
+        }
+        if (next >= nruns) break;
+        run = next;
+        cur = nxt;
+    }
+}
+
 // ---------------------------------------------------------------- attend --
 // Level 0: each item's pairs against the parent's tokens, the pairs' softmax
 // states and P.V in one pass; the logits go through LDS from the score tile's
@@ -1366,8 +1461,14 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
                 return e;
             hipLaunchKernelGGL((tp_score<D, KC>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
             if ((e = launch_select(a, dbg, l, maxc, smw, s)) != hipSuccess) return e;
-            if ((e = persistent_grid((const void *)tp_pv<D, KC>, 0, ib, grid)) != hipSuccess) return e;
-            hipLaunchKernelGGL((tp_pv<D, KC>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+            if constexpr (KC == 1) {
+                const unsigned rb = (unsigned)((items / kRun + 1 + 3) / 4);
+                if ((e = persistent_grid((const void *)tp_pv_runs<D>, 0, rb, grid)) != hipSuccess) return e;
+                hipLaunchKernelGGL((tp_pv_runs<D>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+            } else {
+                if ((e = persistent_grid((const void *)tp_pv<D, KC>, 0, ib, grid)) != hipSuccess) return e;
+                hipLaunchKernelGGL((tp_pv<D, KC>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+            }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
