@@ -1287,12 +1287,13 @@ __device__ __forceinline__ void final_one(const TP &a, int64_t t, int D4) {
         const int np = a.nplev[row * a.lv + l];
         const float2 *ml = a.pml + l * pslice + row * (a.k + 1);
         const float4 *pa = base + l * pslice * D4;
-        #pragma unroll 4
+        // branch-free, so the loads of several pairs are in flight together (a pair
+        // without entries has m = -inf and a zero sum: weight 0)
+        #pragma unroll 8
         for (int r = 0; r < np; ++r) {
             const float2 s = ml[r];
-            if (s.x == -INFINITY) continue;
-            const float e = __expf(s.x - M);
             const float4 x = pa[r * D4];
+            const float e = s.x == -INFINITY ? 0.f : __expf(s.x - M);
             L += e * s.y;
             v.x += e * x.x; v.y += e * x.y; v.z += e * x.z; v.w += e * x.w;
         }
