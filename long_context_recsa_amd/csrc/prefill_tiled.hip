@@ -345,6 +345,43 @@ __global__ __launch_bounds__(256) void tp_scan_write(TP a, int64_t nb) {
     }
 }
 
+// Both scans in one workgroup, chunk after chunk with a carry: for few buckets
+// (every level above the tokens) one launch instead of three.
+constexpr int64_t kScanSmall = 4 * kScanChunk;
+
+__global__ __launch_bounds__(256) void tp_scan_small(TP a, int64_t nb) {
+    int2 carry = make_int2(0, 0);
+    for (int64_t base = 0; base < nb; base += kScanChunk) {
+        const int64_t e0 = base + threadIdx.x * kScanPer;
+        int32_t c[kScanPer];
+        scan_load(a, nb, e0, c);
+        int2 v = make_int2(0, 0);
+        #pragma unroll
+        for (int i = 0; i < kScanPer; ++i) {
+            v.x += c[i];
+            v.y += (c[i] + kTile - 1) / kTile;
+        }
+        int2 total;
+        int2 ex = block_scan(v, total);
+        ex.x += carry.x;
+        ex.y += carry.y;
+        for (int i = 0; i < kScanPer && e0 + i < nb; ++i) {
+            a.offs[e0 + i] = ex.x;
+            a.itemoff[e0 + i] = ex.y;
+            ex.x += c[i];
+            ex.y += (c[i] + kTile - 1) / kTile;
+            a.counts[e0 + i] = 0;
+        }
+        carry.x += total.x;
+        carry.y += total.y;
+    }
+    if (threadIdx.x == 0) {
+        a.offs[nb] = carry.x;
+        a.itemoff[nb] = carry.y;
+        *a.n_items = carry.y;
+    }
+}
+
 // Pairs into bucket order, each with what scoring needs: (row, rank, the
 // query's RoPE position n - rank*b, the parent's children in the row's view);
 // one item per tile of a bucket.
@@ -1424,9 +1461,13 @@ hipError_t bucket_level(const TP &a, const DebugView &dbg, int l, int32_t NP, hi
     const int64_t nchunks = (nb + kScanChunk - 1) / kScanChunk;
     hipError_t e;
     if ((e = launch_count(a, l, NP, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tp_scan_sums, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
-    hipLaunchKernelGGL(tp_scan_chunks, dim3(1), dim3(256), 0, s, a, nb, nchunks);
-    hipLaunchKernelGGL(tp_scan_write, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+    if (nb <= kScanSmall) {
+        hipLaunchKernelGGL(tp_scan_small, dim3(1), dim3(256), 0, s, a, nb);
+    } else {
+        hipLaunchKernelGGL(tp_scan_sums, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+        hipLaunchKernelGGL(tp_scan_chunks, dim3(1), dim3(256), 0, s, a, nb, nchunks);
+        hipLaunchKernelGGL(tp_scan_write, dim3((unsigned)nchunks), dim3(256), 0, s, a, nb);
+    }
     hipLaunchKernelGGL(tp_scatter, dim3((unsigned)((a.rows + nb + 255) / 256)), dim3(256), 0, s, a, dbg, l, NP,
                        nb);
     return hipGetLastError();
