@@ -365,18 +365,22 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     const int l = t.level;
     // level 1 with write_tokens: dk, dv are written (this is the first contribution to them)
     const bool wr = l == 1 && t.write_tokens != 0 && t.dk != nullptr;
-    // persistent waves, each over a contiguous range of (head, node): dw stays in
-    // registers while the head does not change (one set of atomics per head and wave,
-    // not per node, which would serialize on dw's few addresses)
-    const int64_t total = (int64_t)t.Hkv * t.nodes;
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const int64_t chunk = (total + nwaves - 1) / nwaves;
-    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wave) * chunk;
-    const int64_t w1 = w0 + chunk < total ? w0 + chunk : total;
+    // persistent waves: the S waves of head g take its nodes s, s + S, s + 2S, ..., so the
+    // nodes read at one time lie close together (a window of S nodes per head), and dw
+    // stays in registers for the head (one set of atomics per head and wave, not per
+    // node, which would serialize on dw's few addresses)
+    // (node counts and wave counts stay below 2^31)
+    const int32_t nwaves = (int32_t)gridDim.x * 4;
+    const int32_t wid = (int32_t)blockIdx.x * 4 + wave;
+    const int32_t hstep = nwaves < t.Hkv ? nwaves : t.Hkv;          // heads g0, g0 + hstep, ...
+    const int32_t S = nwaves < t.Hkv ? 1 : nwaves / t.Hkv;           // waves per head
+    if (wid >= S * hstep) return;
+    const int g0 = wid % hstep;
+    const int32_t s0 = wid / hstep;
+    const int32_t nodes = (int32_t)t.nodes;
     float dw[NE];
     #pragma unroll
     for (int e = 0; e < NE; ++e) dw[e] = 0.f;
-    int gcur = w0 < w1 ? (int)(w0 / t.nodes) : 0;
     auto flush = [&](int gg) {
         float v[NE];
         #pragma unroll
@@ -394,13 +398,8 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
             for (int e = 0; e < NE; ++e) atomicAdd(t.dw + (int64_t)gg * D + e0 + e, v[e]);
         }
     };
-    for (int64_t widx = w0; widx < w1; ++widx) {
-    const int g = (int)(widx / t.nodes);
-    const int64_t j = widx - (int64_t)g * t.nodes;
-    if (g != gcur) {
-        flush(gcur);
-        gcur = g;
-    }
+    for (int g = g0; g < t.Hkv; g += hstep) {
+    for (int32_t j = s0; j < nodes; j += S) {
     const float *gkp = t.gk + ((int64_t)g * tv.node_cap[l] + j) * D + e0;
     const float *gvp = t.gv + ((int64_t)g * tv.node_cap[l] + j) * D + e0;
     float gk[NE], gv[NE], w[NE];
@@ -532,7 +531,146 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (w0 < w1) flush(gcur);
+    flush(g);
+    }
+}
+
+// Level 1 without token gradients (only dw; the distillation step): one pass over a
+// node's children with an online softmax.  With e_c = exp(a_c - m), q_c = <g, x_c>
+// and r a reference (child 0's q),
+//   l = sum e_c,  A = sum e_c x_c,  S = sum e_c (q_c - r),  B = sum e_c (q_c - r) x_c,
+// the node adds s_p (B / l - (S / l)(A / l)) = s_p sum_c da_c x_c to dw (the shift by r
+// cancels; it keeps the subtraction well conditioned when the q_c share a large part).
+// Each lane group takes children grp, grp + 4, ..., all of its (up to 8) rows in
+// flight at once, so a node waits on memory once.  Persistent waves keep dw per head:
+// the S waves of head g take its nodes s, s + S, s + 2S, ..., so the nodes read at one
+// time lie close together (a window of S nodes per head) and each wave adds to dw once.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_tree_dw(TreeView tv, BwdTreeArgs t) {
+    constexpr int NE = D / 16;              // contiguous elements per lane
+    constexpr int RIF = 8;                  // rows of a lane group in flight
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int grp = lane >> 4, sub = lane & 15;
+    const int e0 = sub * NE;
+    const int32_t b = t.b;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t hstep = nwaves < t.Hkv ? nwaves : t.Hkv;          // heads g0, g0 + hstep, ...
+    const int64_t S = nwaves < t.Hkv ? 1 : nwaves / t.Hkv;           // waves per head
+    if (wid >= S * hstep) return;
+    const int g0 = (int)(wid % hstep);
+    const int64_t s0 = wid / hstep;
+    float dw[NE], w[NE];
+    #pragma unroll
+    for (int e = 0; e < NE; ++e) dw[e] = 0.f;
+    auto flush = [&](int gg) {
+        float v[NE];
+        #pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            v[e] = dw[e];
+            v[e] += __shfl_xor(v[e], 16);
+            v[e] += __shfl_xor(v[e], 32);
+            dw[e] = 0.f;
+        }
+        if (grp == 0) {
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) atomicAdd(t.dw + (int64_t)gg * D + e0 + e, v[e]);
+        }
+    };
+    // sum over the 16 lanes of a group, in every lane of it
+    auto gsum = [](float v) {
+        v += __shfl_xor(v, 8, 16);
+        v += __shfl_xor(v, 4, 16);
+        v += __shfl_xor(v, 2, 16);
+        v += __shfl_xor(v, 1, 16);
+        return v;
+    };
+    for (int g = g0; g < t.Hkv; g += (int)hstep) {
+    Vec<float, NE>::load(t.pool_w + (int64_t)g * D + e0, w);
+    for (int64_t j = s0; j < t.nodes; j += S) {
+        float gk[NE];
+        Vec<float, NE>::load(t.gk + ((int64_t)g * tv.node_cap[1] + j) * D + e0, gk);
+        const T *xk = static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + j * b) * D + e0;
+        float m = -INFINITY, l = 0.f, Sq = 0.f, r = 0.f, A[NE], B[NE];
+        #pragma unroll
+        for (int e = 0; e < NE; ++e) { A[e] = 0.f; B[e] = 0.f; }
+        for (int32_t c0 = grp; c0 < b; c0 += 4 * RIF) {
+            float x[RIF][NE];
+            #pragma unroll
+            for (int u = 0; u < RIF; ++u) {
+                const int32_t c = c0 + 4 * u;
+                Vec<T, NE>::load(xk + (int64_t)(c < b ? c : b - 1) * D, x[u]);
+            }
+            #pragma unroll
+            for (int u = 0; u < RIF; ++u) {
+                const int32_t c = c0 + 4 * u;
+                float pa = 0.f, pq = 0.f;
+                #pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    pa += w[e] * x[u][e];
+                    pq += gk[e] * x[u][e];
+                }
+                pa = t.pool_scale * gsum(pa);
+                pq = gsum(pq);
+                if (c0 == grp && u == 0) r = __shfl(pq, 0);   // child 0's q, uniform
+                if (c < b) {                                   // uniform within a lane group
+                    const float mn = fmaxf(m, pa);
+                    const float cs = __expf(m - mn);          // m = -inf on the first row: 0
+                    const float p = __expf(pa - mn);
+                    const float pd = p * (pq - r);
+                    l = l * cs + p;
+                    Sq = Sq * cs + pd;
+                    #pragma unroll
+                    for (int e = 0; e < NE; ++e) {
+                        A[e] = A[e] * cs + p * x[u][e];
+                        B[e] = B[e] * cs + pd * x[u][e];
+                    }
+                    m = mn;
+                }
+            }
+        }
+        // merge the four lane groups (all hold a row: b >= 4 is not assumed, so guard -inf)
+        #pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off), so = __shfl_xor(Sq, off);
+            const float mn = fmaxf(m, mo);
+            const float ca = m == -INFINITY ? 0.f : __expf(m - mn);
+            const float cb = mo == -INFINITY ? 0.f : __expf(mo - mn);
+            l = l * ca + lo * cb;
+            Sq = Sq * ca + so * cb;
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const float ao = __shfl_xor(A[e], off), bo = __shfl_xor(B[e], off);
+                A[e] = A[e] * ca + ao * cb;
+                B[e] = B[e] * ca + bo * cb;
+            }
+            m = mn;
+        }
+        if (grp == 0) {                     // every group holds the merged state; count it once
+            const float il = 1.f / l, sbar = Sq * il;
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) dw[e] += t.pool_scale * (B[e] * il - sbar * A[e] * il);
+        }
+    }
+    flush(g);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_tree_dw_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
+    const int64_t nodes = (int64_t)t.Hkv * t.nodes;
+    if (nodes == 0) return hipSuccess;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree_dw<T, D>, 256, 0);
+    if (e != hipSuccess) return e;
+    const int64_t want = (nodes + 3) / 4;
+    const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t blocks = want < cap ? want : cap;
+    hipLaunchKernelGGL((bwd_tree_dw<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, tv, t);
+    return hipGetLastError();
 }
 
 __global__ void fill_zero(uint4 *p, int64_t n16) {
@@ -618,6 +756,10 @@ hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, c
 
 hipError_t launch_backward_tree(const TreeView &tv, recsa_dtype st, int32_t D, const BwdTreeArgs &t,
                                 hipStream_t s) {
+    if (t.level == 1 && t.dk == nullptr) {  // only dw: the one-pass kernel
+        if (st == RECSA_BF16) return D == 128 ? launch_tree_dw_t<bf16_t, 128>(tv, t, s) : launch_tree_dw_t<bf16_t, 64>(tv, t, s);
+        return D == 128 ? launch_tree_dw_t<float, 128>(tv, t, s) : launch_tree_dw_t<float, 64>(tv, t, s);
+    }
     if (st == RECSA_BF16) return D == 128 ? launch_tree_t<bf16_t, 128>(tv, t, s) : launch_tree_t<bf16_t, 64>(tv, t, s);
     return D == 128 ? launch_tree_t<float, 128>(tv, t, s) : launch_tree_t<float, 64>(tv, t, s);
 }
