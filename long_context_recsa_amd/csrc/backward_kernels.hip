@@ -535,18 +535,21 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     }
 }
 
-// Level 1 without token gradients (only dw; the distillation step): one pass over a
-// node's children with an online softmax.  With e_c = exp(a_c - m), q_c = <g, x_c>
-// and r a reference (child 0's q),
+// Level 1 in one pass over a node's children with an online softmax: dw only (the
+// distillation step), or dw and the tokens' dk, dv written (WR; fanout <= 32).  With
+// e_c = exp(a_c - m), q_c = <g, x_c> and r a reference (child 0's q),
 //   l = sum e_c,  A = sum e_c x_c,  S = sum e_c (q_c - r),  B = sum e_c (q_c - r) x_c,
 // the node adds s_p (B / l - (S / l)(A / l)) = s_p sum_c da_c x_c to dw (the shift by r
 // cancels; it keeps the subtraction well conditioned when the q_c share a large part).
+// A child's gradients need only its a_c and q_c: alpha_c = e_c / l,
+// da_c = alpha_c (q_c - r - S / l), dk_c = alpha_c g + s_p da_c w, dv_c = g_v / b, so
+// WR keeps them in registers and writes each token row once, reading no key twice.
 // Each lane group takes children grp, grp + 4, ..., all of its (up to 8) rows in
 // flight at once, so a node waits on memory once.  Persistent waves keep dw per head:
 // the S waves of head g take its nodes s, s + S, s + 2S, ..., so the nodes read at one
 // time lie close together (a window of S nodes per head) and each wave adds to dw once.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_tree_dw(TreeView tv, BwdTreeArgs t) {
+template <typename T, int D, bool WR>
+__global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) {
     constexpr int NE = D / 16;              // contiguous elements per lane
     constexpr int RIF = 8;                  // rows of a lane group in flight
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -588,10 +591,12 @@ __global__ __launch_bounds__(256) void bwd_tree_dw(TreeView tv, BwdTreeArgs t) {
     for (int g = g0; g < t.Hkv; g += (int)hstep) {
     Vec<float, NE>::load(t.pool_w + (int64_t)g * D + e0, w);
     for (int64_t j = s0; j < t.nodes; j += S) {
-        float gk[NE];
+        float gk[NE], gv[NE];
         Vec<float, NE>::load(t.gk + ((int64_t)g * tv.node_cap[1] + j) * D + e0, gk);
+        if (WR) Vec<float, NE>::load(t.gv + ((int64_t)g * tv.node_cap[1] + j) * D + e0, gv);
         const T *xk = static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + j * b) * D + e0;
         float m = -INFINITY, l = 0.f, Sq = 0.f, r = 0.f, A[NE], B[NE];
+        float za[RIF], zq[RIF];             // WR: this group's children's a_c and q_c (one batch)
         #pragma unroll
         for (int e = 0; e < NE; ++e) { A[e] = 0.f; B[e] = 0.f; }
         for (int32_t c0 = grp; c0 < b; c0 += 4 * RIF) {
@@ -613,6 +618,10 @@ __global__ __launch_bounds__(256) void bwd_tree_dw(TreeView tv, BwdTreeArgs t) {
                 pa = t.pool_scale * gsum(pa);
                 pq = gsum(pq);
                 if (c0 == grp && u == 0) r = __shfl(pq, 0);   // child 0's q, uniform
+                if (WR) {
+                    za[u] = pa;
+                    zq[u] = pq;
+                }
                 if (c < b) {                                   // uniform within a lane group
                     const float mn = fmaxf(m, pa);
                     const float cs = __expf(m - mn);          // m = -inf on the first row: 0
@@ -646,30 +655,50 @@ __global__ __launch_bounds__(256) void bwd_tree_dw(TreeView tv, BwdTreeArgs t) {
             }
             m = mn;
         }
+        const float il = 1.f / l, sbar = Sq * il;
         if (grp == 0) {                     // every group holds the merged state; count it once
-            const float il = 1.f / l, sbar = Sq * il;
             #pragma unroll
             for (int e = 0; e < NE; ++e) dw[e] += t.pool_scale * (B[e] * il - sbar * A[e] * il);
+        }
+        if (WR) {                           // the group's children: one batch (b <= 4 * RIF)
+            float *dk0 = t.dk + ((int64_t)g * tv.cap + j * b) * D + e0;
+            float *dv0 = t.dv + ((int64_t)g * tv.cap + j * b) * D + e0;
+            float ov[NE];
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) ov[e] = gv[e] * (1.f / (float)b);
+            #pragma unroll
+            for (int u = 0; u < RIF; ++u) {
+                const int32_t c = grp + 4 * u;
+                if (c < b) {
+                    const float al = __expf(za[u] - m) * il;
+                    const float dac = t.pool_scale * al * (zq[u] - r - sbar);
+                    float ok[NE];
+                    #pragma unroll
+                    for (int e = 0; e < NE; ++e) ok[e] = al * gk[e] + dac * w[e];
+                    Vec<float, NE>::store(dk0 + (int64_t)c * D, ok);
+                    Vec<float, NE>::store(dv0 + (int64_t)c * D, ov);
+                }
+            }
         }
     }
     flush(g);
     }
 }
 
-template <typename T, int D>
-hipError_t launch_tree_dw_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
+template <typename T, int D, bool WR>
+hipError_t launch_tree_one_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
     const int64_t nodes = (int64_t)t.Hkv * t.nodes;
     if (nodes == 0) return hipSuccess;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree_dw<T, D>, 256, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree_one<T, D, WR>, 256, 0);
     if (e != hipSuccess) return e;
     const int64_t want = (nodes + 3) / 4;
     const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t blocks = want < cap ? want : cap;
-    hipLaunchKernelGGL((bwd_tree_dw<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, tv, t);
+    hipLaunchKernelGGL((bwd_tree_one<T, D, WR>), dim3((unsigned)blocks), dim3(256), 0, s, tv, t);
     return hipGetLastError();
 }
 
@@ -756,9 +785,16 @@ hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, c
 
 hipError_t launch_backward_tree(const TreeView &tv, recsa_dtype st, int32_t D, const BwdTreeArgs &t,
                                 hipStream_t s) {
-    if (t.level == 1 && t.dk == nullptr) {  // only dw: the one-pass kernel
-        if (st == RECSA_BF16) return D == 128 ? launch_tree_dw_t<bf16_t, 128>(tv, t, s) : launch_tree_dw_t<bf16_t, 64>(tv, t, s);
-        return D == 128 ? launch_tree_dw_t<float, 128>(tv, t, s) : launch_tree_dw_t<float, 64>(tv, t, s);
+    // level 1 in one pass: dw only, or the tokens' gradients written (fanout <= 32)
+    if (t.level == 1 && t.dk == nullptr) {
+        if (st == RECSA_BF16)
+            return D == 128 ? launch_tree_one_t<bf16_t, 128, false>(tv, t, s) : launch_tree_one_t<bf16_t, 64, false>(tv, t, s);
+        return D == 128 ? launch_tree_one_t<float, 128, false>(tv, t, s) : launch_tree_one_t<float, 64, false>(tv, t, s);
+    }
+    if (t.level == 1 && t.write_tokens != 0 && t.b <= 32) {
+        if (st == RECSA_BF16)
+            return D == 128 ? launch_tree_one_t<bf16_t, 128, true>(tv, t, s) : launch_tree_one_t<bf16_t, 64, true>(tv, t, s);
+        return D == 128 ? launch_tree_one_t<float, 128, true>(tv, t, s) : launch_tree_one_t<float, 64, true>(tv, t, s);
     }
     if (st == RECSA_BF16) return D == 128 ? launch_tree_t<bf16_t, 128>(tv, t, s) : launch_tree_t<bf16_t, 64>(tv, t, s);
     return D == 128 ? launch_tree_t<float, 128>(tv, t, s) : launch_tree_t<float, 64>(tv, t, s);
