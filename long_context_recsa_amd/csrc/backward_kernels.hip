@@ -27,9 +27,11 @@
 // so with g = dkey: dx_c = alpha_c g + s_p da_c w and dw += s_p sum da_c x_c,
 // da_c = alpha_c (<g, x_c> - sum alpha <g, x>).  Children belong to one node,
 // so their gradients are read, added to and written without atomics; dw is
-// added with atomics.  At level 1 with write_tokens the tokens' dk and dv are
-// written instead (the rows' own token entries are added afterwards), which
-// halves the traffic of the one pass that touches every token.  Storage
+// added with atomics.  With write_children the children's gradients are
+// written instead, and the rows' own entries of the child level are added
+// afterwards: at level 1 that halves the traffic of the one pass that touches
+// every token (the tokens' dk, dv are never read back); above it the
+// parent-major path does the same with the summaries' gradients.  Storage
 // rounding of summaries passes gradients through.
 #include <math.h>
 
@@ -363,8 +365,8 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     T *kc = reinterpret_cast<T *>(smem + tree_stats_bytes(b)) + (size_t)wave * b * D;
     const bool cache = t.cache_keys != 0;
     const int l = t.level;
-    // level 1 with write_tokens: dk, dv are written (this is the first contribution to them)
-    const bool wr = l == 1 && t.write_tokens != 0 && t.dk != nullptr;
+    // write_children: the children's gradients are written (this is the first contribution)
+    const bool wr = t.write_children != 0 && (l >= 2 || t.dk != nullptr);
     // persistent waves: the S waves of head g take its nodes s, s + S, s + 2S, ..., so the
     // nodes read at one time lie close together (a window of S nodes per head), and dw
     // stays in registers for the head (one set of atomics per head and wave, not per
@@ -410,27 +412,25 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
     #pragma unroll
     for (int u = 0; u < NE; ++u) any = any || gk[u] != 0.f || gv[u] != 0.f;
     const int64_t c0 = j * b;
-    if (__ballot(any) == 0) {               // no row read this node
-        if (wr) {                           // its tokens' gradients are still written: zero
-            float *ck0 = t.dk + ((int64_t)g * tv.cap + c0) * D, *cv0 = t.dv + ((int64_t)g * tv.cap + c0) * D;
-            float z[NE];
-            #pragma unroll
-            for (int e = 0; e < NE; ++e) z[e] = 0.f;
-            for (int32_t c = grp; c < b; c += 4) {
-                Vec<float, NE>::store(ck0 + (int64_t)c * D + e0, z);
-                Vec<float, NE>::store(cv0 + (int64_t)c * D + e0, z);
-            }
-        }
-        continue;
-    }
-
     // the children: stored keys of level l - 1 (tokens at l = 1) and their gradients
-    const T *xk = l == 1 ? static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + c0) * D
-                         : static_cast<const T *>(tv.key[l - 1]) + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
     float *ck = l == 1 ? t.dk + ((int64_t)g * tv.cap + c0) * D
                        : t.gk_child + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
     float *cv = l == 1 ? t.dv + ((int64_t)g * tv.cap + c0) * D
                        : t.gv_child + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
+    if (__ballot(any) == 0) {               // no row read this node
+        if (wr) {                           // its children's gradients are still written: zero
+            float z[NE];
+            #pragma unroll
+            for (int e = 0; e < NE; ++e) z[e] = 0.f;
+            for (int32_t c = grp; c < b; c += 4) {
+                Vec<float, NE>::store(ck + (int64_t)c * D + e0, z);
+                Vec<float, NE>::store(cv + (int64_t)c * D + e0, z);
+            }
+        }
+        continue;
+    }
+    const T *xk = l == 1 ? static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + c0) * D
+                         : static_cast<const T *>(tv.key[l - 1]) + ((int64_t)g * tv.node_cap[l - 1] + c0) * D;
     // child of this group's batch slot u (clamped to the last child; the result is then unused)
     auto child = [&](int32_t cb, int u) {
         const int32_t c = cb + grp + 4 * u;
@@ -791,7 +791,7 @@ hipError_t launch_backward_tree(const TreeView &tv, recsa_dtype st, int32_t D, c
             return D == 128 ? launch_tree_one_t<bf16_t, 128, false>(tv, t, s) : launch_tree_one_t<bf16_t, 64, false>(tv, t, s);
         return D == 128 ? launch_tree_one_t<float, 128, false>(tv, t, s) : launch_tree_one_t<float, 64, false>(tv, t, s);
     }
-    if (t.level == 1 && t.write_tokens != 0 && t.b <= 32) {
+    if (t.level == 1 && t.write_children != 0 && t.dk != nullptr && t.b <= 32) {
         if (st == RECSA_BF16)
             return D == 128 ? launch_tree_one_t<bf16_t, 128, true>(tv, t, s) : launch_tree_one_t<bf16_t, 64, true>(tv, t, s);
         return D == 128 ? launch_tree_one_t<float, 128, true>(tv, t, s) : launch_tree_one_t<float, 64, true>(tv, t, s);

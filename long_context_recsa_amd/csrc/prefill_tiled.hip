@@ -100,6 +100,7 @@ struct TB {
     const int32_t *sel;        // [rows][n_levels][k] kept nodes by level, -1 padded
     int64_t cap;               // token capacity (row stride of a head in dk, dv)
     int64_t node_cap[kMaxLevels + 1];
+    BwdTreeArgs tree;          // the tree pass's arguments common to every level (interleaved runs)
 };
 
 struct RowLevel {
@@ -1534,14 +1535,16 @@ size_t tiled_backward_lds_bytes(int32_t D, int32_t b) {
 namespace {
 
 // Backward of one pass of rows: the forward (recording the selections and each row's
-// softmax statistics), <dO, out>, then per level the same buckets and tb_item.
-// Phase 1 stops before the token level, phase 2 runs only that level (after phase 1
-// of the same pass, whose selections and row statistics are still in the workspace).
+// softmax statistics), <dO, out>, then per level from the top the same buckets and
+// tb_item.  With `tree` (one pass of rows) the tree pass runs between the levels: after
+// level l's items it writes level l - 1's gradients (the tokens' at l = 1), which
+// level l - 1's items then add to, so no gradient is read back and only the top level
+// and the children past each level's last complete node need clearing.
 template <int D, int KC>
 hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *kth_gap, int64_t max_ctx,
-                             const Plan &P, int32_t maxc, int32_t phase, hipStream_t s) {
+                             const Plan &P, int32_t maxc, bool tree, hipStream_t s) {
     hipError_t e;
-    if (phase != 2) {
+    {
         DebugView fd{};
         fd.selected = const_cast<int32_t *>(t.sel);
         fd.kth_gap = kth_gap;
@@ -1551,10 +1554,14 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
         hipLaunchKernelGGL(tb_rowdot, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, t.dout, out,
                            const_cast<float *>(t.rowD), a.rows, D);
     }
+    if (tree && a.top >= 1) {
+        const int64_t ntop = a.length / a.pw[a.top];
+        if ((e = launch_zero_rows(t.gk[a.top], a.Hkv, t.node_cap[a.top], 0, ntop, D, s)) != hipSuccess) return e;
+        if ((e = launch_zero_rows(t.gv[a.top], a.Hkv, t.node_cap[a.top], 0, ntop, D, s)) != hipSuccess) return e;
+    }
     const DebugView none{};
     const size_t lds = tiled_backward_lds_bytes(D, a.b);
-    const int l_lo = phase == 1 ? 1 : 0;
-    for (int l = phase == 2 ? 0 : a.top; l >= l_lo; --l) {
+    for (int l = a.top; l >= 0; --l) {
         const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
         const int64_t nb = (int64_t)a.Hkv * NP;
         hipLaunchKernelGGL(tb_parents, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, s, a, t.sel, l);
@@ -1567,18 +1574,43 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
             return e;
         hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, t, l, NP);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (tree && l >= 1) {
+            BwdTreeArgs tt = t.tree;
+            tt.level = l;
+            tt.nodes = a.length / a.pw[l];
+            tt.gk = t.gk[l];
+            tt.gv = t.gv[l];
+            tt.gk_child = l >= 2 ? t.gk[l - 1] : nullptr;
+            tt.gv_child = l >= 2 ? t.gv[l - 1] : nullptr;
+            tt.dk = t.dk;
+            tt.dv = t.dv;
+            tt.write_children = 1;
+            if ((e = launch_backward_tree(tv, RECSA_BF16, D, tt, s)) != hipSuccess) return e;
+            // children past the last complete node of level l have no parent to write them
+            const int64_t under = tt.nodes * a.b;
+            if (l >= 2) {
+                const int64_t nc = a.length / a.pw[l - 1];
+                if ((e = launch_zero_rows(t.gk[l - 1], a.Hkv, t.node_cap[l - 1], under, nc, D, s)) != hipSuccess)
+                    return e;
+                if ((e = launch_zero_rows(t.gv[l - 1], a.Hkv, t.node_cap[l - 1], under, nc, D, s)) != hipSuccess)
+                    return e;
+            } else if (t.dk != nullptr) {
+                if ((e = launch_zero_rows(t.dk, a.Hkv, t.cap, under, a.length, D, s)) != hipSuccess) return e;
+                if ((e = launch_zero_rows(t.dv, a.Hkv, t.cap, under, a.length, D, s)) != hipSuccess) return e;
+            }
+        }
     }
     return hipSuccess;
 }
 
 template <int D>
 hipError_t run_backward_pass_d(const TreeView &tv, const TP &a, const TB &t, float *out, float *kth_gap,
-                               int64_t max_ctx, const Plan &P, int32_t maxc, int32_t phase, hipStream_t s) {
+                               int64_t max_ctx, const Plan &P, int32_t maxc, bool tree, hipStream_t s) {
     switch ((a.b + 31) / 32) {
-        case 1: return run_backward_pass<D, 1>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
-        case 2: return run_backward_pass<D, 2>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
-        case 3: return run_backward_pass<D, 3>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
-        default: return run_backward_pass<D, 4>(tv, a, t, out, kth_gap, max_ctx, P, maxc, phase, s);
+        case 1: return run_backward_pass<D, 1>(tv, a, t, out, kth_gap, max_ctx, P, maxc, tree, s);
+        case 2: return run_backward_pass<D, 2>(tv, a, t, out, kth_gap, max_ctx, P, maxc, tree, s);
+        case 3: return run_backward_pass<D, 3>(tv, a, t, out, kth_gap, max_ctx, P, maxc, tree, s);
+        default: return run_backward_pass<D, 4>(tv, a, t, out, kth_gap, max_ctx, P, maxc, tree, s);
     }
 }
 
@@ -1691,9 +1723,9 @@ bool tiled_backward_one_pass(int64_t rows, int32_t Hq) { return pass_rows(rows, 
 
 hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                  int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
-                                 float *dbg_kth_gap, int32_t phase, void *ws, hipStream_t s) {
+                                 float *dbg_kth_gap, const BwdTreeArgs *tree, void *ws, hipStream_t s) {
     const int64_t per = pass_rows(da.rows, da.Hq);
-    if (phase != 0 && per < da.rows) return hipErrorInvalidValue;      // phases need one pass
+    if (tree != nullptr && per < da.rows) return hipErrorInvalidValue;   // interleaving needs one pass
     const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
     const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels);
     unsigned char *w = static_cast<unsigned char *>(ws);
@@ -1709,6 +1741,7 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
         t.node_cap[l] = tv.node_cap[l];
     }
     t.cap = tv.cap;
+    if (tree != nullptr) t.tree = *tree;
     t.rowml = a.rowml;
     t.rowD = reinterpret_cast<const float *>(w + B.off_rowD);
     t.sel = reinterpret_cast<const int32_t *>(w + B.off_sel);
@@ -1718,11 +1751,11 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
         t.dout = ba.dout + r0 * D;
         t.dq = ba.dq + r0 * D;
         float *kth = dbg_kth_gap != nullptr ? dbg_kth_gap + r0 * tv.n_levels : nullptr;
-        const hipError_t e =
-            D == 128 ? run_backward_pass_d<128>(tv, a, t, out, kth, max_ctx, P, da.max_cand, phase, s)
-                     : run_backward_pass_d<64>(tv, a, t, out, kth, max_ctx, P, da.max_cand, phase, s);
+        const bool il = tree != nullptr;
+        const hipError_t e = D == 128 ? run_backward_pass_d<128>(tv, a, t, out, kth, max_ctx, P, da.max_cand, il, s)
+                                      : run_backward_pass_d<64>(tv, a, t, out, kth, max_ctx, P, da.max_cand, il, s);
         if (e != hipSuccess) return e;
-        if (phase != 2 && dbg_selected != nullptr && tv.n_levels > 0) {
+        if (dbg_selected != nullptr && tv.n_levels > 0) {
             const hipError_t c = hipMemcpyAsync(dbg_selected + r0 * tv.n_levels * da.k, t.sel,
                                                 (size_t)rows * tv.n_levels * da.k * 4, hipMemcpyDeviceToDevice, s);
             if (c != hipSuccess) return c;

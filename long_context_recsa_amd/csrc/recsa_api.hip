@@ -351,26 +351,40 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     size_t grad_bytes = 0;
     for (int l = 1; l <= L.n_levels; ++l)
         grad_bytes += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
-    hipError_t e = launch_fill_zero(ws, grad_bytes, s);
-    if (e == hipSuccess) e = launch_fill_zero(d_w, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
-    if (e != hipSuccess) return hip_fail(e, "workspace clear");
-    // Every gradient is written.  Where the rows' token entries can be added after the
-    // tree pass (row-wise, in two phases; parent-major in one pass of rows), the tree
-    // pass's level 1 writes the tokens' dk, dv first and nothing reads them back;
-    // otherwise they are cleared and the tree pass adds to them.
+    hipError_t e = launch_fill_zero(d_w, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
+    if (e != hipSuccess) return hip_fail(e, "gradient clear");
+    // Every gradient is written.  Wherever the order allows, the tree pass writes a
+    // level's children's gradients before the rows' entries of that child level are
+    // added to them, so no gradient is read back:
+    //   parent-major in one pass of rows: the tree pass runs between the levels' items;
+    //   row-wise: the summaries' entries and dq first (phase 1), the tree pass (the
+    //     tokens' gradients written at level 1; above it, added to what the rows left),
+    //     then the rows' token entries (phase 2);
+    //   parent-major over several passes of rows: everything cleared, then added to.
     const bool tiled = use_tiled_backward(p, rows);
     const bool tokens = d_k != nullptr;
-    const bool split = tokens && (!tiled || tiled_backward_one_pass(rows, p->n_q_heads));
-    if (tokens && !split) {
+    const bool interleave = tiled && tiled_backward_one_pass(rows, p->n_q_heads);
+    const bool split = tokens && !tiled;
+    BwdTreeArgs common{};
+    common.Hkv = p->n_kv_heads;
+    common.b = p->fanout_b;
+    common.pool_scale = p->pool_scale;
+    common.pool_w = desc->pool_w;
+    common.dw = d_w;
+    if (!interleave) {
+        e = launch_fill_zero(ws, grad_bytes, s);
+        if (e != hipSuccess) return hip_fail(e, "workspace clear");
+    }
+    if (tiled && tokens && !interleave) {
         e = launch_zero_rows(d_k, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
         if (e == hipSuccess) e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
     }
-    DescendArgs da{};
     if (tiled) {
         // parent-major: dq is a sum over items
         e = launch_fill_zero(d_q, (size_t)rows * p->head_dim * sizeof(float), s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
+        DescendArgs da{};
         da.q = q;
         da.out = nullptr;
         da.rows = rows;
@@ -385,8 +399,9 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         da.scale = a.scale;
         e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a,
                                   dbg != nullptr ? dbg->selected : nullptr, dbg != nullptr ? dbg->kth_gap : nullptr,
-                                  split ? 1 : 0, static_cast<char *>(ws) + grad_bytes, s);
+                                  interleave ? &common : nullptr, static_cast<char *>(ws) + grad_bytes, s);
         if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
+        if (interleave) return RECSA_OK;
     } else {
         a.phase = split ? 1 : 0;
         e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
@@ -403,21 +418,16 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     for (int l = top; l >= 1; --l) {
         int64_t pl = 1;
         for (int i = 0; i < l; ++i) pl *= p->fanout_b;
-        BwdTreeArgs t{};
+        BwdTreeArgs t = common;
         t.level = l;
-        t.Hkv = p->n_kv_heads;
         t.nodes = desc->length / pl;
-        t.b = p->fanout_b;
-        t.pool_scale = p->pool_scale;
-        t.pool_w = desc->pool_w;
         t.gk = a.gk[l];
         t.gv = a.gv[l];
         t.gk_child = l >= 2 ? a.gk[l - 1] : nullptr;
         t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
         t.dk = d_k;
         t.dv = d_v;
-        t.write_tokens = split ? 1 : 0;
-        t.dw = d_w;
+        t.write_children = split && l == 1 ? 1 : 0;
         e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
         if (e != hipSuccess) return hip_fail(e, "backward tree launch");
     }
@@ -429,15 +439,9 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
             e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
         // then the rows' own token entries
-        if (tiled) {
-            e = launch_backward_tiled(tv, p->head_dim, da, p->n_kv_heads, desc->length, p->capacity, a, nullptr,
-                                      nullptr, 2, static_cast<char *>(ws) + grad_bytes, s);
-            if (e != hipSuccess) return hip_fail(e, "tiled backward launch");
-        } else {
-            a.phase = 2;
-            e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, DebugView{}, s);
-            if (e != hipSuccess) return hip_fail(e, "backward rows launch");
-        }
+        a.phase = 2;
+        e = launch_backward_rows(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, DebugView{}, s);
+        if (e != hipSuccess) return hip_fail(e, "backward rows launch");
     }
     return RECSA_OK;
 }

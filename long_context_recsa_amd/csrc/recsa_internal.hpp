@@ -194,7 +194,8 @@ struct BwdTreeArgs {
     const float *gk, *gv;      // the level's gradients
     float *gk_child, *gv_child;  // level - 1's (level >= 2)
     float *dk, *dv;            // token gradients (level 1)
-    int32_t write_tokens;      // level 1: write dk, dv (zeros under nodes without gradient), not add
+    int32_t write_children;    // write the children's gradients (tokens' dk, dv at level 1), not add
+                               // to them; children of nodes without gradient get zeros
     float *dw;                 // [Hkv][D] (added to)
     int32_t cache_keys;        // set by the launch: the children's keys stay in LDS between passes
 };
@@ -230,12 +231,14 @@ size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D)
 size_t tiled_backward_lds_bytes(int32_t D, int32_t b);
 size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
                                       int32_t maxc, int64_t capacity, int32_t n_levels);
-// phase 0: every level in each pass of rows; 1 (one pass only): the forward and the
-// levels >= 1; 2: then the token level, from the workspace phase 1 left
+// tree == NULL: every level's items in each pass of rows (the caller clears the
+// gradients and runs the tree pass after); else (one pass of rows only) the tree pass
+// runs between the levels with these common arguments, writing each level's children's
+// gradients before that level's items add to them: nothing to clear or run after
 bool tiled_backward_one_pass(int64_t rows, int32_t Hq);
 hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArgs &da, int32_t Hkv,
                                  int64_t length, int64_t capacity, const BwdArgs &ba, int32_t *dbg_selected,
-                                 float *dbg_kth_gap, int32_t phase, void *ws, hipStream_t s);
+                                 float *dbg_kth_gap, const BwdTreeArgs *tree, void *ws, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 // zeros rows [r0, r1) of each of Hkv heads of a [Hkv][cap][D] fp32 array
 hipError_t launch_zero_rows(float *p, int32_t Hkv, int64_t cap, int64_t r0, int64_t r1, int32_t D, hipStream_t s);
