@@ -1558,6 +1558,10 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
         const int64_t ntop = a.length / a.pw[a.top];
         if ((e = launch_zero_rows(t.gk[a.top], a.Hkv, t.node_cap[a.top], 0, ntop, D, s)) != hipSuccess) return e;
         if ((e = launch_zero_rows(t.gv[a.top], a.Hkv, t.node_cap[a.top], 0, ntop, D, s)) != hipSuccess) return e;
+    } else if (tree && t.dk != nullptr) {
+        // no level above the tokens (fewer than b tokens): no tree pass writes them
+        if ((e = launch_zero_rows(t.dk, a.Hkv, t.cap, 0, a.length, D, s)) != hipSuccess) return e;
+        if ((e = launch_zero_rows(t.dv, a.Hkv, t.cap, 0, a.length, D, s)) != hipSuccess) return e;
     }
     const DebugView none{};
     const size_t lds = tiled_backward_lds_bytes(D, a.b);
