@@ -239,9 +239,8 @@ __global__ __launch_bounds__(256) void dense_mfma(DenseArgs a) {
     __shared__ __align__(16) __bf16 klo[kTok][KP];
     __shared__ __align__(16) uint16_t vt[D][VP];
     __shared__ __align__(16) float pbuf[4][16][PS];
-    __shared__ float2 cs0[H];             // (cos, sin) of t0 theta_j for the step
+    __shared__ float2 cs0[2][H];          // (cos, sin) of t0 theta_j for the step, by step parity
     __shared__ float2 csn[H];             // (cos, sin) of n theta_j
-    __shared__ double theta[H];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int i16 = lane & 15, grp = lane >> 4;
     const int split = blockIdx.x, g = blockIdx.y;
@@ -253,10 +252,18 @@ __global__ __launch_bounds__(256) void dense_mfma(DenseArgs a) {
     const uint16_t *kc = static_cast<const uint16_t *>(a.k_cache) + (int64_t)g * a.cap * D;
     const uint16_t *vc = static_cast<const uint16_t *>(a.v_cache) + (int64_t)g * a.cap * D;
 
-    for (int j = threadIdx.x; j < H; j += 256) {
-        theta[j] = pow(a.base, -2.0 * (double)j / (double)D);
-        const double ang = (double)n * theta[j];
-        csn[j] = make_float2((float)cos(ang), (float)sin(ang));
+    // lanes j < H: the steps' base rotations by angle addition in double precision,
+    // cos/sin(t0 theta_j) for t0 = t_begin, t_begin + kTok, ... (no slow large-argument
+    // cos/sin per step)
+    double2 csd = make_double2(1.0, 0.0), rot = make_double2(1.0, 0.0);
+    if (threadIdx.x < H) {
+        const int j = threadIdx.x;
+        const double th = pow(a.base, -2.0 * (double)j / (double)D);
+        const double an = (double)n * th, a0 = (double)t_begin * th, ak = (double)kTok * th;
+        csn[j] = make_float2((float)cos(an), (float)sin(an));
+        csd = make_double2(cos(a0), sin(a0));
+        rot = make_double2(cos(ak), sin(ak));
+        cs0[0][j] = make_float2((float)csd.x, (float)csd.y);
     }
     __syncthreads();
     // this lane's query row (A row i16 of the wave's tile), rotated to position n
@@ -286,24 +293,36 @@ __global__ __launch_bounds__(256) void dense_mfma(DenseArgs a) {
     #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTok) {
-        __syncthreads();            // the previous step's LDS reads are done
-        for (int j = threadIdx.x; j < H; j += 256) {
-            const double ang = (double)t0 * theta[j];
-            cs0[j] = make_float2((float)cos(ang), (float)sin(ang));
-        }
-        __syncthreads();
-        // keys rotated to their positions and split; values transposed
-        for (int e = threadIdx.x; e < kTok * (H / 4); e += 256) {
+    // this thread's share of a step's keys and values (NE groups of 4 pairs), raw: the
+    // next step's are loaded while the current step computes
+    constexpr int NE = kTok * (H / 4) / 256;
+    uint2 rk1[NE], rk2[NE], rv1[NE], rv2[NE];
+    auto load_raw = [&](int64_t tb) {
+        #pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = threadIdx.x + 256 * q;
             const int tt = e / (H / 4), j = (e - tt * (H / 4)) * 4;
-            const int64_t t = t0 + tt;
-            uint2 k1 = make_uint2(0u, 0u), k2 = k1, v1 = k1, v2 = k1;
+            const int64_t t = tb + tt;
+            rk1[q] = rk2[q] = rv1[q] = rv2[q] = make_uint2(0u, 0u);
             if (t < t_end) {
-                k1 = *reinterpret_cast<const uint2 *>(kc + t * D + j);
-                k2 = *reinterpret_cast<const uint2 *>(kc + t * D + H + j);
-                v1 = *reinterpret_cast<const uint2 *>(vc + t * D + j);
-                v2 = *reinterpret_cast<const uint2 *>(vc + t * D + H + j);
+                rk1[q] = *reinterpret_cast<const uint2 *>(kc + t * D + j);
+                rk2[q] = *reinterpret_cast<const uint2 *>(kc + t * D + H + j);
+                rv1[q] = *reinterpret_cast<const uint2 *>(vc + t * D + j);
+                rv2[q] = *reinterpret_cast<const uint2 *>(vc + t * D + H + j);
             }
+        }
+    };
+    load_raw(t_begin);
+    int step = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kTok, ++step) {
+        __syncthreads();            // the previous step's LDS reads are done; cs0[step & 1] is written
+        const float2 *cb = cs0[step & 1];
+        // keys rotated to their positions and split; values transposed
+        #pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = threadIdx.x + 256 * q;
+            const int tt = e / (H / 4), j = (e - tt * (H / 4)) * 4;
+            const uint2 k1 = rk1[q], k2 = rk2[q], v1 = rv1[q], v2 = rv2[q];
             const uint16_t ka[4] = {(uint16_t)(k1.x & 0xFFFFu), (uint16_t)(k1.x >> 16),
                                     (uint16_t)(k1.y & 0xFFFFu), (uint16_t)(k1.y >> 16)};
             const uint16_t kb[4] = {(uint16_t)(k2.x & 0xFFFFu), (uint16_t)(k2.x >> 16),
@@ -312,21 +331,34 @@ __global__ __launch_bounds__(256) void dense_mfma(DenseArgs a) {
                                     (uint16_t)(v1.y & 0xFFFFu), (uint16_t)(v1.y >> 16)};
             const uint16_t vb[4] = {(uint16_t)(v2.x & 0xFFFFu), (uint16_t)(v2.x >> 16),
                                     (uint16_t)(v2.y & 0xFFFFu), (uint16_t)(v2.y >> 16)};
+            __bf16 h1[4], l1[4], h2[4], l2[4];
             #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float2 b0 = cs0[j + u], inc = a.incr[tt * H + j + u];
+                const float2 b0 = cb[j + u], inc = a.incr[tt * H + j + u];
                 const float cn = b0.x * inc.x - b0.y * inc.y, sn = b0.y * inc.x + b0.x * inc.y;
                 const float x1 = bf16_to_f32(ka[u]), x2 = bf16_to_f32(kb[u]);
                 const float r1 = x1 * cn - x2 * sn, r2 = x2 * cn + x1 * sn;
-                const __bf16 h1 = (__bf16)r1, h2 = (__bf16)r2;
-                khi[tt][j + u] = h1;
-                klo[tt][j + u] = (__bf16)(r1 - (float)h1);
-                khi[tt][H + j + u] = h2;
-                klo[tt][H + j + u] = (__bf16)(r2 - (float)h2);
+                h1[u] = (__bf16)r1;
+                h2[u] = (__bf16)r2;
+                l1[u] = (__bf16)(r1 - (float)h1[u]);
+                l2[u] = (__bf16)(r2 - (float)h2[u]);
                 vt[j + u][tt] = va[u];
                 vt[H + j + u][tt] = vb[u];
             }
+            // four consecutive elements per array: one 8-byte store each (rows are 8-byte aligned)
+            *reinterpret_cast<uint2 *>(&khi[tt][j]) = __builtin_bit_cast(uint2, h1);
+            *reinterpret_cast<uint2 *>(&klo[tt][j]) = __builtin_bit_cast(uint2, l1);
+            *reinterpret_cast<uint2 *>(&khi[tt][H + j]) = __builtin_bit_cast(uint2, h2);
+            *reinterpret_cast<uint2 *>(&klo[tt][H + j]) = __builtin_bit_cast(uint2, l2);
         }
+        // the next step's base rotation (the other buffer) and its keys and values, in
+        // flight while this step computes
+        if (threadIdx.x < H) {
+            const double cx = csd.x * rot.x - csd.y * rot.y, sx = csd.y * rot.x + csd.x * rot.y;
+            csd = make_double2(cx, sx);
+            cs0[(step + 1) & 1][threadIdx.x] = make_float2((float)cx, (float)sx);
+        }
+        if (t0 + kTok < t_end) load_raw(t0 + kTok);
         __syncthreads();
         // logits of the wave's 16 rows against the step's 64 tokens: 4 tiles of 16
         f32x4 st[4];
@@ -440,8 +472,11 @@ hipError_t launch_t(const DenseArgs &a, hipStream_t s) {
 }  // namespace
 
 int64_t dense_span(int64_t length) {
-    // spans of a multiple of the staging step, about 1024 of them over the cache
-    int64_t span = (length + 1023) / 1024;
+    // spans of a multiple of the staging step, at most kDenseMaxSpans (256) of them over
+    // the cache: with 8 KV heads that is 2048 workgroups, four rounds of what the chip
+    // holds at once, and a quarter of the per-span states 1024 spans would leave to
+    // write and merge
+    int64_t span = (length + kDenseMaxSpans - 1) / kDenseMaxSpans;
     span = (span + kTok - 1) / kTok * kTok;
     return span < kTok ? kTok : span;
 }

@@ -446,9 +446,10 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     return RECSA_OK;
 }
 
-// Per-span partial states of dense attention: at most 1024 spans whatever the length.
+// Per-span partial states of dense attention: at most kDenseMaxSpans spans whatever the length.
 size_t dense_part_bytes(const recsa_params *p, int32_t batch) {
-    return align_up((size_t)p->n_kv_heads * 1024 * (size_t)batch * (size_t)(p->n_q_heads / p->n_kv_heads) *
+    return align_up((size_t)p->n_kv_heads * (size_t)kDenseMaxSpans * (size_t)batch *
+                    (size_t)(p->n_q_heads / p->n_kv_heads) *
                     (size_t)(p->head_dim + 2) * sizeof(float));
 }
 

@@ -216,6 +216,8 @@ struct DenseArgs {
     float scale;
     float2 *incr;              // bf16 storage: [64][D/2] (cos, sin) of tt * theta_j, filled by the launch
 };
+// spans of dense attention: at most kDenseMaxSpans over any length (the workspace bound)
+constexpr int64_t kDenseMaxSpans = 256;
 int64_t dense_span(int64_t length);
 hipError_t launch_dense(recsa_dtype st, int32_t D, const DenseArgs &a, hipStream_t s);
 

@@ -225,7 +225,8 @@ def test_dense_and_distill_validate_before_any_hip_call():
     p = _p(capacity=1000)
     fake = 1 << 20
     d = R.recsa_tree_desc(fake, fake, fake, fake, 10)
-    assert R.recsa_dense_workspace_bytes(p, 2) >= 8 * 1024 * 2 * 4 * 130 * 4
+    # per-span states of up to 256 spans: 8 KV heads x 2 queries x 4 heads per group x (d + 2)
+    assert R.recsa_dense_workspace_bytes(p, 2) >= 8 * 256 * 2 * 4 * 130 * 4
     assert R.recsa_distill_workspace_bytes(p, 2) > R.recsa_backward_workspace_bytes(p, 2 * 32)
     assert R.recsa_dense_workspace_bytes(p, 0) == 0 and R.recsa_distill_workspace_bytes(p, 0) == 0
     cases = [
