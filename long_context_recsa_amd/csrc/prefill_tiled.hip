@@ -1097,6 +1097,13 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
     const int32_t b = a.b;
     const bool grads_here = l > 0 || t.dk != nullptr;
     for_items(a, NP, lane, [&](const Item &it) {
+        // a token-level bucket of one item is the only writer of its parent's tokens'
+        // gradients in this launch: it reads, adds and stores them instead of adding with
+        // atomics (~280 G float atomics/s across the chip, which the token level's
+        // ~1 G adds per 4096-query chunk would wait on)
+        const int64_t bkt = (int64_t)it.g * NP + it.p;
+        const bool excl = l == 0 && grads_here &&
+                          __builtin_amdgcn_readfirstlane(a.itemoff[bkt + 1] - a.itemoff[bkt]) == 1;
         const bf16_t *keys = level_rows(tv, false, l, it.g, D);
         const bf16_t *vals = level_rows(tv, true, l, it.g, D);
         const int64_t c0 = it.p * b;
@@ -1238,10 +1245,19 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                                            : t.gk[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
                         float *gv = l == 0 ? t.dv + ((int64_t)it.g * t.cap + c0 + c) * D
                                            : t.gv[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
-                        atomicAdd(gv + j, v1);
-                        atomicAdd(gv + H + j, v2);
-                        atomicAdd(gk + j, k1 * cs.x + k2 * cs.y);             // R(-c theta)
-                        atomicAdd(gk + H + j, k2 * cs.x - k1 * cs.y);
+                        const float dk1 = k1 * cs.x + k2 * cs.y, dk2 = k2 * cs.x - k1 * cs.y;   // R(-c theta)
+                        if (excl) {
+                            const float a0 = gv[j], a1 = gv[H + j], a2 = gk[j], a3 = gk[H + j];
+                            gv[j] = a0 + v1;
+                            gv[H + j] = a1 + v2;
+                            gk[j] = a2 + dk1;
+                            gk[H + j] = a3 + dk2;
+                        } else {
+                            atomicAdd(gv + j, v1);
+                            atomicAdd(gv + H + j, v2);
+                            atomicAdd(gk + j, dk1);
+                            atomicAdd(gk + H + j, dk2);
+                        }
                     }
                     const float x1 = bf16_to_f32(Kb[ccl * D + j]), x2 = bf16_to_f32(Kb[ccl * D + H + j]);
                     const float r1 = x1 * cs.x - x2 * cs.y, r2 = x2 * cs.x + x1 * cs.y;   // R(c theta) k_c
