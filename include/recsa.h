@@ -216,7 +216,8 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t m
  * Nothing is added to what the buffers held: a caller accumulating over calls
  * adds the results itself.  The summaries' gradients reach the tokens first
  * (written, so the tokens' gradients are never read back), then the rows' own
- * token entries are added with atomics; with more than one pass of rows on the
+ * token entries are added (fp32 atomics, or read-add-store where one work
+ * item owns a node's tokens); with more than one pass of rows on the
  * parent-major path (over 131072 rows) the tokens' gradients are cleared
  * first and added to instead.
  * Rounding a summary to store_dtype passes the gradient through unchanged.
