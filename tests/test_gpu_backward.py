@@ -117,22 +117,24 @@ def _run(name, L, n_kv, n_q, n, causal, kw):
     _say("backward", {k: f"{e:.2e}/{t:.2e}" for k, (e, t) in rep.items()})
 
 
-@pytest.mark.parametrize("path,dtype,nq,L", [("rowwise", "f32", 2, 2000), ("tiled", "bf16", 64, 2000),
-                                            ("rowwise", "bf16", 2, 10), ("tiled", "bf16", 8, 10)])
-def test_backward_overwrites_given_gradients(monkeypatch, path, dtype, nq, L):
+@pytest.mark.parametrize("path,dtype,nq,L,b", [("rowwise", "f32", 2, 2000, 16), ("tiled", "bf16", 64, 2000, 16),
+                                              ("rowwise", "bf16", 2, 10, 16), ("tiled", "bf16", 8, 10, 16),
+                                              ("rowwise", "f32", 2, 3000, 40), ("tiled", "bf16", 64, 3000, 40)])
+def test_backward_overwrites_given_gradients(monkeypatch, path, dtype, nq, L, b):
     """dk, dv (tokens [0, length)) and dw are written whatever the buffers held; rows
     from the length on are left alone.  Row-wise (two phases around the tree pass) and
     parent-major in one pass of rows (the tree pass between the levels), each also with
-    fewer tokens than one node (no tree pass at all)."""
+    fewer tokens than one node (no tree pass at all) and with a fanout above 32 (the
+    general tree kernel writes the children, two 32-child chunks per parent)."""
     monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
     cap = L + 100
-    w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], L, prefill_n=0, n_q=2, dtype=dtype)
+    w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], L, prefill_n=0, n_q=2, dtype=dtype, b=b)
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
     layer = P.make_layer(w, capacity=cap)
     P.load_cache(layer, K, V, W, L, w.dtype)
     layer.build(L)
-    _say(f"case overwrite {path} {dtype} nq={nq} L={L}")
+    _say(f"case overwrite {path} {dtype} nq={nq} L={L} b={b}")
     rng = np.random.default_rng(9)
     q = P.to_device(synth.to_storage(rng.standard_normal((nq, 2, w.d)).astype(np.float32), w.dtype), w.dtype)
     dO = torch.from_numpy(rng.standard_normal((nq, 2, w.d)).astype(np.float32)).cuda()
