@@ -1212,7 +1212,42 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                     o2[pr] = live ? t.dout[(int64_t)row * D + H + j] : 0.f;
                 }
                 const int nc = b - 32 * kk < 32 ? b - 32 * kk : 32;      // children in this chunk
+                // exclusive bucket: this lane's old dV, dK values of the child kAhead steps
+                // ahead are loaded before the current child's arithmetic, to hide their latency
+                auto grad_rows = [&](int c, float *&gk, float *&gv) {
+                    gk = l == 0 ? t.dk + ((int64_t)it.g * t.cap + c0 + c) * D
+                                : t.gk[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
+                    gv = l == 0 ? t.dv + ((int64_t)it.g * t.cap + c0 + c) * D
+                                : t.gv[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
+                };
+                auto fetch_old = [&](int cc, float *o) {
+                    const int c = 32 * kk + cc;
+                    if (cc < nc && c0 + c < nexist) {
+                        float *gk, *gv;
+                        grad_rows(c, gk, gv);
+                        o[0] = gv[j];
+                        o[1] = gv[H + j];
+                        o[2] = gk[j];
+                        o[3] = gk[H + j];
+                    }
+                };
+                constexpr int kAhead = 2;
+                float ring[kAhead][4];
+                #pragma unroll
+                for (int u = 0; u < kAhead; ++u) {
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q) ring[u][q] = 0.f;
+                    if (excl) fetch_old(u * SUB + sb, ring[u]);
+                }
                 for (int s0 = 0; s0 < nc; s0 += SUB) {
+                    float cur[4];
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        cur[q] = ring[0][q];
+                        #pragma unroll
+                        for (int u = 0; u + 1 < kAhead; ++u) ring[u][q] = ring[u + 1][q];
+                    }
+                    if (excl) fetch_old(s0 + kAhead * SUB + sb, ring[kAhead - 1]);
                     const int cc = s0 + sb;
                     const bool inb = cc < nc;
                     const int ccl = inb ? cc : 0;
@@ -1241,17 +1276,14 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                     }
                     const float2 cs = crot[c * crot_stride(D) + j];         // (cos, sin) of c theta_j
                     if (any && grads_here && c0 + c < nexist) {
-                        float *gk = l == 0 ? t.dk + ((int64_t)it.g * t.cap + c0 + c) * D
-                                           : t.gk[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
-                        float *gv = l == 0 ? t.dv + ((int64_t)it.g * t.cap + c0 + c) * D
-                                           : t.gv[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
+                        float *gk, *gv;
+                        grad_rows(c, gk, gv);
                         const float dk1 = k1 * cs.x + k2 * cs.y, dk2 = k2 * cs.x - k1 * cs.y;   // R(-c theta)
                         if (excl) {
-                            const float a0 = gv[j], a1 = gv[H + j], a2 = gk[j], a3 = gk[H + j];
-                            gv[j] = a0 + v1;
-                            gv[H + j] = a1 + v2;
-                            gk[j] = a2 + dk1;
-                            gk[H + j] = a3 + dk2;
+                            gv[j] = cur[0] + v1;
+                            gv[H + j] = cur[1] + v2;
+                            gk[j] = cur[2] + dk1;
+                            gk[H + j] = cur[3] + dk2;
                         } else {
                             atomicAdd(gv + j, v1);
                             atomicAdd(gv + H + j, v2);
