@@ -1097,12 +1097,12 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
     const int32_t b = a.b;
     const bool grads_here = l > 0 || t.dk != nullptr;
     for_items(a, NP, lane, [&](const Item &it) {
-        // a token-level bucket of one item is the only writer of its parent's tokens'
-        // gradients in this launch: it reads, adds and stores them instead of adding with
-        // atomics (~280 G float atomics/s across the chip, which the token level's
-        // ~1 G adds per 4096-query chunk would wait on)
+        // a bucket of one item is the only writer of its parent's children's gradients in
+        // this launch: it reads, adds and stores them instead of adding with atomics
+        // (~280 G float atomics/s across the chip, which the token level's ~1 G adds per
+        // 4096-query chunk would wait on)
         const int64_t bkt = (int64_t)it.g * NP + it.p;
-        const bool excl = l == 0 && grads_here &&
+        const bool excl = grads_here &&
                           __builtin_amdgcn_readfirstlane(a.itemoff[bkt + 1] - a.itemoff[bkt]) == 1;
         const bf16_t *keys = level_rows(tv, false, l, it.g, D);
         const bf16_t *vals = level_rows(tv, true, l, it.g, D);
