@@ -883,12 +883,12 @@ __global__ __launch_bounds__(256) void tp_pv(TreeView tv, TP a, int l, int32_t N
     });
 }
 
-// Level l >= 1, fanout <= 32: the same per pair, over runs of kRun consecutive
+// Level l >= 1, fanout <= 32: the same per pair, over runs of RUN consecutive
 // items per wave.  A bucket's items are consecutive, so a run mostly shares one
 // parent: every item's logits are loaded at the run's start and the parent's
 // values once per parent, so a run waits on memory about twice instead of once
-// per item.
-constexpr int kRun = 4;
+// per item.  Long runs suit many items; with few, they leave waves idle.
+constexpr int64_t kLongRunRows = 16384;   // rows per pass from which runs are 8 items long
 
 __device__ __forceinline__ Item make_item(int4 rec, int4 pr, int32_t NP, int grp) {
     Item it;
@@ -906,7 +906,7 @@ __device__ __forceinline__ Item make_item(int4 rec, int4 pr, int32_t NP, int grp
     return it;
 }
 
-template <int D>
+template <int D, int kRun>
 __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int32_t NP) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, i16 = lane & 15;
@@ -1553,9 +1553,15 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
             hipLaunchKernelGGL((tp_score<D, KC>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
             if ((e = launch_select(a, dbg, l, maxc, smw, s)) != hipSuccess) return e;
             if constexpr (KC == 1) {
-                const unsigned rb = (unsigned)((items / kRun + 1 + 3) / 4);
-                if ((e = persistent_grid((const void *)tp_pv_runs<D>, 0, rb, grid)) != hipSuccess) return e;
-                hipLaunchKernelGGL((tp_pv_runs<D>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+                if (rows >= kLongRunRows) {
+                    const unsigned rb = (unsigned)((items / 8 + 1 + 3) / 4);
+                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 8>, 0, rb, grid)) != hipSuccess) return e;
+                    hipLaunchKernelGGL((tp_pv_runs<D, 8>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+                } else {
+                    const unsigned rb = (unsigned)((items / 4 + 1 + 3) / 4);
+                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 4>, 0, rb, grid)) != hipSuccess) return e;
+                    hipLaunchKernelGGL((tp_pv_runs<D, 4>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+                }
             } else {
                 if ((e = persistent_grid((const void *)tp_pv<D, KC>, 0, ib, grid)) != hipSuccess) return e;
                 hipLaunchKernelGGL((tp_pv<D, KC>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
