@@ -101,6 +101,8 @@ struct TB {
     int64_t cap;               // token capacity (row stride of a head in dk, dv)
     int64_t node_cap[kMaxLevels + 1];
     BwdTreeArgs tree;          // the tree pass's arguments common to every level (interleaved runs)
+    int32_t dq_slots;          // dq shares to per-pair slots, added per level by tb_dq_add (many
+                               // rows); else fp32 atomics straight into dq (few rows)
 };
 
 struct RowLevel {
@@ -1302,7 +1304,11 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
             }
             wave_sync();                    // the next chunk rewrites Kb, Pt and dZt
         }
-        // dq += R(-(n - r b) theta) of the sums, pair by pair
+        // dq share of each pair, R(-(n - r b) theta) of the sums.  With many rows, to the
+        // pair's own slot (row, rank) of the forward's per-pair buffer, free once its
+        // output is merged: plain stores, which tb_dq_add then adds to the rows' dq (an
+        // atomic add per dimension and pair would wait on the chip's atomic rate); with
+        // few rows, atomics (no extra launch)
         if (SUB == 2) {
             #pragma unroll
             for (int pr = 0; pr < kTile; ++pr) {
@@ -1314,16 +1320,44 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
         for (int pr = 0; pr < kTile; ++pr) {
             if (pr < it.cnt) {
                 const int row = __builtin_amdgcn_readlane(it.pr.x, pr);
+                const int rank = __builtin_amdgcn_readlane(it.pr.y, pr);
                 const int pos = __builtin_amdgcn_readlane(it.pr.z, pr);
                 if (sb == 0) {
                     const float2 r = tv.rope[(int64_t)pos * H + j];
-                    float *dq = t.dq + (int64_t)row * D;
-                    atomicAdd(dq + j, dq1[pr] * r.x + dq2[pr] * r.y);
-                    atomicAdd(dq + H + j, dq2[pr] * r.x - dq1[pr] * r.y);
+                    const float x1 = dq1[pr] * r.x + dq2[pr] * r.y, x2 = dq2[pr] * r.x - dq1[pr] * r.y;
+                    if (t.dq_slots) {
+                        float *slot = a.partial + ((int64_t)row * (a.k + 1) + rank) * D;
+                        slot[j] = x1;
+                        slot[H + j] = x2;
+                    } else {
+                        float *dq = t.dq + (int64_t)row * D;
+                        atomicAdd(dq + j, x1);
+                        atomicAdd(dq + H + j, x2);
+                    }
                 }
             }
         }
     });
+}
+
+// dq of each row += the dq shares tb_item stored for its pairs of level l (slots
+// (row, rank) for rank < the row's pairs at l); one thread per (row, 4 dimensions).
+__global__ __launch_bounds__(256) void tb_dq_add(TP a, float *dq, int l) {
+    const int D4 = a.D / 4;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.rows * D4;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = div32(t, D4);
+        const int j = (int)(t - row * D4);
+        const int np = a.nplev[row * a.lv + l];
+        const float4 *src = reinterpret_cast<const float4 *>(a.partial) + row * (a.k + 1) * D4 + j;
+        float4 *dst = reinterpret_cast<float4 *>(dq) + row * D4 + j;
+        float4 v = *dst;
+        for (int r = 0; r < np; ++r) {
+            const float4 x = src[(int64_t)r * D4];
+            v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+        }
+        *dst = v;
+    }
 }
 
 // The kept nodes of level l + 1 (the parents of level l) from the forward's record.
@@ -1598,6 +1632,7 @@ template <int D, int KC>
 hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *kth_gap, int64_t max_ctx,
                              const Plan &P, int32_t maxc, bool tree, hipStream_t s) {
     hipError_t e;
+    t.dq_slots = a.rows >= kLongRunRows ? 1 : 0;
     {
         DebugView fd{};
         fd.selected = const_cast<int32_t *>(t.sel);
@@ -1632,6 +1667,13 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
             return e;
         hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, t, l, NP);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (t.dq_slots) {
+            unsigned dg;
+            if ((e = persistent_grid((const void *)tb_dq_add, 0, (unsigned)((a.rows * (D / 4) + 255) / 256), dg)) !=
+                hipSuccess)
+                return e;
+            hipLaunchKernelGGL(tb_dq_add, dim3(dg), dim3(256), 0, s, a, t.dq, l);
+        }
         if (tree && l >= 1) {
             BwdTreeArgs tt = t.tree;
             tt.level = l;
