@@ -379,7 +379,7 @@ def run_backward_chunk(args, name, n):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "storage": w.dtype, "L": w.L, "n_kv_heads": w.n_kv,
                    "n_q_heads": w.n_q, "head_dim": w.d, "b": w.b, "k": w.k, "chunk": n,
-                   "rows": n * w.n_q, "path": os.environ.get("RECSA_BACKWARD_PATH", "default")},
+                   "rows": n * w.n_q, "path": "auto"},
         "ms": {"backward": ms},
     }
     print(json.dumps(res), flush=True)

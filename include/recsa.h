@@ -55,6 +55,18 @@ typedef enum {
 
 typedef enum { RECSA_FP32 = 0, RECSA_BF16 = 1 } recsa_dtype;
 
+/* How recsa_prefill and recsa_backward lay out their work (recsa_params.path).
+ * Both layouts compute the same rule; they differ in speed and in the precision
+ * of the entry logits (fp32 row-wise, split-bf16 MFMA products of about 16
+ * significant bits parent-major).  The choice is part of the params, so a
+ * workspace-sizing call and the call that uses the workspace always agree. */
+typedef enum {
+    RECSA_PATH_AUTO = 0,          /* the library chooses by storage, fanout and row count */
+    RECSA_PATH_ROWWISE = 1,       /* one workgroup per row (query x query head) */
+    RECSA_PATH_PARENT_MAJOR = 2   /* rows grouped by the parents they keep (bf16 storage,
+                                     fanout <= 128; RECSA_ERR_UNSUPPORTED elsewhere) */
+} recsa_path;
+
 typedef struct {
     int32_t n_kv_heads;      /* >= 1 */
     int32_t n_q_heads;       /* multiple of n_kv_heads */
@@ -63,7 +75,8 @@ typedef struct {
     int32_t budget_k;        /* candidates kept per level, 1 <= k */
     int32_t store_dtype;     /* recsa_dtype of K, V, Q and summaries */
     int32_t out_dtype;       /* recsa_dtype of the attention output */
-    int32_t reserved;        /* must be 0 */
+    int32_t path;            /* recsa_path; RECSA_PATH_AUTO (0) unless a test or a
+                                measurement needs one layout */
     double  rope_base;       /* RoPE base (1e6 for the Qwen3 family); > 0 */
     float   softmax_scale;   /* logit scale s, usually 1/sqrt(head_dim) */
     float   pool_scale;      /* pooler logit scale, usually 1/sqrt(head_dim) */

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "librecsa.so")
 
 RECSA_OK, RECSA_ERR_INVALID_ARG, RECSA_ERR_UNSUPPORTED, RECSA_ERR_CAPACITY, RECSA_ERR_HIP = range(5)
 RECSA_FP32, RECSA_BF16 = 0, 1
+RECSA_PATH_AUTO, RECSA_PATH_ROWWISE, RECSA_PATH_PARENT_MAJOR = 0, 1, 2
+PATHS = {"auto": RECSA_PATH_AUTO, "rowwise": RECSA_PATH_ROWWISE, "parent_major": RECSA_PATH_PARENT_MAJOR}
 
 EXPORTED = (
     "recsa_num_levels", "recsa_tree_bytes", "recsa_tree_layout", "recsa_max_candidates",
@@ -32,7 +34,7 @@ class recsa_params(ctypes.Structure):
         ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("fanout_b", ctypes.c_int32),
         ("budget_k", ctypes.c_int32), ("store_dtype", ctypes.c_int32),
-        ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32),
         ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
         ("pool_scale", ctypes.c_float), ("capacity", ctypes.c_int64),
     ]
@@ -204,11 +206,13 @@ def recsa_decode_multi(p, descs, n_seq, q_ptr, out_ptr, dbg=None, ws=None, strea
 
 def make_params(n_kv_heads, n_q_heads, head_dim, fanout_b, budget_k, capacity,
                 store="bf16", out="f32", rope_base=1e6, softmax_scale=None,
-                pool_scale=None) -> recsa_params:
+                pool_scale=None, path="auto") -> recsa_params:
+    """path: "auto", "rowwise" or "parent_major" (recsa_path: the layout of prefill and
+    backward work)."""
     dt = {"f32": RECSA_FP32, "bf16": RECSA_BF16}
     s = 1.0 / head_dim ** 0.5
     return recsa_params(n_kv_heads, n_q_heads, head_dim, fanout_b, budget_k, dt[store], dt[out],
-                        0, rope_base, s if softmax_scale is None else softmax_scale,
+                        PATHS[path], rope_base, s if softmax_scale is None else softmax_scale,
                         s if pool_scale is None else pool_scale, capacity)
 
 

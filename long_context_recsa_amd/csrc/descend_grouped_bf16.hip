@@ -7,29 +7,16 @@ namespace recsa {
 namespace {
 using namespace descend;
 
-// Launch shape: 8 waves per row by default (a group's row carries G heads' work, and
-// there are G times fewer rows than with one head per row); RECSA_DESCEND_SHAPE="4,x"
-// selects 4 waves (for tuning sweeps).
+// Launch shape: 8 waves per row (a group's row carries G heads' work, and there are
+// G times fewer rows than with one head per row).
 template <int D>
 hipError_t dispatch_grouped(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
                             hipStream_t s) {
-    int nw = 8;
-    if (const char *e = getenv("RECSA_DESCEND_SHAPE")) {
-        int x = 0, y = 0;
-        if (sscanf(e, "%d,%d", &x, &y) == 2) nw = x;
-    }
     switch (a.gs) {
-        case 2:
-            if (nw == 4) return launch_kt<bf16_t, D, 4, 4, 2>(tv, a, dbg, s);
-            return launch_kt<bf16_t, D, 8, 4, 2>(tv, a, dbg, s);
-        case 4:
-            if (nw == 4) return launch_kt<bf16_t, D, 4, 4, 4>(tv, a, dbg, s);
-            return launch_kt<bf16_t, D, 8, 4, 4>(tv, a, dbg, s);
-        case 8:
-            if (nw == 4) return launch_kt<bf16_t, D, 4, 2, 8>(tv, a, dbg, s);
-            return launch_kt<bf16_t, D, 8, 2, 8>(tv, a, dbg, s);
-        default:
-            return hipErrorInvalidValue;
+        case 2: return launch_kt<bf16_t, D, 8, 4, 2>(tv, a, dbg, s);
+        case 4: return launch_kt<bf16_t, D, 8, 4, 4>(tv, a, dbg, s);
+        case 8: return launch_kt<bf16_t, D, 8, 2, 8>(tv, a, dbg, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -6,19 +6,12 @@ namespace recsa {
 namespace {
 using namespace descend;
 
-// Launch shape: (waves per row, ranks per slot per pass).
-// RECSA_DESCEND_SHAPE="NW,CB" overrides the choice (for tuning sweeps).
+// Launch shape: 4 waves per row; decode (one context length for all rows) keeps 4
+// ranks per slot in flight, row-wise prefill (many rows) 2, for fewer registers and
+// more rows resident per CU.
 template <typename T, int D>
 hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &dbg, hipStream_t s) {
-    int nw = 4, cb = a.ctx_step == 0 ? 4 : 2;
-    if (const char *e = getenv("RECSA_DESCEND_SHAPE")) {
-        int x = 0, y = 0;
-        if (sscanf(e, "%d,%d", &x, &y) == 2) { nw = x; cb = y; }
-    }
-    // decode (one context length for all rows): more candidates per slot in flight;
-    // prefill (many rows): fewer registers, more rows resident per CU
-    if (nw == 8 && cb == 4) return launch_kt<T, D, 8, 4, 1>(tv, a, dbg, s);
-    if (nw == 4 && cb == 2) return launch_kt<T, D, 4, 2, 1>(tv, a, dbg, s);
+    if (a.ctx_step != 0) return launch_kt<T, D, 4, 2, 1>(tv, a, dbg, s);
     return launch_kt<T, D, 4, 4, 1>(tv, a, dbg, s);
 }
 

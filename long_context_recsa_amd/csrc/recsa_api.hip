@@ -51,33 +51,35 @@ size_t elem_bytes(int32_t dt) { return dt == RECSA_BF16 ? 2 : 4; }
 
 // Prefill of at least this many rows (queries x query heads) over bf16 storage
 // runs parent-major (rows grouped by the parents they keep, bf16 MFMA); fewer
-// rows, fp32 storage or a fanout above 128 run one workgroup per row.  RECSA_PREFILL_PATH=rowwise
-// or =tiled forces one of the two.
+// rows, fp32 storage or a fanout above 128 run one workgroup per row.
+// params.path = RECSA_PATH_ROWWISE or RECSA_PATH_PARENT_MAJOR fixes one of the two
+// (check_path has already refused a parent-major request the path cannot serve).
 constexpr int64_t kTiledMinRows = 4096;
 
+bool tiled_possible(const recsa_params *p) {
+    return p->store_dtype == RECSA_BF16 && p->fanout_b <= tiled_max_fanout();
+}
+
 bool use_tiled(const recsa_params *p, int64_t rows) {
-    if (p->store_dtype != RECSA_BF16 || p->fanout_b > tiled_max_fanout()) return false;
-    if (const char *e = getenv("RECSA_PREFILL_PATH")) {
-        if (strcmp(e, "rowwise") == 0) return false;
-        if (strcmp(e, "tiled") == 0) return true;
-    }
+    if (p->path == RECSA_PATH_ROWWISE || !tiled_possible(p)) return false;
+    if (p->path == RECSA_PATH_PARENT_MAJOR) return true;
     return rows >= kTiledMinRows;
 }
 
 // The backward's parent-major path: the same storage and fanout conditions as the
-// forward's, its own switch and threshold.  It runs the forward again with its bucket
+// forward's, its own threshold.  It runs the forward again with its bucket
 // set-up (a fixed ~0.2 ms at 524K tokens), so the row-wise backward stays faster up to
 // about 128 rows; from 256 rows on the parent-major one is (1.6-2x at 1024 rows, 19x
 // at 131072 rows, 524K tokens, Qwen3-4B layer).
 constexpr int64_t kTiledBackwardMinRows = 256;
 
+bool tiled_backward_possible(const recsa_params *p) {
+    return tiled_possible(p) && tiled_backward_lds_bytes(p->head_dim, p->fanout_b) <= kMaxLds;
+}
+
 bool use_tiled_backward(const recsa_params *p, int64_t rows) {
-    if (p->store_dtype != RECSA_BF16 || p->fanout_b > tiled_max_fanout()) return false;
-    if (tiled_backward_lds_bytes(p->head_dim, p->fanout_b) > kMaxLds) return false;
-    if (const char *e = getenv("RECSA_BACKWARD_PATH")) {
-        if (strcmp(e, "rowwise") == 0) return false;
-        if (strcmp(e, "tiled") == 0) return true;
-    }
+    if (p->path == RECSA_PATH_ROWWISE || !tiled_backward_possible(p)) return false;
+    if (p->path == RECSA_PATH_PARENT_MAJOR) return true;
     return rows >= kTiledBackwardMinRows;
 }
 
@@ -107,7 +109,9 @@ recsa_status check_params(const recsa_params *p) {
         return fail(RECSA_ERR_INVALID_ARG, "store_dtype must be RECSA_FP32 or RECSA_BF16");
     if (p->out_dtype != RECSA_FP32 && p->out_dtype != RECSA_BF16)
         return fail(RECSA_ERR_INVALID_ARG, "out_dtype must be RECSA_FP32 or RECSA_BF16");
-    if (p->reserved != 0) return fail(RECSA_ERR_INVALID_ARG, "reserved must be 0");
+    if (p->path != RECSA_PATH_AUTO && p->path != RECSA_PATH_ROWWISE &&
+        p->path != RECSA_PATH_PARENT_MAJOR)
+        return fail(RECSA_ERR_INVALID_ARG, "path must be a recsa_path value");
     if (!(p->rope_base > 0.0) || !isfinite(p->rope_base))
         return fail(RECSA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
     if (!isfinite(p->softmax_scale) || !isfinite(p->pool_scale))
@@ -295,6 +299,10 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     if ((st = check_limits(p, L)) != RECSA_OK) return st;
     if ((st = check_desc(p, desc)) != RECSA_OK) return st;
     if (desc->length < 1) return fail(RECSA_ERR_INVALID_ARG, "the backward needs at least one cached token");
+    if (p->path == RECSA_PATH_PARENT_MAJOR && !tiled_backward_possible(p))
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "the parent-major backward needs bf16 storage, fanout_b <= %d and its item "
+                    "kernel's LDS within a CU's", (int)tiled_max_fanout());
     if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
     if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (causal && n_q > desc->length)
@@ -639,6 +647,10 @@ recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, c
     if (desc != nullptr && n_q > desc->length)
         return fail(RECSA_ERR_INVALID_ARG, "n_q (%lld) exceeds the tree length (%lld); append first",
                     (long long)n_q, (long long)desc->length);
+    if (check_params(p) == RECSA_OK && p->path == RECSA_PATH_PARENT_MAJOR && !tiled_possible(p))
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "the parent-major prefill needs bf16 storage and fanout_b <= %d",
+                    (int)tiled_max_fanout());
     const bool tiled = check_params(p) == RECSA_OK && use_tiled(p, n_q * p->n_q_heads);
     return run_descend(p, desc, q, n_q, desc ? desc->length - n_q + 1 : 0, 1, out, dbg, tiled, ws,
                        static_cast<hipStream_t>(stream));

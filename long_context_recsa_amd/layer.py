@@ -6,7 +6,7 @@ import ctypes
 
 import torch
 
-from . import (RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
+from . import (PATHS, RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
                recsa_build_tree, recsa_dense_decode, recsa_dense_workspace_bytes, recsa_distill_step,
                recsa_distill_workspace_bytes, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
@@ -52,6 +52,11 @@ class RecsaLayer:
             self._ws = None
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return _ptr(self._ws)
+
+    def set_path(self, path: str) -> None:
+        """Layout of prefill and backward work: "auto", "rowwise" or "parent_major"
+        (the recsa_params.path field; sizing and running calls read the same field)."""
+        self.p.path = PATHS[path]
 
     @property
     def length(self) -> int:
@@ -192,6 +197,12 @@ def decode_multi(layers, q: torch.Tensor, debug: bool = False, out: torch.Tensor
     tree) answers query q[i] at its own length.  q: [n][n_q_heads][head_dim]."""
     first = layers[0]
     n = len(layers)
+    # the kernel addresses every sequence's cache and tree with the first one's layout
+    key = [f for f, _ in recsa_params._fields_ if f != "path"]
+    for i, l in enumerate(layers[1:], 1):
+        if l.device != first.device or any(getattr(l.p, f) != getattr(first.p, f) for f in key):
+            raise ValueError(f"decode_multi: layer {i} differs from layer 0 in its params or device; "
+                             "every sequence must share one layout")
     shape = (n, first.p.n_q_heads, first.p.head_dim)
     first._check_dev(q, shape, first.store)
     if out is None:

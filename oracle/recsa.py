@@ -547,13 +547,23 @@ def distill_loss(tree: Tree, Q: np.ndarray, teacher: np.ndarray, k: int, base: f
     return loss, grads
 
 
-def distill_step(K, V, w, b, store, pool_scale, L, Q, teacher, k, base, scale, lr, mu, vel):
-    """One step: build the tree from w, the loss and dloss/dw, then the update.
-    Returns (loss before the step, new w, new velocity)."""
+def sgd_momentum(w, vel, grad, lr, mu):
+    """Heavy-ball SGD, the update of the distillation reading: the velocity first
+    takes mu times itself plus the gradient, then w moves by -lr times the new
+    velocity (no dampening, no look-ahead).  Returns (new w, new velocity)."""
+    vel = mu * np.asarray(vel, F64) + np.asarray(grad, F64)
+    return np.asarray(w, F64) - lr * vel, vel
+
+
+def distill_step(K, V, w, b, store, pool_scale, L, Q, teacher, k, base, scale, lr, mu, vel,
+                 force=None):
+    """One step: build the tree from w, the loss and dloss/dw (selection held at
+    `force` where given), then the update.  Returns (loss before the step, new w,
+    new velocity)."""
     tree = build_tree(K, V, w, b, store, pool_scale, L)
-    loss, grads = distill_loss(tree, Q, teacher, k, base, scale)
-    vel = mu * np.asarray(vel, F64) + grads["dw"]
-    return loss, np.asarray(w, F64) - lr * vel, vel
+    loss, grads = distill_loss(tree, Q, teacher, k, base, scale, force=force)
+    w_new, vel = sgd_momentum(w, vel, grads["dw"], lr, mu)
+    return loss, w_new, vel
 
 
 # ----------------------------------------------------------------------------

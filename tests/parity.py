@@ -3,8 +3,17 @@ compare the GPU's per-level selections and outputs with the oracle's.
 
 Selections must match exactly, except where the oracle's k-th and (k+1)-th
 logits of that level differ by less than 1e-3 relative
-(gap < 1e-3 * max(|z_k|, |z_k+1|, 1e-6)); such a row is then compared with the
-oracle replaying the GPU's selection from that level down.
+(gap < 1e-3 * max(|z_k|, |z_k+1|, 1e-6)) and every candidate the two sides
+disagree on scores inside that band around the boundary; such a row is then
+compared with the oracle replaying the GPU's selection from that level down
+(its keys-read count included).
+
+Outputs: fp32 storage within 1e-5 max-abs; bf16 storage within 2e-2 x the RMS
+of the oracle's output over the checked rows (the bar the hot path's
+specification sets), and also within a regression bound REG_REL x that RMS,
+which sits near the errors the GPU path reaches (fp32 arithmetic against the
+oracle's f64 on the same bf16 inputs) and far below what one wrong summary
+entry would cause.
 """
 from __future__ import annotations
 
@@ -16,6 +25,10 @@ import synth
 from oracle import recsa as O
 
 TIE_REL = 1e-3
+# Regression bound for bf16 storage, relative to the oracle's output RMS.  One
+# summary entry with a wrong value row moves a row's output by about its softmax
+# weight times the row's difference, ~1e-3 x RMS at the workloads' shapes.
+REG_REL = 2e-4
 
 
 def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -51,6 +64,27 @@ def sorted_topk_gap(z: np.ndarray, m: int):
     return float(zs[m - 1]), float(zs[m])
 
 
+def _near_tie(lt, got, what):
+    """Excuse a differing selection at one level: the k-th and (k+1)-th oracle logits
+    lie within the relative tie band, and so does every candidate the two sides
+    disagree on."""
+    m = len(lt.sel_pos)
+    zk, zk1 = sorted_topk_gap(lt.z, m)
+    band = TIE_REL * max(abs(zk), abs(zk1), 1e-6)
+    want = lt.cand[lt.sel_pos]
+    if not (zk - zk1 < band):
+        raise AssertionError(
+            f"{what} differs at level {lt.level}: oracle {want.tolist()} gpu {got.tolist()}; "
+            f"k-th/k+1-th logits {zk:.7g} {zk1:.7g}")
+    pos = {int(c): i for i, c in enumerate(lt.cand)}
+    for node in set(want.tolist()) ^ set(got.tolist()):
+        assert node in pos, f"level {lt.level}: gpu kept node {node}, not a candidate"
+        z = lt.z[pos[node]]
+        assert zk1 - band <= z <= zk + band, (
+            f"{what} at level {lt.level}: node {node} (logit {z:.7g}) is kept by one side only "
+            f"but lies outside the tie band [{zk1 - band:.7g}, {zk + band:.7g}]")
+
+
 def check_row(tree, q, g, n_ctx, k, base, scale, gpu_sel_row, max_excuses=3):
     """Compare one row's per-level selections with the oracle; returns
     (oracle RowResult to compare the output with, number of excused levels)."""
@@ -70,21 +104,33 @@ def check_row(tree, q, g, n_ctx, k, base, scale, gpu_sel_row, max_excuses=3):
         if bad is None:
             return res, len(force)
         lt, got = bad
-        zk, zk1 = sorted_topk_gap(lt.z, len(lt.sel_pos))
-        if not (zk - zk1 < TIE_REL * max(abs(zk), abs(zk1), 1e-6)):
-            raise AssertionError(
-                f"selection differs at level {lt.level} (n_ctx {n_ctx}, head {g}): oracle "
-                f"{lt.cand[lt.sel_pos].tolist()} gpu {got.tolist()}; k-th/k+1-th logits {zk:.7g} {zk1:.7g}")
+        _near_tie(lt, got, f"selection (n_ctx {n_ctx}, head {g})")
         assert len(force) < max_excuses, "too many near-tie levels in one row"
         force[lt.level] = got.copy()
     raise AssertionError("replay did not converge")
 
 
-def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype,
-               all_out_rms=None, head_of=None):
+def _check_out(err_rows, want, dtype):
+    """Spec bar and regression bound on the stacked outputs of the checked rows."""
+    err = float(np.abs(err_rows).max()) if err_rows.size else 0.0
+    if dtype == "f32":
+        tol = 1e-5
+        assert err <= tol, f"max abs error {err:.3g} > {tol:.3g}"
+        return err, tol, None
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    tol = 2e-2 * rms
+    assert err <= tol, f"max abs error {err:.3g} > {tol:.3g} (2e-2 x oracle RMS {rms:.3g})"
+    assert err <= REG_REL * rms, (f"max abs error {err:.3g} > regression bound {REG_REL} x oracle RMS "
+                                  f"{rms:.3g} = {REG_REL * rms:.3g}")
+    return err, tol, err / rms if rms > 0 else 0.0
+
+
+def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype, head_of=None):
     """rows: list of (query index, head); Q [n][Hq][d] host fp32; gpu_out [n][Hq][d];
-    dbg: the debug dict (device tensors).  Asserts selection parity and the output
-    tolerance (1e-5 max-abs for fp32 storage, 2e-2 * RMS of the oracle output for bf16)."""
+    dbg: the debug dict (device tensors).  Asserts selection parity, the keys-read
+    count of every row (of the replay where a near tie was excused) and the output
+    bars (1e-5 max-abs for fp32 storage; for bf16, 2e-2 and REG_REL x the RMS of the
+    oracle's output over these rows)."""
     Hq = Q.shape[1]
     sel = dbg["selected"].cpu().numpy()
     nkeys = dbg["n_keys"].cpu().numpy()
@@ -97,18 +143,12 @@ def check_rows(tree, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, G, dtype,
         g = h // G if head_of is None else head_of(h)
         res, ex = check_row(tree, Q[qi, h], g, n_ctx_of(qi), k, base, scale, sel[r])
         excused += ex > 0
-        if ex == 0:
-            assert nkeys[r] == res.keys_read, (qi, h, nkeys[r], res.keys_read)
+        assert nkeys[r] == res.keys_read, (qi, h, nkeys[r], res.keys_read)
         want[idx] = res.out
         got[idx] = gout[qi, h]
-    err = np.abs(got - want).max()
-    if dtype == "f32":
-        tol = 1e-5
-    else:
-        rms = all_out_rms if all_out_rms is not None else float(np.sqrt(np.mean(want ** 2)))
-        tol = 2e-2 * rms
-    assert err <= tol, f"max abs error {err:.3g} > {tol:.3g}"
-    return {"max_abs_err": float(err), "tol": tol, "excused_rows": excused, "rows": len(rows)}
+    err, tol, rel = _check_out(got - want, want, dtype)
+    return {"max_abs_err": err, "tol": tol, "err_over_rms": rel, "excused_rows": excused,
+            "rows": len(rows)}
 
 
 def head_tree(K, V, W, g, w, length):
@@ -137,21 +177,17 @@ def check_group(tree, Qg, n_ctx, k, base, scale, gpu_sel_row, max_excuses=3):
         if bad is None:
             return res, len(force)
         lt, got = bad
-        zk, zk1 = sorted_topk_gap(lt.z, len(lt.sel_pos))
-        if not (zk - zk1 < TIE_REL * max(abs(zk), abs(zk1), 1e-6)):
-            raise AssertionError(
-                f"group selection differs at level {lt.level} (n_ctx {n_ctx}): oracle "
-                f"{lt.cand[lt.sel_pos].tolist()} gpu {got.tolist()}; k-th/k+1-th scores {zk:.7g} {zk1:.7g}")
+        _near_tie(lt, got, f"group selection (n_ctx {n_ctx})")
         assert len(force) < max_excuses, "too many near-tie levels in one row"
         force[lt.level] = got.copy()
     raise AssertionError("replay did not converge")
 
 
-def check_groups(trees, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, n_kv, dtype,
-                 all_out_rms=None):
+def check_groups(trees, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, n_kv, dtype):
     """rows: list of (query index, KV head g); trees: {g: oracle tree of head g};
     Q [n][Hq][d] host fp32; gpu_out [n][Hq][d]; dbg rows are i * n_kv + g.  Asserts
-    selection parity per group and the output tolerance on every head of the group."""
+    selection parity per group, the keys-read count and the output bars on every
+    head of the group."""
     Hq = Q.shape[1]
     G = Hq // n_kv
     sel = dbg["selected"].cpu().numpy()
@@ -164,16 +200,10 @@ def check_groups(trees, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, n_kv, d
         res, ex = check_group(trees[g], Q[qi, g * G:(g + 1) * G], n_ctx_of(qi), k, base, scale,
                               sel[r])
         excused += ex > 0
-        if ex == 0:
-            assert nkeys[r] == sum(len(t.cand) for t in res.levels), (qi, g, nkeys[r])
+        assert nkeys[r] == sum(len(t.cand) for t in res.levels), (qi, g, nkeys[r])
         want.append(res.out)
         got.append(gout[qi, g * G:(g + 1) * G])
     want, got = np.concatenate(want), np.concatenate(got)
-    err = np.abs(got - want).max()
-    if dtype == "f32":
-        tol = 1e-5
-    else:
-        rms = all_out_rms if all_out_rms is not None else float(np.sqrt(np.mean(want ** 2)))
-        tol = 2e-2 * rms
-    assert err <= tol, f"max abs error {err:.3g} > {tol:.3g}"
-    return {"max_abs_err": float(err), "tol": tol, "excused_rows": excused, "rows": len(rows)}
+    err, tol, rel = _check_out(got - want, want, dtype)
+    return {"max_abs_err": err, "tol": tol, "err_over_rms": rel, "excused_rows": excused,
+            "rows": len(rows)}

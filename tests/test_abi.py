@@ -253,3 +253,32 @@ def test_dense_and_distill_validate_before_any_hip_call():
         with pytest.raises(R.RecsaError) as e:
             fn()
         assert e.value.status == status, (i, str(e.value))
+
+
+def test_path_field_sizes_and_runs_alike():
+    """recsa_params.path picks the layout of prefill and backward work; the sizing
+    calls read the same field as the running calls, and a parent-major request the
+    path cannot serve is refused on the host."""
+    fake = 1 << 20
+    rows = 4096 * 32
+    auto = _p()
+    assert R.recsa_workspace_bytes(auto, rows) > 0                       # parent-major by default
+    assert R.recsa_workspace_bytes(_p(path="rowwise"), rows) == 0
+    assert R.recsa_workspace_bytes(_p(path="parent_major"), 64) > 0      # forced at few rows
+    summaries = R.recsa_backward_workspace_bytes(_p(path="rowwise"), 4096)
+    assert R.recsa_backward_workspace_bytes(auto, 4096) > summaries
+    assert R.recsa_backward_workspace_bytes(_p(path="parent_major"), 8) > summaries
+    bad = _p()
+    bad.path = 7
+    assert R.recsa_tree_bytes(bad) == 0
+    # fp32 storage and fanouts above 128 have no parent-major layout
+    for p in (_p(store="f32", path="parent_major", capacity=1000),
+              _p(fanout_b=200, path="parent_major", capacity=100000)):
+        assert R.recsa_workspace_bytes(p, rows) == 0
+        d = R.recsa_tree_desc(fake, fake, fake, fake, 900)
+        with pytest.raises(R.RecsaError) as e:
+            R.recsa_prefill(p, d, fake, 4, fake, ws=fake)
+        assert e.value.status == R.RECSA_ERR_UNSUPPORTED
+        with pytest.raises(R.RecsaError) as e:
+            R.recsa_backward(p, d, fake, 2, 0, fake, fake, fake, fake, fake, ws=fake)
+        assert e.value.status == R.RECSA_ERR_UNSUPPORTED

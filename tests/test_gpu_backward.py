@@ -53,31 +53,29 @@ def _tol(ref, dtype):
 
 
 @pytest.mark.parametrize("name,L,n_kv,n_q,n,causal,kw", CASES)
-def test_backward(name, L, n_kv, n_q, n, causal, kw, monkeypatch):
-    monkeypatch.setenv("RECSA_BACKWARD_PATH", "rowwise")
+def test_backward(name, L, n_kv, n_q, n, causal, kw):
     _say(f"case backward {name} L={L} n_kv={n_kv} n_q={n_q} n={n} causal={causal} {kw}")
-    _run(name, L, n_kv, n_q, n, causal, kw)
+    _run(name, L, n_kv, n_q, n, causal, kw, "rowwise")
 
 
 @pytest.mark.parametrize("name,L,n_kv,n_q,n,causal,kw", TILED_CASES)
-def test_backward_tiled(name, L, n_kv, n_q, n, causal, kw, monkeypatch):
-    monkeypatch.setenv("RECSA_BACKWARD_PATH", "tiled")
+def test_backward_tiled(name, L, n_kv, n_q, n, causal, kw):
     _say(f"case backward tiled {name} L={L} n_kv={n_kv} n_q={n_q} n={n} causal={causal} {kw}")
-    _run(name, L, n_kv, n_q, n, causal, kw)
+    _run(name, L, n_kv, n_q, n, causal, kw, "parent_major")
 
 
-def test_backward_default_path(monkeypatch):
+def test_backward_default_path():
     """256 rows of a causal chunk: the library's own choice (the parent-major path)."""
-    monkeypatch.delenv("RECSA_BACKWARD_PATH", raising=False)
     _say("case backward default path qwen3_4b_131k L=9000 n=8 causal")
-    _run("qwen3_4b_131k", 9000, 8, 32, 8, True, {})
+    _run("qwen3_4b_131k", 9000, 8, 32, 8, True, {}, "auto")
 
 
-def _run(name, L, n_kv, n_q, n, causal, kw):
+def _run(name, L, n_kv, n_q, n, causal, kw, path):
     w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=0, n_kv=n_kv, n_q=n_q, **kw)
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
     layer = P.make_layer(w, capacity=L)
+    layer.set_path(path)
     P.load_cache(layer, K, V, W, L, w.dtype)
     layer.build(L)
     rng = np.random.default_rng(L + n)
@@ -117,21 +115,21 @@ def _run(name, L, n_kv, n_q, n, causal, kw):
     _say("backward", {k: f"{e:.2e}/{t:.2e}" for k, (e, t) in rep.items()})
 
 
-@pytest.mark.parametrize("path,dtype,nq,L,b", [("rowwise", "f32", 2, 2000, 16), ("tiled", "bf16", 64, 2000, 16),
-                                              ("rowwise", "bf16", 2, 10, 16), ("tiled", "bf16", 8, 10, 16),
-                                              ("rowwise", "f32", 2, 3000, 40), ("tiled", "bf16", 64, 3000, 40)])
-def test_backward_overwrites_given_gradients(monkeypatch, path, dtype, nq, L, b):
+@pytest.mark.parametrize("path,dtype,nq,L,b", [("rowwise", "f32", 2, 2000, 16), ("parent_major", "bf16", 64, 2000, 16),
+                                              ("rowwise", "bf16", 2, 10, 16), ("parent_major", "bf16", 8, 10, 16),
+                                              ("rowwise", "f32", 2, 3000, 40), ("parent_major", "bf16", 64, 3000, 40)])
+def test_backward_overwrites_given_gradients(path, dtype, nq, L, b):
     """dk, dv (tokens [0, length)) and dw are written whatever the buffers held; rows
     from the length on are left alone.  Row-wise (two phases around the tree pass) and
     parent-major in one pass of rows (the tree pass between the levels), each also with
     fewer tokens than one node (no tree pass at all) and with a fanout above 32 (the
     general tree kernel writes the children, two 32-child chunks per parent)."""
-    monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
     cap = L + 100
     w = synth.scaled(synth.WORKLOADS["tiny_f32_4k"], L, prefill_n=0, n_q=2, dtype=dtype, b=b)
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
     layer = P.make_layer(w, capacity=cap)
+    layer.set_path(path)
     P.load_cache(layer, K, V, W, L, w.dtype)
     layer.build(L)
     _say(f"case overwrite {path} {dtype} nq={nq} L={L} b={b}")
@@ -149,13 +147,14 @@ def test_backward_overwrites_given_gradients(monkeypatch, path, dtype, nq, L, b)
     torch.testing.assert_close(twice["dq"], once["dq"], rtol=1e-5, atol=1e-6)
 
 
-def test_backward_tiled_full_131k(monkeypatch):
+def test_backward_tiled_full_131k():
     """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 4224
     queries (135168 rows: the parent-major path's two passes of at most 131072 rows):
     the parent-major backward against the row-wise one (itself pinned to the oracle
     above).  Rows whose selections differ between the two (a near-tie under the
-    parent-major forward's split-bf16 logits) get dO = 0, which removes them from
-    every gradient on both paths; all four gradients must then agree to the bf16 bar
+    parent-major forward's split-bf16 logits) are each checked against the oracle
+    (both selections valid under the near-tie rule), then get dO = 0, which removes
+    them from every gradient on both paths; all four gradients must then agree to the bf16 bar
     (the parent-major run writes over buffers that held other values).  Sampled rows' dq, in both passes, is also checked against the oracle on the GPU's
     selections."""
     w = synth.WORKLOADS["qwen3_4b_131k"]
@@ -172,23 +171,37 @@ def test_backward_tiled_full_131k(monkeypatch):
     dO = torch.from_numpy(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)).cuda()
 
     def run(path, d, grads=None):
-        monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
+        layer.set_path(path)
         g, dbg = layer.backward(q, d, causal=True, debug=True, grads=grads)
         torch.cuda.synchronize()
         return g, dbg
 
-    gt, dt = run("tiled", dO)
+    gt, dt = run("parent_major", dO)
     gr, dr = run("rowwise", dO)
     bad = (dt["selected"] != dr["selected"]).flatten(1).any(1)
     _say(f"rows with another selection: {int(bad.sum())} of {bad.numel()}")
     assert int(bad.sum()) <= 32, "too many rows select differently for near-ties alone"
+    # each such row: both paths' selections against the oracle (a near tie of the
+    # oracle's logits, every disputed candidate inside the tie band)
+    G = w.n_q // w.n_kv
+    sel_t, sel_r = dt["selected"].cpu().numpy(), dr["selected"].cpu().numpy()
+    trees = {}
+    for r in torch.nonzero(bad).flatten().tolist():
+        i, h = divmod(r, w.n_q)
+        g = h // G
+        if g not in trees:
+            trees[g] = P.head_tree(K, V, W, g, w, L)
+        for sel_ in (sel_t, sel_r):
+            _, ex = P.check_row(trees[g], Q[i, h].astype(np.float64), 0, L - n + i + 1, w.k, w.rope_base,
+                                w.softmax_scale, sel_[r])
+        _say(f"row {r}: both selections valid under the near-tie rule")
     dO2 = dO.clone().view(-1, w.d)
     dO2[bad] = 0
     dO2 = dO2.view_as(dO)
     # two passes of rows clear the token gradients first: start the parent-major run
     # from buffers that hold something else
     junk = {k: torch.full_like(gt[k], -3.25) for k in ("dk", "dv", "dw")}
-    gt, dt = run("tiled", dO2, junk)
+    gt, dt = run("parent_major", dO2, junk)
     gr, _ = run("rowwise", dO2)
     rep = {}
     for key in ("dq", "dk", "dv", "dw"):
@@ -200,10 +213,8 @@ def test_backward_tiled_full_131k(monkeypatch):
     _say("tiled vs rowwise", rep)
     # sampled rows' dq against the oracle on the parent-major path's selections
     sel = dt["selected"].cpu().numpy()
-    G = w.n_q // w.n_kv
     dq_gpu = gt["dq"].cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
     dOn = dO2.cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
-    trees = {}
     refs, gots = [], []
     for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, 131072 + 5, n * w.n_q - 1):
         if bool(bad[r]):

@@ -80,10 +80,9 @@ def test_distill_steps_follow_the_oracle():
                             sel[i * 2 + h])
                 N = O.level_sizes(w.L, w.b)
                 force[(i, h)] = {l: sel[i * 2 + h, l - 1][sel[i * 2 + h, l - 1] >= 0] for l in range(1, len(N))}
-        want_loss, g = O.distill_loss(tree, Q.astype(np.float64), T, w.k, w.rope_base, w.softmax_scale,
-                                      force=force)
-        velo = mu * velo + g["dw"]
-        Wo = Wo - lr * velo
+        want_loss, Wo, velo = O.distill_step(K, V, Wo, w.b, "f32", w.pool_scale, w.L,
+                                             Q.astype(np.float64), T, w.k, w.rope_base,
+                                             w.softmax_scale, lr, mu, velo, force=force)
         layer.distill_step(q, teacher, lr, mu, vel, loss)
         torch.cuda.synchronize()
         got_loss = float(loss.item())

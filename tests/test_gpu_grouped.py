@@ -53,9 +53,8 @@ def test_grouped_decode(name, L, n_kv, n_q, kw):
     heads = list(range(n_kv)) if n_kv <= 2 else [0, n_kv - 1]
     trees = {g: P.head_tree(K, V, W, g, w, L) for g in heads}
     rows = [(i, g) for i in range(B) for g in heads]
-    rms = float(np.sqrt(np.mean(P.to_host(out) ** 2)))
     rep = P.check_groups(trees, Q.astype(np.float64), rows, lambda i: L, w.k, w.rope_base,
-                         w.softmax_scale, out, dbg, n_kv, w.dtype, all_out_rms=rms)
+                         w.softmax_scale, out, dbg, n_kv, w.dtype)
     _say("grouped", rep)
 
 

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_recsa_amd as R
 import synth
 from oracle import recsa as O
 from tests import parity as P
@@ -16,6 +17,19 @@ pytestmark = pytest.mark.gpu
 
 def _say(*a):
     print(*a, flush=True)
+
+
+def _bf16_close(a, b, what):
+    """bf16 summaries: the two sides round an fp32 and an f64 value, so an element may
+    land one bf16 ulp away, and a parent pooled from a child that rounded the other
+    way moves by at most that child's ulp.  Bound: one ulp of the element plus half an
+    ulp of the node's largest element; at most 1% of the elements differ at all."""
+    if a.size == 0:
+        return
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
+    row = 2.0 ** -8 * np.abs(b).max(axis=1, keepdims=True)
+    assert np.all(np.abs(a - b) <= ulp + row), (what, np.abs(a - b).max())
+    assert np.mean(a != b) < 1e-2, (what, np.mean(a != b))
 
 
 def _tree_levels_match(layer, tree, w, L, exact_rel):
@@ -29,15 +43,8 @@ def _tree_levels_match(layer, tree, w, L, exact_rel):
                 np.testing.assert_allclose(ok, tree.keys[l][g], rtol=0, atol=exact_rel)
                 np.testing.assert_allclose(ov, tree.vals[l][g], rtol=0, atol=exact_rel)
             else:
-                # bf16 summaries: the two sides round an fp32 and an f64 value, so an
-                # element may land one bf16 ulp away, and a parent pooled from a child
-                # that rounded the other way moves by at most that child's ulp.  Bound:
-                # one ulp of the element plus half an ulp of the node's largest element.
-                for a, b in ((ok, tree.keys[l][g]), (ov, tree.vals[l][g])):
-                    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
-                    row = 2.0 ** -8 * np.abs(b).max(axis=1, keepdims=True)
-                    assert np.all(np.abs(a - b) <= ulp + row), (l, g, np.abs(a - b).max())
-                    assert np.mean(a != b) < 1e-2, (l, g, np.mean(a != b))
+                _bf16_close(ok, tree.keys[l][g], (l, g, "key"))
+                _bf16_close(ov, tree.vals[l][g], (l, g, "value"))
 
 
 def _decode_case(w, B, k=None, L=None, out="f32", check_tree=True):
@@ -113,6 +120,9 @@ def test_bf16_decode_needles_small():
 
 @pytest.mark.parametrize("chunks", [[1, 31, 32, 1000, 3], [4096], [0, 5000]])
 def test_append_equals_build(chunks):
+    """Appending in chunks gives the tree of a whole build, bit for bit, and every node
+    the appends created equals the oracle's incremental extension of its tree (within
+    the bf16 rounding bound of the build check)."""
     w = synth.scaled(synth.WORKLOADS["qwen3_4b_524k"], 8192, prefill_n=sum(chunks))
     L0, Lt = w.L, w.L + sum(chunks)
     K, V = synth.gen_kv(w, 0, Lt)
@@ -123,12 +133,14 @@ def test_append_equals_build(chunks):
     inc = P.make_layer(w, capacity=Lt)
     P.load_cache(inc, K, V, W, L0, w.dtype)
     inc.build(L0)
+    tree = O.build_tree(K, V, W, w.b, w.dtype, w.pool_scale, L0)
     at = L0
     for n in chunks:
         kn = P.to_device(np.ascontiguousarray(K[:, at:at + n].transpose(1, 0, 2)), w.dtype)
         vn = P.to_device(np.ascontiguousarray(V[:, at:at + n].transpose(1, 0, 2)), w.dtype)
         inc.append(kn, vn)
         at += n
+        tree = O.extend_tree(tree, K, V, at)
     torch.cuda.synchronize()
     assert inc.length == Lt
     assert torch.equal(inc.k_cache, full.k_cache) and torch.equal(inc.v_cache, full.v_cache)
@@ -137,6 +149,18 @@ def test_append_equals_build(chunks):
         fk, fv = full.level(l)
         ik, iv = inc.level(l)
         assert torch.equal(fk[:, :n], ik[:, :n]) and torch.equal(fv[:, :n], iv[:, :n]), l
+    # the appended nodes (those past the build's) against the oracle's extension
+    new_nodes = 0
+    for l in range(1, len(tree.keys)):
+        n0 = L0 // w.b ** l
+        n1 = Lt // w.b ** l
+        ik, iv = inc.level(l)
+        for g in range(w.n_kv):
+            _bf16_close(P.to_host(ik[g, n0:n1]), tree.keys[l][g][n0:n1], (l, g, "key"))
+            _bf16_close(P.to_host(iv[g, n0:n1]), tree.vals[l][g][n0:n1], (l, g, "value"))
+        new_nodes += n1 - n0
+    _say(f"appended nodes checked against the oracle: {new_nodes} per KV head")
+    assert new_nodes > 0
 
 
 PREFILL_CASES = [
@@ -153,19 +177,28 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["tiled", "rowwise"])
+@pytest.mark.parametrize("path", ["parent_major", "rowwise"])
 @pytest.mark.parametrize("name,L,n,kw", PREFILL_CASES)
-def test_prefill_small(name, L, n, kw, path, monkeypatch):
+def test_prefill_small(name, L, n, kw, path):
     """Causal prefill against the oracle, parent-major (bf16 MFMA, the default for
-    large bf16 chunks) and one workgroup per row (fp32 storage always runs this way)."""
-    monkeypatch.setenv("RECSA_PREFILL_PATH", path)
+    large bf16 chunks) and one workgroup per row (fp32 storage always runs this way:
+    asking it for the parent-major layout is refused)."""
     w = synth.scaled(synth.WORKLOADS[name], L, prefill_n=n, **kw)
+    if path == "parent_major" and w.dtype == "f32":
+        layer = P.make_layer(w, capacity=L + n)
+        layer.set_path(path)
+        layer.build(1)
+        with pytest.raises(R.RecsaError) as e:
+            layer.prefill(P.to_device(synth.prefill_queries(w, 1), w.dtype))
+        assert e.value.status == R.RECSA_ERR_UNSUPPORTED
+        return
     _say(f"case prefill {name} L={L} n={n} {kw} path={path}")
     Lt = L + n
     K, V = synth.gen_kv(w, 0, Lt)
     W = synth.pool_w(w)
     Q = synth.prefill_queries(w, n)
     layer = P.make_layer(w, capacity=Lt)
+    layer.set_path(path)
     P.load_cache(layer, K, V, W, L, w.dtype)
     layer.build(L)
     layer.append(P.to_device(np.ascontiguousarray(K[:, L:].transpose(1, 0, 2)), w.dtype),

@@ -1,8 +1,8 @@
 """GPU parity over a seeded sweep of small random configurations: fanout, budget,
 context length, head dim, storage, KV heads and group size drawn at random (fixed
 seed), each call of the path checked against the oracle on the same inputs:
-decode, grouped decode, causal prefill (row-wise and parent-major), and the
-backward (row-wise and parent-major).  The shapes reach what the fixed cases do
+decode, grouped decode, causal prefill (row-wise, and parent-major for bf16
+storage), and the backward (the same two layouts).  The shapes reach what the fixed cases do
 not: fanouts from 2 (deep trees) to 47, budgets from 1 to 9 (levels where every
 candidate is kept), contexts shorter than one node, odd head groupings."""
 import numpy as np
@@ -55,7 +55,7 @@ def _tol(ref, dtype):
 
 
 @pytest.mark.parametrize("c", CONFIGS, ids=[f"cfg{c['idx']}" for c in CONFIGS])
-def test_sweep(c, monkeypatch):
+def test_sweep(c):
     L = c["L"]
     nP = min(c["nP"], L)
     w = synth.scaled(synth.WORKLOADS[c["base"]], L, prefill_n=0, n_kv=c["n_kv"],
@@ -90,8 +90,9 @@ def test_sweep(c, monkeypatch):
     # causal prefill of the last nP tokens' queries, both paths
     Qp = synth.to_storage(rng.standard_normal((nP, w.n_q, w.d)).astype(np.float32), w.dtype)
     rows = [(j, h) for j in range(nP) for h in range(w.n_q)]
-    for path in ("rowwise", "tiled"):
-        monkeypatch.setenv("RECSA_PREFILL_PATH", path)
+    paths = ("rowwise", "parent_major") if w.dtype == "bf16" else ("rowwise",)
+    for path in paths:
+        layer.set_path(path)
         out_p, dbg_p = layer.prefill(P.to_device(Qp, w.dtype), debug=True)
         torch.cuda.synchronize()
         rep = P.check_rows(tree, Qp.astype(np.float64), rows, lambda j: L - nP + j + 1, w.k, w.rope_base,
@@ -102,8 +103,8 @@ def test_sweep(c, monkeypatch):
     for causal, n in ((False, c["B"]), (True, nP)):
         Q = Qd if not causal else Qp
         dO = rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)
-        for path in ("rowwise", "tiled"):
-            monkeypatch.setenv("RECSA_BACKWARD_PATH", path)
+        for path in paths:
+            layer.set_path(path)
             grads, bdbg = layer.backward(P.to_device(Q, w.dtype), torch.from_numpy(dO).cuda(), causal=causal,
                                          debug=True)
             torch.cuda.synchronize()
