@@ -27,8 +27,11 @@ from oracle import recsa as O
 TIE_REL = 1e-3
 # Regression bound for bf16 storage, relative to the oracle's output RMS.  One
 # summary entry with a wrong value row moves a row's output by about its softmax
-# weight times the row's difference, ~1e-3 x RMS at the workloads' shapes.
-REG_REL = 2e-4
+# weight times the row's difference, ~1e-3 x RMS at the workloads' shapes.  The
+# GPU path reaches at most 2.1e-4 x RMS (a fanout-3 tree of ten levels, where
+# summaries that round one bf16 ulp away from the oracle's are most frequent) and
+# below 1e-4 x RMS on every workload shape.
+REG_REL = 5e-4
 
 
 def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
