@@ -5,11 +5,18 @@ build the tree over the L cached tokens, decode a batch at length L (per
 query head, then again with one selection per KV group), the backward of that
 decode batch (selection fixed; a synthetic output gradient), append the
 prefill chunk (growing the tree) and run the causal prefill of that chunk.
-Each call is timed with HIP events on the stream it is launched on.  The
-roofline line follows the forward calls.
+Each call is timed with HIP events on the stream it is launched on; times are
+the median (with p10 and p90) over the timed steps.  The roofline line follows
+the dominant forward call.
 
-Prints one JSON line: value = decode queries/s; prefill tokens/s, tree-build
-bandwidth and the roofline fractions of every kernel ride along.
+The headline workload is the 524K-token Qwen3-4B-shaped layer.  The other
+workloads of the path (131K; 1M with block drift; 2M) are measured after it in
+the same run, each with its own build, decode batches and (1M) append + prefill,
+and reported under "configs".  Before any GPU work, the oracle is timed on the
+host's cores (the CPU baseline).
+
+Prints one JSON line: value = decode queries/s at 524K; prefill tokens/s,
+tree-build bandwidth and the roofline fractions of every call ride along.
 """
 from __future__ import annotations
 
@@ -132,36 +139,124 @@ def algorithmic(w, B):
                 decode_entries_per_row=kd + vd)
 
 
-def cpu_baseline(w, B, seconds=15.0, queries=None):
-    """The oracle (never tuned) on the host: tree over one KV head, then decode
-    rows of that head until about `seconds` have passed."""
+def cpu_cores():
+    """Host threads the oracle may use: the process's CPU affinity, capped by the
+    thread budget the environment sets (OMP_NUM_THREADS)."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "") or aff)
+    except ValueError:
+        cap = aff
+    return max(1, min(aff, cap))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+# state the forked oracle workers inherit (set before the fork, read-only after)
+_CPU = {}
+
+
+def _oracle_rows(args):
+    """Run oracle descents for `seconds`: kind 'decode' (rows of the decode batch at
+    length L) or 'prefill' (rows of the causal chunk), starting at row `start` and
+    striding by `stride`.  Returns the number of rows done and the time taken."""
+    from oracle import recsa as O
+    kind, start, stride, seconds = args
+    st = _CPU
+    w = st["w"]
+    G = w.n_q // w.n_kv
+    done = 0
+    r = start
+    t0 = time.perf_counter()
+    while True:
+        if kind == "decode":
+            i, h = divmod(r % (st["B"] * G), G)
+            O.descend(st["tree"], st["Qd"][i, h], 0, w.L, w.k, w.rope_base, w.softmax_scale)
+        else:
+            j, h = divmod(r % (w.prefill_n * G), G)
+            O.descend(st["tree_p"], st["Qp"][j, h], 0, w.L + j + 1, w.k, w.rope_base,
+                      w.softmax_scale)
+        done += 1
+        r += stride
+        if time.perf_counter() - t0 > seconds:
+            break
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, B, seconds=20.0, queries=None):
+    """The oracle (never tuned) on the host: the tree of KV head 0, then decode rows
+    (and causal-prefill rows when the workload has a chunk) of that head's query
+    heads, on one thread and on every core (independent rows over forked worker
+    processes).  Runs before the process touches the GPU, so the workers fork a
+    process without GPU state.  A query (token) counts n_q rows."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
     import synth
     from oracle import recsa as O
+    cores = cpu_cores()
+    kinds = ["decode"] + (["prefill"] if w.prefill_n else [])
+    per = seconds / (2 * len(kinds))
     with threadpool_limits(1):
-        K, V = synth.gen_kv(w, 0, w.L, heads=[0])
+        Lt = w.L + w.prefill_n
+        K, V = synth.gen_kv(w, 0, Lt, heads=[0])
         W = synth.pool_w(w)[:1]
-        Q = synth.decode_queries(w, B) if queries is None else queries
         t0 = time.perf_counter()
         tree = O.build_tree(K, V, W, w.b, w.dtype, w.pool_scale, w.L)
         t_build = time.perf_counter() - t0
-        rows = 0
-        t0 = time.perf_counter()
-        G = w.n_q // w.n_kv
-        while True:
-            i, h = divmod(rows, G)
-            O.descend(tree, Q[i % B, h].astype(np.float64), 0, w.L, w.k, w.rope_base,
-                      w.softmax_scale)
-            rows += 1
-            if time.perf_counter() - t0 > seconds:
-                break
-        t_dec = time.perf_counter() - t0
-    return {
-        "value": rows / t_dec / w.n_q, "unit": "decode queries/s", "cores": 1, "kind": "oracle",
-        "sample": f"{rows} decode rows (query x head) of KV head 0 at L={w.L}, single thread, "
-                  f"after building that head's tree in {t_build:.1f} s; queries/s = rows/s / {w.n_q}",
+        Qd = synth.decode_queries(w, B) if queries is None else queries
+        _CPU.update(w=w, B=B, tree=tree, Qd=np.asarray(Qd, np.float64))
+        if w.prefill_n:
+            _CPU.update(tree_p=O.build_tree(K, V, W, w.b, w.dtype, w.pool_scale, Lt),
+                        Qp=synth.prefill_queries(w).astype(np.float64))
+        del K, V
+        res = {}
+        for kind in kinds:
+            n1, t1 = _oracle_rows((kind, 0, 1, per))
+            with mp.get_context("fork").Pool(cores) as pool:
+                t0 = time.perf_counter()
+                outs = pool.map(_oracle_rows, [(kind, c, cores, per) for c in range(cores)])
+                tall = time.perf_counter() - t0
+            nall = sum(o[0] for o in outs)
+            res[kind] = {"one_thread": n1 / t1 / w.n_q, "all_cores": nall / tall / w.n_q,
+                         "rows_one_thread": n1, "rows_all_cores": nall}
+    _CPU.clear()
+    out = {
+        "value": res["decode"]["all_cores"], "unit": "decode queries/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "decode_queries_per_s": {"one_thread": res["decode"]["one_thread"],
+                                 "all_cores": res["decode"]["all_cores"]},
+        "build_tokens_per_s_one_thread": w.L / t_build,
+        "sample": (f"KV head 0 of the workload at L={w.L}: its tree built once ({t_build:.2f} s, one "
+                   f"thread), then decode rows (query x head of that KV head) for {per:.0f} s on one "
+                   f"thread ({res['decode']['rows_one_thread']} rows) and {per:.0f} s on {cores} forked "
+                   f"workers ({res['decode']['rows_all_cores']} rows); rows/s / {w.n_q} = queries/s"),
     }
+    if w.prefill_n:
+        out["prefill_tokens_per_s"] = {"one_thread": res["prefill"]["one_thread"],
+                                       "all_cores": res["prefill"]["all_cores"]}
+        out["sample"] += (f"; causal-prefill rows of the {w.prefill_n}-query chunk over the tree at "
+                          f"L+{w.prefill_n} for {per:.0f} s each way ({res['prefill']['rows_one_thread']} / "
+                          f"{res['prefill']['rows_all_cores']} rows); rows/s / {w.n_q} = tokens/s")
+    return out
+
+
+def timing(samples):
+    """Median, p10, p90 and mean of per-launch times (ms)."""
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
 
 
 def run_serve(args, name):
@@ -175,6 +270,10 @@ def run_serve(args, name):
 
     seqs, Q = synth.serve_batch(name)
     w0 = seqs[0]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(seqs[0], 1, args.cpu_seconds, queries=Q[:1])
+        cpu["sample"] += " (sequence 0 of the batch)"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cap = max(w.L for w in seqs)
@@ -220,7 +319,7 @@ def run_serve(args, name):
         evs.append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = timing([a.elapsed_time(b) for a, b in evs])["median"]
     row_b = w0.d * (2 if w0.dtype == "bf16" else 4)
     nbytes = sum(w.n_q * sum(row_entries(w.L, w.b, w.k)) * row_b for w in seqs)
     ach = nbytes / ms / 1e6
@@ -241,9 +340,8 @@ def run_serve(args, name):
                      "traffic": None if tr is None else tr["fetch"] + tr["write"]},
         "setup_s": t_setup,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(seqs[0], 1, args.cpu_seconds, queries=Q[:1])
-        res["cpu_baseline"]["sample"] += " (sequence 0 of the batch)"
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
@@ -307,7 +405,7 @@ def run_distill(args, name):
         evs.append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = timing([a.elapsed_time(b) for a, b in evs])["median"]
     lv = losses.cpu().numpy().tolist()
     res = {
         "metric": "pooler distillation steps/s (decode + loss + dw + update + tree rebuild per step)",
@@ -371,7 +469,7 @@ def run_backward_chunk(args, name, n):
         evs.append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = timing([a.elapsed_time(b) for a, b in evs])["median"]
     res = {
         "metric": "causal-chunk backward query tokens/s (dq, dk, dv, dw; selection fixed)",
         "value": n / (ms * 1e-3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -385,15 +483,176 @@ def run_backward_chunk(args, name, n):
     print(json.dumps(res), flush=True)
 
 
+# Workloads measured after the headline in a default run (each with its own
+# build, decode batches and, where it has a chunk, append + prefill).
+OTHER_WORKLOADS = ["qwen3_4b_131k", "qwen3_4b_1m_drift", "qwen3_4b_2m"]
+PRECISION = ("fp32 arithmetic on bf16 storage; the parent-major prefill's q.k and P.V "
+             "products are split-bf16 MFMA (hi + lo halves, about 16 significant bits) "
+             "with fp32 accumulation")
+
+
+def dev_store(x, dtype, dev):
+    import synth
+    import torch
+    bits = synth.storage_bits(x, dtype)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def measure_workload(w, batches, steps, warmup, backward=True):
+    """Time every call of the path on one workload: build, decode at each batch,
+    grouped decode (largest batch), the decode batch's backward (optional), append
+    + prefill (when the workload has a chunk).  Returns per-op timings (ms) and the
+    algorithmic-roofline figures."""
+    import torch
+
+    import long_context_recsa_amd as R
+    import synth
+
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    Lt = w.L + w.prefill_n
+    K, V = synth.gen_kv(w, 0, Lt)
+    W = synth.pool_w(w)
+    Bmax = max(batches)
+    Qd = synth.decode_queries(w, Bmax)
+    p = R.make_params(w.n_kv, w.n_q, w.d, w.b, w.k, Lt, store=w.dtype, out="f32",
+                      rope_base=w.rope_base, softmax_scale=w.softmax_scale, pool_scale=w.pool_scale)
+    layer = R.RecsaLayer(p, dev)
+    for g in range(w.n_kv):
+        layer.k_cache[g, :w.L].copy_(dev_store(K[g, :w.L], w.dtype, dev))
+        layer.v_cache[g, :w.L].copy_(dev_store(V[g, :w.L], w.dtype, dev))
+    layer.pool_w.copy_(torch.from_numpy(W))
+    q_dec = {B: dev_store(Qd[:B], w.dtype, dev) for B in batches}
+    out_dec = {B: torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev) for B in batches}
+    out_grp = torch.empty_like(out_dec[Bmax])
+    if w.prefill_n:
+        k_new = dev_store(np.ascontiguousarray(K[:, w.L:].transpose(1, 0, 2)), w.dtype, dev)
+        v_new = dev_store(np.ascontiguousarray(V[:, w.L:].transpose(1, 0, 2)), w.dtype, dev)
+        q_pre = dev_store(synth.prefill_queries(w), w.dtype, dev)
+        out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
+    if backward:
+        # the output gradient is synthetic; every step writes the same gradient buffers
+        d_out = torch.from_numpy(np.random.default_rng(5).standard_normal((Bmax, w.n_q, w.d))
+                                 .astype(np.float32)).to(dev)
+        grads = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
+                 "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
+                 "dw": torch.zeros((w.n_kv, w.d), dtype=torch.float32, device=dev)}
+    del K, V
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    ops = (["build"] + [f"decode_B{B}" for B in batches] + ["decode_grouped"]
+           + (["backward"] if backward else []) + (["append", "prefill"] if w.prefill_n else []))
+    ev = {o: [] for o in ops}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+        marks[0].record()
+        i = 1
+        layer.build(w.L)
+        marks[i].record(); i += 1
+        for B in batches:
+            layer.decode(q_dec[B], out=out_dec[B])
+            marks[i].record(); i += 1
+        layer.decode_grouped(q_dec[Bmax], out=out_grp)
+        marks[i].record(); i += 1
+        if backward:
+            layer.backward(q_dec[Bmax], d_out, grads=grads)
+            marks[i].record(); i += 1
+        if w.prefill_n:
+            layer.append(k_new, v_new)
+            marks[i].record(); i += 1
+            layer.prefill(q_pre, out=out_pre)
+            marks[i].record(); i += 1
+        if record:
+            for j, o in enumerate(ops):
+                ev[o].append((marks[j], marks[j + 1]))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {o: timing([a.elapsed_time(b) for a, b in ev[o]]) for o in ops}
+    del layer
+    torch.cuda.empty_cache()
+
+    kern = {}
+    alg = {B: algorithmic(w, B) for B in batches}
+    a0 = alg[Bmax]
+    med = {o: ms[o]["median"] for o in ops}
+    kern["tree_build"] = {"bound": "hbm", "bytes": a0["build"], "ms": med["build"],
+                          "achieved": a0["build"] / med["build"] / 1e6, "unit": "GB/s"}
+    for B in batches:
+        kern[f"decode_B{B}"] = {"bound": "hbm", "bytes": alg[B]["decode"], "ms": med[f"decode_B{B}"],
+                                "achieved": alg[B]["decode"] / med[f"decode_B{B}"] / 1e6, "unit": "GB/s"}
+    kern["decode_grouped"] = {"bound": "hbm", "bytes": a0["decode_grouped"], "ms": med["decode_grouped"],
+                              "achieved": a0["decode_grouped"] / med["decode_grouped"] / 1e6, "unit": "GB/s"}
+    if backward:
+        # the backward's bytes depend on which nodes the rows read (its tree pass writes the
+        # fp32 gradients of every token), so its floor is the rows' gathers plus the token
+        # gradients written once: see backward_bytes
+        bb = backward_bytes(w, Bmax)
+        kern["backward"] = {"bound": "hbm", "bytes": bb, "ms": med["backward"],
+                            "achieved": bb / med["backward"] / 1e6, "unit": "GB/s"}
+    if w.prefill_n:
+        # the chunk's rows share parents, so the HBM floor is reading every reachable K/V row,
+        # tree node and query once and writing the output; the bytes the rows would gather
+        # one by one ride along for context
+        kern["prefill"] = {"bound": "hbm", "bytes": a0["prefill_read_once"], "flops": a0["prefill_flops"],
+                           "ms": med["prefill"],
+                           "achieved": a0["prefill_read_once"] / med["prefill"] / 1e6, "unit": "GB/s",
+                           "per_row_gather_bytes": a0["prefill"],
+                           "mfma_frac": a0["prefill_flops"] / med["prefill"] / 1e9 / BF16_PEAK_TFLOPS}
+        kern["append"] = {"bound": "hbm", "bytes": a0["append"], "ms": med["append"],
+                          "achieved": a0["append"] / med["append"] / 1e6, "unit": "GB/s"}
+    for name_, v in kern.items():
+        op = "decode" if name_.startswith("decode_B") else name_
+        t_ = measured_traffic(w.name, op)
+        v["traffic"] = None if t_ is None else t_["fetch"] + t_["write"]
+        v["frac"] = v["achieved"] / HBM_PEAK_GBS
+    res = {
+        "L": w.L, "storage": w.dtype, "b": w.b, "k": w.k, "decode_batches": list(batches),
+        "prefill_chunk": w.prefill_n, "ms": ms, "kernels": kern,
+        "decode_queries_per_s": {f"B={B}": B / (med[f"decode_B{B}"] / 1e3) for B in batches},
+        "grouped_decode_queries_per_s": Bmax / (med["decode_grouped"] / 1e3),
+        "prefill_tokens_per_s": (w.prefill_n / ((med["append"] + med["prefill"]) / 1e3)
+                                 if w.prefill_n else None),
+        "setup_s": t_setup, "timed_wall_s": wall,
+    }
+    return res, wall
+
+
+def backward_bytes(w, B):
+    """Read-once floor of the decode batch's backward: the forward's gathers of every
+    row (keys and values read again), the fp32 token gradients dk, dv of every cached
+    token written once (the tree pass writes them all), and the summaries' fp32
+    gradients written and read once."""
+    esz = 2 if w.dtype == "bf16" else 4
+    kd, vd = row_entries(w.L, w.b, w.k)
+    N = level_sizes(w.L, w.b)
+    gathers = B * w.n_q * (kd + vd) * w.d * esz
+    tokens = 2 * w.n_kv * w.L * w.d * 4
+    summaries = 2 * 2 * w.n_kv * sum(N[1:]) * w.d * 4
+    return gathers + tokens + summaries
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_4b_524k")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the headline workload only (not the 131K, 1M and 2M workloads)")
     ap.add_argument("--distill", action="store_true",
                     help="time pooler distillation steps on the workload instead of the hot path")
     ap.add_argument("--lr", type=float, default=1000.0, help="distillation learning rate")
@@ -430,153 +689,57 @@ def main():
         return run_backward_chunk(args, args.workload, args.backward_chunk)
     w = synth.WORKLOADS[args.workload]
     B = args.batch or w.max_batch
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t_setup = time.perf_counter()
-    Lt = w.L + w.prefill_n
-    K, V = synth.gen_kv(w, 0, Lt)
-    W = synth.pool_w(w)
-    Qd = synth.decode_queries(w, B)
-    Qp = synth.prefill_queries(w) if w.prefill_n else None
+    # the oracle's leg first: its worker processes fork a process that has not touched the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, B, args.cpu_seconds)
+    R.load_library()
+    torch.cuda.set_device(0)
+    head, wall = measure_workload(w, [B], args.steps, args.warmup, backward=True)
+    configs = {}
+    if not args.no_configs and args.workload == "qwen3_4b_524k":
+        for name in OTHER_WORKLOADS:
+            wo = synth.WORKLOADS[name]
+            configs[name], _ = measure_workload(wo, list(wo.decode_batches), args.steps, args.warmup,
+                                                backward=False)
+            print(f"measured {name}", file=sys.stderr, flush=True)
 
-    def dev_store(x):
-        bits = synth.storage_bits(x, w.dtype)
-        if w.dtype == "f32":
-            return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    p = R.make_params(w.n_kv, w.n_q, w.d, w.b, w.k, Lt, store=w.dtype, out="f32",
-                      rope_base=w.rope_base, softmax_scale=w.softmax_scale, pool_scale=w.pool_scale)
-    layer = R.RecsaLayer(p, dev)
-    for g in range(w.n_kv):
-        layer.k_cache[g, :w.L].copy_(dev_store(K[g, :w.L]))
-        layer.v_cache[g, :w.L].copy_(dev_store(V[g, :w.L]))
-    layer.pool_w.copy_(torch.from_numpy(W))
-    q_dec = dev_store(Qd)
-    if w.prefill_n:
-        k_new = dev_store(np.ascontiguousarray(K[:, w.L:].transpose(1, 0, 2)))
-        v_new = dev_store(np.ascontiguousarray(V[:, w.L:].transpose(1, 0, 2)))
-        q_pre = dev_store(Qp)
-        out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
-    out_dec = torch.empty((B, w.n_q, w.d), dtype=torch.float32, device=dev)
-    out_grp = torch.empty_like(out_dec)
-    # backward of the decode batch: the output gradient is synthetic; every step writes
-    # the same token and pooler gradient buffers
-    d_out = torch.from_numpy(np.random.default_rng(5).standard_normal((B, w.n_q, w.d)).astype(np.float32)).to(dev)
-    grads = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
-             "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
-             "dw": torch.zeros((w.n_kv, w.d), dtype=torch.float32, device=dev)}
-    del K, V
-    torch.cuda.synchronize()
-    t_setup = time.perf_counter() - t_setup
-
-    ops = ["build", "decode", "decode_grouped", "backward"] + (["append", "prefill"] if w.prefill_n else [])
-    ev = {o: [] for o in ops}
-
-    def step(record):
-        marks = {}
-        def mark(name):
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            marks[name] = e
-        mark("t0")
-        layer.build(w.L)
-        mark("build")
-        layer.decode(q_dec, out=out_dec)
-        mark("decode")
-        layer.decode_grouped(q_dec, out=out_grp)
-        mark("decode_grouped")
-        layer.backward(q_dec, d_out, grads=grads)
-        mark("backward")
-        if w.prefill_n:
-            layer.append(k_new, v_new)
-            mark("append")
-            layer.prefill(q_pre, out=out_pre)
-            mark("prefill")
-        if record:
-            order = ["t0"] + ops
-            ev_pairs = [(order[i], order[i + 1]) for i in range(len(ops))]
-            for a_, b_ in ev_pairs:
-                ev[b_].append((marks[a_], marks[b_]))
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = {o: float(np.mean([a.elapsed_time(b) for a, b in ev[o]])) for o in ops}
-
-    alg = algorithmic(w, B)
-    kern = {}
-    kern["tree_build"] = {"bound": "hbm", "bytes": alg["build"], "ms": ms["build"],
-                          "achieved": alg["build"] / ms["build"] / 1e6, "unit": "GB/s"}
-    kern["decode"] = {"bound": "hbm", "bytes": alg["decode"], "ms": ms["decode"],
-                      "achieved": alg["decode"] / ms["decode"] / 1e6, "unit": "GB/s"}
-    # the backward's bytes depend on which nodes the rows read (its tree pass rewrites the
-    # fp32 gradients of every token under a touched node), so it is reported by its measured
-    # HBM traffic alone
-    kern["backward"] = {"bound": "hbm", "bytes": None, "ms": ms["backward"], "achieved": None,
-                        "unit": "GB/s"}
-    kern["decode_grouped"] = {"bound": "hbm", "bytes": alg["decode_grouped"], "ms": ms["decode_grouped"],
-                              "achieved": alg["decode_grouped"] / ms["decode_grouped"] / 1e6,
-                              "unit": "GB/s"}
-    if w.prefill_n:
-        # the chunk's rows share parents, so the HBM floor is reading every reachable K/V row,
-        # tree node and query once and writing the output; the bytes the rows would gather
-        # one by one ride along for context
-        kern["prefill"] = {"bound": "hbm", "bytes": alg["prefill_read_once"], "flops": alg["prefill_flops"],
-                           "ms": ms["prefill"],
-                           "achieved": alg["prefill_read_once"] / ms["prefill"] / 1e6, "unit": "GB/s",
-                           "per_row_gather_bytes": alg["prefill"],
-                           "mfma_frac": alg["prefill_flops"] / ms["prefill"] / 1e9 / BF16_PEAK_TFLOPS}
-        kern["append"] = {"bound": "hbm", "bytes": alg["append"], "ms": ms["append"],
-                          "achieved": alg["append"] / ms["append"] / 1e6, "unit": "GB/s"}
-    for name_, v in kern.items():
-        t_ = measured_traffic(w.name, name_)
-        v["traffic"] = None if t_ is None else t_["fetch"] + t_["write"]
-        if v["achieved"] is None and v["traffic"] is not None:
-            v["traffic_GBs"] = v["traffic"] / v["ms"] / 1e6
-            v["frac"] = v["traffic_GBs"] / HBM_PEAK_GBS
-        else:
-            v["frac"] = None if v["achieved"] is None else v["achieved"] / HBM_PEAK_GBS
-    # the roofline line follows the forward path; the backward rides along in `kernels`
+    kern = head["kernels"]
+    ms = {o: v["median"] for o, v in head["ms"].items()}
+    ms["decode"] = ms[f"decode_B{B}"]
+    # the roofline line follows the forward path's dominant call; the backward rides along
     dom = max((n for n in kern if n != "backward"), key=lambda n: kern[n]["ms"])
-    tr = measured_traffic(w.name, dom)
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": kern[dom]["achieved"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac"],
-            "traffic": None if tr is None else tr["fetch"] + tr["write"]}
+            "traffic": kern[dom]["traffic"]}
+    tr = measured_traffic(w.name, dom)
     if tr is not None:
         roof["traffic_split"] = tr
     if dom == "prefill":
         roof["mfma_frac"] = kern["prefill"]["mfma_frac"]
-        roof["per_row_gather_bytes"] = alg["prefill"]
+        roof["per_row_gather_bytes"] = kern["prefill"]["per_row_gather_bytes"]
 
-    step_ms = wall / args.steps * 1e3
     res = {
         "metric": "decode queries/s & prefill tokens/s at L=524K; % of HBM / bf16-MFMA roofline",
-        "value": B / (ms["decode"] / 1e3),
+        "value": B / (ms[f"decode_B{B}"] / 1e3),
         "unit": "decode queries/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32",
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "precision": PRECISION,
         "data": "synthetic",
         "config": {"workload": w.name, "storage": w.dtype, "L": w.L, "n_kv_heads": w.n_kv,
                    "n_q_heads": w.n_q,
                    "head_dim": w.d, "b": w.b, "k": w.k, "decode_batch": B,
                    "prefill_chunk": w.prefill_n},
-        "grouped_decode_queries_per_s": B / (ms["decode_grouped"] / 1e3),
-        "prefill_tokens_per_s": (w.prefill_n / ((ms["append"] + ms["prefill"]) / 1e3)
-                                 if w.prefill_n else None),
+        "grouped_decode_queries_per_s": head["grouped_decode_queries_per_s"],
+        "prefill_tokens_per_s": head["prefill_tokens_per_s"],
         "ms": ms,
+        "timing": head["ms"],
         "kernels": kern,
         "roofline": roof,
-        "setup_s": t_setup,
+        "configs": configs,
+        "setup_s": head["setup_s"],
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, B, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
