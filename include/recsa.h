@@ -15,6 +15,8 @@
  *  - All tensors are caller-owned device memory.  The library allocates
  *    nothing, frees nothing and keeps no pointer after a call returns; inputs
  *    are borrowed for the stream-ordered duration of the work it enqueues.
+ *    Its one piece of state is the fixed sequence table of
+ *    recsa_decode_multi_noalloc (static device memory, one per GPU).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work of a call is enqueued on it; no call synchronizes the device.
  *  - Arguments are validated on the host before any HIP call.  A failure
@@ -192,6 +194,20 @@ RECSA_API size_t recsa_multi_workspace_bytes(int32_t n_seq);
 RECSA_API recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs,
                                 int32_t n_seq, const void *q, void *out, const recsa_debug *dbg,
                                 void *ws, void *stream);
+
+/* recsa_decode_multi for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call with no workspace argument.  For more than 32 sequences the sequence
+ * table goes to a fixed table inside the library instead of a caller workspace:
+ * device memory of 4096 entries (160 KB) per GPU, held from the first such call on
+ * that GPU (the device current at the call) until the process ends.  At most 4096
+ * sequences (RECSA_ERR_INVALID_ARG beyond).  The call allocates nothing and frees
+ * nothing.  Every such call on one GPU shares that table: calls whose work overlaps
+ * on one GPU (other streams, other threads) race and must be ordered by the caller.
+ * Arguments, results and errors otherwise as recsa_decode_multi. */
+RECSA_API recsa_status recsa_decode_multi_noalloc(const recsa_params *p, const recsa_tree_desc *descs,
+                                        int32_t n_seq, const void *q, void *out,
+                                        const recsa_debug *dbg, void *stream);
 
 /* Causal prefill of the last n_q tokens of the tree (append them first):
  * q[n_q][n_q_heads][head_dim]; query j sits at token L0 + j, L0 = length - n_q,

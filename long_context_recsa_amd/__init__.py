@@ -25,7 +25,7 @@ EXPORTED = (
     "recsa_prefill", "recsa_status_string", "recsa_last_error", "recsa_multi_workspace_bytes",
     "recsa_decode_multi", "recsa_decode_grouped", "recsa_backward_workspace_bytes",
     "recsa_backward", "recsa_dense_workspace_bytes", "recsa_dense_decode",
-    "recsa_distill_workspace_bytes", "recsa_distill_step",
+    "recsa_distill_workspace_bytes", "recsa_distill_step", "recsa_decode_multi_noalloc",
 )
 
 
@@ -89,6 +89,7 @@ def load_library():
         "recsa_last_error": (ctypes.c_char_p, []),
         "recsa_multi_workspace_bytes": (ctypes.c_size_t, [i32]),
         "recsa_decode_multi": (i32, [P, D, i32, v, v, G, v, v]),
+        "recsa_decode_multi_noalloc": (i32, [P, D, i32, v, v, G, v]),
         "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
         "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P, i64]),
         "recsa_backward": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
@@ -202,6 +203,14 @@ def recsa_decode_multi(p, descs, n_seq, q_ptr, out_ptr, dbg=None, ws=None, strea
     _check(load_library().recsa_decode_multi(ctypes.byref(p), descs, n_seq, q_ptr, out_ptr,
                                              ctypes.byref(dbg) if dbg is not None else None,
                                              ws, stream))
+
+
+def recsa_decode_multi_noalloc(p, descs, n_seq, q_ptr, out_ptr, dbg=None, stream=None) -> None:
+    """As recsa_decode_multi, with the sequence table in the library's fixed device table
+    (no workspace; at most 4096 sequences)."""
+    _check(load_library().recsa_decode_multi_noalloc(ctypes.byref(p), descs, n_seq, q_ptr, out_ptr,
+                                                     ctypes.byref(dbg) if dbg is not None else None,
+                                                     stream))
 
 
 def make_params(n_kv_heads, n_q_heads, head_dim, fanout_b, budget_k, capacity,

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "recsa_internal.hpp"
@@ -454,6 +455,95 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     return RECSA_OK;
 }
 
+// The sequence table of recsa_decode_multi_noalloc for more than kInlineSeqs
+// sequences: file-scope device memory, one copy per GPU, held until the process ends.
+// Host code reaches it only through the address hipGetSymbolAddress gives on each
+// device (the array's own name is a host-side stand-in).
+constexpr int32_t kNoAllocSeqs = 4096;
+static __device__ __attribute__((aligned(256))) SeqEntry scratch[kNoAllocSeqs];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The table's device address on the current device, looked up once per device.
+hipError_t scratch_address(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Multi-sequence decode: `table` is device memory for the sequence table when n_seq >
+// kInlineSeqs (the caller's workspace or the no-allocation scratch).  With
+// validate_only, only the argument checks run.
+recsa_status run_multi(const recsa_params *p, const recsa_tree_desc *descs, int32_t n_seq,
+                       const void *q, void *out, const recsa_debug *dbg, void *table, hipStream_t s,
+                       bool validate_only = false) {
+    recsa_status st = check_params(p);
+    if (st != RECSA_OK) return st;
+    const Layout L = make_layout(p);
+    if ((st = check_limits(p, L)) != RECSA_OK) return st;
+    if (descs == nullptr || n_seq < 1)
+        return fail(RECSA_ERR_INVALID_ARG, "need at least one sequence descriptor");
+    for (int32_t i = 0; i < n_seq; ++i) {
+        if ((st = check_desc(p, &descs[i])) != RECSA_OK) return st;
+        if (descs[i].length < 1)
+            return fail(RECSA_ERR_INVALID_ARG, "sequence %d has no cached token", (int)i);
+    }
+    if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(RECSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if ((int64_t)n_seq * p->n_q_heads > 0x7FFFFFFF)
+        return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    if (validate_only) return RECSA_OK;
+    DescendArgs a{};
+    hipError_t e = hipSuccess;
+    if (n_seq <= kInlineSeqs) {
+        // the sequence table travels in the kernel arguments
+        a.n_inline = n_seq;
+        for (int32_t i = 0; i < n_seq; ++i) memcpy(&a.seq_inline[i], &descs[i], sizeof(SeqEntry));
+    } else {
+        // the caller's descriptors are the table (SeqEntry mirrors recsa_tree_desc); a
+        // pageable source is staged before the copy call returns
+        e = hipMemcpyAsync(table, descs, (size_t)n_seq * sizeof(SeqEntry), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "sequence table copy");
+        a.seqs = static_cast<const SeqEntry *>(table);
+    }
+    const TreeView tv = make_view(p, &descs[0], L);
+    a.q = q;
+    a.out = out;
+    a.rows = (int64_t)n_seq * p->n_q_heads;
+    a.Hq = p->n_q_heads;
+    a.G = p->n_q_heads / p->n_kv_heads;
+    a.gs = 1;
+    a.ctx_base = 0;
+    a.ctx_step = 0;
+    a.b = p->fanout_b;
+    a.k = p->budget_k;
+    a.max_cand = (int32_t)L.max_cand;
+    a.scale = p->softmax_scale;
+    a.out_bf16 = p->out_dtype == RECSA_BF16;
+    DebugView dv{};
+    if (dbg != nullptr) {
+        dv.selected = dbg->selected;
+        dv.kth_gap = dbg->kth_gap;
+        dv.n_keys = dbg->n_keys;
+    }
+    e = launch_descend(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "descend launch");
+    return RECSA_OK;
+}
+
 // Per-span partial states of dense attention: at most kDenseMaxSpans spans whatever the length.
 size_t dense_part_bytes(const recsa_params *p, int32_t batch) {
     return align_up((size_t)p->n_kv_heads * (size_t)kDenseMaxSpans * (size_t)batch *
@@ -576,68 +666,29 @@ size_t recsa_multi_workspace_bytes(int32_t n_seq) {
 recsa_status recsa_decode_multi(const recsa_params *p, const recsa_tree_desc *descs, int32_t n_seq,
                                 const void *q, void *out, const recsa_debug *dbg, void *ws,
                                 void *stream) {
-    recsa_status st = check_params(p);
-    if (st != RECSA_OK) return st;
-    const Layout L = make_layout(p);
-    if ((st = check_limits(p, L)) != RECSA_OK) return st;
-    if (descs == nullptr || n_seq < 1)
-        return fail(RECSA_ERR_INVALID_ARG, "need at least one sequence descriptor");
-    for (int32_t i = 0; i < n_seq; ++i) {
-        if ((st = check_desc(p, &descs[i])) != RECSA_OK) return st;
-        if (descs[i].length < 1)
-            return fail(RECSA_ERR_INVALID_ARG, "sequence %d has no cached token", (int)i);
-    }
-    if (q == nullptr || out == nullptr) return fail(RECSA_ERR_INVALID_ARG, "q and out must be non-NULL");
-    if (!aligned(q, 16) || !aligned(out, 16))
-        return fail(RECSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
     if (n_seq > kInlineSeqs && (ws == nullptr || !aligned(ws, 16)))
         return fail(RECSA_ERR_INVALID_ARG,
                     "a 16-byte aligned workspace of recsa_multi_workspace_bytes(%d) bytes is needed",
                     (int)n_seq);
-    if ((int64_t)n_seq * p->n_q_heads > 0x7FFFFFFF)
-        return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    DescendArgs a{};
-    hipError_t e = hipSuccess;
-    if (n_seq <= kInlineSeqs) {
-        // the sequence table travels in the kernel arguments
-        a.n_inline = n_seq;
-        for (int32_t i = 0; i < n_seq; ++i)
-            a.seq_inline[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
-    } else {
-        // copied into the workspace on the caller's stream (a pageable source is staged
-        // before the copy call returns)
-        thread_local std::vector<SeqEntry> table;
-        table.resize((size_t)n_seq);
-        for (int32_t i = 0; i < n_seq; ++i)
-            table[i] = SeqEntry{descs[i].k_cache, descs[i].v_cache, descs[i].tree, descs[i].length};
-        e = hipMemcpyAsync(ws, table.data(), (size_t)n_seq * sizeof(SeqEntry), hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return hip_fail(e, "sequence table copy");
-        a.seqs = static_cast<const SeqEntry *>(ws);
+    return run_multi(p, descs, n_seq, q, out, dbg, ws, static_cast<hipStream_t>(stream));
+}
+
+recsa_status recsa_decode_multi_noalloc(const recsa_params *p, const recsa_tree_desc *descs,
+                                        int32_t n_seq, const void *q, void *out,
+                                        const recsa_debug *dbg, void *stream) {
+    if (n_seq > kNoAllocSeqs)
+        return fail(RECSA_ERR_INVALID_ARG,
+                    "%d sequences exceed the %d the no-allocation decode's table holds", (int)n_seq,
+                    (int)kNoAllocSeqs);
+    void *table = nullptr;
+    if (n_seq > kInlineSeqs) {
+        // validate first, so a refused call touches no HIP state
+        recsa_status st = run_multi(p, descs, n_seq, q, out, dbg, nullptr, nullptr, true);
+        if (st != RECSA_OK) return st;
+        hipError_t e = scratch_address(&table);
+        if (e != hipSuccess) return hip_fail(e, "scratch address");
     }
-    const TreeView tv = make_view(p, &descs[0], L);
-    a.q = q;
-    a.out = out;
-    a.rows = (int64_t)n_seq * p->n_q_heads;
-    a.Hq = p->n_q_heads;
-    a.G = p->n_q_heads / p->n_kv_heads;
-    a.gs = 1;
-    a.ctx_base = 0;
-    a.ctx_step = 0;
-    a.b = p->fanout_b;
-    a.k = p->budget_k;
-    a.max_cand = (int32_t)L.max_cand;
-    a.scale = p->softmax_scale;
-    a.out_bf16 = p->out_dtype == RECSA_BF16;
-    DebugView dv{};
-    if (dbg != nullptr) {
-        dv.selected = dbg->selected;
-        dv.kth_gap = dbg->kth_gap;
-        dv.n_keys = dbg->n_keys;
-    }
-    e = launch_descend(tv, (recsa_dtype)p->store_dtype, p->head_dim, a, dv, s);
-    if (e != hipSuccess) return hip_fail(e, "descend launch");
-    return RECSA_OK;
+    return run_multi(p, descs, n_seq, q, out, dbg, table, static_cast<hipStream_t>(stream));
 }
 
 recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, const void *q,

@@ -1,5 +1,6 @@
 // Internal definitions shared by the RecSA host library and its gfx950 kernels.
 #pragma once
+#include <stddef.h>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -135,13 +136,18 @@ hipError_t launch_level(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32_t
 constexpr int kInlineSeqs = 32;    // sequences whose table travels in the kernel arguments
 
 // One sequence of a multi-sequence decode: its cache, its tree (same layout as the
-// others') and its length.
+// others'), its pooler vectors (unused by the descent) and its length.  The layout is
+// recsa_tree_desc's, so a caller's descriptor array is copied to the device as it is.
 struct SeqEntry {
     const void *k_cache;
     const void *v_cache;
     const void *tree;
+    const float *pool_w;
     int64_t length;
 };
+static_assert(sizeof(SeqEntry) == sizeof(recsa_tree_desc), "SeqEntry mirrors recsa_tree_desc");
+static_assert(offsetof(SeqEntry, tree) == offsetof(recsa_tree_desc, tree), "SeqEntry mirrors recsa_tree_desc");
+static_assert(offsetof(SeqEntry, length) == offsetof(recsa_tree_desc, length), "SeqEntry mirrors recsa_tree_desc");
 
 struct DescendArgs {
     const void *q;             // [rows / Hq][Hq][D]

@@ -8,7 +8,7 @@ import torch
 
 from . import (PATHS, RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
                recsa_build_tree, recsa_dense_decode, recsa_dense_workspace_bytes, recsa_distill_step,
-               recsa_distill_workspace_bytes, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_max_candidates, recsa_multi_workspace_bytes,
+               recsa_distill_workspace_bytes, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_decode_multi_noalloc, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
                recsa_tree_layout, recsa_workspace_bytes)
 
@@ -192,9 +192,11 @@ class RecsaLayer:
 
 
 def decode_multi(layers, q: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None,
-                 ws: torch.Tensor | None = None):
+                 ws: torch.Tensor | None = None, noalloc: bool = False):
     """One decode step for a batch of sequences: layers[i] (same params, own cache and
-    tree) answers query q[i] at its own length.  q: [n][n_q_heads][head_dim]."""
+    tree) answers query q[i] at its own length.  q: [n][n_q_heads][head_dim].
+    noalloc: call recsa_decode_multi_noalloc (no workspace; pass `out`, and no debug,
+    for a call that allocates nothing)."""
     first = layers[0]
     n = len(layers)
     # the kernel addresses every sequence's cache and tree with the first one's layout
@@ -208,6 +210,10 @@ def decode_multi(layers, q: torch.Tensor, debug: bool = False, out: torch.Tensor
     if out is None:
         out = torch.empty(shape, dtype=first.out_dtype, device=first.device)
     descs = (recsa_tree_desc * n)(*[l.desc for l in layers])
+    if noalloc:
+        d, dbg = first._debug(n * first.p.n_q_heads, debug)
+        recsa_decode_multi_noalloc(first.p, descs, n, _ptr(q), _ptr(out), dbg, first.stream())
+        return (out, d) if debug else out
     nbytes = recsa_multi_workspace_bytes(n)
     if nbytes and (ws is None or ws.numel() < nbytes):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=first.device)

@@ -282,3 +282,23 @@ def test_path_field_sizes_and_runs_alike():
         with pytest.raises(R.RecsaError) as e:
             R.recsa_backward(p, d, fake, 2, 0, fake, fake, fake, fake, fake, ws=fake)
         assert e.value.status == R.RECSA_ERR_UNSUPPORTED
+
+
+def test_multi_noalloc_validates_before_any_hip_call():
+    p = _p(capacity=1000)
+    fake = 1 << 20
+    good = (R.recsa_tree_desc * 40)(*([R.recsa_tree_desc(fake, fake, fake, fake, 10)] * 40))
+    bad = (R.recsa_tree_desc * 40)(*([R.recsa_tree_desc(fake, fake, fake, fake, 10)] * 39 +
+                                     [R.recsa_tree_desc(fake, fake, fake, fake, 0)]))
+    many = (R.recsa_tree_desc * 4097)(*([good[0]] * 4097))
+    cases = [
+        (lambda: R.recsa_decode_multi_noalloc(p, many, 4097, fake, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi_noalloc(p, bad, 40, fake, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi_noalloc(p, good, 40, None, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi_noalloc(p, good, 0, fake, fake), R.RECSA_ERR_INVALID_ARG),
+        (lambda: R.recsa_decode_multi_noalloc(_p(head_dim=96), good, 40, fake, fake), R.RECSA_ERR_UNSUPPORTED),
+    ]
+    for i, (fn, status) in enumerate(cases):
+        with pytest.raises(R.RecsaError) as e:
+            fn()
+        assert e.value.status == status, (i, str(e.value))
