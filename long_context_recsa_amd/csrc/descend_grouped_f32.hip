@@ -14,7 +14,7 @@ template <int D>
 hipError_t dispatch_grouped(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
                             hipStream_t s) {
     switch (a.gs) {
-        case 2: return launch_kt<float, D, 8, 4, 2>(tv, a, dbg, s);
+        case 2: return launch_kt<float, D, 8, 2, 2>(tv, a, dbg, s);
         case 4: return launch_kt<float, D, 8, 2, 4>(tv, a, dbg, s);
         case 8: return launch_kt<float, D, 8, 1, 8>(tv, a, dbg, s);
         default: return hipErrorInvalidValue;

@@ -132,17 +132,26 @@ __device__ __forceinline__ uint32_t node_rc(int32_t i, int32_t r, int32_t c, con
 }
 
 // One pass over this slot's candidates of two levels: entries of level A (values,
-// logits zA, kept ones flagged when maskA) fold into the running softmax, and the
-// candidates of level S are scored into zS.  Either level may be empty.
+// logits zA, kept ones flagged) fold into the running softmax, and the candidates of
+// level S are scored into zS.  HAS_A: level A has entries (not so above the top);
+// ONLINE: the S candidates are tokens, entries as soon as they are scored, whose
+// values (vS) come in with their keys and join this slot's softmax online (M is
+// then per slot).  Level S is never empty.
 //
 // GS query heads share the pass (GS > 1: one selection per KV group).  Head j's logits
 // are row j of zA / zS (rows zstride apart) and its rotated queries start at U + j * ustride;
 // each value or key row is loaded once for all GS heads.  With GS > 1 the group score
 // (the sum of the heads' logits) goes to gS for the selection, and lane 15 of each slot
 // keeps, in smax, the largest logit per head that it scored.
-template <typename T, int D, int NW, int CB, int GS>
+//
+// The slot's batches (child offset c, CB ranks) run two at a time (one for a group of
+// eight heads): both batches' loads are issued before the first is folded in, so a
+// pass waits on memory about half as often as batches it has.  Which loads a batch issues is fixed at compile time (no
+// branch around a load), which lets the compiler wait for the first batch's loads
+// alone; an odd last batch is paired with a dead one whose loads read row 0.
+template <typename T, int D, int NW, int CB, int GS, bool HAS_A, bool ONLINE>
 __device__ __forceinline__ void fused_pass(
-    sel::Cands A, const int32_t *parA, const float *zA, const uint8_t *flagA, bool maskA,
+    sel::Cands A, const int32_t *parA, const float *zA, const uint8_t *flagA,
     const T *vA, sel::Cands S, const int32_t *parS, const T *kS, float *zS, float *gS,
     uint8_t *flagS, const T *vS, const float *U, int32_t ustride, const float2 *rope,
     int32_t maxc, int32_t zstride, int32_t kmax, int slot, int sub, float scale, float (&M)[GS],
@@ -151,7 +160,7 @@ __device__ __forceinline__ void fused_pass(
     constexpr int H2 = D / 2, PP = D / 32, NSLOT = NW * 4;
     constexpr uint32_t ROWB = D * sizeof(T);
     constexpr float kLog2e = 1.4426950408889634f;
-    const int32_t b = A.n > 0 ? A.b : S.b;
+    const int32_t b = S.b;
     const int32_t nmax = A.n > S.n ? A.n : S.n;
     const int32_t R = (nmax + b - 1) / b;
     const int j0 = sub * PP;
@@ -160,15 +169,12 @@ __device__ __forceinline__ void fused_pass(
     const uint32_t j0b = (uint32_t)(j0 * sizeof(T));
     const char *vAb = reinterpret_cast<const char *>(vA);
     const char *kSb = reinterpret_cast<const char *>(kS);
-    // vS: the S candidates are tokens, entries as soon as they are scored; their values
-    // come in with their keys and join this slot's softmax online (M is then per slot)
-    const bool online = vS != nullptr;
-    const char *vSb = reinterpret_cast<const char *>(online ? vS : kS);
+    const char *vSb = reinterpret_cast<const char *>(vS);
     // The slot's batches: child offsets c = slot, slot + NSLOT, ... and for each the ranks
-    // in groups of CB, in that order, as one flat loop.  A batch issues all its loads,
-    // then folds them in.
+    // in groups of CB, in that order, as one flat sequence.
     struct Batch {
         int32_t c, r0;
+        bool live;
         float ea[CB][GS];
         float cr[PP], sr[PP];
         Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
@@ -176,11 +182,12 @@ __device__ __forceinline__ void fused_pass(
     const int32_t nc = slot < b ? (b - slot + NSLOT - 1) / NSLOT : 0;
     const int32_t nrb = (R + CB - 1) / CB;
     const int32_t NB = nc * nrb;
-    auto issue = [&](Batch &B, int32_t ci, int32_t ri) __attribute__((always_inline)) {
-        B.c = slot + ci * NSLOT;
-        B.r0 = ri * CB;
+    auto issue = [&](Batch &B, int32_t ci, int32_t ri, bool live) __attribute__((always_inline)) {
+        B.live = live;
+        B.c = live ? slot + ci * NSLOT : 0;
+        B.r0 = live ? ri * CB : 0;
         const int32_t c = B.c;
-        if (S.n > 0) load_cs<PP>(rope + (int64_t)c * H2 + j0, B.cr, B.sr);
+        load_cs<PP>(rope + (int64_t)c * H2 + j0, B.cr, B.sr);
         uint32_t offA[CB], offS[CB];
         #pragma unroll
         for (int t = 0; t < CB; ++t) {
@@ -188,37 +195,37 @@ __device__ __forceinline__ void fused_pass(
             const int32_t i = r * b + c;
             const int32_t ic = i < maxc ? i : maxc - 1;
             const int32_t rc = r < kmax ? r : kmax - 1;
-            const bool okA = (i < A.n) && !(maskA && flagA[ic]);
-            #pragma unroll
-            for (int j = 0; j < GS; ++j) B.ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
-            offA[t] = (okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u) + j0b;
-            offS[t] = ((i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u) + j0b;
+            if constexpr (HAS_A) {
+                const bool okA = live && (i < A.n) && !flagA[ic];
+                #pragma unroll
+                for (int j = 0; j < GS; ++j) B.ea[t][j] = okA ? zA[j * zstride + ic] * kLog2e : -INFINITY;
+                offA[t] = (okA ? node_rc(i, rc, c, A, parA) * ROWB : 0u) + j0b;
+            }
+            offS[t] = ((live && i < S.n) ? node_rc(i, rc, c, S, parS) * ROWB : 0u) + j0b;
         }
-        if (online) {
+        if constexpr (ONLINE) {
             #pragma unroll
             for (int t = 0; t < CB; ++t) {
                 B.sa[t].load(reinterpret_cast<const T *>(vSb + offS[t]));
                 B.sb[t].load(reinterpret_cast<const T *>(vSb + offS[t] + H2 * sizeof(T)));
             }
         }
-        if (A.n > 0) {
+        if constexpr (HAS_A) {
             #pragma unroll
             for (int t = 0; t < CB; ++t) {
                 B.va[t].load(reinterpret_cast<const T *>(vAb + offA[t]));
                 B.vb[t].load(reinterpret_cast<const T *>(vAb + offA[t] + H2 * sizeof(T)));
             }
         }
-        if (S.n > 0) {
-            #pragma unroll
-            for (int t = 0; t < CB; ++t) {
-                B.ka[t].load(reinterpret_cast<const T *>(kSb + offS[t]));
-                B.kb[t].load(reinterpret_cast<const T *>(kSb + offS[t] + H2 * sizeof(T)));
-            }
+        #pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            B.ka[t].load(reinterpret_cast<const T *>(kSb + offS[t]));
+            B.kb[t].load(reinterpret_cast<const T *>(kSb + offS[t] + H2 * sizeof(T)));
         }
     };
     auto consume = [&](const Batch &B) __attribute__((always_inline)) {
         const int32_t c = B.c;
-        if (A.n > 0) {
+        if constexpr (HAS_A) {
             #pragma unroll
             for (int t = 0; t < CB; ++t) {
                 float fa[PP], fb[PP];
@@ -236,75 +243,82 @@ __device__ __forceinline__ void fused_pass(
                 }
             }
         }
-        if (S.n > 0) {
+        #pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const int32_t r = B.r0 + t;
+            const int32_t i = r * b + c;
+            const int32_t ru = (i < S.n) ? r : 0;
+            float fa[PP], fb[PP], ra[PP], rb[PP];
+            B.ka[t].get(fa);
+            B.kb[t].get(fb);
             #pragma unroll
-            for (int t = 0; t < CB; ++t) {
-                const int32_t r = B.r0 + t;
-                const int32_t i = r * b + c;
-                const int32_t ru = (i < S.n) ? r : 0;
-                float fa[PP], fb[PP], ra[PP], rb[PP];
-                B.ka[t].get(fa);
-                B.kb[t].get(fb);
+            for (int p = 0; p < PP; ++p) {
+                ra[p] = fa[p] * B.cr[p] - fb[p] * B.sr[p];
+                rb[p] = fb[p] * B.cr[p] + fa[p] * B.sr[p];
+            }
+            float fa2[PP], fb2[PP];
+            if constexpr (ONLINE) {
+                B.sa[t].get(fa2);
+                B.sb[t].get(fb2);
+            }
+            float gsum = 0.f;
+            #pragma unroll
+            for (int j = 0; j < GS; ++j) {
+                float ua[PP], ub[PP];
+                const float *Uj = U + (size_t)j * ustride + (size_t)ru * D;
+                Vec<float, PP>::load(Uj + j0, ua);
+                Vec<float, PP>::load(Uj + H2 + j0, ub);
+                float dot = 0.f;
                 #pragma unroll
-                for (int p = 0; p < PP; ++p) {
-                    ra[p] = fa[p] * B.cr[p] - fb[p] * B.sr[p];
-                    rb[p] = fb[p] * B.cr[p] + fa[p] * B.sr[p];
-                }
-                float fa2[PP], fb2[PP];
-                if (online) {
-                    B.sa[t].get(fa2);
-                    B.sb[t].get(fb2);
-                }
-                float gsum = 0.f;
-                #pragma unroll
-                for (int j = 0; j < GS; ++j) {
-                    float ua[PP], ub[PP];
-                    const float *Uj = U + (size_t)j * ustride + (size_t)ru * D;
-                    Vec<float, PP>::load(Uj + j0, ua);
-                    Vec<float, PP>::load(Uj + H2 + j0, ub);
-                    float dot = 0.f;
-                    #pragma unroll
-                    for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
-                    dot = row_sum16(dot);
-                    if (online) {
-                        // the logit to all 16 lanes of the slot, then an online softmax step
-                        const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
-                        if (i < S.n) {
-                            const float Mn = fmaxf(M[j], z);
-                            const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
-                            const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
-                            lsum[j] = lsum[j] * sc + pz;
-                            #pragma unroll
-                            for (int p = 0; p < PP; ++p) {
-                                acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
-                                acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
-                            }
-                            M[j] = Mn;
+                for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
+                dot = row_sum16(dot);
+                if constexpr (ONLINE) {
+                    // the logit to all 16 lanes of the slot, then an online softmax step
+                    const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
+                    if (i < S.n) {
+                        const float Mn = fmaxf(M[j], z);
+                        const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
+                        const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
+                        lsum[j] = lsum[j] * sc + pz;
+                        #pragma unroll
+                        for (int p = 0; p < PP; ++p) {
+                            acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
+                            acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
                         }
-                    } else if (sub == 15 && i < S.n) {
-                        const float z = scale * dot;
-                        zS[j * zstride + i] = z;
-                        if constexpr (GS > 1) {
-                            gsum += z;
-                            smax[j] = fmaxf(smax[j], z);
-                        }
+                        M[j] = Mn;
+                    }
+                } else if (sub == 15 && i < S.n) {
+                    const float z = scale * dot;
+                    zS[j * zstride + i] = z;
+                    if constexpr (GS > 1) {
+                        gsum += z;
+                        smax[j] = fmaxf(smax[j], z);
                     }
                 }
-                if (!online && sub == 15 && i < S.n) {
+            }
+            if constexpr (!ONLINE) {
+                if (sub == 15 && i < S.n) {
                     if constexpr (GS > 1) gS[i] = gsum;
                     flagS[i] = 0;
                 }
             }
         }
     };
-    Batch B;
+    // A group of eight heads keeps 64 accumulators per lane: one batch in flight.
+    constexpr bool kPair = GS < 8;
+    Batch B0, B1;
     int32_t ci = 0, ri = 0;
-    for (int32_t k = 0; k < NB; ++k) {
-        issue(B, ci, ri);
-        consume(B);
-        if (++ri == nrb) {
-            ri = 0;
-            ++ci;
+    for (int32_t k = 0; k < NB; k += kPair ? 2 : 1) {
+        issue(B0, ci, ri, true);
+        if (++ri == nrb) { ri = 0; ++ci; }
+        if constexpr (kPair) {
+            const bool two = k + 1 < NB;
+            issue(B1, ci, ri, two);
+            if (two && ++ri == nrb) { ri = 0; ++ci; }
+            consume(B0);
+            if (two) consume(B1);
+        } else {
+            consume(B0);
         }
     }
 }
@@ -556,10 +570,16 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
             const T *kH = H == 0 ? kcache : lkey(H);
             const int buf = H & 1;
             // with no level above the tokens, the top candidates are tokens: entries at once
-            fused_pass<T, D, NW, CB, GS>(none, kept, zbuf, flagbuf, false, kH, cA, kept, kH,
-                                         zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
-                                         H == 0 ? vcache : nullptr, U, ustride, rope, maxc, mz, a.k, slot,
-                                         sub, a.scale, M, lsum, acc_a, acc_b, smax);
+            if (H == 0)
+                fused_pass<T, D, NW, CB, GS, false, true>(none, kept, zbuf, flagbuf, kH, cA, kept, kH,
+                                                          zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
+                                                          vcache, U, ustride, rope, maxc, mz, a.k, slot,
+                                                          sub, a.scale, M, lsum, acc_a, acc_b, smax);
+            else
+                fused_pass<T, D, NW, CB, GS, false, false>(none, kept, zbuf, flagbuf, kH, cA, kept, kH,
+                                                           zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
+                                                           nullptr, U, ustride, rope, maxc, mz, a.k, slot,
+                                                           sub, a.scale, M, lsum, acc_a, acc_b, smax);
             if (H > 0) publish_max(smax, buf);
         }
         keys_scored += cA.n;
@@ -619,10 +639,16 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         }
         const T *vA = lval(l);
         const T *kS = l == 1 ? kcache : lkey(l - 1);
-        fused_pass<T, D, NW, CB, GS>(cA, parentsA, zrow(bufA, 0), flagA, true, vA, cS, keptA, kS,
-                                     zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
-                                     l == 1 ? vcache : nullptr, U, ustride, rope, maxc, mz, a.k, slot, sub,
-                                     a.scale, M, lsum, acc_a, acc_b, smax);
+        if (l == 1)
+            fused_pass<T, D, NW, CB, GS, true, true>(cA, parentsA, zrow(bufA, 0), flagA, vA, cS, keptA, kS,
+                                                     zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
+                                                     vcache, U, ustride, rope, maxc, mz, a.k, slot, sub,
+                                                     a.scale, M, lsum, acc_a, acc_b, smax);
+        else
+            fused_pass<T, D, NW, CB, GS, true, false>(cA, parentsA, zrow(bufA, 0), flagA, vA, cS, keptA, kS,
+                                                      zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
+                                                      nullptr, U, ustride, rope, maxc, mz, a.k, slot, sub,
+                                                      a.scale, M, lsum, acc_a, acc_b, smax);
         if (l > 1) publish_max(smax, bufS);
         keys_scored += cS.n;
         cA = cS;
