@@ -64,12 +64,14 @@ def sources_digest(op):
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` (read + write) from the committed counter summary
-    for this workload: lines 'traffic <kernel> fetch_bytes=F write_bytes=W sources=<sha256>'.
-    None when there is no summary or the kernels changed since it was taken."""
+    for this workload: lines 'traffic <kernel> fetch_bytes=F write_bytes=W sources=<sha256>'
+    (decode per batch as decode_B<batch>).  None when there is no summary or the kernels
+    changed since it was taken."""
     path = COUNTERS.format(workload=workload)
     if not os.path.exists(path):
         return None
-    digest = sources_digest(kernel) if kernel in OP_SOURCES else None
+    op = "decode" if kernel.startswith("decode_B") else kernel
+    digest = sources_digest(op) if op in OP_SOURCES else None
     with open(path) as fh:
         for line in fh:
             parts = line.strip().strip("`").split()
@@ -612,8 +614,7 @@ def measure_workload(w, batches, steps, warmup, backward=True):
         kern["append"] = {"bound": "hbm", "bytes": a0["append"], "ms": med["append"],
                           "achieved": a0["append"] / med["append"] / 1e6, "unit": "GB/s"}
     for name_, v in kern.items():
-        op = "decode" if name_.startswith("decode_B") else name_
-        t_ = measured_traffic(w.name, op)
+        t_ = measured_traffic(w.name, name_)
         v["traffic"] = None if t_ is None else t_["fetch"] + t_["write"]
         v["frac"] = v["achieved"] / HBM_PEAK_GBS
     res = {
@@ -688,12 +689,13 @@ def main():
     if args.backward_chunk:
         return run_backward_chunk(args, args.workload, args.backward_chunk)
     w = synth.WORKLOADS[args.workload]
-    B = args.batch or w.max_batch
+    batches = [args.batch] if args.batch else list(w.decode_batches)
+    B = max(batches)
     # the oracle's leg first: its worker processes fork a process that has not touched the GPU
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, B, args.cpu_seconds)
     R.load_library()
     torch.cuda.set_device(0)
-    head, wall = measure_workload(w, [B], args.steps, args.warmup, backward=True)
+    head, wall = measure_workload(w, batches, args.steps, args.warmup, backward=True)
     configs = {}
     if not args.no_configs and args.workload == "qwen3_4b_524k":
         for name in OTHER_WORKLOADS:

@@ -23,9 +23,46 @@ namespace {
 constexpr int kNodesPerBlock = 4;     // one wave per node
 constexpr int kRowsInFlight = 4;      // child rows per lane group loaded before use
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// E consecutive elements of a child row, widened to fp32.  NT (the token caches, which
+// the build reads once): nontemporal loads, so the scan of K and V does not push out
+// of the caches the tree levels and tables that the descent reads next.
+template <typename T, int E, bool NT>
+__device__ __forceinline__ void row_load(const T *p, float *out) {
+    if constexpr (!NT) {
+        Vec<T, E>::load(p, out);
+    } else if constexpr (sizeof(T) == 2) {
+        static_assert(E == 4 || E == 8, "bf16 row slice");
+        uint32_t w[E / 2];
+        if constexpr (E == 8) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            w[0] = v.x; w[1] = v.y;
+        }
+        #pragma unroll
+        for (int i = 0; i < E / 2; ++i) {
+            out[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            out[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    } else {
+        static_assert(E % 4 == 0, "fp32 row slice");
+        #pragma unroll
+        for (int i = 0; i < E; i += 4) {
+            const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p + i));
+            out[i] = v.x; out[i + 1] = v.y; out[i + 2] = v.z; out[i + 3] = v.w;
+        }
+    }
+}
+
 // KO (keys only): the pooled keys alone, for a pooler vector that changed while the
-// cache did not (the means do not depend on it); child values are not read.
-template <typename TK, typename TVC, typename TS, int D, bool KO>
+// cache did not (the means do not depend on it); child values are not read.  NT: the
+// children are the token caches (level 1), read with nontemporal loads.
+template <typename TK, typename TVC, typename TS, int D, bool KO, bool NT>
 __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
     const TK *__restrict__ child_key, int64_t child_key_stride,
     const TVC *__restrict__ child_val, int64_t child_val_stride,
@@ -55,8 +92,8 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
         for (int t = 0; t < kRowsInFlight; ++t) {
             const int r = r0 + 4 * t;
             if (r < b) {
-                Vec<TK, E>::load(ck + (int64_t)r * D, kf[t]);
-                if constexpr (!KO) Vec<TVC, E>::load(cv + (int64_t)r * D, vf[t]);
+                row_load<TK, E, NT>(ck + (int64_t)r * D, kf[t]);
+                if constexpr (!KO) row_load<TVC, E, NT>(cv + (int64_t)r * D, vf[t]);
             }
         }
         #pragma unroll
@@ -117,18 +154,18 @@ __global__ __launch_bounds__(64 * kNodesPerBlock) void level_kernel(
     }
 }
 
-template <typename TK, typename TVC, typename TS, int D>
+template <typename TK, typename TVC, typename TS, int D, bool NT>
 hipError_t launch_level_t(const TK *ck, int64_t cks, const TVC *cv, int64_t cvs, TS *ok, TS *ov,
                           float *om, int64_t os, int32_t Hkv, int32_t b, int64_t n0, int64_t n1,
                           const float *pool_w, float pool_scale, bool keys_only, hipStream_t s) {
     const int64_t nodes = n1 - n0;
     dim3 grid((unsigned)((nodes + kNodesPerBlock - 1) / kNodesPerBlock), (unsigned)Hkv);
     if (keys_only)
-        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, true>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
-                           cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
+        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, true, NT>), grid, dim3(64 * kNodesPerBlock), 0, s,
+                           ck, cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
     else
-        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, false>), grid, dim3(64 * kNodesPerBlock), 0, s, ck,
-                           cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
+        hipLaunchKernelGGL((level_kernel<TK, TVC, TS, D, false, NT>), grid, dim3(64 * kNodesPerBlock), 0, s,
+                           ck, cks, cv, cvs, ok, ov, om, os, pool_w, pool_scale, b, n0, n1);
     return hipGetLastError();
 }
 
@@ -140,16 +177,16 @@ hipError_t launch_level_d(const TreeView &tv, int32_t Hkv, int32_t b, int32_t le
     float *om = tv.mean[level];
     const int64_t os = tv.node_cap[level] * D;
     if (level == 1) {
-        return launch_level_t<T, T, T, D>(static_cast<const T *>(tv.k_cache), tv.cap * D,
+        return launch_level_t<T, T, T, D, true>(static_cast<const T *>(tv.k_cache), tv.cap * D,
                                           static_cast<const T *>(tv.v_cache), tv.cap * D, ok, ov,
                                           om, os, Hkv, b, n0, n1, pool_w, pool_scale, ko, s);
     }
     const T *ck = static_cast<const T *>(tv.key[level - 1]);
     const int64_t cs = tv.node_cap[level - 1] * D;
     if (tv.mean[level - 1] != nullptr)                   // bf16 storage: fp32 child means
-        return launch_level_t<T, float, T, D>(ck, cs, tv.mean[level - 1], cs, ok, ov, om, os, Hkv,
+        return launch_level_t<T, float, T, D, false>(ck, cs, tv.mean[level - 1], cs, ok, ov, om, os, Hkv,
                                               b, n0, n1, pool_w, pool_scale, ko, s);
-    return launch_level_t<T, T, T, D>(ck, cs, static_cast<const T *>(tv.val[level - 1]), cs, ok,
+    return launch_level_t<T, T, T, D, false>(ck, cs, static_cast<const T *>(tv.val[level - 1]), cs, ok,
                                       ov, om, os, Hkv, b, n0, n1, pool_w, pool_scale, ko, s);
 }
 
