@@ -445,6 +445,10 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
             load_cs<PP>(rope + (int64_t)cc * H2 + j0, tc[t], ts[t]);
         }
     }
+    // The top level has one rank (r = 0) and the query sits at its candidate count: the
+    // rotation R(n theta) of its rotated queries comes in with the query.
+    float topc[PP], tops[PP];
+    load_cs<PP>(rope + (int64_t)cA.n * H2 + j0, topc, tops);
     // the row's queries: in registers for one head, in LDS for a group
     float qa[PP], qb[PP];
     const T *qrow = static_cast<const T *>(a.q) + (qi * a.Hq + h0) * D;
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     // U[j][r] = R((n - r*b) theta) q_j for the ranks r < ceil(n / b) of a level with n
     // candidates; slots from first_slot on share the (head, rank) pairs.
     const int32_t ustride = nrank * D;
-    auto build_ranks = [&](int32_t n, int first_slot) {
+    auto build_ranks = [&](int32_t n, int first_slot, bool top) {
         const int32_t R = (n + b - 1) / b;
         for (int32_t x = slot - first_slot; x < GS * R; x += NSLOT - first_slot) {
             const int j = GS == 1 ? 0 : x / R;
@@ -489,7 +493,12 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
                 Vec<float, PP>::load(qs + j * D + j0, xa);
                 Vec<float, PP>::load(qs + j * D + H2 + j0, xb);
             }
-            load_cs<PP>(rope + (int64_t)(n - r * b) * H2 + j0, c, s);
+            if (top) {
+                #pragma unroll
+                for (int p = 0; p < PP; ++p) { c[p] = topc[p]; s[p] = tops[p]; }
+            } else {
+                load_cs<PP>(rope + (int64_t)(n - r * b) * H2 + j0, c, s);
+            }
             #pragma unroll
             for (int p = 0; p < PP; ++p) {
                 ua[p] = xa[p] * c[p] - xb[p] * s[p];
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
 
     // ---- top level: score all of its candidates -------------------------------------
     {
-        build_ranks(cA.n, 0);
+        build_ranks(cA.n, 0, true);
         __syncthreads();
         if (top_early) {
             const int buf = H & 1;
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
                 for (int q = lane; q < a.k; q += 64) ds[q] = q < mA ? keptA[q] : -1;
             }
         } else {
-            build_ranks(cS.n, 4);
+            build_ranks(cS.n, 4, false);
         }
         __syncthreads();
 
