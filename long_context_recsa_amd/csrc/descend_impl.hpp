@@ -103,23 +103,21 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Candidates of level l of a row over n_ctx tokens (pw = b^l), below a level that
-// kept `kept_above` nodes.
-__device__ __forceinline__ sel::Cands level_cands(int64_t n_ctx, int64_t pw, int32_t b, bool top,
+// Candidates of level l of a row, from its node counts Nl = N_l and Nup = N_{l+1}
+// (N_l = floor(n_ctx / b^l)), below a level that kept `kept_above` nodes.
+__device__ __forceinline__ sel::Cands level_cands(int32_t Nl, int32_t Nup, int32_t b, bool top,
                                                   int32_t kept_above) {
     sel::Cands c;
-    const int64_t Nl = n_ctx / pw;
     c.b = b;
     c.top = top;
     if (top) {
-        c.n = (int32_t)Nl;
+        c.n = Nl;
         c.nchild = 0;
         c.orphan0 = 0;
     } else {
-        const int64_t Nup = n_ctx / (pw * b);
         c.nchild = b * kept_above;
-        c.orphan0 = (int32_t)(Nup * b);
-        c.n = c.nchild + (int32_t)(Nl - Nup * b);
+        c.orphan0 = Nup * b;
+        c.n = c.nchild + (Nl - Nup * b);
     }
     return c;
 }
@@ -323,6 +321,10 @@ __device__ __forceinline__ void fused_pass(
     }
 }
 
+// The row's node counts N_0..N_H (N_l = floor(n_ctx / b^l)) in LDS: 32-bit entries,
+// room for every level the capacity allows, padded to keep 16-byte alignment.
+constexpr int kNodeTab = (kMaxLevels + 4) & ~3;
+
 template <int NW, int GS>
 struct Smem {
     // logit rows per buffer: one per head, then (GS > 1) the group score
@@ -332,7 +334,8 @@ struct Smem {
     static size_t bytes(int32_t maxc, int32_t k, int32_t b, int D) {
         const size_t nrank = ((size_t)maxc + b - 1) / b;
         const size_t floats = 2 * NZ * (size_t)zstride(maxc) + GS * nrank * D + (size_t)NW * GS * D +
-                              2 * (size_t)NW * GS + (GS > 1 ? 2 * (size_t)NW * GS + (size_t)GS * D : 0) + 4;
+                              2 * (size_t)NW * GS + (GS > 1 ? 2 * (size_t)NW * GS + (size_t)GS * D : 0) + 4 +
+                              kNodeTab;
         return sizeof(float) * floats + sel::kScratchBytes + sizeof(int32_t) * 2 * (size_t)k +
                2 * (size_t)maxc;
     }
@@ -361,7 +364,8 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     float *lmax = red_m + NW * GS;                    // GS > 1: [2][NW][GS] level maxima
     float *qs = lmax + (GS > 1 ? 2 * NW * GS : 0);    // GS > 1: [GS][D] the queries
     float *misc = qs + (GS > 1 ? GS * D : 0);                             // [4]
-    unsigned char *scratch = reinterpret_cast<unsigned char *>(misc + 4); // selection scratch
+    int32_t *ntab = reinterpret_cast<int32_t *>(misc + 4);                // [kNodeTab] N_l
+    unsigned char *scratch = reinterpret_cast<unsigned char *>(ntab + kNodeTab); // selection scratch
     int32_t *kept = reinterpret_cast<int32_t *>(scratch + sel::kScratchBytes);  // [2][k]
     uint8_t *flagbuf = reinterpret_cast<uint8_t *>(kept + 2 * a.k);       // [2][maxc]
     // head j's logits and the selection score of buffer `buf`
@@ -373,23 +377,24 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     // KV-head-major order (KV head, query, head within the group), so each XCD takes a
     // contiguous run of rows that read the same KV head's tree (at 8 KV heads, one head
     // per XCD).  A group row (GS = G) already has its KV head at x mod 8.
-    int64_t row = blockIdx.x;
+    // (rows < 2^31, checked on the host: 32-bit index arithmetic)
+    uint32_t row = blockIdx.x;
     if constexpr (GS == 1) {
-        constexpr int kXcds = 8;
-        const int64_t R = gridDim.x;
+        constexpr uint32_t kXcds = 8;
+        const uint32_t R = gridDim.x;
         if (R % kXcds == 0) {
-            const int64_t rp = (int64_t)(blockIdx.x % kXcds) * (R / kXcds) + blockIdx.x / kXcds;
-            const int64_t per_g = (R / a.Hq) * a.G;         // rows of one KV head
-            const int64_t gg = rp / per_g, rem = rp - gg * per_g;
-            const int64_t qq = rem / a.G;
-            row = qq * a.Hq + gg * a.G + (rem - qq * a.G);
+            const uint32_t rp = (blockIdx.x % kXcds) * (R / kXcds) + blockIdx.x / kXcds;
+            const uint32_t per_g = (R / (uint32_t)a.Hq) * (uint32_t)a.G;   // rows of one KV head
+            const uint32_t gg = rp / per_g, rem = rp - gg * per_g;
+            const uint32_t qq = rem / (uint32_t)a.G;
+            row = qq * (uint32_t)a.Hq + gg * (uint32_t)a.G + (rem - qq * (uint32_t)a.G);
         }
     }
-    const int32_t rows_per_q = a.Hq / GS;
-    const int64_t qi = row / rows_per_q;
+    const uint32_t rows_per_q = (uint32_t)(a.Hq / GS);
+    const uint32_t qi = row / rows_per_q;
     const int h0 = (int)(row - qi * rows_per_q) * GS;     // first query head of the row
     const int g = h0 / a.G;
-    int64_t n_ctx = a.ctx_base + qi * a.ctx_step;
+    int64_t n_ctx = a.ctx_base + (int64_t)qi * a.ctx_step;
     // multi-sequence decode: this query's sequence, as byte offsets from sequence 0's buffers
     int64_t dk = 0, dv = 0, dt = 0;
     if (a.seqs != nullptr || a.n_inline > 0) {
@@ -421,16 +426,22 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     const int nlev = tv.n_levels;
     const float2 *rope = tv.rope;
 
-    // levels above the tokens for this row: H = max{l : n_ctx / b^l >= 1}
+    // levels above the tokens for this row, H = max{l : n_ctx / b^l >= 1}, and the node
+    // counts N_l by repeated 32-bit division (n_ctx < 2^31; floor(N_l / b) = N_{l+1})
     int H = 0;
-    int64_t pwH = 1;
-    while (n_ctx / (pwH * b) >= 1) { pwH *= b; ++H; }
+    int32_t NH = (int32_t)n_ctx;
+    if (threadIdx.x == 0) ntab[0] = NH;
+    while (NH >= b) {
+        NH /= b;
+        ++H;
+        if (threadIdx.x == 0) ntab[H] = NH;
+    }
 
     // The top level (H >= 1) has fewer than b nodes, all of them candidates at rank 0:
     // with at most 64 of them, their keys and child-offset rotations are loaded now,
     // alongside the query, instead of after the query's rotation is built.
     constexpr int CT = NSLOT >= 64 ? 1 : 64 / NSLOT;
-    sel::Cands cA = level_cands(n_ctx, pwH, b, true, 0);
+    sel::Cands cA = level_cands(NH, 0, b, true, 0);
     const bool top_early = H >= 1 && cA.n <= CT * NSLOT;
     Raw<T, PP> tka[CT], tkb[CT];
     float tc[CT][PP], ts[CT][PP];
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     load_cs<PP>(rope + (int64_t)cA.n * H2 + j0, topc, tops);
     // the row's queries: in registers for one head, in LDS for a group
     float qa[PP], qb[PP];
-    const T *qrow = static_cast<const T *>(a.q) + (qi * a.Hq + h0) * D;
+    const T *qrow = static_cast<const T *>(a.q) + (int64_t)(qi * a.Hq + h0) * D;
     if constexpr (GS == 1) {
         Vec<T, PP>::load(qrow + j0, qa);
         Vec<T, PP>::load(qrow + H2 + j0, qb);
@@ -467,8 +478,8 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     if (threadIdx.x == 0) {
         for (int l = H + 1; l <= nlev; ++l) {
             if (dbg.selected != nullptr)
-                for (int t = 0; t < a.k; ++t) dbg.selected[(row * nlev + l - 1) * a.k + t] = -1;
-            if (dbg.kth_gap != nullptr) dbg.kth_gap[row * nlev + l - 1] = NAN;
+                for (int t = 0; t < a.k; ++t) dbg.selected[((int64_t)row * nlev + l - 1) * a.k + t] = -1;
+            if (dbg.kth_gap != nullptr) dbg.kth_gap[(int64_t)row * nlev + l - 1] = NAN;
         }
     }
 
@@ -597,15 +608,14 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     // Levels H..1: select level l, then one pass over level l's entries and level l-1's
     // candidates.  At l = 1 those are tokens, which join the softmax as they are scored,
     // so the tokens' keys and values come in one round trip.
-    int64_t pw = pwH;
-    for (int l = H; l >= 1; --l, pw /= b) {
+    for (int l = H; l >= 1; --l) {
         __syncthreads();
         const int bufA = l & 1, bufS = (l + 1) & 1;
         uint8_t *flagA = flagbuf + bufA * maxc;
         const int32_t mA = a.k < cA.n ? a.k : cA.n;
         const int32_t *parentsA = kept + bufS * a.k;
         int32_t *keptA = kept + bufA * a.k;
-        const sel::Cands cS = level_cands(n_ctx, pw / b, b, false, mA);
+        const sel::Cands cS = level_cands(ntab[l - 1], ntab[l], b, false, mA);
         // ---- selection at level l (wave 0); the other waves build level l-1's ranks -----
         if (wave == 0) {
             const float *zA = zsel(bufA);
@@ -618,9 +628,9 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
                 sel::select<0>(zA, flagA, keptA, mA, cA, parentsA, lane, scratch, misc);
             }
             if (lane == 0 && dbg.kth_gap != nullptr)
-                dbg.kth_gap[row * nlev + l - 1] = misc[1] - misc[2];
+                dbg.kth_gap[(int64_t)row * nlev + l - 1] = misc[1] - misc[2];
             if (dbg.selected != nullptr) {
-                int32_t *ds = dbg.selected + (row * nlev + l - 1) * a.k;
+                int32_t *ds = dbg.selected + ((int64_t)row * nlev + l - 1) * a.k;
                 for (int q = lane; q < a.k; q += 64) ds[q] = q < mA ? keptA[q] : -1;
             }
         } else {
@@ -717,7 +727,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         }
         #pragma unroll
         for (int p = 0; p < PP; ++p) { oa[p] /= L; ob[p] /= L; }
-        const int64_t orow = qi * a.Hq + h0 + j;
+        const int64_t orow = (int64_t)qi * a.Hq + h0 + j;
         if (a.out_bf16) {
             bf16_t *o = static_cast<bf16_t *>(a.out) + orow * D;
             Vec<bf16_t, PP>::store(o + j0, oa);
