@@ -75,6 +75,7 @@ __device__ __forceinline__ sel::Cands level_cands(int64_t n_ctx, int64_t pw, int
     sel::Cands c;
     const int64_t Nl = n_ctx / pw;
     c.b = b;
+    c.bmul = sel::fanout_magic((uint32_t)b);
     c.top = top;
     if (top) {
         c.n = (int32_t)Nl;

@@ -109,6 +109,7 @@ __device__ __forceinline__ sel::Cands level_cands(int32_t Nl, int32_t Nup, int32
                                                   int32_t kept_above) {
     sel::Cands c;
     c.b = b;
+    c.bmul = sel::fanout_magic((uint32_t)b);
     c.top = top;
     if (top) {
         c.n = Nl;

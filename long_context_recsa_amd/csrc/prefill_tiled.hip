@@ -742,6 +742,7 @@ __device__ __forceinline__ void select_row(const TP &a, const DebugView &dbg, in
     cd.n = n;
     cd.nchild = rl.m * a.b;
     cd.b = a.b;
+    cd.bmul = sel::fanout_magic((uint32_t)a.b);
     cd.top = 0;
     cd.orphan0 = (int32_t)(rl.part * a.b);
     sel::select<KT>(zr, flag, kept, mm, cd, parl, lane, scratch, outv);
@@ -799,6 +800,7 @@ __device__ __forceinline__ void select_row_in(const TP &a, const DebugView &dbg,
     cd.n = n;
     cd.nchild = rl.m * a.b;
     cd.b = a.b;
+    cd.bmul = sel::fanout_magic((uint32_t)a.b);
     cd.top = 0;
     cd.orphan0 = (int32_t)(rl.part * a.b);
     uint32_t kk[KT];

@@ -93,12 +93,18 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane
 struct Cands {
     int32_t n, nchild, b, top;
     int32_t orphan0;
+    uint32_t bmul;      // fanout_magic(b): i / b == umulhi(i, bmul) for candidate indexes
 };
+
+// The multiplier m = floor((2^32 - 1) / b) + 1 (b >= 2).  With m b = 2^32 + e, 0 <= e < b,
+// i m / 2^32 = i / b + i e / (b 2^32), whose floor is floor(i / b) whenever i b < 2^32:
+// far above any level's candidate count times its fanout.
+__host__ __device__ __forceinline__ uint32_t fanout_magic(uint32_t b) { return 0xFFFFFFFFu / b + 1u; }
 
 __device__ __forceinline__ int32_t node_id(int32_t i, const Cands &c, const int32_t *parents) {
     if (c.top) return i;
     if (i < c.nchild) {
-        const int32_t q = i / c.b;
+        const int32_t q = (int32_t)__umulhi((uint32_t)i, c.bmul);
         return parents[q] * c.b + (i - q * c.b);
     }
     return c.orphan0 + (i - c.nchild);
