@@ -544,6 +544,7 @@ def measure_workload(w, batches, steps, warmup, backward=True):
     del K, V
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    dense = dense_context(layer, w, q_dec[Bmax])
 
     ops = (["build"] + [f"decode_B{B}" for B in batches] + ["decode_grouped"]
            + (["backward"] if backward else []) + (["append", "prefill"] if w.prefill_n else []))
@@ -626,7 +627,31 @@ def measure_workload(w, batches, steps, warmup, backward=True):
                                  if w.prefill_n else None),
         "setup_s": t_setup, "timed_wall_s": wall,
     }
+    if dense is not None:
+        # context only: the same batch through dense causal attention (recsa_dense_decode,
+        # every cached token) on the same cache; the pages quote RecSA against dense
+        # attention on their own hardware
+        res["dense_context"] = {"dense_decode_ms": dense, "batch": Bmax,
+                                "recsa_decode_speedup": dense / med[f"decode_B{Bmax}"]}
     return res, wall
+
+
+def dense_context(layer, w, q, reps=5):
+    """Median time (ms) of dense decode of the batch q over the first w.L tokens: one
+    untimed call, then `reps` timed ones, outside the timed steps."""
+    import torch
+    layer.build(w.L)
+    out = torch.empty((q.shape[0], w.n_q, w.d), dtype=torch.float32, device=q.device)
+    layer.dense_decode(q, out=out)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.dense_decode(q, out=out)
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ts]))
 
 
 def backward_bytes(w, B):
@@ -740,6 +765,8 @@ def main():
         "configs": configs,
         "setup_s": head["setup_s"],
     }
+    if "dense_context" in head:
+        res["dense_context"] = head["dense_context"]
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

@@ -918,6 +918,9 @@ __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int3
     float *slice = a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D;
     const int64_t n = *a.n_items;
     const int64_t nruns = (n + kRun - 1) / kRun;
+    // a rank's logits start 16-byte aligned (zs is a multiple of 4), and the 32 slots
+    // the lane groups read from the last rank's start (k b) lie inside the row
+    const bool vec_z = (a.b & 3) == 0 && a.k * a.b + 32 <= a.zs;
     const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
     // each run's item records (bucket and pair count, uniform; this lane's pair)
     struct Recs {
@@ -950,13 +953,25 @@ __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int3
         #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             const int32_t nc = (u < nit && i16 < cnt[u]) ? pr[u].w : 0;
-            const float *zr = a.z + (int64_t)pr[u].x * a.zs + pr[u].y * a.b;
-            #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const int c = 8 * grp + v;
-                const float zz = zr[c < nc ? c : 0];
-                w[u][0][v] = c < nc ? zz : -INFINITY;
+            const int32_t seg = pr[u].y * a.b + 8 * grp;          // this lane's 8 logits in the row
+            const float *zr = a.z + (int64_t)pr[u].x * a.zs;
+            float zz[8];
+            if (vec_z) {
+                // two 16-byte loads (the slots past the children read the row's next
+                // logits, which the mask below drops)
+                const float4 x0 = *reinterpret_cast<const float4 *>(zr + seg);
+                const float4 x1 = *reinterpret_cast<const float4 *>(zr + seg + 4);
+                zz[0] = x0.x; zz[1] = x0.y; zz[2] = x0.z; zz[3] = x0.w;
+                zz[4] = x1.x; zz[5] = x1.y; zz[6] = x1.z; zz[7] = x1.w;
+            } else {
+                #pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const int c = 8 * grp + v;
+                    zz[v] = zr[c < nc ? seg - 8 * grp + c : 0];
+                }
             }
+            #pragma unroll
+            for (int v = 0; v < 8; ++v) w[u][0][v] = 8 * grp + v < nc ? zz[v] : -INFINITY;
         }
         VRaw<D> vr;
         int32_t held = -1;                  // the bucket whose values vr holds

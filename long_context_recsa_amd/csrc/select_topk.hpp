@@ -169,14 +169,13 @@ __device__ __noinline__ void select_bisect(const float *z, uint8_t *flag, int32_
 // per lane live in registers (KT == 0: bisection over LDS).  Results in out[0..3):
 // level max, m-th and (m+1)-th largest logit (NaN when n == m); visible to the
 // calling wave on return.
-// Bisection for the m-th largest key with the keys in registers (narrow levels:
-// ballot rounds over KT registers beat the filter's LDS round trips there).
-// The largest threshold T with at least m of the keys (NT registers per lane;
-// unused slots 0) >= T, bit by bit from bit `top` down, starting from T (a value
-// with at least m keys >= it, zero below bit `top`).  Once exactly m keys are >=
-// the trial threshold, every threshold in that gap keeps the same m keys: stop there.
+// Bisection with the keys in registers: a threshold T with at least m of the keys
+// (NT registers per lane; unused slots 0) >= T, raised bit by bit from bit `top`
+// down, starting from T (a value with at least m keys >= it, zero below bit `top`).
+// It stops as soon as at most `cap` keys are >= the threshold (they include the m
+// largest, which the caller then ranks), else at the m-th largest key itself.
 template <int NT>
-__device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m, uint32_t T, int top) {
+__device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m, uint32_t T, int top, int cap) {
     for (int bit = top; bit >= 0; --bit) {
         const uint32_t trial = T | (1u << bit);
         int c = 0;
@@ -184,10 +183,20 @@ __device__ __forceinline__ uint32_t bisect_threshold(const uint32_t *kk, int m, 
         for (int t = 0; t < NT; ++t) c += __popcll(__ballot(kk[t] >= trial));
         if (c >= m) {
             T = trial;
-            if (c == m) break;
+            if (c <= cap) break;
         }
     }
     return T;
+}
+
+// Number of keys >= x over the first nT registers (x >= 1: unused slots hold 0).
+template <int KT>
+__device__ __forceinline__ int count_ge(const uint32_t (&kk)[KT], int nT, uint32_t x) {
+    int c = 0;
+    #pragma unroll
+    for (int t = 0; t < KT; ++t)
+        if (t < nT) c += __popcll(__ballot(kk[t] >= x));
+    return c;
 }
 
 // The ordered keys of candidates lane, lane + 64, ... of z[0..n) (0 past n: valid
@@ -201,10 +210,42 @@ __device__ __forceinline__ void load_keys(const float *z, int32_t n, int lane, u
     }
 }
 
+// The m largest of c <= 64 survivor keys (every key >= T, the rest are < T), listed
+// in ascending candidate order in cs[0..c) (keys) and cs[64..64+c) (candidate
+// indexes): each survivor's rank is counted exactly, as in select_small.  `below` is
+// this lane's largest key under T (the (m+1)-th largest when exactly m survive).
+__device__ __forceinline__ void rank_survivors(const uint32_t *cs, int32_t c, uint32_t kmax, uint32_t below,
+                                               uint8_t *flag, int32_t *kept, int32_t m, Cands cd,
+                                               const int32_t *parents, int lane, float *out) {
+    const bool valid = lane < c;
+    const uint32_t key = valid ? cs[lane] : 0u;
+    const int32_t idx = valid ? (int32_t)cs[64 + lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < c; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+        rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+    }
+    const bool keep = valid && rank < m;
+    const uint64_t km = __ballot(keep);
+    if (keep) {
+        kept[__popcll(km & lanes_below(lane))] = node_id(idx, cd, parents);
+        flag[idx] = 1;
+    }
+    const uint64_t rm1 = __ballot(valid && rank == m - 1);
+    const uint64_t rm = __ballot(valid && rank == m);
+    const uint32_t kb = wave_umax(below);
+    if (lane == 0) {
+        out[0] = from_ordered(kmax);
+        out[1] = from_ordered((uint32_t)__builtin_amdgcn_readlane((int)key, (int)__builtin_ctzll(rm1)));
+        out[2] = c > m ? from_ordered((uint32_t)__builtin_amdgcn_readlane((int)key, (int)__builtin_ctzll(rm)))
+                       : (cd.n > m ? from_ordered(kb) : NAN);
+    }
+}
+
 template <int KT>
 __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uint8_t *flag, int32_t *kept,
                                                    int32_t m, Cands cd, const int32_t *parents,
-                                                   int lane, float *out) {
+                                                   int lane, uint32_t *cs, float *out) {
     // wave-uniform counts in scalar registers (they may come from a vector load)
     const int32_t n = __builtin_amdgcn_readfirstlane(cd.n);
     m = __builtin_amdgcn_readfirstlane(m);
@@ -220,6 +261,10 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
     // there: the threshold with those bits and zeros below has >= m keys above it.
     uint32_t T = 0;
     int top = 31;
+    // survivors: keys >= a threshold that at least m and at most 64 keys reach; they
+    // are then ranked exactly.  The lower bound tau often leaves few enough already.
+    uint32_t Ts = 0;
+    int cT = 0;
     if (m <= 32) {
         uint32_t gmax;
         if (m <= 4) gmax = group_umax<16>(lmax);
@@ -230,17 +275,49 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
         const uint32_t d = tau ^ kmax;
         top = d == 0u ? -1 : 31 - (int)__builtin_clz(d);
         T = top < 0 ? kmax : (top == 31 ? 0u : kmax & ~((2u << top) - 1u));
+        Ts = tau > 1u ? tau : 1u;
+        cT = count_ge<KT>(kk, nT, Ts);
     }
-    if (nT <= 1)
-        T = bisect_threshold<1>(kk, m, T, top);
-    else if (nT <= 2 || KT <= 2)
-        T = bisect_threshold<(KT < 2 ? KT : 2)>(kk, m, T, top);
-    else if (nT <= 3 || KT <= 3)
-        T = bisect_threshold<(KT < 3 ? KT : 3)>(kk, m, T, top);
-    else if (nT <= 4 || KT <= 4)
-        T = bisect_threshold<(KT < 4 ? KT : 4)>(kk, m, T, top);
-    else
-        T = bisect_threshold<KT>(kk, m, T, top);
+    if (cT == 0 || cT > 64) {
+        if (nT <= 1)
+            T = bisect_threshold<1>(kk, m, T, top, 64);
+        else if (nT <= 2 || KT <= 2)
+            T = bisect_threshold<(KT < 2 ? KT : 2)>(kk, m, T, top, 64);
+        else if (nT <= 3 || KT <= 3)
+            T = bisect_threshold<(KT < 3 ? KT : 3)>(kk, m, T, top, 64);
+        else if (nT <= 4 || KT <= 4)
+            T = bisect_threshold<(KT < 4 ? KT : 4)>(kk, m, T, top, 64);
+        else
+            T = bisect_threshold<KT>(kk, m, T, top, 64);
+        Ts = T > 1u ? T : 1u;
+        cT = count_ge<KT>(kk, nT, Ts);
+    }
+    if (cT <= 64) {
+        // compact the survivors, in ascending candidate order, into cs
+        int32_t base = 0;
+        uint32_t below = 0;
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            if (t >= nT) break;
+            const int32_t i = lane + 64 * t;
+            const bool sv = kk[t] >= Ts;
+            const uint64_t mask = __ballot(sv);
+            if (sv) {
+                const int32_t p = base + __popcll(mask & lanes_below(lane));
+                cs[p] = kk[t];
+                cs[64 + p] = (uint32_t)i;
+            } else if (i < n) {
+                below = max(below, kk[t]);
+            }
+            base += __popcll(mask);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        rank_survivors(cs, cT, kmax, below, flag, kept, m, cd, parents, lane, out);
+        return;
+    }
+    // more than 64 keys tie at the m-th largest: T is that key
     // kept: every key > T, then keys == T in ascending index until m are kept
     int gt = 0;
     #pragma unroll
@@ -322,7 +399,7 @@ __device__ __forceinline__ void select_from_keys(const uint32_t (&kk)[KT], const
         __threadfence_block();
         return;
     }
-    select_bisect_regs<KT>(kk, flag, kept, m, cd, parents, lane, out);
+    select_bisect_regs<KT>(kk, flag, kept, m, cd, parents, lane, reinterpret_cast<uint32_t *>(scratch), out);
     __threadfence_block();
 }
 
