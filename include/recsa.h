@@ -247,7 +247,7 @@ RECSA_API size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t m
  * (written, so the tokens' gradients are never read back), then the rows' own
  * token entries are added (fp32 atomics, or read-add-store where one work
  * item owns a node's tokens); with more than one pass of rows on the
- * parent-major path (over 131072 rows) the tokens' gradients are cleared
+ * parent-major path (over 262144 rows) the tokens' gradients are cleared
  * first and added to instead.
  * Rounding a summary to store_dtype passes the gradient through unchanged.
  * Entry logits, softmax and the selection are recomputed as in the forward.

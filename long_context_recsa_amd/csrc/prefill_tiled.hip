@@ -52,7 +52,7 @@ constexpr int64_t kHistRows = 2048;
 constexpr int kRange = 2048;            // else: parents per counting block
 constexpr int kScanPer = 16;            // bucket sizes per thread in the scans
 constexpr int kScanChunk = kScanPer * 256;
-constexpr int64_t kRowsPerPass = 1 << 17;
+constexpr int64_t kRowsPerPass = 1 << 18;   // rows per pass: 8192 queries of 32 heads
 
 struct TP {
     const bf16_t *q;           // [rows][D]

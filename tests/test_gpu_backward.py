@@ -148,8 +148,8 @@ def test_backward_overwrites_given_gradients(path, dtype, nq, L, b):
 
 
 def test_backward_tiled_full_131k():
-    """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 4224
-    queries (135168 rows: the parent-major path's two passes of at most 131072 rows):
+    """The Qwen3-4B layer at its full 131072-token context, a causal chunk of 8320
+    queries (266240 rows: the parent-major path's two passes of at most 262144 rows):
     the parent-major backward against the row-wise one (itself pinned to the oracle
     above).  Rows whose selections differ between the two (a near-tie under the
     parent-major forward's split-bf16 logits) are each checked against the oracle
@@ -158,7 +158,7 @@ def test_backward_tiled_full_131k():
     (the parent-major run writes over buffers that held other values).  Sampled rows' dq, in both passes, is also checked against the oracle on the GPU's
     selections."""
     w = synth.WORKLOADS["qwen3_4b_131k"]
-    L, n = w.L, 4224
+    L, n = w.L, 8320
     _say(f"case backward tiled vs rowwise qwen3_4b_131k L={L} n={n} causal")
     K, V = synth.gen_kv(w, 0, L)
     W = synth.pool_w(w)
@@ -216,7 +216,7 @@ def test_backward_tiled_full_131k():
     dq_gpu = gt["dq"].cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
     dOn = dO2.cpu().numpy().astype(np.float64).reshape(n * w.n_q, w.d)
     refs, gots = [], []
-    for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, 131072 + 5, n * w.n_q - 1):
+    for r in (0, 5 * w.n_q + 7, (n // 2) * w.n_q + 20, 262144 + 5, n * w.n_q - 1):
         if bool(bad[r]):
             continue
         i, h = divmod(r, w.n_q)
