@@ -910,7 +910,7 @@ __device__ __forceinline__ Item make_item(int4 rec, int4 pr, int32_t NP, int grp
     return it;
 }
 
-template <int D, int kRun>
+template <int D, int KC, int kRun>
 __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int32_t NP) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, i16 = lane & 15;
@@ -918,9 +918,9 @@ __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int3
     float *slice = a.partial + (int64_t)l * a.rows_cap * (a.k + 1) * D;
     const int64_t n = *a.n_items;
     const int64_t nruns = (n + kRun - 1) / kRun;
-    // a rank's logits start 16-byte aligned (zs is a multiple of 4), and the 32 slots
+    // a rank's logits start 16-byte aligned (zs is a multiple of 4), and the 32 KC slots
     // the lane groups read from the last rank's start (k b) lie inside the row
-    const bool vec_z = (a.b & 3) == 0 && a.k * a.b + 32 <= a.zs;
+    const bool vec_z = (a.b & 3) == 0 && a.k * a.b + 32 * KC <= a.zs;
     const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
     // each run's item records (bucket and pair count, uniform; this lane's pair)
     struct Recs {
@@ -949,45 +949,51 @@ __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int3
         const int nit = (int)__builtin_amdgcn_readfirstlane((int32_t)min<int64_t>(kRun, n - i0));
         const int32_t *bkt = cur.bkt, *cnt = cur.cnt;
         const int4 *pr = cur.pr;
-        float w[kRun][1][8];
+        float w[kRun][KC][8];
         #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             const int32_t nc = (u < nit && i16 < cnt[u]) ? pr[u].w : 0;
-            const int32_t seg = pr[u].y * a.b + 8 * grp;          // this lane's 8 logits in the row
             const float *zr = a.z + (int64_t)pr[u].x * a.zs;
-            float zz[8];
-            if (vec_z) {
-                // two 16-byte loads (the slots past the children read the row's next
-                // logits, which the mask below drops)
-                const float4 x0 = *reinterpret_cast<const float4 *>(zr + seg);
-                const float4 x1 = *reinterpret_cast<const float4 *>(zr + seg + 4);
-                zz[0] = x0.x; zz[1] = x0.y; zz[2] = x0.z; zz[3] = x0.w;
-                zz[4] = x1.x; zz[5] = x1.y; zz[6] = x1.z; zz[7] = x1.w;
-            } else {
-                #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const int c = 8 * grp + v;
-                    zz[v] = zr[c < nc ? seg - 8 * grp + c : 0];
-                }
-            }
             #pragma unroll
-            for (int v = 0; v < 8; ++v) w[u][0][v] = 8 * grp + v < nc ? zz[v] : -INFINITY;
+            for (int kk = 0; kk < KC; ++kk) {
+                const int32_t seg = pr[u].y * a.b + 32 * kk + 8 * grp;   // this lane's 8 logits in the row
+                float zz[8];
+                if (vec_z) {
+                    // two 16-byte loads (the slots past the children read the row's next
+                    // logits, which the mask below drops)
+                    const float4 x0 = *reinterpret_cast<const float4 *>(zr + seg);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(zr + seg + 4);
+                    zz[0] = x0.x; zz[1] = x0.y; zz[2] = x0.z; zz[3] = x0.w;
+                    zz[4] = x1.x; zz[5] = x1.y; zz[6] = x1.z; zz[7] = x1.w;
+                } else {
+                    #pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        const int c = 32 * kk + 8 * grp + v;
+                        zz[v] = zr[c < nc ? pr[u].y * a.b + c : 0];
+                    }
+                }
+                #pragma unroll
+                for (int v = 0; v < 8; ++v) w[u][kk][v] = 32 * kk + 8 * grp + v < nc ? zz[v] : -INFINITY;
+            }
         }
-        VRaw<D> vr;
+        VRaw<D> vr[KC];
         int32_t held = -1;                  // the bucket whose values vr holds
         #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             if (u < nit) {
                 const Item it = make_item(make_int4(bkt[u], 0, cnt[u], 0), pr[u], NP, grp);
                 if (bkt[u] != held) {
-                    load_values<D>(level_rows(tv, true, l, it.g, D), it.p * a.b, nexist, a.b, 0, lane, vr);
+                    const bf16_t *vals = level_rows(tv, true, l, it.g, D);
+                    #pragma unroll
+                    for (int kk = 0; kk < KC; ++kk) load_values<D>(vals, it.p * a.b, nexist, a.b, kk, lane, vr[kk]);
                     held = bkt[u];
                 }
-                pair_softmax<1>(a, it, l, lane, w[u]);
+                pair_softmax<KC>(a, it, l, lane, w[u]);
                 f32x4 acc[D / 16];
                 #pragma unroll
                 for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pv_accumulate<D>(vr, w[u][0], acc);
+                #pragma unroll
+                for (int kk = 0; kk < KC; ++kk) pv_accumulate<D>(vr[kk], w[u][kk], acc);
                 pv_store<D>(a, it, lane, acc, slice);
             }
         }
@@ -1606,13 +1612,18 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
             if constexpr (KC == 1) {
                 if (rows >= kLongRunRows) {
                     const unsigned rb = (unsigned)((items / 8 + 1 + 3) / 4);
-                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 8>, 0, rb, grid)) != hipSuccess) return e;
-                    hipLaunchKernelGGL((tp_pv_runs<D, 8>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 1, 8>, 0, rb, grid)) != hipSuccess) return e;
+                    hipLaunchKernelGGL((tp_pv_runs<D, 1, 8>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
                 } else {
                     const unsigned rb = (unsigned)((items / 4 + 1 + 3) / 4);
-                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 4>, 0, rb, grid)) != hipSuccess) return e;
-                    hipLaunchKernelGGL((tp_pv_runs<D, 4>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
+                    if ((e = persistent_grid((const void *)tp_pv_runs<D, 1, 4>, 0, rb, grid)) != hipSuccess) return e;
+                    hipLaunchKernelGGL((tp_pv_runs<D, 1, 4>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
                 }
+            } else if constexpr (KC == 2) {
+                // two chunks of children per item: runs of 2 items keep 2 waves per SIMD
+                const unsigned rb = (unsigned)((items / 2 + 1 + 3) / 4);
+                if ((e = persistent_grid((const void *)tp_pv_runs<D, 2, 2>, 0, rb, grid)) != hipSuccess) return e;
+                hipLaunchKernelGGL((tp_pv_runs<D, 2, 2>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
             } else {
                 if ((e = persistent_grid((const void *)tp_pv<D, KC>, 0, ib, grid)) != hipSuccess) return e;
                 hipLaunchKernelGGL((tp_pv<D, KC>), dim3(grid), dim3(256), 0, s, tv, a, l, NP);
