@@ -1003,6 +1003,82 @@ __global__ __launch_bounds__(256) void tp_pv_runs(TreeView tv, TP a, int l, int3
     }
 }
 
+// tp_score over runs of kRun consecutive items: the items of one (head, parent)
+// bucket are consecutive, so a run mostly scores one parent's children, and those
+// keys are loaded once per parent rather than once per item (at the upper levels a
+// parent has tens of items, and re-reading its keys from L2 bounds the kernel).
+template <int D, int KC, int kRun>
+__global__ __launch_bounds__(256) void tp_score_runs(TreeView tv, TP a, int l, int32_t NP) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float2 *crot = reinterpret_cast<float2 *>(smem);
+    load_crot(tv, a.b, D, crot);
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, i16 = lane & 15;
+    const int64_t nexist = a.length / a.pw[l];
+    const int64_t n = *a.n_items;
+    const int64_t nruns = (n + kRun - 1) / kRun;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    struct Recs {
+        int32_t bkt[kRun], cnt[kRun];
+        int4 pr[kRun];
+    };
+    auto fetch = [&](int64_t run, Recs &r) {
+        const int64_t i0 = run * kRun;
+        #pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            const int64_t i = i0 + u < n ? i0 + u : i0;
+            const int4 rec = a.items[i];
+            r.bkt[u] = __builtin_amdgcn_readfirstlane(rec.x);
+            r.cnt[u] = __builtin_amdgcn_readfirstlane(rec.z);
+            r.pr[u] = a.sorted[i * kTile + i16];
+        }
+    };
+    int64_t run = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
+    if (run >= nruns) return;
+    Recs cur, nxt;
+    fetch(run, cur);
+    for (;;) {
+        const int64_t next = run + nw;
+        if (next < nruns) fetch(next, nxt);
+        const int64_t i0 = run * kRun;
+        const int nit = (int)__builtin_amdgcn_readfirstlane((int32_t)min<int64_t>(kRun, n - i0));
+        KRaw<D> kr[KC];
+        int32_t held = -1;                  // the bucket whose keys kr holds
+        #pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            if (u < nit) {
+                const Item it = make_item(make_int4(cur.bkt[u], 0, cur.cnt[u], 0), cur.pr[u], NP, grp);
+                const int64_t c0 = it.p * a.b;
+                QRaw<D> qr;
+                load_query<D>(tv, a, it, lane, qr);
+                if (cur.bkt[u] != held) {
+                    const bf16_t *keys = level_rows(tv, false, l, it.g, D);
+                    #pragma unroll
+                    for (int kk = 0; kk < KC; ++kk) load_keys<D>(keys, c0, nexist, a.b, kk, lane, kr[kk]);
+                    held = cur.bkt[u];
+                }
+                bf16x8 ah[D / 32], al[D / 32];
+                query_operands<D>(qr, it, lane, ah, al);
+                #pragma unroll
+                for (int kk = 0; kk < KC; ++kk) {
+                    #pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 acc = score_tile<D>(kr[kk], t, crot, c0, nexist, a.b, kk, lane, ah, al);
+                        const int c = 32 * kk + 16 * t + i16;
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (c < it.onc[v])
+                                a.z[(int64_t)it.orow[v] * a.zs + it.orank[v] * a.b + c] = a.scale * acc[v];
+                    }
+                }
+            }
+        }
+        if (next >= nruns) break;
+        run = next;
+        cur = nxt;
+    }
+}
+
 // ---------------------------------------------------------------- attend --
 // Level 0: each item's pairs against the parent's tokens, the pairs' softmax
 // states and P.V in one pass; the logits go through LDS from the score tile's
@@ -1605,9 +1681,18 @@ hipError_t run_pass(const TreeView &tv, TP a, const DebugView &dbg, int64_t max_
             hipLaunchKernelGGL((tp_attend<D, KC>), dim3(grid), dim3(256), sm, s, tv, a, NP);
         } else {
             unsigned grid;
-            if ((e = persistent_grid((const void *)tp_score<D, KC>, crot_bytes, ib, grid)) != hipSuccess)
-                return e;
-            hipLaunchKernelGGL((tp_score<D, KC>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
+            if constexpr (KC <= 2) {
+                constexpr int kR = 4;
+                const unsigned rb = (unsigned)((items / kR + 1 + 3) / 4);
+                if ((e = persistent_grid((const void *)tp_score_runs<D, KC, kR>, crot_bytes, rb, grid)) !=
+                    hipSuccess)
+                    return e;
+                hipLaunchKernelGGL((tp_score_runs<D, KC, kR>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
+            } else {
+                if ((e = persistent_grid((const void *)tp_score<D, KC>, crot_bytes, ib, grid)) != hipSuccess)
+                    return e;
+                hipLaunchKernelGGL((tp_score<D, KC>), dim3(grid), dim3(256), crot_bytes, s, tv, a, l, NP);
+            }
             if ((e = launch_select(a, dbg, l, maxc, smw, s)) != hipSuccess) return e;
             if constexpr (KC == 1) {
                 if (rows >= kLongRunRows) {
