@@ -509,32 +509,33 @@ __device__ __forceinline__ void unpack8(uint4 x, float *f) {
     f[6] = bf16_to_f32(x.w & 0xFFFFu); f[7] = bf16_to_f32(x.w >> 16);
 }
 
-// rotate (x1, x2) by the 8 (cos, sin) pairs in cs, times `live`, and split to bf16
-__device__ __forceinline__ void rotate_split(uint4 a1, uint4 a2, const float4 *cs, float live,
-                                             bf16x8 &h1, bf16x8 &l1, bf16x8 &h2, bf16x8 &l2) {
+// rotate (x1, x2) by the 8 (cos, sin) pairs in cs and split to bf16
+__device__ __forceinline__ void rotate_split(uint4 a1, uint4 a2, const float4 *cs, bf16x8 &h1, bf16x8 &l1,
+                                             bf16x8 &h2, bf16x8 &l2) {
     float x1[8], x2[8], r1[8], r2[8];
     unpack8(a1, x1);
     unpack8(a2, x2);
     #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const float4 v = cs[u];
-        r1[2 * u] = live * (x1[2 * u] * v.x - x2[2 * u] * v.y);
-        r2[2 * u] = live * (x2[2 * u] * v.x + x1[2 * u] * v.y);
-        r1[2 * u + 1] = live * (x1[2 * u + 1] * v.z - x2[2 * u + 1] * v.w);
-        r2[2 * u + 1] = live * (x2[2 * u + 1] * v.z + x1[2 * u + 1] * v.w);
+        r1[2 * u] = x1[2 * u] * v.x - x2[2 * u] * v.y;
+        r2[2 * u] = x2[2 * u] * v.x + x1[2 * u] * v.y;
+        r1[2 * u + 1] = x1[2 * u + 1] * v.z - x2[2 * u + 1] * v.w;
+        r2[2 * u + 1] = x2[2 * u + 1] * v.z + x1[2 * u + 1] * v.w;
     }
     split8(r1, h1, l1);
     split8(r2, h2, l2);
 }
 
+// (Slots past the item's pairs rotate row 0's query: their rows of every product are
+// dropped by the consumers' masks, so they need no zeroing.)
 template <int D>
 __device__ __forceinline__ void query_operands(const QRaw<D> &r, const Item &it, int lane, bf16x8 *ah,
                                                bf16x8 *al) {
     constexpr int KS1 = D / 64;
-    const float live = (lane & 15) < it.cnt ? 1.f : 0.f;
     #pragma unroll
     for (int pc = 0; pc < KS1; ++pc)
-        rotate_split(r.q[2 * pc], r.q[2 * pc + 1], &r.cs[4 * pc], live, ah[pc], al[pc], ah[pc + KS1],
+        rotate_split(r.q[2 * pc], r.q[2 * pc + 1], &r.cs[4 * pc], ah[pc], al[pc], ah[pc + KS1],
                      al[pc + KS1]);
 }
 
@@ -575,6 +576,8 @@ __device__ __forceinline__ f32x4 score_tile(const KRaw<D> &r, int t, const float
     const int i16 = lane & 15, grp = lane >> 4;
     const int c = 32 * kk + 16 * t + i16;
     const bool ok = c < b && c0 + c < nexist;
+    // a missing child's column is scored against the base row and dropped by every
+    // consumer's mask (c < the pair's children), so it needs no zeroing
     const float4 *cs = reinterpret_cast<const float4 *>(crot + (ok ? c : 0) * crot_stride(D) + grp * PG);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
@@ -583,7 +586,7 @@ __device__ __forceinline__ f32x4 score_tile(const KRaw<D> &r, int t, const float
         #pragma unroll
         for (int u = 0; u < 4; ++u) c4[u] = cs[4 * pc + u];
         bf16x8 h1, l1, h2, l2;
-        rotate_split(r.k[t][2 * pc], r.k[t][2 * pc + 1], c4, ok ? 1.f : 0.f, h1, l1, h2, l2);
+        rotate_split(r.k[t][2 * pc], r.k[t][2 * pc + 1], c4, h1, l1, h2, l2);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], h1, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[pc], l1, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[pc], h1, acc, 0, 0, 0);
@@ -1511,7 +1514,9 @@ __device__ __forceinline__ void final_one(const TP &a, int64_t t, int D4) {
         #pragma unroll 8
         for (int r = 0; r < np; ++r) {
             const float2 s = ml[r];
-            const float4 x = pa[r * D4];
+            // the pair states are read once: nontemporal
+            const f32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(pa + r * D4));
+            const float4 x = make_float4(xv[0], xv[1], xv[2], xv[3]);
             const float e = s.x == -INFINITY ? 0.f : __expf(s.x - M);
             L += e * s.y;
             v.x += e * x.x; v.y += e * x.y; v.z += e * x.z; v.w += e * x.w;
