@@ -740,7 +740,7 @@ __device__ __forceinline__ void select_row(const TP &a, const DebugView &dbg, in
     const int32_t *par = a.par[l & 1] + row * a.k;
     for (int r = lane; r < rl.m; r += 64) parl[r] = par[r];
     for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<uint32_t *>(flag + i) = 0u;
-    __threadfence_block();
+    sel::wave_fence();
     sel::Cands cd;
     cd.n = n;
     cd.nchild = rl.m * a.b;
@@ -796,9 +796,12 @@ __device__ __forceinline__ void select_row_in(const TP &a, const DebugView &dbg,
     if (n == 0) return;
     float *zr = a.z + row * a.zs;
     const int32_t *par = a.par[l & 1] + row * a.k;
-    for (int r = lane; r < rl.m; r += 64) parl[r] = r == lane ? f.par : par[r];
+    // ranks below 64 come from the prefetch; only wider budgets load the rest here
+    // (a load waited on here would also wait for the next row's prefetch)
+    if (lane < rl.m) parl[lane] = f.par;
+    for (int r = lane + 64; r < rl.m; r += 64) parl[r] = par[r];
     for (int i = 4 * lane; i < n; i += 256) *reinterpret_cast<uint32_t *>(flag + i) = 0u;
-    __threadfence_block();
+    sel::wave_fence();
     sel::Cands cd;
     cd.n = n;
     cd.nchild = rl.m * a.b;
@@ -839,15 +842,18 @@ __global__ __launch_bounds__(256) void tp_select(TP a, DebugView dbg, int l, int
         for (; row < a.rows; row += stride) select_row<KT>(a, dbg, l, row, lane, scratch, outv, kept, parl, flag);
     } else {
         if (row >= a.rows) return;
+        // every row's inputs arrive in nxt and are copied to cur at the top of its
+        // iteration (the one wait for them), so nothing in the selection waits on a
+        // load; the next row's loads are then in flight during the selection
         SelIn<KT> cur, nxt;
-        sel_fetch<KT>(a, l, row, lane, cur);
+        sel_fetch<KT>(a, l, row, lane, nxt);
         for (;;) {
+            cur = nxt;
             const int64_t next = row + stride;
             if (next < a.rows) sel_fetch<KT>(a, l, next, lane, nxt);
             select_row_in<KT>(a, dbg, l, row, lane, cur, scratch, outv, kept, parl, flag);
             if (next >= a.rows) break;
             row = next;
-            cur = nxt;
         }
     }
 }
@@ -1120,13 +1126,13 @@ __global__ __launch_bounds__(256) void tp_attend(TreeView tv, TP a, int32_t NP) 
                 for (int v = 0; v < 4; ++v) zw[(4 * grp + v) * ZS + c] = c < it.onc[v] ? a.scale * acc[v] : -INFINITY;
             }
         }
-        __threadfence_block();
+        sel::wave_fence();      // the tile is this wave's: no wait for its loads in flight
         float w[KC][8];
         #pragma unroll
         for (int kk = 0; kk < KC; ++kk)
             #pragma unroll
             for (int v = 0; v < 8; ++v) w[kk][v] = zw[i16 * ZS + 32 * kk + 8 * grp + v];
-        __threadfence_block();
+        sel::wave_fence();
         pair_softmax<KC>(a, it, 0, lane, w);
         f32x4 acc[D / 16];
         #pragma unroll

@@ -87,6 +87,16 @@ __device__ __forceinline__ uint32_t group_umax(uint32_t v) {
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
+// Orders LDS writes of some lanes of a wave before later reads by other lanes of the
+// same wave.  (Readers in other waves need a workgroup barrier as well.)  A
+// workgroup-scope fence would also wait for every global load the wave has in
+// flight, such as the next row's prefetched logits.
+__device__ __forceinline__ void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Candidates of one level: i < nchild is child (i mod b) of kept parent
 // parents[i / b]; the rest are orphans from node orphan0 on; at the top
 // level (top != 0) candidate i is node i.
@@ -165,7 +175,8 @@ __device__ __noinline__ void select_bisect(const float *z, uint8_t *flag, int32_
 }
 
 // Keep the m largest of z[0..cd.n) (1 <= m <= n): kept[0..m) gets their node ids in
-// ascending candidate order and flag[i] = 1 marks them.  KT >= ceil(n / 64) logits
+// ascending candidate order and flag[i] = 1 marks them (ordered for the calling wave
+// on return; other waves read them after a barrier).  KT >= ceil(n / 64) logits
 // per lane live in registers (KT == 0: bisection over LDS).  Results in out[0..3):
 // level max, m-th and (m+1)-th largest logit (NaN when n == m); visible to the
 // calling wave on return.
@@ -311,9 +322,7 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
             }
             base += __popcll(mask);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_fence();
         rank_survivors(cs, cT, kmax, below, flag, kept, m, cd, parents, lane, out);
         return;
     }
@@ -396,11 +405,11 @@ __device__ __forceinline__ void select_from_keys(const uint32_t (&kk)[KT], const
     static_assert(KT > 0, "register keys");
     if (cd.n <= 64) {
         select_small(kk[0], flag, kept, m, cd, parents, lane, out);
-        __threadfence_block();
+        wave_fence();
         return;
     }
     select_bisect_regs<KT>(kk, flag, kept, m, cd, parents, lane, reinterpret_cast<uint32_t *>(scratch), out);
-    __threadfence_block();
+    wave_fence();
 }
 
 template <int KT>
@@ -409,7 +418,7 @@ __device__ __forceinline__ void select(const float *z, uint8_t *flag, int32_t *k
                                        unsigned char *scratch, float *out) {
     if constexpr (KT == 0) {
         select_bisect(z, flag, kept, m, cd, parents, lane, out);
-        __threadfence_block();
+        wave_fence();
     } else {
         uint32_t kk[KT];
         load_keys<KT>(z, cd.n, lane, kk);
