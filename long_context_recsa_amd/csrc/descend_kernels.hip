@@ -1,17 +1,44 @@
 // Level-wise descent, one query head per row (the RecSA rule: every head selects for
 // itself), for decode and row-wise prefill.  The kernels are in descend_impl.hpp.
+#include <atomic>
+
 #include "descend_impl.hpp"
 
 namespace recsa {
 namespace {
 using namespace descend;
 
+// Compute units of the current device (0 if unknown), queried once per device.
+int device_cus() {
+    constexpr int kDevs = 64;
+    static std::atomic<int> cached[kDevs];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kDevs) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kDevs) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 // Launch shape: 4 waves per row; decode (one context length for all rows) keeps 4
 // ranks per slot in flight, row-wise prefill (many rows) 2, for fewer registers and
-// more rows resident per CU.
+// more rows resident per CU.  A decode of at most one row per CU takes 8 waves per
+// row: each CU holds one row either way, and the row's passes then have twice the
+// loads in flight.  A query keeps its selections whatever batch it is decoded in;
+// its output can differ in the last bits between a small batch (8 waves, 32 slots)
+// and a large one (4 waves, 16 slots), which fold the softmax in other groupings.
 template <typename T, int D>
 hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &dbg, hipStream_t s) {
     if (a.ctx_step != 0) return launch_kt<T, D, 4, 2, 1>(tv, a, dbg, s);
+    if (a.rows <= device_cus()) {
+        // (fp32 rows: 2 ranks per batch, or 8 waves' 256 registers would spill)
+        if constexpr (sizeof(T) == 2) return launch_kt<T, D, 8, 4, 1>(tv, a, dbg, s);
+        else return launch_kt<T, D, 8, 2, 1>(tv, a, dbg, s);
+    }
     return launch_kt<T, D, 4, 4, 1>(tv, a, dbg, s);
 }
 

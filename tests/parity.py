@@ -210,3 +210,14 @@ def check_groups(trees, Q, rows, n_ctx_of, k, base, scale, gpu_out, dbg, n_kv, d
     err, tol, rel = _check_out(got - want, want, dtype)
     return {"max_abs_err": err, "tol": tol, "err_over_rms": rel, "excused_rows": excused,
             "rows": len(rows)}
+
+
+def assert_same_query(out_a, dbg_a, out_b, dbg_b, rows_a, rows_b):
+    """One query decoded in two calls of different batch sizes: the same selections
+    at every level, bit for bit, and the same output up to fp32 summation order (a
+    decode of at most one row per compute unit runs eight waves per row, a larger one
+    four, and the two fold the softmax in different groupings)."""
+    import torch
+    sa, sb = dbg_a["selected"][rows_a], dbg_b["selected"][rows_b]
+    assert torch.equal(sa, sb), "the same query selected differently in two batch sizes"
+    torch.testing.assert_close(out_a, out_b, rtol=1e-5, atol=1e-6)

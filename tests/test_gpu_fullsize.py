@@ -81,9 +81,9 @@ def test_full_2m_needles():
     Q = synth.decode_queries(w, 32)
     layer = _layer_at(w, K, V, W, w.L, w.L)
     out32, dbg = layer.decode(P.to_device(Q, w.dtype), debug=True)
-    out1 = layer.decode(P.to_device(Q[:1], w.dtype))
+    out1, dbg1 = layer.decode(P.to_device(Q[:1], w.dtype), debug=True)
     torch.cuda.synchronize()
-    assert torch.equal(out1[0], out32[0])
+    P.assert_same_query(out1[0], dbg1, out32[0], dbg, slice(0, w.n_q), slice(0, w.n_q))
     pairs = synth.needle_pairs(w)
     sel = dbg["selected"].cpu().numpy()
     reached = 0

@@ -51,9 +51,9 @@ def test_decode_multi_ragged(name, lengths, kw):
     G = w0.n_q // w0.n_kv
     gout = P.to_host(out)
     for i, (w, K, V, W, layer) in enumerate(seqs):
-        single = layer.decode(P.to_device(Q[i:i + 1], w.dtype))
+        single, sdbg = layer.decode(P.to_device(Q[i:i + 1], w.dtype), debug=True)
         torch.cuda.synchronize()
-        assert torch.equal(single[0], out[i]), f"sequence {i}: batch and single decode differ"
+        P.assert_same_query(single[0], sdbg, out[i], dbg, slice(0, w.n_q), slice(i * w.n_q, (i + 1) * w.n_q))
         heads = range(w.n_kv) if w.n_kv <= 2 else [0, w.n_kv - 1]
         for g in heads:
             tree = P.head_tree(K, V, W, g, w, w.L)
@@ -111,9 +111,9 @@ def test_decode_multi_device_table():
     out, dbg = decode_multi(layers, P.to_device(Q, "f32"), debug=True)
     torch.cuda.synchronize()
     for i, (w, K, V, W, layer) in enumerate(seqs):
-        single = layer.decode(P.to_device(Q[i:i + 1], "f32"))
+        single, sdbg = layer.decode(P.to_device(Q[i:i + 1], "f32"), debug=True)
         torch.cuda.synchronize()
-        assert torch.equal(single[0], out[i]), f"sequence {i}: batch and single decode differ"
+        P.assert_same_query(single[0], sdbg, out[i], dbg, slice(0, w.n_q), slice(i * w.n_q, (i + 1) * w.n_q))
     for i in (0, 17, 33):
         w, K, V, W, _ = seqs[i]
         tree = P.head_tree(K, V, W, 0, w, w.L)

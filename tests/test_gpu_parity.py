@@ -218,6 +218,6 @@ def test_full_131k_decode():
     """The 131K-token Qwen3-4B-shaped workload at full size: build, decode B=1 and B=8."""
     w = synth.WORKLOADS["qwen3_4b_131k"]
     layer, tree, out_t, dbg, Q = _decode_case(w, 8, check_tree=True)
-    out1 = layer.decode(P.to_device(Q[:1], w.dtype))
+    out1, dbg1 = layer.decode(P.to_device(Q[:1], w.dtype), debug=True)
     torch.cuda.synchronize()
-    assert torch.equal(out1[0], out_t[0])
+    P.assert_same_query(out1[0], dbg1, out_t[0], dbg, slice(0, w.n_q), slice(0, w.n_q))
