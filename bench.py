@@ -48,6 +48,7 @@ OP_SOURCES = {
                        "select_topk.hpp"],
     "prefill": ["prefill_tiled.hip", "select_topk.hpp"],
     "backward": ["backward_kernels.hip", "prefill_tiled.hip", "select_topk.hpp"],
+    "backward_bf16": ["backward_kernels.hip", "prefill_tiled.hip", "select_topk.hpp"],
 }
 COMMON_SOURCES = ["recsa_internal.hpp", "recsa_api.hip"]
 
@@ -534,6 +535,8 @@ def measure_workload(w, batches, steps, warmup, backward=True):
         v_new = dev_store(np.ascontiguousarray(V[:, w.L:].transpose(1, 0, 2)), w.dtype, dev)
         q_pre = dev_store(synth.prefill_queries(w), w.dtype, dev)
         out_pre = torch.empty((w.prefill_n, w.n_q, w.d), dtype=torch.float32, device=dev)
+    # the same backward with bf16 token gradients (recsa_backward_bf16), where it runs
+    bwd16 = backward and w.dtype == "bf16" and w.b <= 32
     if backward:
         # the output gradient is synthetic; every step writes the same gradient buffers
         d_out = torch.from_numpy(np.random.default_rng(5).standard_normal((Bmax, w.n_q, w.d))
@@ -541,13 +544,18 @@ def measure_workload(w, batches, steps, warmup, backward=True):
         grads = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
                  "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.float32, device=dev),
                  "dw": torch.zeros((w.n_kv, w.d), dtype=torch.float32, device=dev)}
+    if bwd16:
+        grads16 = {"dk": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.bfloat16, device=dev),
+                   "dv": torch.zeros((w.n_kv, Lt, w.d), dtype=torch.bfloat16, device=dev),
+                   "dw": torch.zeros((w.n_kv, w.d), dtype=torch.float32, device=dev)}
     del K, V
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     dense = dense_context(layer, w, q_dec[Bmax])
 
     ops = (["build"] + [f"decode_B{B}" for B in batches] + ["decode_grouped"]
-           + (["backward"] if backward else []) + (["append", "prefill"] if w.prefill_n else []))
+           + (["backward"] if backward else []) + (["backward_bf16"] if bwd16 else [])
+           + (["append", "prefill"] if w.prefill_n else []))
     ev = {o: [] for o in ops}
 
     def step(record):
@@ -563,6 +571,9 @@ def measure_workload(w, batches, steps, warmup, backward=True):
         marks[i].record(); i += 1
         if backward:
             layer.backward(q_dec[Bmax], d_out, grads=grads)
+            marks[i].record(); i += 1
+        if bwd16:
+            layer.backward(q_dec[Bmax], d_out, grads=grads16, grad_dtype="bf16")
             marks[i].record(); i += 1
         if w.prefill_n:
             layer.append(k_new, v_new)
@@ -603,6 +614,10 @@ def measure_workload(w, batches, steps, warmup, backward=True):
         bb = backward_bytes(w, Bmax)
         kern["backward"] = {"bound": "hbm", "bytes": bb, "ms": med["backward"],
                             "achieved": bb / med["backward"] / 1e6, "unit": "GB/s"}
+    if bwd16:
+        bb = backward_bytes(w, Bmax, token_bytes=2)
+        kern["backward_bf16"] = {"bound": "hbm", "bytes": bb, "ms": med["backward_bf16"],
+                                 "achieved": bb / med["backward_bf16"] / 1e6, "unit": "GB/s"}
     if w.prefill_n:
         # the chunk's rows share parents, so the HBM floor is reading every reachable K/V row,
         # tree node and query once and writing the output; the bytes the rows would gather
@@ -654,16 +669,16 @@ def dense_context(layer, w, q, reps=5):
     return float(np.median([a.elapsed_time(b) for a, b in ts]))
 
 
-def backward_bytes(w, B):
+def backward_bytes(w, B, token_bytes=4):
     """Read-once floor of the decode batch's backward: the forward's gathers of every
-    row (keys and values read again), the fp32 token gradients dk, dv of every cached
-    token written once (the tree pass writes them all), and the summaries' fp32
-    gradients written and read once."""
+    row (keys and values read again), the token gradients dk, dv of every cached token
+    written once (the tree pass writes them all; fp32, or bf16 with token_bytes=2), and
+    the summaries' fp32 gradients written and read once."""
     esz = 2 if w.dtype == "bf16" else 4
     kd, vd = row_entries(w.L, w.b, w.k)
     N = level_sizes(w.L, w.b)
     gathers = B * w.n_q * (kd + vd) * w.d * esz
-    tokens = 2 * w.n_kv * w.L * w.d * 4
+    tokens = 2 * w.n_kv * w.L * w.d * token_bytes
     summaries = 2 * 2 * w.n_kv * sum(N[1:]) * w.d * 4
     return gathers + tokens + summaries
 
@@ -733,7 +748,7 @@ def main():
     ms = {o: v["median"] for o, v in head["ms"].items()}
     ms["decode"] = ms[f"decode_B{B}"]
     # the roofline line follows the forward path's dominant call; the backward rides along
-    dom = max((n for n in kern if n != "backward"), key=lambda n: kern[n]["ms"])
+    dom = max((n for n in kern if not n.startswith("backward")), key=lambda n: kern[n]["ms"])
     roof = {"kernel": dom, "bound": kern[dom]["bound"], "achieved": kern[dom]["achieved"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac"],
             "traffic": kern[dom]["traffic"]}

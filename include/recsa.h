@@ -267,6 +267,34 @@ RECSA_API recsa_status recsa_backward(const recsa_params *p, const recsa_tree_de
                             float *d_k, float *d_v, float *d_w, const recsa_debug *dbg, void *ws,
                             void *stream);
 
+/* Workspace bytes recsa_backward_bf16 needs for up to `max_rows` rows: those of the
+ * parent-major backward plus two fp32 staging buffers of
+ * (ceil(max_rows * (budget_k + 1) / 16) + min(max_rows * (budget_k + 1),
+ *  n_kv_heads * (capacity / fanout_b + 1))) * fanout_b * head_dim floats each.
+ * 0 on invalid params or where recsa_backward_bf16 is unsupported. */
+RECSA_API size_t recsa_backward_bf16_workspace_bytes(const recsa_params *p, int64_t max_rows);
+
+/* recsa_backward with the tokens' gradients in bf16 (the cache's storage type), for
+ * training loops that keep the key and value gradients in the cache's precision.
+ * Same operation, rows, arguments and write semantics as recsa_backward, except:
+ *   d_k, d_v [n_kv_heads][capacity][head_dim] bf16, both required, WRITTEN for tokens
+ *     [0, length): each token row is its full fp32 gradient (the summaries' part plus the
+ *     rows' own token entries, summed in fp32) rounded once to bf16, nearest even;
+ *   d_q, d_w: fp32, as recsa_backward computes them.
+ * Each row's own token entries are first summed per (level-1 parent, item of up to 16
+ * rows) into an fp32 staging buffer in ws; the pass over the level-1 nodes then adds a
+ * node's staged sums to its tree part as it writes each token once.  Half the token
+ * gradient bytes of recsa_backward's fp32 output; it pays where the rows keep few
+ * distinct level-1 nodes (decode batches), since the staging grows with the kept pairs.
+ * Supported with bf16 storage, fanout_b <= 32, path other than RECSA_PATH_ROWWISE and at
+ * most one pass of rows (n_q * n_q_heads <= 262144 rounded down to a multiple of
+ * n_q_heads); RECSA_ERR_UNSUPPORTED otherwise.  Always runs
+ * the parent-major path (any row count).  ws: recsa_backward_bf16_workspace_bytes(p,
+ * n_q * n_q_heads) bytes, 256-byte aligned. */
+RECSA_API recsa_status recsa_backward_bf16(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                                 int64_t n_q, int32_t causal, const float *d_out, float *d_q, void *d_k,
+                                 void *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream);
+
 /* Workspace bytes recsa_dense_decode needs for `batch` queries (device
  * memory, 16-byte aligned): per-span partial softmax states and, for bf16
  * storage, a table of 64 x head_dim/2 RoPE rotation increments the call fills.

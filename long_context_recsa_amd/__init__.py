@@ -26,6 +26,7 @@ EXPORTED = (
     "recsa_decode_multi", "recsa_decode_grouped", "recsa_backward_workspace_bytes",
     "recsa_backward", "recsa_dense_workspace_bytes", "recsa_dense_decode",
     "recsa_distill_workspace_bytes", "recsa_distill_step", "recsa_decode_multi_noalloc",
+    "recsa_backward_bf16_workspace_bytes", "recsa_backward_bf16",
 )
 
 
@@ -93,6 +94,8 @@ def load_library():
         "recsa_decode_grouped": (i32, [P, D, v, i32, v, G, v, v]),
         "recsa_backward_workspace_bytes": (ctypes.c_size_t, [P, i64]),
         "recsa_backward": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
+        "recsa_backward_bf16_workspace_bytes": (ctypes.c_size_t, [P, i64]),
+        "recsa_backward_bf16": (i32, [P, D, v, i64, i32, v, v, v, v, v, G, v, v]),
         "recsa_dense_workspace_bytes": (ctypes.c_size_t, [P, i32]),
         "recsa_dense_decode": (i32, [P, D, v, i32, v, v, v]),
         "recsa_distill_workspace_bytes": (ctypes.c_size_t, [P, i32]),
@@ -173,6 +176,17 @@ def recsa_backward(p, desc, q_ptr, n_q, causal, dout_ptr, dq_ptr, dk_ptr, dv_ptr
     _check(load_library().recsa_backward(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q, int(causal),
                                          dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr,
                                          ctypes.byref(dbg) if dbg is not None else None, ws, stream))
+
+
+def recsa_backward_bf16_workspace_bytes(p, max_rows: int) -> int:
+    return load_library().recsa_backward_bf16_workspace_bytes(ctypes.byref(p), max_rows)
+
+
+def recsa_backward_bf16(p, desc, q_ptr, n_q, causal, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr, dbg=None,
+                        ws=None, stream=None) -> None:
+    _check(load_library().recsa_backward_bf16(ctypes.byref(p), ctypes.byref(desc), q_ptr, n_q, int(causal),
+                                              dout_ptr, dq_ptr, dk_ptr, dv_ptr, dw_ptr,
+                                              ctypes.byref(dbg) if dbg is not None else None, ws, stream))
 
 
 def recsa_dense_workspace_bytes(p, batch: int) -> int:

@@ -549,7 +549,9 @@ __global__ __launch_bounds__(256) void bwd_tree(TreeView tv, BwdTreeArgs t) {
 // flight at once, so a node waits on memory once.  Persistent waves keep dw per head:
 // the S waves of head g take its nodes s, s + S, s + 2S, ..., so the nodes read at one
 // time lie close together (a window of S nodes per head) and each wave adds to dw once.
-template <typename T, int D, bool WR>
+// BF (with WR): the token rows are bf16; each adds the staged sums of the rows' own
+// entries (the node's level-0 items) to its tree part before the one rounding.
+template <typename T, int D, bool WR, bool BF>
 __global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) {
     constexpr int NE = D / 16;              // contiguous elements per lane
     constexpr int RIF = 8;                  // rows of a lane group in flight
@@ -595,6 +597,12 @@ __global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) 
         float gk[NE], gv[NE];
         Vec<float, NE>::load(t.gk + ((int64_t)g * tv.node_cap[1] + j) * D + e0, gk);
         if (WR) Vec<float, NE>::load(t.gv + ((int64_t)g * tv.node_cap[1] + j) * D + e0, gv);
+        int32_t st0 = 0, st1 = 0;           // BF: the node's staged items
+        if (BF) {
+            const int32_t *so = t.stage_item + (int64_t)g * t.stage_np + j;
+            st0 = __builtin_amdgcn_readfirstlane(so[0]);
+            st1 = __builtin_amdgcn_readfirstlane(so[1]);
+        }
         const T *xk = static_cast<const T *>(tv.k_cache) + ((int64_t)g * tv.cap + j * b) * D + e0;
         float m = -INFINITY, l = 0.f, Sq = 0.f, r = 0.f, A[NE], B[NE];
         float za[RIF], zq[RIF];             // WR: this group's children's a_c and q_c (one batch)
@@ -662,8 +670,7 @@ __global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) 
             for (int e = 0; e < NE; ++e) dw[e] += t.pool_scale * (B[e] * il - sbar * A[e] * il);
         }
         if (WR) {                           // the group's children: one batch (b <= 4 * RIF)
-            float *dk0 = t.dk + ((int64_t)g * tv.cap + j * b) * D + e0;
-            float *dv0 = t.dv + ((int64_t)g * tv.cap + j * b) * D + e0;
+            const int64_t row0 = ((int64_t)g * tv.cap + j * b) * D + e0;
             float ov[NE];
             #pragma unroll
             for (int e = 0; e < NE; ++e) ov[e] = gv[e] * (1.f / (float)b);
@@ -676,8 +683,26 @@ __global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) 
                     float ok[NE];
                     #pragma unroll
                     for (int e = 0; e < NE; ++e) ok[e] = al * gk[e] + dac * w[e];
-                    Vec<float, NE>::store(dk0 + (int64_t)c * D, ok);
-                    Vec<float, NE>::store(dv0 + (int64_t)c * D, ov);
+                    if (BF) {
+                        float vv[NE];
+                        #pragma unroll
+                        for (int e = 0; e < NE; ++e) vv[e] = ov[e];
+                        for (int32_t it = st0; it < st1; ++it) {
+                            float sk[NE], sv[NE];
+                            Vec<float, NE>::load(t.stage_k + ((int64_t)it * b + c) * D + e0, sk);
+                            Vec<float, NE>::load(t.stage_v + ((int64_t)it * b + c) * D + e0, sv);
+                            #pragma unroll
+                            for (int e = 0; e < NE; ++e) {
+                                ok[e] += sk[e];
+                                vv[e] += sv[e];
+                            }
+                        }
+                        Vec<bf16_t, NE>::store(t.dk16 + row0 + (int64_t)c * D, ok);
+                        Vec<bf16_t, NE>::store(t.dv16 + row0 + (int64_t)c * D, vv);
+                    } else {
+                        Vec<float, NE>::store(t.dk + row0 + (int64_t)c * D, ok);
+                        Vec<float, NE>::store(t.dv + row0 + (int64_t)c * D, ov);
+                    }
                 }
             }
         }
@@ -686,7 +711,7 @@ __global__ __launch_bounds__(256) void bwd_tree_one(TreeView tv, BwdTreeArgs t) 
     }
 }
 
-template <typename T, int D, bool WR>
+template <typename T, int D, bool WR, bool BF>
 hipError_t launch_tree_one_t(const TreeView &tv, const BwdTreeArgs &t, hipStream_t s) {
     const int64_t nodes = (int64_t)t.Hkv * t.nodes;
     if (nodes == 0) return hipSuccess;
@@ -694,12 +719,12 @@ hipError_t launch_tree_one_t(const TreeView &tv, const BwdTreeArgs &t, hipStream
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree_one<T, D, WR>, 256, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)bwd_tree_one<T, D, WR, BF>, 256, 0);
     if (e != hipSuccess) return e;
     const int64_t want = (nodes + 3) / 4;
     const int64_t cap = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t blocks = want < cap ? want : cap;
-    hipLaunchKernelGGL((bwd_tree_one<T, D, WR>), dim3((unsigned)blocks), dim3(256), 0, s, tv, t);
+    hipLaunchKernelGGL((bwd_tree_one<T, D, WR, BF>), dim3((unsigned)blocks), dim3(256), 0, s, tv, t);
     return hipGetLastError();
 }
 
@@ -786,16 +811,22 @@ hipError_t launch_backward_rows(const TreeView &tv, recsa_dtype st, int32_t D, c
 
 hipError_t launch_backward_tree(const TreeView &tv, recsa_dtype st, int32_t D, const BwdTreeArgs &t,
                                 hipStream_t s) {
-    // level 1 in one pass: dw only, or the tokens' gradients written (fanout <= 32)
+    // level 1 in one pass: bf16 token gradients with their staged entries (bf16 storage,
+    // fanout <= 32), dw only, or the tokens' gradients written (fanout <= 32)
+    if (t.level == 1 && t.dk16 != nullptr) {
+        if (st != RECSA_BF16 || t.b > 32 || t.write_children == 0 || t.stage_k == nullptr) return hipErrorInvalidValue;
+        return D == 128 ? launch_tree_one_t<bf16_t, 128, true, true>(tv, t, s)
+                        : launch_tree_one_t<bf16_t, 64, true, true>(tv, t, s);
+    }
     if (t.level == 1 && t.dk == nullptr) {
         if (st == RECSA_BF16)
-            return D == 128 ? launch_tree_one_t<bf16_t, 128, false>(tv, t, s) : launch_tree_one_t<bf16_t, 64, false>(tv, t, s);
-        return D == 128 ? launch_tree_one_t<float, 128, false>(tv, t, s) : launch_tree_one_t<float, 64, false>(tv, t, s);
+            return D == 128 ? launch_tree_one_t<bf16_t, 128, false, false>(tv, t, s) : launch_tree_one_t<bf16_t, 64, false, false>(tv, t, s);
+        return D == 128 ? launch_tree_one_t<float, 128, false, false>(tv, t, s) : launch_tree_one_t<float, 64, false, false>(tv, t, s);
     }
     if (t.level == 1 && t.write_children != 0 && t.dk != nullptr && t.b <= 32) {
         if (st == RECSA_BF16)
-            return D == 128 ? launch_tree_one_t<bf16_t, 128, true>(tv, t, s) : launch_tree_one_t<bf16_t, 64, true>(tv, t, s);
-        return D == 128 ? launch_tree_one_t<float, 128, true>(tv, t, s) : launch_tree_one_t<float, 64, true>(tv, t, s);
+            return D == 128 ? launch_tree_one_t<bf16_t, 128, true, false>(tv, t, s) : launch_tree_one_t<bf16_t, 64, true, false>(tv, t, s);
+        return D == 128 ? launch_tree_one_t<float, 128, true, false>(tv, t, s) : launch_tree_one_t<float, 64, true, false>(tv, t, s);
     }
     if (st == RECSA_BF16) return D == 128 ? launch_tree_t<bf16_t, 128>(tv, t, s) : launch_tree_t<bf16_t, 64>(tv, t, s);
     return D == 128 ? launch_tree_t<float, 128>(tv, t, s) : launch_tree_t<float, 64>(tv, t, s);

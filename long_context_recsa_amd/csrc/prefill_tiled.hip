@@ -103,6 +103,8 @@ struct TB {
     BwdTreeArgs tree;          // the tree pass's arguments common to every level (interleaved runs)
     int32_t dq_slots;          // dq shares to per-pair slots, added per level by tb_dq_add (many
                                // rows); else fp32 atomics straight into dq (few rows)
+    float *stage_k, *stage_v;  // bf16 token gradients: level 0's items store their sums here,
+                               // [items][b][D] fp32, for the tree pass at level 1 to add (NULL: no)
 };
 
 struct RowLevel {
@@ -429,6 +431,7 @@ struct Item {
     int cnt;        // pairs
     int4 pr;        // this lane's pair (L%16): row, rank, query position, children
     int32_t orow[4], orank[4], onc[4];   // pairs 4*grp + v, the D rows of this lane
+    int64_t idx;    // the item's index in the level's item list
 };
 
 template <typename F>
@@ -448,6 +451,7 @@ __device__ __forceinline__ void for_items(const TP &a, int32_t NP, int lane, F &
             pn = a.sorted[next * kTile + i16];
         }
         Item it;
+        it.idx = item;
         const int32_t bkt = __builtin_amdgcn_readfirstlane(rec.x);   // uniform over the wave
         // (the division runs on the vector unit; bring the uniform results back to scalars)
         it.g = __builtin_amdgcn_readfirstlane(bkt / NP);
@@ -1205,14 +1209,17 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
     uint32_t *kmask = reinterpret_cast<uint32_t *>(dZt + 32 * kTile); // [16][4] kept children bits
     const int64_t nexist = a.length / a.pw[l];
     const int32_t b = a.b;
-    const bool grads_here = l > 0 || t.dk != nullptr;
+    // staged: the tokens' gradients go to the item's own rows of the staging buffer,
+    // every child of the parent stored (zeros included), no atomics and nothing read
+    const bool staged = l == 0 && t.stage_k != nullptr;
+    const bool grads_here = l > 0 || t.dk != nullptr || staged;
     for_items(a, NP, lane, [&](const Item &it) {
         // a bucket of one item is the only writer of its parent's children's gradients in
         // this launch: it reads, adds and stores them instead of adding with atomics
         // (~280 G float atomics/s across the chip, which the token level's ~1 G adds per
         // 4096-query chunk would wait on)
         const int64_t bkt = (int64_t)it.g * NP + it.p;
-        const bool excl = grads_here &&
+        const bool excl = grads_here && !staged &&
                           __builtin_amdgcn_readfirstlane(a.itemoff[bkt + 1] - a.itemoff[bkt]) == 1;
         const bf16_t *keys = level_rows(tv, false, l, it.g, D);
         const bf16_t *vals = level_rows(tv, true, l, it.g, D);
@@ -1325,6 +1332,11 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                 // exclusive bucket: this lane's old dV, dK values of the child kAhead steps
                 // ahead are loaded before the current child's arithmetic, to hide their latency
                 auto grad_rows = [&](int c, float *&gk, float *&gv) {
+                    if (staged) {
+                        gk = t.stage_k + (it.idx * b + c) * D;
+                        gv = t.stage_v + (it.idx * b + c) * D;
+                        return;
+                    }
                     gk = l == 0 ? t.dk + ((int64_t)it.g * t.cap + c0 + c) * D
                                 : t.gk[l] + ((int64_t)it.g * t.node_cap[l] + c0 + c) * D;
                     gv = l == 0 ? t.dv + ((int64_t)it.g * t.cap + c0 + c) * D
@@ -1385,11 +1397,11 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                         k2 += dz[pr] * u2[pr];
                     }
                     const float2 cs = crot[c * crot_stride(D) + j];         // (cos, sin) of c theta_j
-                    if (any && grads_here && c0 + c < nexist) {
+                    if ((any || staged) && inb && grads_here && c0 + c < nexist) {
                         float *gk, *gv;
                         grad_rows(c, gk, gv);
                         const float dk1 = k1 * cs.x + k2 * cs.y, dk2 = k2 * cs.x - k1 * cs.y;   // R(-c theta)
-                        if (excl) {
+                        if (excl || staged) {
                             gv[j] = cur[0] + v1;
                             gv[H + j] = cur[1] + v2;
                             gk[j] = cur[2] + dk1;
@@ -1465,6 +1477,32 @@ __global__ __launch_bounds__(256) void tb_dq_add(TP a, float *dq, int l) {
             v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
         }
         *dst = v;
+    }
+}
+
+// Staged bf16 token gradients of tokens [n1 * b, length) of head blockIdx.x, the
+// children of the partial level-1 parent n1 (all tokens when n1 = 0): the sums of
+// the staged items of their bucket (head, parent n1), zeros when no row reads them.
+__global__ __launch_bounds__(256) void tb_stage_tail(const int32_t *itemoff, const float *sk, const float *sv,
+                                                     bf16_t *dk16, bf16_t *dv16, int64_t cap, int32_t b,
+                                                     int32_t D, int32_t NP0, int64_t n1, int64_t length) {
+    const int g = blockIdx.x;
+    const int64_t bkt = (int64_t)g * NP0 + n1;
+    const int32_t i0 = itemoff[bkt], i1 = itemoff[bkt + 1];
+    const int32_t ntok = (int32_t)(length - n1 * b);
+    const int32_t D4 = D / 4;
+    for (int32_t x = threadIdx.x; x < ntok * D4; x += blockDim.x) {
+        const int32_t c = x / D4, e = (x - c * D4) * 4;
+        float k[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int32_t it = i0; it < i1; ++it) {
+            const float4 a = *reinterpret_cast<const float4 *>(sk + ((int64_t)it * b + c) * D + e);
+            const float4 w = *reinterpret_cast<const float4 *>(sv + ((int64_t)it * b + c) * D + e);
+            k[0] += a.x; k[1] += a.y; k[2] += a.z; k[3] += a.w;
+            v[0] += w.x; v[1] += w.y; v[2] += w.z; v[3] += w.w;
+        }
+        const int64_t o = ((int64_t)g * cap + n1 * b + c) * D + e;
+        Vec<bf16_t, 4>::store(dk16 + o, k);
+        Vec<bf16_t, 4>::store(dv16 + o, v);
     }
 }
 
@@ -1767,6 +1805,12 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
         hipLaunchKernelGGL(tb_rowdot, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, t.dout, out,
                            const_cast<float *>(t.rowD), a.rows, D);
     }
+    // bf16 token gradients (staged): level 0's items run before the tree pass at level 1
+    // and leave their sums in the staging buffer, which that pass adds as it writes each
+    // token row once; tokens past the last complete level-1 node get theirs from
+    // tb_stage_tail.  Needs one pass of rows (the tree pass interleaved).
+    const bool staged = tree && t.tree.dk16 != nullptr;
+    if (staged && t.stage_k == nullptr) return hipErrorInvalidValue;
     if (tree && a.top >= 1) {
         const int64_t ntop = a.length / a.pw[a.top];
         if ((e = launch_zero_rows(t.gk[a.top], a.Hkv, t.node_cap[a.top], 0, ntop, D, s)) != hipSuccess) return e;
@@ -1778,25 +1822,52 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
     }
     const DebugView none{};
     const size_t lds = tiled_backward_lds_bytes(D, a.b);
-    for (int l = a.top; l >= 0; --l) {
+    TB t0 = t;                              // level 0's items: to the staging buffer when staged
+    if (staged) {
+        t0.dk = nullptr;
+        t0.dv = nullptr;
+    } else {
+        t0.stage_k = nullptr;
+        t0.stage_v = nullptr;
+    }
+    auto items = [&](int l) -> hipError_t {
         const int32_t NP = (int32_t)(max_ctx / a.pw[l + 1] + 1);
         const int64_t nb = (int64_t)a.Hkv * NP;
         hipLaunchKernelGGL(tb_parents, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, s, a, t.sel, l);
-        if ((e = bucket_level(a, none, l, NP, s)) != hipSuccess) return e;
+        hipError_t r;
+        if ((r = bucket_level(a, none, l, NP, s)) != hipSuccess) return r;
         const int64_t pairs = a.rows * (int64_t)std::min(a.k + 1, (int)NP);
-        const int64_t items = pairs / kTile + nb + 1;
+        const int64_t n_items = pairs / kTile + nb + 1;
         unsigned grid;
-        if ((e = persistent_grid((const void *)tb_item<D, KC>, lds, (unsigned)((items + 3) / 4), grid)) !=
+        if ((r = persistent_grid((const void *)tb_item<D, KC>, lds, (unsigned)((n_items + 3) / 4), grid)) !=
             hipSuccess)
-            return e;
-        hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, t, l, NP);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+            return r;
+        hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, l == 0 ? t0 : t, l, NP);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
         if (t.dq_slots) {
             unsigned dg;
-            if ((e = persistent_grid((const void *)tb_dq_add, 0, (unsigned)((a.rows * (D / 4) + 255) / 256), dg)) !=
+            if ((r = persistent_grid((const void *)tb_dq_add, 0, (unsigned)((a.rows * (D / 4) + 255) / 256), dg)) !=
                 hipSuccess)
-                return e;
+                return r;
             hipLaunchKernelGGL(tb_dq_add, dim3(dg), dim3(256), 0, s, a, t.dq, l);
+        }
+        return hipSuccess;
+    };
+    // the staged tokens past the last complete level-1 node (all tokens when there is no
+    // level above them): the items of their bucket (head g, parent length / b) summed
+    auto stage_tail = [&]() -> hipError_t {
+        const int64_t n1 = a.length / a.b;
+        if (n1 * a.b >= a.length) return hipSuccess;
+        const int32_t NP0 = (int32_t)(max_ctx / a.pw[1] + 1);
+        hipLaunchKernelGGL(tb_stage_tail, dim3((unsigned)a.Hkv), dim3(256), 0, s, a.itemoff, t.stage_k,
+                           t.stage_v, t.tree.dk16, t.tree.dv16, t.cap, a.b, D, NP0, n1, a.length);
+        return hipGetLastError();
+    };
+    for (int l = a.top; l >= 0; --l) {
+        if (staged && l == 0 && a.top >= 1) break;   // level 0 ran before the tree pass at 1
+        if ((e = items(l)) != hipSuccess) return e;
+        if (staged && l == 0) {
+            if ((e = stage_tail()) != hipSuccess) return e;
         }
         if (tree && l >= 1) {
             BwdTreeArgs tt = t.tree;
@@ -1809,6 +1880,16 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
             tt.dk = t.dk;
             tt.dv = t.dv;
             tt.write_children = 1;
+            if (staged && l == 1) {
+                if ((e = items(0)) != hipSuccess) return e;
+                tt.stage_k = t.stage_k;
+                tt.stage_v = t.stage_v;
+                tt.stage_item = a.itemoff;
+                tt.stage_np = (int32_t)(max_ctx / a.pw[1] + 1);
+            } else {
+                tt.dk16 = nullptr;
+                tt.dv16 = nullptr;
+            }
             if ((e = launch_backward_tree(tv, RECSA_BF16, D, tt, s)) != hipSuccess) return e;
             // children past the last complete node of level l have no parent to write them
             const int64_t under = tt.nodes * a.b;
@@ -1818,6 +1899,8 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
                     return e;
                 if ((e = launch_zero_rows(t.gv[l - 1], a.Hkv, t.node_cap[l - 1], under, nc, D, s)) != hipSuccess)
                     return e;
+            } else if (staged) {
+                if ((e = stage_tail()) != hipSuccess) return e;
             } else if (t.dk != nullptr) {
                 if ((e = launch_zero_rows(t.dk, a.Hkv, t.cap, under, a.length, D, s)) != hipSuccess) return e;
                 if ((e = launch_zero_rows(t.dv, a.Hkv, t.cap, under, a.length, D, s)) != hipSuccess) return e;
@@ -1920,10 +2003,21 @@ int64_t set_pass(TP &a, const DescendArgs &da, int64_t r0, int64_t rows, int32_t
 // The backward's own buffers after the forward's plan: out [rows][D] fp32, the
 // selections [rows][n_levels][k], (max, sum) and <dO, out> per row.
 struct BwdPlan {
-    size_t off_out, off_sel, off_ml, off_rowD, total;
+    size_t off_out, off_sel, off_ml, off_rowD, off_stk, off_stv, total;
 };
 
-BwdPlan make_bwd_plan(const Plan &P, int32_t D, int32_t k, int32_t n_levels) {
+// Items of level 0 (the staging buffer's rows of b children): at most one per 16 pairs
+// plus one per non-empty bucket, and there are at most rows * (k + 1) pairs and
+// Hkv * (capacity / b + 1) buckets.
+int64_t stage_items(int64_t rows, int32_t k, int32_t Hkv, int32_t b, int64_t capacity) {
+    const int64_t pairs = rows * (k + 1);
+    const int64_t nb = (int64_t)Hkv * (capacity / b + 1);
+    return (pairs + kTile - 1) / kTile + std::min(pairs, nb);
+}
+
+// stage: bf16 token gradients, with the staging buffers [items][b][D] fp32 for k and v
+BwdPlan make_bwd_plan(const Plan &P, int32_t D, int32_t k, int32_t n_levels, bool stage, int32_t Hkv,
+                      int32_t b, int64_t capacity) {
     BwdPlan B{};
     size_t o = P.total;
     auto put = [&](size_t bytes) { const size_t at = o; o = up256(o + bytes); return at; };
@@ -1931,6 +2025,11 @@ BwdPlan make_bwd_plan(const Plan &P, int32_t D, int32_t k, int32_t n_levels) {
     B.off_sel = put((size_t)P.rows * (n_levels > 0 ? n_levels : 1) * k * 4);
     B.off_ml = put((size_t)P.rows * 8);
     B.off_rowD = put((size_t)P.rows * 4);
+    if (stage) {
+        const size_t bytes = (size_t)stage_items(P.rows, k, Hkv, b, capacity) * b * D * 4;
+        B.off_stk = put(bytes);
+        B.off_stv = put(bytes);
+    }
     B.total = o;
     return B;
 }
@@ -1938,9 +2037,9 @@ BwdPlan make_bwd_plan(const Plan &P, int32_t D, int32_t k, int32_t n_levels) {
 }  // namespace
 
 size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
-                                      int32_t maxc, int64_t capacity, int32_t n_levels) {
+                                      int32_t maxc, int64_t capacity, int32_t n_levels, bool bf16_grads) {
     const Plan P = make_plan(pass_rows(rows, Hq), Hkv, D, b, k, maxc, capacity, n_levels);
-    return make_bwd_plan(P, D, k, n_levels).total;
+    return make_bwd_plan(P, D, k, n_levels, bf16_grads, Hkv, b, capacity).total;
 }
 
 bool tiled_backward_one_pass(int64_t rows, int32_t Hq) { return pass_rows(rows, Hq) >= rows; }
@@ -1951,7 +2050,8 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
     const int64_t per = pass_rows(da.rows, da.Hq);
     if (tree != nullptr && per < da.rows) return hipErrorInvalidValue;   // interleaving needs one pass
     const Plan P = make_plan(per, Hkv, D, da.b, da.k, da.max_cand, capacity, tv.n_levels);
-    const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels);
+    const bool staged = tree != nullptr && tree->dk16 != nullptr;
+    const BwdPlan B = make_bwd_plan(P, D, da.k, tv.n_levels, staged, Hkv, da.b, capacity);
     unsigned char *w = static_cast<unsigned char *>(ws);
     TP a = make_tp(tv, D, da, Hkv, length, P, ws);
     a.rowml = reinterpret_cast<float2 *>(w + B.off_ml);
@@ -1969,6 +2069,10 @@ hipError_t launch_backward_tiled(const TreeView &tv, int32_t D, const DescendArg
     t.rowml = a.rowml;
     t.rowD = reinterpret_cast<const float *>(w + B.off_rowD);
     t.sel = reinterpret_cast<const int32_t *>(w + B.off_sel);
+    if (staged) {
+        t.stage_k = reinterpret_cast<float *>(w + B.off_stk);
+        t.stage_v = reinterpret_cast<float *>(w + B.off_stv);
+    }
     for (int64_t r0 = 0; r0 < da.rows; r0 += per) {
         const int64_t rows = std::min(per, da.rows - r0);
         const int64_t max_ctx = set_pass(a, da, r0, rows, D);

@@ -291,9 +291,36 @@ recsa_status run_descend(const recsa_params *p, const recsa_tree_desc *d, const 
     return RECSA_OK;
 }
 
+// bf16 token gradients: the parent-major backward in one pass of rows, with the tree
+// pass at level 1 in one pass over each node's children (fanout <= 32)
+bool bf16_grads_possible(const recsa_params *p) {
+    return p->path != RECSA_PATH_ROWWISE && tiled_backward_possible(p) && p->fanout_b <= 32;
+}
+
+size_t backward_grad_bytes(const recsa_params *p, const Layout &L) {
+    size_t total = 0;
+    for (int l = 1; l <= L.n_levels; ++l)
+        total += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+    return total;
+}
+
+size_t backward_ws_bytes(const recsa_params *p, int64_t max_rows, bool bf16_grads) {
+    if (check_params(p) != RECSA_OK || max_rows < 0) return 0;
+    if (bf16_grads && !bf16_grads_possible(p)) return 0;
+    const Layout L = make_layout(p);
+    size_t total = backward_grad_bytes(p, L);
+    if (bf16_grads || use_tiled_backward(p, max_rows))
+        total += tiled_backward_workspace_bytes(max_rows, p->n_q_heads, p->n_kv_heads, p->head_dim, p->fanout_b,
+                                                p->budget_k, (int32_t)L.max_cand, p->capacity, L.n_levels,
+                                                bf16_grads);
+    return total;
+}
+
+// d_k, d_v: fp32, or bf16 with bf16_grads
 recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
-                          int64_t n_q, int32_t causal, const float *d_out, float *d_q, float *d_k,
-                          float *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
+                          int64_t n_q, int32_t causal, const float *d_out, float *d_q, void *d_k,
+                          void *d_v, bool bf16_grads, float *d_w, const recsa_debug *dbg, void *ws,
+                          void *stream) {
     recsa_status st = check_params(p);
     if (st != RECSA_OK) return st;
     const Layout L = make_layout(p);
@@ -304,6 +331,10 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         return fail(RECSA_ERR_UNSUPPORTED,
                     "the parent-major backward needs bf16 storage, fanout_b <= %d and its item "
                     "kernel's LDS within a CU's", (int)tiled_max_fanout());
+    if (bf16_grads && !bf16_grads_possible(p))
+        return fail(RECSA_ERR_UNSUPPORTED,
+                    "bf16 token gradients need bf16 storage, fanout_b <= 32, the parent-major path "
+                    "(path not RECSA_PATH_ROWWISE) and its item kernel's LDS within a CU's");
     if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
     if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (causal && n_q > desc->length)
@@ -316,15 +347,21 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     }
     if ((d_k == nullptr) != (d_v == nullptr))
         return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must both be given or both be NULL");
+    if (bf16_grads && d_k == nullptr) return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must be non-NULL");
     if (!aligned(d_k, 16) || !aligned(d_v, 16))
         return fail(RECSA_ERR_INVALID_ARG, "d_k and d_v must be 16-byte aligned");
-    const int64_t rows_all = n_q * p->n_q_heads;
-    const size_t ws_bytes = recsa_backward_workspace_bytes(p, rows_all);
-    if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
-        return fail(RECSA_ERR_INVALID_ARG,
-                    "the backward needs a 256-byte aligned workspace of recsa_backward_workspace_bytes() bytes");
     const int64_t rows = n_q * p->n_q_heads;
     if (rows > 0x7FFFFFFF) return fail(RECSA_ERR_INVALID_ARG, "too many rows in one call");
+    if (bf16_grads && !tiled_backward_one_pass(rows, p->n_q_heads))
+        return fail(RECSA_ERR_UNSUPPORTED, "bf16 token gradients take at most one pass of rows (%lld rows given)",
+                    (long long)rows);
+    const size_t ws_bytes = backward_ws_bytes(p, rows, bf16_grads);
+    if (ws_bytes > 0 && (ws == nullptr || !aligned(ws, 256)))
+        return fail(RECSA_ERR_INVALID_ARG,
+                    bf16_grads ? "the backward needs a 256-byte aligned workspace of "
+                                 "recsa_backward_bf16_workspace_bytes() bytes"
+                               : "the backward needs a 256-byte aligned workspace of "
+                                 "recsa_backward_workspace_bytes() bytes");
     if (backward_rows_lds_bytes((int32_t)L.max_cand, p->budget_k, L.n_levels, p->head_dim) > kMaxLds)
         return fail(RECSA_ERR_UNSUPPORTED, "budget_k and fanout_b need more LDS than a CU has");
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -333,8 +370,8 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     a.q = q;
     a.dout = d_out;
     a.dq = d_q;
-    a.dk = d_k;
-    a.dv = d_v;
+    a.dk = bf16_grads ? nullptr : static_cast<float *>(d_k);
+    a.dv = bf16_grads ? nullptr : static_cast<float *>(d_v);
     char *w = static_cast<char *>(ws);
     for (int l = 1; l <= L.n_levels; ++l) {
         const size_t bytes = align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
@@ -357,9 +394,7 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         dv.kth_gap = dbg->kth_gap;
         dv.n_keys = nullptr;
     }
-    size_t grad_bytes = 0;
-    for (int l = 1; l <= L.n_levels; ++l)
-        grad_bytes += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
+    const size_t grad_bytes = backward_grad_bytes(p, L);
     hipError_t e = launch_fill_zero(d_w, (size_t)p->n_kv_heads * p->head_dim * sizeof(float), s);
     if (e != hipSuccess) return hip_fail(e, "gradient clear");
     // Every gradient is written.  Wherever the order allows, the tree pass writes a
@@ -370,8 +405,8 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     //     tokens' gradients written at level 1; above it, added to what the rows left),
     //     then the rows' token entries (phase 2);
     //   parent-major over several passes of rows: everything cleared, then added to.
-    const bool tiled = use_tiled_backward(p, rows);
-    const bool tokens = d_k != nullptr;
+    const bool tiled = bf16_grads || use_tiled_backward(p, rows);
+    const bool tokens = d_k != nullptr && !bf16_grads;
     const bool interleave = tiled && tiled_backward_one_pass(rows, p->n_q_heads);
     const bool split = tokens && !tiled;
     BwdTreeArgs common{};
@@ -380,13 +415,17 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     common.pool_scale = p->pool_scale;
     common.pool_w = desc->pool_w;
     common.dw = d_w;
+    if (bf16_grads) {
+        common.dk16 = static_cast<bf16_t *>(d_k);
+        common.dv16 = static_cast<bf16_t *>(d_v);
+    }
     if (!interleave) {
         e = launch_fill_zero(ws, grad_bytes, s);
         if (e != hipSuccess) return hip_fail(e, "workspace clear");
     }
     if (tiled && tokens && !interleave) {
-        e = launch_zero_rows(d_k, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
-        if (e == hipSuccess) e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
+        e = launch_zero_rows(a.dk, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
+        if (e == hipSuccess) e = launch_zero_rows(a.dv, p->n_kv_heads, p->capacity, 0, desc->length, p->head_dim, s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
     }
     if (tiled) {
@@ -434,8 +473,8 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
         t.gv = a.gv[l];
         t.gk_child = l >= 2 ? a.gk[l - 1] : nullptr;
         t.gv_child = l >= 2 ? a.gv[l - 1] : nullptr;
-        t.dk = d_k;
-        t.dv = d_v;
+        t.dk = a.dk;
+        t.dv = a.dv;
         t.write_children = split && l == 1 ? 1 : 0;
         e = launch_backward_tree(tv, (recsa_dtype)p->store_dtype, p->head_dim, t, s);
         if (e != hipSuccess) return hip_fail(e, "backward tree launch");
@@ -443,9 +482,9 @@ recsa_status run_backward(const recsa_params *p, const recsa_tree_desc *desc, co
     if (split) {
         // tokens past the last complete level-1 node have no parent to write them
         const int64_t under = desc->length / p->fanout_b * p->fanout_b;
-        e = launch_zero_rows(d_k, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
+        e = launch_zero_rows(a.dk, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
         if (e == hipSuccess)
-            e = launch_zero_rows(d_v, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
+            e = launch_zero_rows(a.dv, p->n_kv_heads, p->capacity, under, desc->length, p->head_dim, s);
         if (e != hipSuccess) return hip_fail(e, "gradient clear");
         // then the rows' own token entries
         a.phase = 2;
@@ -708,21 +747,23 @@ recsa_status recsa_prefill(const recsa_params *p, const recsa_tree_desc *desc, c
 }
 
 size_t recsa_backward_workspace_bytes(const recsa_params *p, int64_t max_rows) {
-    if (check_params(p) != RECSA_OK || max_rows < 0) return 0;
-    const Layout L = make_layout(p);
-    size_t total = 0;
-    for (int l = 1; l <= L.n_levels; ++l)
-        total += 2 * align_up((size_t)p->n_kv_heads * (size_t)L.node_cap[l] * (size_t)p->head_dim * sizeof(float));
-    if (use_tiled_backward(p, max_rows))
-        total += tiled_backward_workspace_bytes(max_rows, p->n_q_heads, p->n_kv_heads, p->head_dim, p->fanout_b,
-                                                p->budget_k, (int32_t)L.max_cand, p->capacity, L.n_levels);
-    return total;
+    return backward_ws_bytes(p, max_rows, false);
 }
 
 recsa_status recsa_backward(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
                             int64_t n_q, int32_t causal, const float *d_out, float *d_q, float *d_k,
                             float *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
-    return run_backward(p, desc, q, n_q, causal, d_out, d_q, d_k, d_v, d_w, dbg, ws, stream);
+    return run_backward(p, desc, q, n_q, causal, d_out, d_q, d_k, d_v, false, d_w, dbg, ws, stream);
+}
+
+size_t recsa_backward_bf16_workspace_bytes(const recsa_params *p, int64_t max_rows) {
+    return backward_ws_bytes(p, max_rows, true);
+}
+
+recsa_status recsa_backward_bf16(const recsa_params *p, const recsa_tree_desc *desc, const void *q,
+                                 int64_t n_q, int32_t causal, const float *d_out, float *d_q, void *d_k,
+                                 void *d_v, float *d_w, const recsa_debug *dbg, void *ws, void *stream) {
+    return run_backward(p, desc, q, n_q, causal, d_out, d_q, d_k, d_v, true, d_w, dbg, ws, stream);
 }
 
 size_t recsa_dense_workspace_bytes(const recsa_params *p, int32_t batch) {
@@ -807,7 +848,7 @@ recsa_status recsa_distill_step(const recsa_params *p, recsa_tree_desc *desc, fl
     hipError_t e = launch_distill_loss(out, teacher, dout, loss, (int64_t)rows * p->head_dim, rows, s);
     if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
     // dloss/dw (written) with the selection fixed; the token gradients are not needed
-    if ((st = run_backward(p, desc, q, batch, 0, dout, dq, nullptr, nullptr, dw, nullptr, bws, stream)) !=
+    if ((st = run_backward(p, desc, q, batch, 0, dout, dq, nullptr, nullptr, false, dw, nullptr, bws, stream)) !=
         RECSA_OK)
         return st;
     e = launch_distill_update(pool_w, velocity, dw, (int64_t)p->n_kv_heads * p->head_dim, lr, momentum, s);

@@ -204,6 +204,14 @@ struct BwdTreeArgs {
                                // to them; children of nodes without gradient get zeros
     float *dw;                 // [Hkv][D] (added to)
     int32_t cache_keys;        // set by the launch: the children's keys stay in LDS between passes
+    // bf16 token gradients (level 1, fanout <= 32; instead of dk, dv): each token row is
+    // written once, its tree part plus the rows' own entries, which level 0's items left
+    // as per-item sums in fp32 (stage_k, stage_v [items][b][D]; the items of the bucket
+    // (head g, level-1 node j) are stage_item[g * stage_np + j] .. [.. + 1] - 1)
+    bf16_t *dk16, *dv16;
+    const float *stage_k, *stage_v;
+    const int32_t *stage_item;
+    int32_t stage_np;
 };
 
 // ---- dense attention (the distillation teacher) ---------------------------------
@@ -237,8 +245,9 @@ size_t backward_rows_lds_bytes(int32_t maxc, int32_t k, int32_t nlev, int32_t D)
 // the pairs bucketed by parent and one item kernel; summary gradients to ba.gk / ba.gv
 // LDS of the parent-major backward's item kernel (per workgroup of four waves).
 size_t tiled_backward_lds_bytes(int32_t D, int32_t b);
+// bf16_grads: with the staging buffers of bf16 token gradients (tree->dk16 set)
 size_t tiled_backward_workspace_bytes(int64_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t b, int32_t k,
-                                      int32_t maxc, int64_t capacity, int32_t n_levels);
+                                      int32_t maxc, int64_t capacity, int32_t n_levels, bool bf16_grads);
 // tree == NULL: every level's items in each pass of rows (the caller clears the
 // gradients and runs the tree pass after); else (one pass of rows only) the tree pass
 // runs between the levels with these common arguments, writing each level's children's

@@ -6,7 +6,8 @@ import ctypes
 
 import torch
 
-from . import (PATHS, RECSA_BF16, recsa_append, recsa_backward, recsa_backward_workspace_bytes,
+from . import (PATHS, RECSA_BF16, recsa_append, recsa_backward, recsa_backward_bf16,
+               recsa_backward_bf16_workspace_bytes, recsa_backward_workspace_bytes,
                recsa_build_tree, recsa_dense_decode, recsa_dense_workspace_bytes, recsa_distill_step,
                recsa_distill_workspace_bytes, recsa_debug, recsa_decode, recsa_decode_grouped, recsa_decode_multi, recsa_decode_multi_noalloc, recsa_max_candidates, recsa_multi_workspace_bytes,
                recsa_num_levels, recsa_params, recsa_prefill, recsa_tree_bytes, recsa_tree_desc,
@@ -127,30 +128,40 @@ class RecsaLayer:
         return (out, d) if debug else out
 
     def backward(self, q: torch.Tensor, dout: torch.Tensor, causal: bool = False, debug: bool = False,
-                 grads: dict | None = None):
+                 grads: dict | None = None, grad_dtype: str = "f32"):
         """Gradients of <dout, out> with the selection held fixed, for the rows of
         decode(q) (causal=False) or prefill(q) (causal=True).  Returns a dict with
-        dq [n][Hq][D] and dk, dv [Hkv][capacity][D], dw [Hkv][D] (fp32); pass
-        `grads` (such a dict) to have dk, dv, dw written into existing tensors (dk, dv
-        rows from the cache's length on are left as they are)."""
+        dq [n][Hq][D] and dk, dv [Hkv][capacity][D], dw [Hkv][D] (fp32; dk and dv in
+        bf16 with grad_dtype="bf16", through recsa_backward_bf16); pass `grads` (such a
+        dict) to have dk, dv, dw written into existing tensors (dk, dv rows from the
+        cache's length on are left as they are)."""
+        if grad_dtype not in ("f32", "bf16"):
+            raise ValueError(f"grad_dtype must be 'f32' or 'bf16', not {grad_dtype!r}")
         n = q.shape[0]
         shape = (n, self.p.n_q_heads, self.p.head_dim)
         self._check_dev(q, shape, self.store)
         self._check_dev(dout, shape, torch.float32)
         Hkv, D, cap = self.p.n_kv_heads, self.p.head_dim, self.p.capacity
+        tdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
         if grads is None:
-            grads = {"dk": torch.zeros((Hkv, cap, D), dtype=torch.float32, device=self.device),
-                     "dv": torch.zeros((Hkv, cap, D), dtype=torch.float32, device=self.device),
+            grads = {"dk": torch.zeros((Hkv, cap, D), dtype=tdt, device=self.device),
+                     "dv": torch.zeros((Hkv, cap, D), dtype=tdt, device=self.device),
                      "dw": torch.zeros((Hkv, D), dtype=torch.float32, device=self.device)}
+        for name in ("dk", "dv"):
+            self._check_dev(grads[name], (Hkv, cap, D), tdt)
+        self._check_dev(grads["dw"], (Hkv, D), torch.float32)
         grads["dq"] = torch.empty(shape, dtype=torch.float32, device=self.device)
-        nbytes = recsa_backward_workspace_bytes(self.p, n * self.p.n_q_heads)
+        rows = n * self.p.n_q_heads
+        sizing = recsa_backward_bf16_workspace_bytes if grad_dtype == "bf16" else recsa_backward_workspace_bytes
+        call = recsa_backward_bf16 if grad_dtype == "bf16" else recsa_backward
+        nbytes = sizing(self.p, rows)
         if nbytes and (self._bws is None or self._bws.numel() < nbytes):
             self._bws = None
             self._bws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        d, dbg = self._debug(n * self.p.n_q_heads, debug)
-        recsa_backward(self.p, self.desc, _ptr(q), n, causal, _ptr(dout), _ptr(grads["dq"]),
-                       _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dw"]), dbg,
-                       _ptr(self._bws) if nbytes else None, self.stream())
+        d, dbg = self._debug(rows, debug)
+        call(self.p, self.desc, _ptr(q), n, causal, _ptr(dout), _ptr(grads["dq"]),
+             _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dw"]), dbg,
+             _ptr(self._bws) if nbytes else None, self.stream())
         return (grads, d) if debug else grads
 
     def dense_decode(self, q: torch.Tensor, out: torch.Tensor | None = None):
