@@ -428,7 +428,8 @@ def run_backward_chunk(args, name, n):
     """Backward of a causal chunk at the end of a workload's cache (training-shaped):
     the last n tokens' queries attend causally over the tree built on the L cached
     tokens; a synthetic output gradient; the selection of the forward held fixed.
-    Step = one recsa_backward (dq, dk, dv, dw written)."""
+    Step = one recsa_backward (dq, dk, dv, dw written), or recsa_backward_bf16 with
+    --grad-dtype bf16."""
     import torch
 
     import long_context_recsa_amd as R
@@ -458,16 +459,17 @@ def run_backward_chunk(args, name, n):
     rng = np.random.default_rng(2024)
     q = dev_store(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32))
     dO = torch.from_numpy(rng.standard_normal((n, w.n_q, w.d)).astype(np.float32)).to(dev)
-    grads = layer.backward(q, dO, causal=True)
+    gd = args.grad_dtype
+    grads = layer.backward(q, dO, causal=True, grad_dtype=gd)
     for _ in range(max(args.warmup - 1, 0)):
-        layer.backward(q, dO, causal=True, grads=grads)
+        layer.backward(q, dO, causal=True, grads=grads, grad_dtype=gd)
     torch.cuda.synchronize()
     evs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        layer.backward(q, dO, causal=True, grads=grads)
+        layer.backward(q, dO, causal=True, grads=grads, grad_dtype=gd)
         b.record()
         evs.append((a, b))
     torch.cuda.synchronize()
@@ -480,7 +482,7 @@ def run_backward_chunk(args, name, n):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "storage": w.dtype, "L": w.L, "n_kv_heads": w.n_kv,
                    "n_q_heads": w.n_q, "head_dim": w.d, "b": w.b, "k": w.k, "chunk": n,
-                   "rows": n * w.n_q, "path": "auto"},
+                   "rows": n * w.n_q, "path": "auto", "token_grad_dtype": gd},
         "ms": {"backward": ms},
     }
     print(json.dumps(res), flush=True)
@@ -699,6 +701,9 @@ def main():
     ap.add_argument("--lr", type=float, default=1000.0, help="distillation learning rate")
     ap.add_argument("--backward-chunk", type=int, default=0, metavar="N",
                     help="time the backward of a causal chunk of N queries at the workload's length")
+    ap.add_argument("--grad-dtype", choices=["f32", "bf16"], default="f32",
+                    help="token gradients of --backward-chunk: fp32 (recsa_backward) or bf16 "
+                         "(recsa_backward_bf16)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()

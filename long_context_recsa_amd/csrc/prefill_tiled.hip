@@ -1192,7 +1192,8 @@ __host__ __device__ constexpr size_t tb_wave_lds() {
     return (size_t)32 * D * 2 + (size_t)2 * 32 * kTile * 4 + (size_t)kTile * 4 * 4;
 }
 
-template <int D, int KC>
+// ST: level 0 with bf16 token gradients (the items' sums go to the staging buffer)
+template <int D, int KC, bool ST>
 __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, int32_t NP) {
     constexpr int H = D / 2, PG = D / 8, KS1 = D / 64;
     constexpr int SUB = 64 / H;                  // children per step of the wave (1 at D = 128, 2 at D = 64)
@@ -1209,9 +1210,9 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
     uint32_t *kmask = reinterpret_cast<uint32_t *>(dZt + 32 * kTile); // [16][4] kept children bits
     const int64_t nexist = a.length / a.pw[l];
     const int32_t b = a.b;
-    // staged: the tokens' gradients go to the item's own rows of the staging buffer,
-    // every child of the parent stored (zeros included), no atomics and nothing read
-    const bool staged = l == 0 && t.stage_k != nullptr;
+    // ST: the tokens' gradients go to the item's own rows of the staging buffer, every
+    // child of the parent stored (zeros included), no atomics and nothing read
+    constexpr bool staged = ST;
     const bool grads_here = l > 0 || t.dk != nullptr || staged;
     for_items(a, NP, lane, [&](const Item &it) {
         // a bucket of one item is the only writer of its parent's children's gradients in
@@ -1397,7 +1398,7 @@ __global__ __launch_bounds__(256) void tb_item(TreeView tv, TP a, TB t, int l, i
                         k2 += dz[pr] * u2[pr];
                     }
                     const float2 cs = crot[c * crot_stride(D) + j];         // (cos, sin) of c theta_j
-                    if ((any || staged) && inb && grads_here && c0 + c < nexist) {
+                    if ((staged ? inb : any) && grads_here && c0 + c < nexist) {
                         float *gk, *gv;
                         grad_rows(c, gk, gv);
                         const float dk1 = k1 * cs.x + k2 * cs.y, dk2 = k2 * cs.x - k1 * cs.y;   // R(-c theta)
@@ -1839,10 +1840,13 @@ hipError_t run_backward_pass(const TreeView &tv, TP a, TB t, float *out, float *
         const int64_t pairs = a.rows * (int64_t)std::min(a.k + 1, (int)NP);
         const int64_t n_items = pairs / kTile + nb + 1;
         unsigned grid;
-        if ((r = persistent_grid((const void *)tb_item<D, KC>, lds, (unsigned)((n_items + 3) / 4), grid)) !=
-            hipSuccess)
-            return r;
-        hipLaunchKernelGGL((tb_item<D, KC>), dim3(grid), dim3(256), lds, s, tv, a, l == 0 ? t0 : t, l, NP);
+        const bool st = staged && l == 0;
+        const void *fn = st ? (const void *)tb_item<D, KC, true> : (const void *)tb_item<D, KC, false>;
+        if ((r = persistent_grid(fn, lds, (unsigned)((n_items + 3) / 4), grid)) != hipSuccess) return r;
+        if (st)
+            hipLaunchKernelGGL((tb_item<D, KC, true>), dim3(grid), dim3(256), lds, s, tv, a, t0, l, NP);
+        else
+            hipLaunchKernelGGL((tb_item<D, KC, false>), dim3(grid), dim3(256), lds, s, tv, a, l == 0 ? t0 : t, l, NP);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         if (t.dq_slots) {
             unsigned dg;
