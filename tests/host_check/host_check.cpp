@@ -105,6 +105,25 @@ static void check_workspace(const recsa_params &p, int64_t chunk) {
     CHECK(recsa_backward_workspace_bytes(&p, rows) >= summaries + partials);
     CHECK(recsa_dense_workspace_bytes(&p, 32) > 0);
     CHECK(recsa_distill_workspace_bytes(&p, 32) >= recsa_backward_workspace_bytes(&p, 32 * p.n_q_heads));
+    // bf16 token gradients (fanout <= 32, not row-wise): the parent-major backward's
+    // workspace plus two staging buffers of ceil(pairs / 16) + min(pairs, buckets) items
+    // of b x d floats, pairs = rows (k + 1) and buckets = Hkv (capacity / b + 1)
+    const size_t ws16 = recsa_backward_bf16_workspace_bytes(&p, rows);
+    if (p.fanout_b <= 32 && p.path != RECSA_PATH_ROWWISE) {
+        const int64_t pairs = rows * (p.budget_k + 1);
+        const int64_t nb = (int64_t)p.n_kv_heads * (p.capacity / p.fanout_b + 1);
+        const size_t items = (size_t)((pairs + 15) / 16 + std::min(pairs, nb));
+        const size_t stage = items * (size_t)p.fanout_b * (size_t)p.head_dim * 4;
+        const size_t base = recsa_backward_workspace_bytes(&p, rows);
+        CHECK(ws16 % 256 == 0);
+        CHECK(ws16 >= base + 2 * stage);
+        CHECK(ws16 <= base + 2 * stage + 2 * 256);
+        CHECK(recsa_backward_bf16_workspace_bytes(&p, rows / 2) <= ws16);
+        CHECK(recsa_backward_bf16_workspace_bytes(&p, 1) > 0);   // any row count runs parent-major
+    } else {
+        CHECK(ws16 == 0);
+    }
+    CHECK(recsa_backward_bf16_workspace_bytes(&rw, rows) == 0);
 }
 
 // Argument checks of every entry point: each call below fails on the host, before any
@@ -149,6 +168,18 @@ static void check_validation(const recsa_params &p) {
     CHECK(recsa_backward(&p, &d, fake, 11, 1, f, f, f, f, f, nullptr, fake, nullptr) == RECSA_ERR_INVALID_ARG);
     CHECK(recsa_backward(&p, &d, fake, 1, 0, f, f, f, nullptr, f, nullptr, fake, nullptr) == RECSA_ERR_INVALID_ARG);
     CHECK(recsa_backward(&p, &d, fake, 1, 0, f, f, f, f, f, nullptr, nullptr, nullptr) == RECSA_ERR_INVALID_ARG);
+    // bf16 token gradients: unsupported storage, fanout or path first; then both token
+    // buffers required, at most one pass of rows, and the workspace
+    const bool bf16_ok = p.store_dtype == RECSA_BF16 && p.fanout_b <= 32 && p.path != RECSA_PATH_ROWWISE;
+    const recsa_status arg = bf16_ok ? RECSA_ERR_INVALID_ARG : RECSA_ERR_UNSUPPORTED;
+    CHECK(recsa_backward_bf16(&p, &d, fake, 1, 0, f, f, nullptr, nullptr, f, nullptr, fake, nullptr) == arg);
+    CHECK(recsa_backward_bf16(&p, &d, fake, 1, 0, f, f, fake, fake, f, nullptr, nullptr, nullptr) == arg);
+    CHECK(recsa_backward_bf16(&p, &d, fake, 300000, 0, f, f, fake, fake, f, nullptr, fake, nullptr) ==
+          RECSA_ERR_UNSUPPORTED);
+    recsa_params rwp = p;
+    rwp.path = RECSA_PATH_ROWWISE;
+    CHECK(recsa_backward_bf16(&rwp, &d, fake, 1, 0, f, f, fake, fake, f, nullptr, fake, nullptr) ==
+          RECSA_ERR_UNSUPPORTED);
     CHECK(recsa_dense_decode(&p, &empty, fake, 1, fake, fake, nullptr) == RECSA_ERR_INVALID_ARG);
     CHECK(recsa_distill_step(&p, &d, f + 1024, fake, 1, f, 0.1f, 0.9f, f, f, fake, nullptr) ==
           RECSA_ERR_INVALID_ARG);
