@@ -2,14 +2,15 @@
  * recsa.h -- C ABI of the RecSA hot path on one AMD Instinct MI355X (gfx950).
  *
  * RecSA ("Recursive Sparse Attention: Million-Token Length Extrapolation at
- * Logarithmic Cost", arXiv 2611.07232, abstract) builds a tree over the KV
- * cache in which every node summarizes its subtree with one key and one
- * mean-pooled value (abstract, sentence on the tree).  The keys come from one
- * pooler per layer shared by all levels (sentence on the pooler).  A query
- * descends the tree, keeping at most k candidates per level; the summaries of
- * the candidates it does not keep share one softmax with the exact tokens it
- * reaches (sentence on selection), and every entry's RoPE position is its
- * index among the candidates of its level (sentence on RoPE).
+ * Logarithmic Cost", arXiv 2611.07232, abstract) puts a tree over the KV
+ * cache; a node stands for its whole subtree through a single key and the
+ * average of the subtree's token values (abstract, sentence on the tree).  One
+ * pooler per layer, the same at every level, makes the keys (sentence on the
+ * pooler).  A query walks down the tree and holds on to no more than k
+ * candidates per level; each candidate it drops joins, through its summary,
+ * the same softmax as the exact tokens it reaches at the bottom (sentence on
+ * selection), and an entry's rotary position is its rank in the candidate list
+ * of its level (sentence on RoPE).
  *
  * Conventions shared by every call
  *  - All tensors are caller-owned device memory.  The library allocates

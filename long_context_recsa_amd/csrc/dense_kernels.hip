@@ -1,6 +1,6 @@
 // Dense causal attention for decode queries, for gfx950: the teacher of the
-// pooler's distillation (RecSA, abstract: the pooler is distilled from dense
-// attention).  out = softmax over tokens t < n of s <rope(q, n), rope(K_t, t)>,
+// pooler's distillation (RecSA, abstract, sentence on the pooler: full attention
+// is the pooler's teacher).  out = softmax over tokens t < n of s <rope(q, n), rope(K_t, t)>,
 // applied to V, with n = the cache's length.
 //
 // Split over the tokens, flash-decoding style: a workgroup takes one KV head, one

@@ -3,11 +3,11 @@
 // instantiated by descend_kernels.hip (one head per row) and descend_grouped_*.hip
 // (a KV group's heads per row, sharing one selection).
 //
-// RecSA, abstract: each level above the tokens keeps at most k candidates;
-// the summaries of the candidates not kept share one softmax with the exact
-// tokens; each entry's RoPE position is its index among its level's
-// candidates.  The query's position at a level is that level's candidate
-// count n.
+// RecSA, abstract (sentences on selection and on RoPE): a level above the tokens
+// keeps no more than k of its candidates; every candidate it drops contributes its
+// summary to the same softmax that the exact tokens reached at the bottom join;
+// the rotary position of an entry is its rank in the candidate list of its level.
+// The query's position at a level is that level's candidate count n.
 //
 // Position split.  Below the top, candidate i of a level is child c of the
 // r-th kept parent (i = r*b + c), or orphan c after the m kept parents'

@@ -1,5 +1,5 @@
-// Pooler distillation from dense attention, for gfx950 (RecSA, abstract: the
-// per-layer pooler is distilled from dense attention).  Two small kernels of one
+// Pooler distillation from dense attention, for gfx950 (RecSA, abstract, sentence
+// on the pooler: each layer's pooler learns from full attention as its teacher).  Two small kernels of one
 // training step; the step's other parts are the library's decode, backward and
 // tree build.
 //   loss = (1 / rows) sum ||out - teacher||^2,  dO = 2 (out - teacher) / rows;

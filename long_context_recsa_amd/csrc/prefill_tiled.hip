@@ -1,9 +1,10 @@
 // Causal prefill, parent-major, on gfx950 (bf16 storage).
 //
-// RecSA, abstract: each level above the tokens keeps at most k candidates;
-// the summaries of the candidates not kept share one softmax with the exact
-// tokens; each entry's RoPE position is its index among its level's
-// candidates (the query sits at the level's candidate count n).
+// RecSA, abstract (sentences on selection and on RoPE): a level above the tokens
+// keeps no more than k of its candidates; every candidate it drops contributes its
+// summary to the same softmax that the exact tokens reached at the bottom join;
+// the rotary position of an entry is its rank in the candidate list of its level
+// (the query sits at the level's candidate count n).
 //
 // A row (one chunk query and one query head) reaches, at level l, the
 // children of its parents: the m nodes it kept at level l+1 (ranks 0..m-1,

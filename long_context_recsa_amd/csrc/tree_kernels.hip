@@ -1,8 +1,9 @@
 // Tree build and append kernels for gfx950.
 //
-// RecSA, abstract: every node of the tree over the KV cache summarizes its
-// subtree with one key and one mean-pooled value; the keys come from one
-// pooler per layer shared by all levels.  The pooler here is attention
+// RecSA, abstract (sentences on the tree and the pooler): a node of the tree
+// over the KV cache stands for its whole subtree through a single key and the
+// average of the subtree's token values; one pooler per layer, the same at every
+// level, makes the keys.  The pooler here is attention
 // pooling with a per-KV-head vector w: alpha_c = softmax_c(pool_scale * w .
 // child_c), key = sum_c alpha_c child_c.
 //

@@ -13,14 +13,15 @@ Source: "Recursive Sparse Attention: Million-Token Length Extrapolation at
 Logarithmic Cost" (arXiv 2611.07232), abstract.  Its sentences are cited
 below by what they say:
 
-* [tree]      the tree over the KV cache; each node summarizes its subtree
-              with one key and one mean-pooled value;
-* [pooler]    the keys come from one pooler per layer, shared by all levels;
-* [selection] each level above the tokens selects at most k candidates; the
-              summaries of unselected candidates share one softmax with the
-              exact tokens;
-* [rope]      each entry's RoPE position is its index among the candidates
-              of its level;
+* [tree]      a tree over the KV cache whose nodes each stand for their whole
+              subtree through a single key and the average of its values;
+* [pooler]    a single pooler per layer, the same at every level, makes the
+              keys;
+* [selection] no more than k candidates survive at each level above the
+              tokens; the dropped ones enter, through their summaries, the
+              same softmax as the exact tokens;
+* [rope]      an entry's rotary position is its rank in its level's
+              candidate list;
 * [cost]      selection cost and entries read are O(log L) per query.
 
 Points the pages leave open are fixed as follows (the pages say nothing that
@@ -227,8 +228,8 @@ def descend(tree: Tree, q: np.ndarray, g: int, n_ctx: int, k: int, base: float,
     and the query at the level's candidate count; keep the min(k, n) best;
     every other candidate becomes a softmax entry with its summary value; the
     kept nodes' children, then the level's orphans, form the next candidates.
-    Level 0: every candidate token is an entry with its exact value.  All
-    entries share one softmax.  `force` maps level -> node ids to select
+    Level 0: every candidate token is an entry with its exact value.  One
+    softmax runs over all the entries.  `force` maps level -> node ids to select
     instead (replay of another selection).
     """
     b = tree.b
