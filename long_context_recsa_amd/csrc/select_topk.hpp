@@ -1,6 +1,6 @@
 // Wave-level selection of the m largest of n fp32 logits for gfx950.
 //
-// RecSA, abstract: each level above the tokens keeps at most k candidates.
+// RecSA, abstract (sentence on selection): no more than k candidates survive a level.
 // Equal logits go to the lower candidate index.
 //
 // On CDNA a wave-wide reduction followed by a read of its result (or an LDS
@@ -211,14 +211,41 @@ __device__ __forceinline__ int count_ge(const uint32_t (&kk)[KT], int nT, uint32
 }
 
 // The ordered keys of candidates lane, lane + 64, ... of z[0..n) (0 past n: valid
-// keys are > 0).
+// keys are > 0).  Every lane reads inside z[0..n) (past n it reads z[n - 1] and drops
+// it), so the KT loads go out together instead of one guarded load at a time.
 template <int KT>
 __device__ __forceinline__ void load_keys(const float *z, int32_t n, int lane, uint32_t (&kk)[KT]) {
+    float v[KT];
     #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int32_t i = lane + 64 * t;
-        kk[t] = (i < n) ? ordered_bits(z[i]) : 0u;
+        v[t] = z[i < n ? i : n - 1];
     }
+    #pragma unroll
+    for (int t = 0; t < KT; ++t) kk[t] = (lane + 64 * t < n) ? ordered_bits(v[t]) : 0u;
+}
+
+// Rank of this lane's key among the keys of lanes [0, c) (c <= 64): the number of them
+// ahead of it, a larger key or an equal key in a lower lane.  Lanes from c on must
+// hold key 0 (below every valid key), so reading up to seven past c changes nothing.
+// Key and lane go into one 64-bit value, key:(63 - lane), so "ahead" is a single
+// unsigned comparison and each lane costs a read, a compare and an add on the vector
+// unit (separate key and index comparisons had chained vector and scalar instructions
+// through the condition masks, about 115 cycles a lane); eight lanes per step keep
+// eight reads in flight.
+__device__ __forceinline__ int rank_among(uint32_t key, int32_t c, int lane) {
+    const uint64_t mine = ((uint64_t)key << 32) | (uint32_t)(63 - lane);
+    int rank = 0;
+    const int32_t c8 = (c + 7) & ~7;
+    for (int32_t j = 0; j < c8; j += 8) {
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j + u);
+            const uint64_t other = ((uint64_t)kj << 32) | (uint32_t)(63 - (j + u));
+            rank += other > mine ? 1 : 0;
+        }
+    }
+    return rank;
 }
 
 // The m largest of c <= 64 survivor keys (every key >= T, the rest are < T), listed
@@ -231,15 +258,13 @@ __device__ __forceinline__ void rank_survivors(const uint32_t *cs, int32_t c, ui
     const bool valid = lane < c;
     const uint32_t key = valid ? cs[lane] : 0u;
     const int32_t idx = valid ? (int32_t)cs[64 + lane] : 0;
-    int rank = 0;
-    for (int j = 0; j < c; ++j) {
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
-        rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
-    }
+    // the node id's parent read goes out before the ranking, which hides it
+    const int32_t nid = node_id(idx, cd, parents);
+    const int rank = rank_among(key, c, lane);
     const bool keep = valid && rank < m;
     const uint64_t km = __ballot(keep);
     if (keep) {
-        kept[__popcll(km & lanes_below(lane))] = node_id(idx, cd, parents);
+        kept[__popcll(km & lanes_below(lane))] = nid;
         flag[idx] = 1;
     }
     const uint64_t rm1 = __ballot(valid && rank == m - 1);
@@ -304,23 +329,26 @@ __device__ __forceinline__ void select_bisect_regs(const uint32_t (&kk)[KT], uin
         cT = count_ge<KT>(kk, nT, Ts);
     }
     if (cT <= 64) {
-        // compact the survivors, in ascending candidate order, into cs
+        // compact the survivors, in ascending candidate order, into cs.  Every register
+        // is visited (those past nT hold 0, below Ts >= 1, and index no candidate), so
+        // the loop is straight-line code: all the ballots first, then the stores.
+        uint64_t mask[KT];
+        #pragma unroll
+        for (int t = 0; t < KT; ++t) mask[t] = __ballot(kk[t] >= Ts);
         int32_t base = 0;
         uint32_t below = 0;
         #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            if (t >= nT) break;
             const int32_t i = lane + 64 * t;
             const bool sv = kk[t] >= Ts;
-            const uint64_t mask = __ballot(sv);
             if (sv) {
-                const int32_t p = base + __popcll(mask & lanes_below(lane));
+                const int32_t p = base + __popcll(mask[t] & lanes_below(lane));
                 cs[p] = kk[t];
                 cs[64 + p] = (uint32_t)i;
             } else if (i < n) {
                 below = max(below, kk[t]);
             }
-            base += __popcll(mask);
+            base += __popcll(mask[t]);
         }
         wave_fence();
         rank_survivors(cs, cT, kmax, below, flag, kept, m, cd, parents, lane, out);
@@ -372,11 +400,7 @@ __device__ __forceinline__ void select_small(uint32_t key, uint8_t *flag, int32_
     const int32_t n = __builtin_amdgcn_readfirstlane(cd.n);
     m = __builtin_amdgcn_readfirstlane(m);
     const bool valid = lane < n;
-    int rank = 0;
-    for (int j = 0; j < n; ++j) {
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
-        rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
-    }
+    const int rank = rank_among(key, n, lane);
     const bool keep = valid && rank < m;
     const uint64_t km = __ballot(keep);
     if (keep) {
