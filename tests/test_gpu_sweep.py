@@ -2,7 +2,8 @@
 context length, head dim, storage, KV heads and group size drawn at random (fixed
 seed), each call of the path checked against the oracle on the same inputs:
 decode, grouped decode, causal prefill (row-wise, and parent-major for bf16
-storage), and the backward (the same two layouts).  The shapes reach what the fixed cases do
+storage), and the backward (the same two layouts, and with bf16 token gradients for bf16
+storage and fanouts up to 32).  The shapes reach what the fixed cases do
 not: fanouts from 2 (deep trees) to 47, budgets from 1 to 9 (levels where every
 candidate is kept), contexts shorter than one node, odd head groupings."""
 import numpy as np
@@ -127,3 +128,18 @@ def test_sweep(c):
                 tol = _tol(ref[key], w.dtype)
                 assert err <= tol, f"backward {path} causal={causal} {key}: {err:.3g} > {tol:.3g}"
             _say("backward", path, "causal" if causal else "decode", "ok")
+            if path == "parent_major" and w.b <= 32:
+                # bf16 token gradients: the same forward (same selections), each token's
+                # gradient rounded once, so within 2^-8 of it beyond the fp32 bar
+                g16, d16 = layer.backward(P.to_device(Q, w.dtype), torch.from_numpy(dO).cuda(), causal=causal,
+                                          debug=True, grad_dtype="bf16")
+                torch.cuda.synchronize()
+                assert np.array_equal(d16["selected"].cpu().numpy(), sel), "bf16-gradient run selected differently"
+                for key in ("dq", "dk", "dv", "dw"):
+                    g_ = g16[key].float().cpu().numpy().astype(np.float64)
+                    g_ = g_ if key in ("dq", "dw") else g_[:, :L]
+                    slack = 2.0 ** -8 * np.abs(ref[key]) if key in ("dk", "dv") else 0.0
+                    over = float((np.abs(g_ - ref[key]) - slack).max())
+                    tol = _tol(ref[key], w.dtype)
+                    assert over <= tol, f"backward bf16 causal={causal} {key}: {over:.3g} > {tol:.3g}"
+                _say("backward bf16 grads", "causal" if causal else "decode", "ok")
