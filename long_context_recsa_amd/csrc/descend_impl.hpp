@@ -96,6 +96,11 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;   // the 16-lane row sum, in the row's lane 15
 }
 
+// Lane 15 of each 16-lane DPP row, to every lane of that row (row_newbcast:15).
+__device__ __forceinline__ float row_bcast15(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x15F, 0xf, 0xf, false));
+}
+
 // A wave-uniform 64-bit value held in scalar registers.
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -242,6 +247,10 @@ __device__ __forceinline__ void fused_pass(
                 }
             }
         }
+        // non-ONLINE: each rank's logits stay in lane 15 of the slot until the batch's
+        // ranks are all scored, then go to LDS under one branch (ranks past the level's
+        // candidates write the pad slot at index maxc, which nothing reads)
+        float zk[ONLINE ? 1 : CB][GS], gk[ONLINE ? 1 : CB];
         #pragma unroll
         for (int t = 0; t < CB; ++t) {
             const int32_t r = B.r0 + t;
@@ -272,33 +281,42 @@ __device__ __forceinline__ void fused_pass(
                 for (int p = 0; p < PP; ++p) dot += ua[p] * ra[p] + ub[p] * rb[p];
                 dot = row_sum16(dot);
                 if constexpr (ONLINE) {
-                    // the logit to all 16 lanes of the slot, then an online softmax step
-                    const float z = scale * __shfl(dot, (threadIdx.x & 63) | 15);
-                    if (i < S.n) {
-                        const float Mn = fmaxf(M[j], z);
-                        const float sc = __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
-                        const float pz = __builtin_amdgcn_exp2f((z - Mn) * kLog2e);
-                        lsum[j] = lsum[j] * sc + pz;
-                        #pragma unroll
-                        for (int p = 0; p < PP; ++p) {
-                            acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
-                            acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
-                        }
-                        M[j] = Mn;
+                    // the logit to all 16 lanes of the slot, then an online softmax step;
+                    // a rank past the level's candidates leaves the state as it is (scale
+                    // 1, weight 0: its value row is row 0, finite)
+                    const float z = scale * row_bcast15(dot);
+                    const bool ok = i < S.n;
+                    const float Mn = ok ? fmaxf(M[j], z) : M[j];
+                    const float sc = ok ? __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e) : 1.f;
+                    const float pz = ok ? __builtin_amdgcn_exp2f((z - Mn) * kLog2e) : 0.f;
+                    lsum[j] = lsum[j] * sc + pz;
+                    #pragma unroll
+                    for (int p = 0; p < PP; ++p) {
+                        acc_a[j][p] = acc_a[j][p] * sc + pz * fa2[p];
+                        acc_b[j][p] = acc_b[j][p] * sc + pz * fb2[p];
                     }
-                } else if (sub == 15 && i < S.n) {
+                    M[j] = Mn;
+                } else {
                     const float z = scale * dot;
-                    zS[j * zstride + i] = z;
+                    zk[t][j] = z;
                     if constexpr (GS > 1) {
                         gsum += z;
-                        smax[j] = fmaxf(smax[j], z);
+                        smax[j] = fmaxf(smax[j], i < S.n ? z : -INFINITY);
                     }
                 }
             }
-            if constexpr (!ONLINE) {
-                if (sub == 15 && i < S.n) {
-                    if constexpr (GS > 1) gS[i] = gsum;
-                    flagS[i] = 0;
+            if constexpr (!ONLINE) gk[t] = gsum;
+        }
+        if constexpr (!ONLINE) {
+            if (sub == 15) {
+                #pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    const int32_t i = (B.r0 + t) * b + c;
+                    const int32_t is = i < S.n ? i : maxc;
+                    #pragma unroll
+                    for (int j = 0; j < GS; ++j) zS[j * zstride + is] = zk[t][j];
+                    if constexpr (GS > 1) gS[is] = gk[t];
+                    flagS[is] = 0;
                 }
             }
         }
@@ -331,14 +349,16 @@ struct Smem {
     // logit rows per buffer: one per head, then (GS > 1) the group score
     static constexpr int NZ = GS == 1 ? 1 : GS + 1;
     // logit rows are padded to a multiple of 4 floats, so every array after them is 16-byte aligned
-    __host__ __device__ static int32_t zstride(int32_t maxc) { return (maxc + 3) & ~3; }
+    // with room for a pad slot at index maxc
+    __host__ __device__ static int32_t zstride(int32_t maxc) { return (maxc + 4) & ~3; }
+    __host__ __device__ static int32_t fstride(int32_t maxc) { return maxc + 4; }
     static size_t bytes(int32_t maxc, int32_t k, int32_t b, int D) {
         const size_t nrank = ((size_t)maxc + b - 1) / b;
         const size_t floats = 2 * NZ * (size_t)zstride(maxc) + GS * nrank * D + (size_t)NW * GS * D +
                               2 * (size_t)NW * GS + (GS > 1 ? 2 * (size_t)NW * GS + (size_t)GS * D : 0) + 4 +
                               kNodeTab;
         return sizeof(float) * floats + sel::kScratchBytes + sizeof(int32_t) * 2 * (size_t)k +
-               2 * (size_t)maxc;
+               2 * (size_t)fstride(maxc);
     }
 };
 
@@ -357,6 +377,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     const int32_t b = a.b;
     const int32_t nrank = (maxc + b - 1) / b;
     const int32_t mz = Smem<NW, GS>::zstride(maxc);
+    const int32_t fs = Smem<NW, GS>::fstride(maxc);
     float *zbuf = reinterpret_cast<float *>(smem);                        // [2][NZ][mz]
     float *U = zbuf + 2 * NZ * mz;                                        // [GS][nrank][D]
     float *red = U + (size_t)GS * nrank * D;                              // [NW][GS][D]
@@ -368,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     int32_t *ntab = reinterpret_cast<int32_t *>(misc + 4);                // [kNodeTab] N_l
     unsigned char *scratch = reinterpret_cast<unsigned char *>(ntab + kNodeTab); // selection scratch
     int32_t *kept = reinterpret_cast<int32_t *>(scratch + sel::kScratchBytes);  // [2][k]
-    uint8_t *flagbuf = reinterpret_cast<uint8_t *>(kept + 2 * a.k);       // [2][maxc]
+    uint8_t *flagbuf = reinterpret_cast<uint8_t *>(kept + 2 * a.k);       // [2][fs]
     // head j's logits and the selection score of buffer `buf`
     auto zrow = [&](int buf, int j) { return zbuf + (size_t)(buf * NZ + j) * mz; };
     auto zsel = [&](int buf) { return zbuf + (size_t)(buf * NZ + (GS == 1 ? 0 : GS)) * mz; };
@@ -550,7 +571,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         __syncthreads();
         if (top_early) {
             const int buf = H & 1;
-            uint8_t *fH = flagbuf + buf * maxc;
+            uint8_t *fH = flagbuf + buf * fs;
             #pragma unroll
             for (int t = 0; t < CT; ++t) {
                 const int32_t c = slot + t * NSLOT;
@@ -593,12 +614,12 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
             // with no level above the tokens, the top candidates are tokens: entries at once
             if (H == 0)
                 fused_pass<T, D, NW, CB, GS, false, true>(none, kept, zbuf, flagbuf, kH, cA, kept, kH,
-                                                          zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
+                                                          zrow(buf, 0), zsel(buf), flagbuf + buf * fs,
                                                           vcache, U, ustride, rope, maxc, mz, a.k, slot,
                                                           sub, a.scale, M, lsum, acc_a, acc_b, smax);
             else
                 fused_pass<T, D, NW, CB, GS, false, false>(none, kept, zbuf, flagbuf, kH, cA, kept, kH,
-                                                           zrow(buf, 0), zsel(buf), flagbuf + buf * maxc,
+                                                           zrow(buf, 0), zsel(buf), flagbuf + buf * fs,
                                                            nullptr, U, ustride, rope, maxc, mz, a.k, slot,
                                                            sub, a.scale, M, lsum, acc_a, acc_b, smax);
             if (H > 0) publish_max(smax, buf);
@@ -612,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     for (int l = H; l >= 1; --l) {
         __syncthreads();
         const int bufA = l & 1, bufS = (l + 1) & 1;
-        uint8_t *flagA = flagbuf + bufA * maxc;
+        uint8_t *flagA = flagbuf + bufA * fs;
         const int32_t mA = a.k < cA.n ? a.k : cA.n;
         const int32_t *parentsA = kept + bufS * a.k;
         int32_t *keptA = kept + bufA * a.k;
@@ -661,12 +682,12 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
         const T *kS = l == 1 ? kcache : lkey(l - 1);
         if (l == 1)
             fused_pass<T, D, NW, CB, GS, true, true>(cA, parentsA, zrow(bufA, 0), flagA, vA, cS, keptA, kS,
-                                                     zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
+                                                     zrow(bufS, 0), zsel(bufS), flagbuf + bufS * fs,
                                                      vcache, U, ustride, rope, maxc, mz, a.k, slot, sub,
                                                      a.scale, M, lsum, acc_a, acc_b, smax);
         else
             fused_pass<T, D, NW, CB, GS, true, false>(cA, parentsA, zrow(bufA, 0), flagA, vA, cS, keptA, kS,
-                                                      zrow(bufS, 0), zsel(bufS), flagbuf + bufS * maxc,
+                                                      zrow(bufS, 0), zsel(bufS), flagbuf + bufS * fs,
                                                       nullptr, U, ustride, rope, maxc, mz, a.k, slot, sub,
                                                       a.scale, M, lsum, acc_a, acc_b, smax);
         if (l > 1) publish_max(smax, bufS);
