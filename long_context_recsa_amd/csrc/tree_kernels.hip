@@ -192,20 +192,29 @@ hipError_t launch_level_d(const TreeView &tv, int32_t Hkv, int32_t b, int32_t le
 }
 
 // ---- scatter of token-major new rows into the head-major cache -------------
-__global__ __launch_bounds__(256) void scatter_kernel(const uint4 *__restrict__ src,
-                                                      uint4 *__restrict__ dst, int64_t n,
-                                                      int32_t Hkv, int32_t row16, int64_t cap16,
-                                                      int64_t at16) {
-    // src: [n][Hkv][row16] 16-byte chunks; dst: [Hkv][cap][row16]
-    const int64_t total = n * Hkv * row16;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t c = i % row16;
-        const int64_t rest = i / row16;
-        const int64_t g = rest % Hkv;
-        const int64_t t = rest / Hkv;
-        dst[g * cap16 + at16 + t * row16 + c] = src[i];
-    }
+// K and V in one launch.  Block (x, g): head g, tokens x * tpb .. x * tpb + tpb - 1 of
+// the chunk (tpb = 256 / row16), one 16-byte piece of a row per thread, so a thread's
+// token and piece come from its index by a shift and a mask (row16 is a power of two).
+__global__ __launch_bounds__(256) void scatter_kernel(const uint4 *__restrict__ k_src,
+                                                      const uint4 *__restrict__ v_src,
+                                                      uint4 *__restrict__ k_dst,
+                                                      uint4 *__restrict__ v_dst, int64_t n,
+                                                      int32_t Hkv, int32_t log_row16,
+                                                      int64_t cap16, int64_t at16) {
+    // src: [n][Hkv][row16] 16-byte pieces; dst: [Hkv][cap][row16]
+    const int32_t row16 = 1 << log_row16;
+    const int32_t tpb = 256 >> log_row16;
+    const int64_t t = (int64_t)blockIdx.x * tpb + (threadIdx.x >> log_row16);
+    if (t >= n) return;
+    const int32_t c = threadIdx.x & (row16 - 1);
+    const int64_t g = blockIdx.y;
+    const int64_t si = (t * Hkv + g) * row16 + c;
+    const int64_t di = g * cap16 + at16 + t * row16 + c;
+    // the new rows are read once: nontemporal
+    const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k_src + si));
+    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v_src + si));
+    *reinterpret_cast<u32x4 *>(k_dst + di) = kv;
+    *reinterpret_cast<u32x4 *>(v_dst + di) = vv;
 }
 
 // ---- RoPE table: (cos, sin) of pos * base^(-2j/D), computed in double --------
@@ -242,18 +251,17 @@ hipError_t launch_scatter(const TreeView &tv, recsa_dtype st, int32_t Hkv, int32
                           const void *k_new, const void *v_new, int64_t at, int64_t n,
                           hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    const int32_t row16 = D * (st == RECSA_BF16 ? 2 : 4) / 16;
-    const int64_t total = n * Hkv * row16;
-    const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+    const int32_t row16 = D * (st == RECSA_BF16 ? 2 : 4) / 16;   // 8, 16 or 32 (D = 64 or 128)
+    int32_t log_row16 = 0;
+    while ((1 << log_row16) < row16) ++log_row16;
+    if ((1 << log_row16) != row16 || row16 > 256 || Hkv > 65535) return hipErrorInvalidValue;
+    const int64_t tpb = 256 / row16;
+    const int64_t bx = (n + tpb - 1) / tpb;
+    if (bx > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t cap16 = tv.cap * row16, at16 = at * row16;
-    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint4 *>(k_new), (uint4 *)tv.k_cache, n, Hkv, row16,
-                       cap16, at16);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint4 *>(v_new), (uint4 *)tv.v_cache, n, Hkv, row16,
-                       cap16, at16);
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)bx, (unsigned)Hkv), dim3(256), 0, s,
+                       static_cast<const uint4 *>(k_new), static_cast<const uint4 *>(v_new),
+                       (uint4 *)tv.k_cache, (uint4 *)tv.v_cache, n, Hkv, log_row16, cap16, at16);
     return hipGetLastError();
 }
 
