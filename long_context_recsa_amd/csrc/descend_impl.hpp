@@ -364,8 +364,10 @@ struct Smem {
 
 // One row is one query and GS query heads of one KV head: GS = 1 (every head selects
 // for itself) or GS = G (the group's heads share one selection per level).
-template <typename T, int D, int NW, int CB, int KT, int GS>
-__global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendArgs a,
+// MINW: waves per SIMD the kernel must leave room for (4 lets two 8-wave rows share a
+// compute unit; the compiler then keeps to 128 registers).
+template <typename T, int D, int NW, int CB, int KT, int GS, int MINW = 1>
+__global__ __launch_bounds__(NW * 64, MINW) void descend_kernel(TreeView tv, DescendArgs a,
                                                           DebugView dbg) {
     constexpr int H2 = D / 2;
     constexpr int PP = D / 32;
@@ -763,30 +765,30 @@ __global__ __launch_bounds__(NW * 64) void descend_kernel(TreeView tv, DescendAr
     if (threadIdx.x == 0 && dbg.n_keys != nullptr) dbg.n_keys[row] = (int32_t)keys_scored;
 }
 
-template <typename T, int D, int NW, int CB, int KT, int GS>
+template <typename T, int D, int NW, int CB, int KT, int GS, int MINW = 1>
 hipError_t launch_descend_t(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
                             hipStream_t s) {
     const size_t smem = Smem<NW, GS>::bytes(a.max_cand, a.k, a.b, D);
     if (smem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)descend_kernel<T, D, NW, CB, KT, GS>,
+        hipError_t e = hipFuncSetAttribute((const void *)descend_kernel<T, D, NW, CB, KT, GS, MINW>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((descend_kernel<T, D, NW, CB, KT, GS>), dim3((unsigned)(a.rows / GS)),
+    hipLaunchKernelGGL((descend_kernel<T, D, NW, CB, KT, GS, MINW>), dim3((unsigned)(a.rows / GS)),
                        dim3(NW * 64), smem, s, tv, a, dbg);
     return hipGetLastError();
 }
 
 // Logits per lane the selection keeps in registers, from the widest level.
-template <typename T, int D, int NW, int CB, int GS>
+template <typename T, int D, int NW, int CB, int GS, int MINW = 1>
 hipError_t launch_kt(const TreeView &tv, const DescendArgs &a, const DebugView &dbg,
                      hipStream_t s) {
     const int32_t n = a.max_cand;
-    if (n <= 64 * 2) return launch_descend_t<T, D, NW, CB, 2, GS>(tv, a, dbg, s);
-    if (n <= 64 * 5) return launch_descend_t<T, D, NW, CB, 5, GS>(tv, a, dbg, s);
-    if (n <= 64 * 9) return launch_descend_t<T, D, NW, CB, 9, GS>(tv, a, dbg, s);
-    if (n <= 64 * 17) return launch_descend_t<T, D, NW, CB, 17, GS>(tv, a, dbg, s);
-    return launch_descend_t<T, D, NW, CB, 0, GS>(tv, a, dbg, s);
+    if (n <= 64 * 2) return launch_descend_t<T, D, NW, CB, 2, GS, MINW>(tv, a, dbg, s);
+    if (n <= 64 * 5) return launch_descend_t<T, D, NW, CB, 5, GS, MINW>(tv, a, dbg, s);
+    if (n <= 64 * 9) return launch_descend_t<T, D, NW, CB, 9, GS, MINW>(tv, a, dbg, s);
+    if (n <= 64 * 17) return launch_descend_t<T, D, NW, CB, 17, GS, MINW>(tv, a, dbg, s);
+    return launch_descend_t<T, D, NW, CB, 0, GS, MINW>(tv, a, dbg, s);
 }
 
 }  // namespace descend
