@@ -24,15 +24,17 @@ int device_cus() {
     return cus;
 }
 
-// Launch shape: 8 waves per row for decode (one context length for all rows).  A
-// decode of at most one row per CU keeps 4 ranks per slot in flight (each CU holds
-// one row either way).  With more rows, bf16 rows take 2 ranks per slot within 128
-// registers, so that two rows share a CU at 4 waves per SIMD: a row's passes are
-// bound by its own instruction stream, and 8 waves give it twice the issue slots of
-// 4 (524K, B = 16: 52.5 -> 49 us).  fp32 rows of more than one per CU keep 4 waves and
-// 4 ranks.  Row-wise prefill (many rows): 4 waves, 2 ranks.  A query keeps its
-// selections whatever batch it is decoded in; its output can differ in the last bits
-// between launch shapes, which fold the softmax in other groupings.
+// Launch shape for decode (one context length for all rows).  At most one row per
+// CU: 8 waves, 4 ranks per slot in flight (each CU holds one row either way).  Up to
+// two rows per CU, bf16: 8 waves and 2 ranks per slot within 128 registers, so that
+// two rows share a CU at 4 waves per SIMD: a row's passes are bound by its own
+// instruction stream, and 8 waves give it twice the issue slots of 4 (524K, B = 16:
+// 52.3 -> 45.6 us).  More rows, bf16: 4 waves and 2 ranks within 128 registers, four
+// rows per CU (2M, B = 32: 213 -> 200 us against two 8-wave rows).  fp32 rows of more
+// than one per CU keep 4 waves and 4 ranks.  Row-wise prefill (many rows): 4 waves, 2
+// ranks.  A query keeps its selections whatever batch it is decoded in; its output
+// can differ in the last bits between launch shapes, which fold the softmax in other
+// groupings.
 template <typename T, int D>
 hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &dbg, hipStream_t s) {
     if (a.ctx_step != 0) return launch_kt<T, D, 4, 2, 1>(tv, a, dbg, s);
@@ -41,7 +43,10 @@ hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &d
         if constexpr (sizeof(T) == 2) return launch_kt<T, D, 8, 4, 1>(tv, a, dbg, s);
         else return launch_kt<T, D, 8, 2, 1>(tv, a, dbg, s);
     }
-    if constexpr (sizeof(T) == 2) return launch_kt<T, D, 8, 2, 1, 4>(tv, a, dbg, s);
+    if constexpr (sizeof(T) == 2) {
+        if (a.rows > 2 * device_cus()) return launch_kt<T, D, 4, 2, 1, 4>(tv, a, dbg, s);
+        return launch_kt<T, D, 8, 2, 1, 4>(tv, a, dbg, s);
+    }
     else return launch_kt<T, D, 4, 4, 1>(tv, a, dbg, s);
 }
 
