@@ -183,13 +183,27 @@ __device__ __forceinline__ void fused_pass(
         float cr[PP], sr[PP];
         Raw<T, PP> va[CB], vb[CB], ka[CB], kb[CB], sa[CB], sb[CB];
     };
-    const int32_t nc = slot < b ? (b - slot + NSLOT - 1) / NSLOT : 0;
-    const int32_t nrb = (R + CB - 1) / CB;
+    // 12 waves (48 slots, not a multiple of the fanout): the (child offset, rank
+    // group) pairs form one flat sequence f = c + b * g, and slot s takes f = s,
+    // s + NSLOT, ... (ci counts the slot's batches; nrb is 1)
+    constexpr bool kFlat = NW == 12;
+    const int32_t ngroups = (R + CB - 1) / CB;
+    const int32_t nflat = b * ngroups;
+    const int32_t nc = kFlat ? (slot < nflat ? (nflat - slot + NSLOT - 1) / NSLOT : 0)
+                             : (slot < b ? (b - slot + NSLOT - 1) / NSLOT : 0);
+    const int32_t nrb = kFlat ? 1 : ngroups;
     const int32_t NB = nc * nrb;
     auto issue = [&](Batch &B, int32_t ci, int32_t ri, bool live) __attribute__((always_inline)) {
         B.live = live;
-        B.c = live ? slot + ci * NSLOT : 0;
-        B.r0 = live ? ri * CB : 0;
+        if constexpr (kFlat) {
+            const uint32_t f = (uint32_t)(slot + ci * NSLOT);
+            const int32_t g = (int32_t)__umulhi(f, S.bmul);
+            B.c = live ? (int32_t)f - g * b : 0;
+            B.r0 = live ? g * CB : 0;
+        } else {
+            B.c = live ? slot + ci * NSLOT : 0;
+            B.r0 = live ? ri * CB : 0;
+        }
         const int32_t c = B.c;
         load_cs<PP>(rope + (int64_t)c * H2 + j0, B.cr, B.sr);
         uint32_t offA[CB], offS[CB];

@@ -56,7 +56,7 @@ size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D, int32_t 
     switch (gs) {
         case 1: return Smem<8, 1>::bytes(maxc, k, b, D);
         case 2: return Smem<8, 2>::bytes(maxc, k, b, D);
-        case 4: return Smem<8, 4>::bytes(maxc, k, b, D);
+        case 4: return Smem<12, 4>::bytes(maxc, k, b, D);
         case 8: return Smem<8, 8>::bytes(maxc, k, b, D);
         default: return ~(size_t)0;
     }
