@@ -25,7 +25,10 @@ int device_cus() {
 }
 
 // Launch shape for decode (one context length for all rows).  At most one row per
-// CU: 8 waves, 4 ranks per slot in flight (each CU holds one row either way).  Up to
+// CU: bf16 rows take 12 waves and 2 ranks per slot within 168 registers (the slots
+// walk a flat sequence of (child offset, rank group) pairs; 131K, B = 8: 33.5 -> 29.9
+// us, 2M, B = 1: 68.5 -> 62.1 us against 8 waves and 4 ranks), fp32 rows 8 waves and
+// 2 ranks.  Up to
 // two rows per CU, bf16: 8 waves and 2 ranks per slot within 128 registers, so that
 // two rows share a CU at 4 waves per SIMD: a row's passes are bound by its own
 // instruction stream, and 8 waves give it twice the issue slots of 4 (524K, B = 16:
@@ -40,7 +43,7 @@ hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &d
     if (a.ctx_step != 0) return launch_kt<T, D, 4, 2, 1>(tv, a, dbg, s);
     if (a.rows <= device_cus()) {
         // (fp32 rows: 2 ranks per batch, or 8 waves' 256 registers would spill)
-        if constexpr (sizeof(T) == 2) return launch_kt<T, D, 8, 4, 1>(tv, a, dbg, s);
+        if constexpr (sizeof(T) == 2) return launch_kt<T, D, 12, 2, 1, 3>(tv, a, dbg, s);
         else return launch_kt<T, D, 8, 2, 1>(tv, a, dbg, s);
     }
     if constexpr (sizeof(T) == 2) {
@@ -54,7 +57,7 @@ hipError_t dispatch(const TreeView &tv, const DescendArgs &a, const DebugView &d
 
 size_t descend_lds_bytes(int32_t maxc, int32_t k, int32_t b, int32_t D, int32_t gs) {
     switch (gs) {
-        case 1: return Smem<8, 1>::bytes(maxc, k, b, D);
+        case 1: return Smem<12, 1>::bytes(maxc, k, b, D);
         case 2: return Smem<8, 2>::bytes(maxc, k, b, D);
         case 4: return Smem<12, 4>::bytes(maxc, k, b, D);
         case 8: return Smem<8, 8>::bytes(maxc, k, b, D);
